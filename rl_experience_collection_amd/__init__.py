@@ -1,0 +1,262 @@
+"""Python binding of librollout.so: fused PPO experience collection on MI355X.
+
+Argument marshalling only.  Every step of the collection runs in the HIP
+kernels behind the C ABI of include/rollout.h; PyTorch supplies device
+memory and the stream.  There is no CPU path: if the library is missing or
+fails to load, importing the functions raises.
+
+The functions carry the C names:
+    rollout_config_default, rollout_create, rollout_set_weights,
+    rollout_collect, gae_scan, rollout_destroy, rollout_last_error
+plus two helpers, `alloc_outputs` and the `Collector` convenience class.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "librollout.so")
+
+ROLLOUT_OK, ROLLOUT_EINVAL, ROLLOUT_ENOMEM, ROLLOUT_EHIP, ROLLOUT_ENOTIMPL = 0, -1, -2, -3, -4
+ROLLOUT_FP32, ROLLOUT_BF16 = 0, 1
+STATE_DIM, N_ACTIONS, N_FEATURES = 54, 45, 51
+EXPORTED = ("rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
+            "gae_scan", "rollout_destroy", "rollout_last_error")
+
+
+class RolloutConfig(C.Structure):
+    _fields_ = [
+        ("n_episodes", C.c_int32), ("n_steps", C.c_int32),
+        ("n_features", C.c_int32), ("state_dim", C.c_int32), ("n_actions", C.c_int32),
+        ("actor_dims", C.c_int32 * 4), ("critic_dims", C.c_int32 * 7), ("cur_dims", C.c_int32 * 3),
+        ("precision", C.c_int32),
+        ("gamma", C.c_float), ("lam", C.c_float),
+        ("profit_take", C.c_float), ("stop_loss", C.c_float), ("max_hold", C.c_int32),
+        ("div_window", C.c_int32), ("div_threshold", C.c_float), ("div_penalty", C.c_float),
+        ("curiosity_coef", C.c_float), ("risk_coef", C.c_float), ("spread", C.c_float),
+        ("barrier_scale", C.c_float),
+        ("exposure", C.c_float * 5), ("cost", C.c_float * 3), ("urgency_mult", C.c_float),
+    ]
+
+
+class RolloutOutputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "states", "actions", "log_probs", "values", "rewards", "dones", "barrier",
+        "advantages", "returns", "logits", "counters")]
+
+
+class RolloutError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load librollout.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
+                          "(or python rl_experience_collection_amd/build.py)")
+    L = C.CDLL(path)
+    vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+    L.rollout_config_default.argtypes = [C.POINTER(RolloutConfig), i32, i32]
+    L.rollout_create.argtypes = [C.POINTER(RolloutConfig), C.POINTER(vp), C.POINTER(vp),
+                                 C.POINTER(vp), vp, vp, i64, vp, C.POINTER(vp)]
+    L.rollout_set_weights.argtypes = [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp]
+    L.rollout_collect.argtypes = [vp, vp, C.c_uint64, C.POINTER(RolloutOutputs), vp]
+    L.gae_scan.argtypes = [vp, vp, vp, vp, i32, i32, C.c_float, C.c_float, vp, vp, vp]
+    L.rollout_destroy.argtypes = [vp]
+    L.rollout_destroy.restype = None
+    L.rollout_last_error.argtypes = []
+    L.rollout_last_error.restype = C.c_char_p
+    for name in ("rollout_config_default", "rollout_create", "rollout_set_weights",
+                 "rollout_collect", "gae_scan"):
+        getattr(L, name).restype = C.c_int
+    _lib = L
+    return L
+
+
+def rollout_last_error() -> str:
+    return load_library().rollout_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != ROLLOUT_OK:
+        raise RolloutError(rc, rollout_last_error())
+
+
+# ----------------------------------------------------------------- marshalling
+def _stream(stream):
+    import torch
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, dtype, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return C.c_void_p(t.data_ptr())
+
+
+def _ptr_array(tensors, shapes, name):
+    import torch
+    if len(tensors) != len(shapes):
+        raise ValueError(f"{name}: expected {len(shapes)} tensors, got {len(tensors)}")
+    arr = (C.c_void_p * len(tensors))()
+    for i, (t, s) in enumerate(zip(tensors, shapes)):
+        arr[i] = _dev_ptr(t, torch.float32, s, f"{name}[{i}]").value
+    return arr
+
+
+ACTOR_SHAPES = [(128, 54), (128,), (64, 128), (64,), (45, 64), (45,)]
+CRITIC_SHAPES = [(512, 54), (512,), (384, 512), (384,), (256, 384), (256,), (128, 256), (128,),
+                 (64, 128), (64,), (1, 64), (1,)]
+CURIOSITY_SHAPES = [(128, 99), (128,), (51, 128), (51,)]
+
+
+def rollout_config_default(n_episodes: int, n_steps: int, settings: dict | None = None,
+                           precision: int = ROLLOUT_FP32) -> RolloutConfig:
+    cfg = RolloutConfig()
+    _check(load_library().rollout_config_default(C.byref(cfg), n_episodes, n_steps))
+    cfg.precision = precision
+    for k, v in (settings or {}).items():
+        if k in ("exposure", "cost"):
+            setattr(cfg, k, (C.c_float * len(v))(*v))
+        elif k == "lambda":
+            cfg.lam = v
+        else:
+            setattr(cfg, k, v)
+    return cfg
+
+
+def rollout_create(cfg: RolloutConfig, actor, critic, curiosity, features, prices, stream=None):
+    """Returns an opaque handle (int).  The market tensors are borrowed."""
+    import torch
+    a = _ptr_array(actor, ACTOR_SHAPES, "actor")
+    c = _ptr_array(critic, CRITIC_SHAPES, "critic")
+    u = _ptr_array(curiosity, CURIOSITY_SHAPES, "curiosity")
+    if features.dim() != 2 or features.shape[1] != N_FEATURES:
+        raise ValueError("features must be [n_bars, 51]")
+    f = _dev_ptr(features, torch.float32, name="features")
+    p = _dev_ptr(prices, torch.float32, (features.shape[0],), "prices")
+    h = C.c_void_p()
+    _check(load_library().rollout_create(C.byref(cfg), a, c, u, f, p, features.shape[0],
+                                         _stream(stream), C.byref(h)))
+    return h.value
+
+
+def rollout_set_weights(handle: int, actor, critic, curiosity, stream=None):
+    a = _ptr_array(actor, ACTOR_SHAPES, "actor")
+    c = _ptr_array(critic, CRITIC_SHAPES, "critic")
+    u = _ptr_array(curiosity, CURIOSITY_SHAPES, "curiosity")
+    _check(load_library().rollout_set_weights(C.c_void_p(handle), a, c, u, _stream(stream)))
+
+
+def alloc_outputs(N: int, L: int, device="cuda", logits: bool = False, counters: bool = True):
+    import torch
+    f32 = dict(dtype=torch.float32, device=device)
+    out = dict(
+        states=torch.empty((L, N, STATE_DIM), **f32),
+        actions=torch.empty((L, N), dtype=torch.int32, device=device),
+        log_probs=torch.empty((L, N), **f32),
+        values=torch.empty((L, N), **f32),
+        rewards=torch.empty((L, N), **f32),
+        dones=torch.empty((L, N), dtype=torch.uint8, device=device),
+        barrier=torch.empty((L, N), dtype=torch.uint8, device=device),
+        advantages=torch.empty((L, N), **f32),
+        returns=torch.empty((L, N), **f32),
+        logits=torch.empty((L, N, N_ACTIONS), **f32) if logits else None,
+        counters=torch.zeros(2, dtype=torch.int32, device=device) if counters else None,
+    )
+    return out
+
+
+def rollout_collect(handle: int, episode_starts, seed: int, outputs: dict, stream=None):
+    import torch
+    L, N = outputs["actions"].shape
+    o = RolloutOutputs()
+    o.states = _dev_ptr(outputs["states"], torch.float32, (L, N, STATE_DIM), "states")
+    o.actions = _dev_ptr(outputs["actions"], torch.int32, (L, N), "actions")
+    o.log_probs = _dev_ptr(outputs["log_probs"], torch.float32, (L, N), "log_probs")
+    o.values = _dev_ptr(outputs["values"], torch.float32, (L, N), "values")
+    o.rewards = _dev_ptr(outputs["rewards"], torch.float32, (L, N), "rewards")
+    o.dones = _dev_ptr(outputs["dones"], torch.uint8, (L, N), "dones")
+    o.barrier = _dev_ptr(outputs["barrier"], torch.uint8, (L, N), "barrier")
+    o.advantages = _dev_ptr(outputs["advantages"], torch.float32, (L, N), "advantages")
+    o.returns = _dev_ptr(outputs["returns"], torch.float32, (L, N), "returns")
+    o.logits = _dev_ptr(outputs.get("logits"), torch.float32, (L, N, N_ACTIONS), "logits")
+    o.counters = _dev_ptr(outputs.get("counters"), torch.int32, (2,), "counters")
+    s = _dev_ptr(episode_starts, torch.int32, (N,), "episode_starts")
+    _check(load_library().rollout_collect(C.c_void_p(handle), s, C.c_uint64(seed), C.byref(o),
+                                          _stream(stream)))
+
+
+def gae_scan(rewards, values, dones, last_values, gamma: float, lam: float, advantages, returns,
+             stream=None):
+    import torch
+    L, N = rewards.shape
+    _check(load_library().gae_scan(
+        _dev_ptr(rewards, torch.float32, (L, N), "rewards"),
+        _dev_ptr(values, torch.float32, (L, N), "values"),
+        _dev_ptr(dones, torch.uint8, (L, N), "dones"),
+        _dev_ptr(last_values, torch.float32, (N,), "last_values"),
+        L, N, gamma, lam,
+        _dev_ptr(advantages, torch.float32, (L, N), "advantages"),
+        _dev_ptr(returns, torch.float32, (L, N), "returns"),
+        _stream(stream)))
+
+
+def rollout_destroy(handle: int):
+    if handle:
+        load_library().rollout_destroy(C.c_void_p(handle))
+
+
+class Collector:
+    """Owns one handle; weights as lists of [out, in] fp32 device tensors."""
+
+    def __init__(self, n_episodes: int, n_steps: int, weights: dict, features, prices,
+                 settings: dict | None = None, precision: int = ROLLOUT_FP32, stream=None):
+        self.N, self.L = n_episodes, n_steps
+        self.cfg = rollout_config_default(n_episodes, n_steps, settings, precision)
+        self.features, self.prices = features, prices  # borrowed by the library
+        self.handle = rollout_create(self.cfg, weights["actor"], weights["critic"],
+                                     weights["curiosity"], features, prices, stream)
+
+    def set_weights(self, weights: dict, stream=None):
+        rollout_set_weights(self.handle, weights["actor"], weights["critic"],
+                            weights["curiosity"], stream)
+
+    def collect(self, episode_starts, seed: int, outputs: dict | None = None, logits=False,
+                stream=None) -> dict:
+        if outputs is None:
+            outputs = alloc_outputs(self.N, self.L, episode_starts.device, logits=logits)
+        rollout_collect(self.handle, episode_starts, seed, outputs, stream)
+        return outputs
+
+    def close(self):
+        if self.handle:
+            rollout_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

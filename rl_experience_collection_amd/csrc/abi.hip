@@ -1,0 +1,396 @@
+// C ABI of librollout.so (declared in include/rollout.h): argument checks,
+// device memory of collectors, weight packing and the launch sequence
+//   actor rollout -> batched critic/curiosity/reward -> GAE scan
+// on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/rollout.h"
+#include "collect.hpp"
+#include "gae.hpp"
+#include "pack.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ROLLOUT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define RL_HIP(call, what)                        \
+  do {                                            \
+    hipError_t _e = (call);                       \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+// Carry scratch of the GAE scan (flags at a fixed offset, epoch-tagged).
+struct GaeScratch {
+  char* mem = nullptr;
+  size_t bytes = 0;
+  int32_t nk = 0, nc = 0, n = 0;
+  uint32_t ticket_base = 0;
+  uint32_t epoch = 0;
+};
+
+int gae_prepare(GaeScratch& s, const rl::GaeShape& shape, int32_t N, hipStream_t st,
+                rl::GaeScratchView* view) {
+  const size_t need = rl::gae_scratch_bytes(shape.nk, shape.nc, N);
+  bool relayout = (shape.nk != s.nk || shape.nc != s.nc || N != s.n);
+  if (s.bytes < need) {
+    if (s.mem) {
+      hipError_t e = hipFree(s.mem);
+      s.mem = nullptr;
+      s.bytes = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFree(gae scratch)");
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, need) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ROLLOUT_ENOMEM, "gae scratch: cannot allocate %zu bytes", need);
+    }
+    s.mem = static_cast<char*>(p);
+    s.bytes = need;
+    RL_HIP(hipMemsetAsync(s.mem, 0, 256, st), "hipMemsetAsync(gae ticket)");
+    s.ticket_base = 0;
+    relayout = true;
+  }
+  const size_t flag_bytes = ((size_t)shape.nk * shape.nc * 4 + 255) / 256 * 256;
+  const size_t agg_bytes = ((size_t)shape.nk * N * 8 + 255) / 256 * 256;
+  if (relayout || s.epoch >= (1u << 29)) {
+    RL_HIP(hipMemsetAsync(s.mem + 256, 0, flag_bytes, st), "hipMemsetAsync(gae flags)");
+    s.epoch = 0;
+    s.nk = shape.nk;
+    s.nc = shape.nc;
+    s.n = N;
+  }
+  s.epoch += 1;
+  view->ticket = reinterpret_cast<uint32_t*>(s.mem);
+  view->error = reinterpret_cast<uint32_t*>(s.mem + 4);
+  view->flags = reinterpret_cast<uint32_t*>(s.mem + 256);
+  view->agg = reinterpret_cast<uint64_t*>(s.mem + 256 + flag_bytes);
+  view->incl = reinterpret_cast<float*>(s.mem + 256 + flag_bytes + agg_bytes);
+  view->ticket_base = s.ticket_base;
+  view->epoch = s.epoch;
+  return ROLLOUT_OK;
+}
+
+int gae_run(GaeScratch& s, const rl::GaeArgs& a, hipStream_t st) {
+  if (a.L == 0 || a.N == 0) return ROLLOUT_OK;
+  auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) % m) == 0; };
+  const bool a16 = al(a.rewards, 16) && al(a.values, 16) && al(a.advantages, 16) &&
+                   al(a.returns, 16) && al(a.dones, 4);
+  const bool a8 = al(a.rewards, 8) && al(a.values, 8) && al(a.advantages, 8) && al(a.returns, 8) &&
+                  al(a.dones, 2);
+  const rl::GaeShape shape = rl::gae_shape(a.L, a.N, a16, a8);
+  if (shape.tiles() >= (int64_t)1 << 31) return fail(ROLLOUT_EINVAL, "gae_scan: too many tiles");
+  rl::GaeScratchView view;
+  int rc = gae_prepare(s, shape, a.N, st, &view);
+  if (rc) return rc;
+  hipError_t e = rl::gae_launch(a, shape, view, st);
+  if (e != hipSuccess) return hip_fail(e, "gae_scan launch");
+  s.ticket_base += (uint32_t)shape.tiles();
+  return ROLLOUT_OK;
+}
+
+// Reserve the scratch for the largest tile grid an (L, N) scan can use.
+int gae_reserve(GaeScratch& s, int32_t L, int32_t N, hipStream_t st) {
+  const rl::GaeShape shape = rl::gae_shape(L, N, false, false);
+  rl::GaeScratchView view;
+  const int rc = gae_prepare(s, shape, N, st, &view);
+  s.epoch -= 1;  // nothing was launched with this epoch
+  return rc;
+}
+
+std::mutex g_gae_mu;
+std::map<std::pair<int, hipStream_t>, GaeScratch>& gae_cache() {
+  static auto* m = new std::map<std::pair<int, hipStream_t>, GaeScratch>();
+  return *m;
+}
+
+const int32_t kActorDims[4] = {54, 128, 64, 45};
+const int32_t kCriticDims[7] = {54, 512, 384, 256, 128, 64, 1};
+const int32_t kCurDims[3] = {99, 128, 51};
+
+rl::EnvParams env_params(const rollout_config& c) {
+  rl::EnvParams p;
+  p.ex0 = c.exposure[0]; p.ex1 = c.exposure[1]; p.ex2 = c.exposure[2];
+  p.ex3 = c.exposure[3]; p.ex4 = c.exposure[4];
+  p.cost0 = c.cost[0]; p.cost1 = c.cost[1]; p.cost2 = c.cost[2];
+  p.urgency_mult = c.urgency_mult;
+  // fp32 threshold multipliers; the barrier compares P[bar+1] with entry * these
+  p.up_pt = 1.0f + c.profit_take;
+  p.dn_sl = 1.0f - c.stop_loss;
+  p.dn_pt = 1.0f - c.profit_take;
+  p.up_sl = 1.0f + c.stop_loss;
+  p.max_hold = c.max_hold;
+  p.div_window = c.div_window;
+  p.div_threshold = c.div_threshold;
+  p.div_penalty = c.div_penalty;
+  p.barrier_scale = c.barrier_scale;
+  p.spread = c.spread;
+  p.risk_coef = c.risk_coef;
+  p.curiosity_coef = c.curiosity_coef;
+  return p;
+}
+
+int check_config(const rollout_config* c) {
+  if (!c) return fail(ROLLOUT_EINVAL, "config is NULL");
+  if (c->n_episodes < 1 || c->n_steps < 1)
+    return fail(ROLLOUT_EINVAL, "n_episodes and n_steps must be >= 1 (got %d, %d)", c->n_episodes,
+                c->n_steps);
+  if ((int64_t)c->n_episodes * c->n_steps >= (int64_t)1 << 40)
+    return fail(ROLLOUT_EINVAL, "n_episodes * n_steps too large");
+  if (c->n_features != 51 || c->state_dim != 54 || c->n_actions != 45)
+    return fail(ROLLOUT_EINVAL, "features/state/actions must be 51/54/45");
+  for (int i = 0; i < 4; ++i)
+    if (c->actor_dims[i] != kActorDims[i]) return fail(ROLLOUT_EINVAL, "actor dims must be 54,128,64,45");
+  for (int i = 0; i < 7; ++i)
+    if (c->critic_dims[i] != kCriticDims[i])
+      return fail(ROLLOUT_EINVAL, "critic dims must be 54,512,384,256,128,64,1");
+  for (int i = 0; i < 3; ++i)
+    if (c->cur_dims[i] != kCurDims[i]) return fail(ROLLOUT_EINVAL, "curiosity dims must be 99,128,51");
+  if (c->precision != ROLLOUT_FP32 && c->precision != ROLLOUT_BF16)
+    return fail(ROLLOUT_EINVAL, "unknown precision %d", c->precision);
+  if (c->precision == ROLLOUT_BF16) return fail(ROLLOUT_ENOTIMPL, "bf16 collection is not built yet");
+  if (c->div_window < 1 || c->div_window > 32)
+    return fail(ROLLOUT_EINVAL, "div_window must be in 1..32 (got %d)", c->div_window);
+  if (c->max_hold < 1) return fail(ROLLOUT_EINVAL, "max_hold must be >= 1");
+  return ROLLOUT_OK;
+}
+
+int check_weights(const float* const actor[6], const float* const critic[12],
+                  const float* const cur[4]) {
+  if (!actor || !critic || !cur) return fail(ROLLOUT_EINVAL, "weight array is NULL");
+  for (int i = 0; i < 6; ++i)
+    if (!actor[i]) return fail(ROLLOUT_EINVAL, "actor tensor %d is NULL", i);
+  for (int i = 0; i < 12; ++i)
+    if (!critic[i]) return fail(ROLLOUT_EINVAL, "critic tensor %d is NULL", i);
+  for (int i = 0; i < 4; ++i)
+    if (!cur[i]) return fail(ROLLOUT_EINVAL, "curiosity tensor %d is NULL", i);
+  return ROLLOUT_OK;
+}
+
+}  // namespace
+
+struct rollout_s {
+  int device = 0;
+  rollout_config cfg;
+  rl::EnvParams ep;
+  const float* features = nullptr;
+  const float* prices = nullptr;
+  int64_t n_bars = 0;
+  float* weights = nullptr;      // packed block
+  int32_t* start_used = nullptr; // [N]
+  GaeScratch gae;
+};
+
+extern "C" {
+
+int rollout_config_default(rollout_config* cfg, int32_t n_episodes, int32_t n_steps) {
+  if (!cfg) return fail(ROLLOUT_EINVAL, "config is NULL");
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->n_episodes = n_episodes;
+  cfg->n_steps = n_steps;
+  cfg->n_features = 51;
+  cfg->state_dim = 54;
+  cfg->n_actions = 45;
+  std::memcpy(cfg->actor_dims, kActorDims, sizeof(kActorDims));
+  std::memcpy(cfg->critic_dims, kCriticDims, sizeof(kCriticDims));
+  std::memcpy(cfg->cur_dims, kCurDims, sizeof(kCurDims));
+  cfg->precision = ROLLOUT_FP32;
+  cfg->gamma = 0.99f;
+  cfg->lambda = 0.95f;
+  cfg->profit_take = 0.02f;
+  cfg->stop_loss = 0.01f;
+  cfg->max_hold = 50;
+  cfg->div_window = 20;
+  cfg->div_threshold = 1.0f;
+  cfg->div_penalty = -0.1f;
+  cfg->curiosity_coef = 0.01f;
+  cfg->risk_coef = 0.01f;
+  cfg->spread = 0.0005f;
+  cfg->barrier_scale = 0.5f;
+  const float ex[5] = {-1.0f, -0.5f, 0.0f, 0.5f, 1.0f};
+  const float co[3] = {0.0002f, 0.0005f, 0.001f};
+  std::memcpy(cfg->exposure, ex, sizeof(ex));
+  std::memcpy(cfg->cost, co, sizeof(co));
+  cfg->urgency_mult = 0.5f;
+  return ROLLOUT_OK;
+}
+
+int rollout_create(const rollout_config* cfg, const float* const actor[6],
+                   const float* const critic[12], const float* const curiosity[4],
+                   const float* features, const float* prices, int64_t n_bars, void* hip_stream,
+                   rollout_handle* out) {
+  if (!out) return fail(ROLLOUT_EINVAL, "out handle pointer is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  rc = check_weights(actor, critic, curiosity);
+  if (rc) return rc;
+  if (!features || !prices) return fail(ROLLOUT_EINVAL, "features/prices are NULL");
+  if (n_bars < (int64_t)cfg->n_steps + 1)
+    return fail(ROLLOUT_EINVAL, "n_bars (%lld) must be >= n_steps + 1", (long long)n_bars);
+  if (n_bars > ((int64_t)1 << 31) - 2) return fail(ROLLOUT_EINVAL, "n_bars too large");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  auto* h = new (std::nothrow) rollout_s();
+  if (!h) return fail(ROLLOUT_ENOMEM, "host allocation failed");
+  h->cfg = *cfg;
+  h->ep = env_params(*cfg);
+  h->features = features;
+  h->prices = prices;
+  h->n_bars = n_bars;
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "hipGetDevice");
+  }
+  const rl::PackedOffsets P = rl::packed_offsets();
+  void* p = nullptr;
+  if (hipMalloc(&p, (size_t)P.total * sizeof(float)) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return fail(ROLLOUT_ENOMEM, "cannot allocate packed weights");
+  }
+  h->weights = static_cast<float*>(p);
+  if (hipMalloc(&p, (size_t)cfg->n_episodes * sizeof(int32_t)) != hipSuccess) {
+    (void)hipGetLastError();
+    rollout_destroy(h);
+    return fail(ROLLOUT_ENOMEM, "cannot allocate start buffer");
+  }
+  h->start_used = static_cast<int32_t*>(p);
+  rc = gae_reserve(h->gae, cfg->n_steps, cfg->n_episodes, st);
+  if (rc) {
+    rollout_destroy(h);
+    return rc;
+  }
+  e = rl::pack_weights(actor, critic, curiosity, h->weights, st);
+  if (e != hipSuccess) {
+    rollout_destroy(h);
+    return hip_fail(e, "weight packing");
+  }
+  *out = h;
+  return ROLLOUT_OK;
+}
+
+int rollout_set_weights(rollout_handle h, const float* const actor[6], const float* const critic[12],
+                        const float* const curiosity[4], void* hip_stream) {
+  if (!h) return fail(ROLLOUT_EINVAL, "handle is NULL");
+  int rc = check_weights(actor, critic, curiosity);
+  if (rc) return rc;
+  hipError_t e = rl::pack_weights(actor, critic, curiosity, h->weights,
+                                  static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "weight packing");
+  return ROLLOUT_OK;
+}
+
+int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t seed,
+                    const rollout_outputs* out, void* hip_stream) {
+  if (!h) return fail(ROLLOUT_EINVAL, "handle is NULL");
+  if (!episode_starts) return fail(ROLLOUT_EINVAL, "episode_starts is NULL");
+  if (!out) return fail(ROLLOUT_EINVAL, "outputs struct is NULL");
+  if (!out->states || !out->actions || !out->log_probs || !out->values || !out->rewards ||
+      !out->dones || !out->barrier || !out->advantages || !out->returns)
+    return fail(ROLLOUT_EINVAL, "a required output buffer is NULL");
+  int dev = -1;
+  RL_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev != h->device)
+    return fail(ROLLOUT_EINVAL, "handle was created on device %d, current device is %d", h->device, dev);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const int32_t N = h->cfg.n_episodes, L = h->cfg.n_steps;
+  if (out->counters) RL_HIP(hipMemsetAsync(out->counters, 0, 2 * sizeof(uint32_t), st), "counters");
+
+  rl::RolloutArgs ra;
+  ra.weights = h->weights;
+  ra.features = h->features;
+  ra.prices = h->prices;
+  ra.n_bars = h->n_bars;
+  ra.starts = episode_starts;
+  ra.seed = seed;
+  ra.N = N;
+  ra.L = L;
+  ra.ep = h->ep;
+  ra.start_used = h->start_used;
+  ra.states = out->states;
+  ra.actions = out->actions;
+  ra.log_probs = out->log_probs;
+  ra.rewards = out->rewards;
+  ra.dones = out->dones;
+  ra.barrier = out->barrier;
+  ra.logits = out->logits;
+  ra.counters = out->counters;
+  RL_HIP(rl::launch_actor_rollout(ra, st), "actor rollout launch");
+
+  rl::ValueArgs va;
+  va.weights = h->weights;
+  va.features = h->features;
+  va.states = out->states;
+  va.actions = out->actions;
+  va.start_used = h->start_used;
+  va.N = N;
+  va.L = L;
+  va.ep = h->ep;
+  va.values = out->values;
+  va.rewards = out->rewards;
+  va.counters = out->counters;
+  RL_HIP(rl::launch_value(va, st), "value launch");
+
+  rl::GaeArgs ga;
+  ga.rewards = out->rewards;
+  ga.values = out->values;
+  ga.dones = out->dones;
+  ga.last_values = nullptr;
+  ga.L = L;
+  ga.N = N;
+  ga.gamma = h->cfg.gamma;
+  ga.lambda = h->cfg.lambda;
+  ga.advantages = out->advantages;
+  ga.returns = out->returns;
+  return gae_run(h->gae, ga, st);
+}
+
+int gae_scan(const float* rewards, const float* values, const uint8_t* dones,
+             const float* last_values, int32_t L, int32_t N, float gamma, float lambda,
+             float* advantages, float* returns, void* hip_stream) {
+  if (L < 0 || N < 0) return fail(ROLLOUT_EINVAL, "gae_scan: negative size (L=%d, N=%d)", L, N);
+  if (L == 0 || N == 0) return ROLLOUT_OK;
+  if (!rewards || !values || !dones || !advantages || !returns)
+    return fail(ROLLOUT_EINVAL, "gae_scan: NULL buffer");
+  if ((int64_t)L * N >= (int64_t)1 << 40) return fail(ROLLOUT_EINVAL, "gae_scan: too large");
+  int dev = -1;
+  RL_HIP(hipGetDevice(&dev), "hipGetDevice");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  rl::GaeArgs ga{rewards, values, dones, last_values, L, N, gamma, lambda, advantages, returns};
+  std::lock_guard<std::mutex> lock(g_gae_mu);
+  return gae_run(gae_cache()[std::make_pair(dev, st)], ga, st);
+}
+
+void rollout_destroy(rollout_handle h) {
+  if (!h) return;
+  if (h->weights) (void)hipFree(h->weights);
+  if (h->start_used) (void)hipFree(h->start_used);
+  if (h->gae.mem) (void)hipFree(h->gae.mem);
+  delete h;
+}
+
+const char* rollout_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Arguments and launchers of the two collection kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nets.hpp"
+
+namespace rl {
+
+// Sequential part: state assembly, actor, draw, portfolio / barrier /
+// diversity, partial reward (everything a later step depends on).
+struct RolloutArgs {
+  const float* weights;   // packed block (packed_offsets layout)
+  const float* features;  // [n_bars][51]
+  const float* prices;    // [n_bars]
+  int64_t n_bars;
+  const int32_t* starts;  // [N]
+  uint64_t seed;
+  int32_t N, L;
+  EnvParams ep;
+  int32_t* start_used;    // [N] clamped starts (read back by the value kernel)
+  float* states;          // [L][N][54]
+  int32_t* actions;       // [L][N]
+  float* log_probs;       // [L][N]
+  float* rewards;         // [L][N] partial: pnl (1 + scale hit) + diversity
+  uint8_t* dones;         // [L][N]
+  uint8_t* barrier;       // [L][N]
+  float* logits;          // [L][N][45] or null
+  uint32_t* counters;     // [2] or null
+};
+
+// Batched part: critic value and curiosity bonus of every stored (t, n),
+// which no later step reads, then the final reward.
+struct ValueArgs {
+  const float* weights;
+  const float* features;
+  const float* states;
+  const int32_t* actions;
+  const int32_t* start_used;
+  int32_t N, L;
+  EnvParams ep;
+  float* values;
+  float* rewards;  // in: partial reward, out: full reward
+  uint32_t* counters;
+};
+
+hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st);
+hipError_t launch_value(const ValueArgs& a, hipStream_t st);
+
+}  // namespace rl

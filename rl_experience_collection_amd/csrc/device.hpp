@@ -1,0 +1,71 @@
+// Device-side building blocks for the gfx950 collection kernels: the
+// counter-based draw, fp32/bf16 MFMA wrappers and the packed-weight layout
+// shared by the pack kernels and the MLP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rl {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kFeatures = 51;
+constexpr int kState = 54;
+constexpr int kActions = 45;
+constexpr int kWave = 64;
+constexpr int kRowsPerWave = 16;  // MFMA N dimension: 16 episodes / rows per wave
+constexpr int kFirstSteps = 14;   // first layer: 54 inputs -> 4 lane groups x 14
+
+// --------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
+// multiplications whose high halves are xored with the other words and the
+// round key; the key advances by the golden-ratio Weyl constants.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Uniform in [0, 1) on a 2^-24 grid for (seed, episode, step, stream).
+__device__ __forceinline__ float draw_uniform(uint64_t seed, uint32_t episode, uint32_t step,
+                                              uint32_t stream) {
+  const uint4 r = philox10(make_uint4(episode, step, stream, 0u), (uint32_t)seed,
+                           (uint32_t)(seed >> 32));
+  return (float)(r.x >> 8) * 5.9604644775390625e-8f;
+}
+
+// --------------------------------------------------------------------------
+// MFMA v_mfma_f32_16x16x4_f32 in the transposed form used throughout:
+//   D[out 16 x rows 16] += W[out 16 x k 4] * X^T[k 4 x rows 16]
+// lane l supplies W[l%16][k(l/16)] and X[row l%16][k(l/16)], and holds
+// D[4*(l/16) + r][l%16] in register r.  Each lane thus holds 4 consecutive
+// outputs of one row; those registers are the next layer's X operand once the
+// next layer's k order is permuted to match (packed into its weights).
+// --------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Packed layout of one fp32 layer ("pk" arrays, built by the pack kernel):
+//   pk[((s * OG + og) * 64 + lane) * 4 + c] = W[o][i]
+//   o = 16 * (4 * og + c) + lane % 16,   i = kperm(s, lane / 16)
+// zero when o >= OUT or i >= IN.  S = k-steps, OG = ceil(ceil(OUT/16)/4).
+// First layer (state input):  kperm(s, g) = 14 g + s,        S = 14.
+// Chained layer:              kperm(s, g) = 16 (s/4) + 4 g + s%4, S = IN/4.
+// Bias: pb[16 * ot + j] = b[16 * ot + j] (zero padded to 16 * OT).
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int out_tiles(int out) { return cdiv(out, 16); }
+__host__ __device__ constexpr int out_groups(int out) { return cdiv(cdiv(out, 16), 4); }
+__host__ __device__ constexpr int packed_floats(int steps, int out) {
+  return steps * out_groups(out) * 64 * 4;
+}
+
+}  // namespace rl

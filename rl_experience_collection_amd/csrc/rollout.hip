@@ -1,0 +1,323 @@
+// Sequential part of PPO experience collection (PPO CUDA Pipeline Design,
+// Kernel Phases, Phase A): the chain that each step's state depends on.
+//
+// A wave owns 16 episodes for all L steps.  Per step it
+//   - assembles the 54-wide state (51 features of the bar, V/V0 - 1, the
+//     exposure held, the spread) and stores it (steps 1-2, 11),
+//   - runs the actor 54 -> 128 -> 64 -> 45 on MFMA with the packed actor
+//     weights resident in LDS for the whole kernel (step 3),
+//   - takes a max-shifted softmax, its CDF and the inverse-CDF draw
+//     a = min{k : u < CDF_k} with u from the counter-based generator, and
+//     log p(a) = (l_a - max) - ln S (step 4),
+//   - steps the portfolio, the triple barrier and the diversity window,
+//     kept in registers, and forms the part of the reward that needs them
+//     (steps 6-8, 10), then resets the episode when a barrier fired (12).
+// The critic value (step 5) and the curiosity bonus (step 9) are not read
+// by any later step, so they are evaluated afterwards by the value kernel
+// in one batched pass over every stored state.
+//
+// MFMA output layout: lane l holds logits 16*ot + 4*(l/16) + r of episode
+// l%16, so each episode's 45 logits sit in the 4 lanes l%16 + 16*g.  All
+// per-episode scalars (draw, portfolio, barrier, window) are computed
+// redundantly by those 4 lanes.
+#include "collect.hpp"
+
+#include <math.h>
+
+namespace rl {
+
+namespace {
+
+constexpr PackedOffsets kP = packed_offsets();
+constexpr int kActorF4 = (int)(kP.actor_end / 4);
+constexpr int kActF4PerWave = 8 * 64;  // widest actor activation: 128 = 8 tiles
+
+__device__ __forceinline__ void load_features(const float* __restrict__ F, int64_t bar, int g,
+                                              float (&f)[kFirstSteps]) {
+  const float* row = F + bar * kFeatures + kFirstSteps * g;
+#pragma unroll
+  for (int s = 0; s < kFirstSteps; ++s) f[s] = (kFirstSteps * g + s < kFeatures) ? row[s] : 0.0f;
+}
+
+template <int WPG>
+__global__ __launch_bounds__(64 * WPG) void actor_rollout_kernel(RolloutArgs a) {
+  __shared__ f32x4 s_w[kActorF4];
+  __shared__ f32x4 s_act[WPG][kActF4PerWave];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+
+  {  // stage the packed actor into LDS
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.weights);
+    for (int i = threadIdx.x; i < kActorF4; i += 64 * WPG) s_w[i] = src[i];
+  }
+  __syncthreads();
+
+  const int32_t n_raw = (blockIdx.x * WPG + wave) * kRowsPerWave + (lane & 15);
+  const bool valid = n_raw < a.N;
+  const int32_t n = valid ? n_raw : a.N - 1;
+  const EnvParams& ep = a.ep;
+
+  // clamp the start so every read stays inside the market buffers
+  const int64_t hi = a.n_bars - (int64_t)a.L - 1;
+  int64_t st = a.starts[n];
+  const bool clamped = st < 0 || st > hi;
+  st = st < 0 ? 0 : (st > hi ? hi : st);
+  if (valid && g == 0) {
+    a.start_used[n] = (int32_t)st;
+    if (clamped && a.counters) atomicAdd(a.counters + 1, 1u);
+  }
+
+  const float* sw = reinterpret_cast<const float*>(s_w);
+  const f32x4* w1 = s_w + kP.actor_w[0] / 4;
+  const f32x4* w2 = s_w + kP.actor_w[1] / 4;
+  const f32x4* w3 = s_w + kP.actor_w[2] / 4;
+  const float* b1 = sw + kP.actor_b[0];
+  const float* b2 = sw + kP.actor_b[1];
+  const float* b3 = sw + kP.actor_b[2];
+  f32x4* act = s_act[wave];
+
+  float fcur[kFirstSteps];
+  load_features(a.features, st, g, fcur);
+  float p0 = a.prices[st], p1 = a.prices[st + 1];
+
+  // episode state (PPO CUDA Pipeline Design, Phase A steps 6-8, 12)
+  float V = 1.0f, e_prev = 0.0f, entry = 0.0f;
+  int armed = 0, side = 0, t_open = 0;
+  int cnt0 = 0, cnt1 = 0, cnt2 = 0, pushed = 0;
+  uint64_t ring = 0;  // 2 bits per window slot
+  const float V0 = 1.0f;
+
+  for (int32_t t = 0; t < a.L; ++t) {
+    const int64_t bar = st + t;
+    const int64_t o = (int64_t)t * a.N + n;
+
+    // ---- steps 1-2: state, as this lane's 16 first-layer k-steps --------
+    float B[16];
+#pragma unroll
+    for (int s = 0; s < kFirstSteps; ++s) B[s] = fcur[s];
+    if (g == 3) {  // k = 42 + s: features up to 50, then the portfolio features
+      B[9] = V / V0 - 1.0f;
+      B[10] = e_prev;
+      B[11] = ep.spread;
+      B[12] = 0.0f;
+      B[13] = 0.0f;
+    }
+    B[14] = 0.0f;
+    B[15] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v;
+      v[0] = B[4 * q]; v[1] = B[4 * q + 1]; v[2] = B[4 * q + 2]; v[3] = B[4 * q + 3];
+      act[q * 64 + lane] = v;
+    }
+    if (valid) {
+      float* srow = a.states + o * kState + kFirstSteps * g;
+#pragma unroll
+      for (int s = 0; s < kFirstSteps; ++s)
+        if (kFirstSteps * g + s < kState) srow[s] = B[s];
+    }
+
+    // prefetch the next bar (independent of this step's outcome)
+    float fnext[kFirstSteps];
+    float p2 = p1;
+    if (t + 1 < a.L) {
+      load_features(a.features, bar + 1, g, fnext);
+      p2 = a.prices[bar + 2];
+    }
+
+    // ---- step 3: actor --------------------------------------------------
+    {
+      f32x4 h[8];
+      mfma_layer<16, 8>(w1, b1, act, h, lane);
+      relu_store<8>(h, act, lane);
+    }
+    {
+      f32x4 h[4];
+      mfma_layer<32, 4>(w2, b2, act, h, lane);
+      relu_store<4>(h, act, lane);
+    }
+    f32x4 lg[3];
+    mfma_layer<16, 3>(w3, b3, act, lg, lane);
+
+    // ---- step 4: softmax, CDF, inverse-CDF draw, log-prob -------------------
+    float l[12], e[12];
+    bool ok[12];
+    int bad = 0;
+#pragma unroll
+    for (int ot = 0; ot < 3; ++ot)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * ot + r;
+        ok[i] = 16 * ot + 4 * g + r < kActions;
+        l[i] = lg[ot][r];
+        if (ok[i] && !isfinite(l[i])) bad = 1;
+      }
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 12; ++i)
+      if (ok[i]) m = fmaxf(m, l[i]);
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+#pragma unroll
+    for (int i = 0; i < 12; ++i) e[i] = ok[i] ? expf(l[i] - m) : 0.0f;
+    float bs[3];
+#pragma unroll
+    for (int ot = 0; ot < 3; ++ot) bs[ot] = ((e[4 * ot] + e[4 * ot + 1]) + e[4 * ot + 2]) + e[4 * ot + 3];
+    float bsg[4][3];
+    const int base = lane & 15;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+      for (int ot = 0; ot < 3; ++ot) bsg[gg][ot] = __shfl(bs[ot], base + 16 * gg);
+    float T[3];
+#pragma unroll
+    for (int ot = 0; ot < 3; ++ot) T[ot] = ((bsg[0][ot] + bsg[1][ot]) + bsg[2][ot]) + bsg[3][ot];
+    const float S = (T[0] + T[1]) + T[2];
+    const float u = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 0u);
+    int first = 64;
+    float before = 0.0f;
+#pragma unroll
+    for (int ot = 0; ot < 3; ++ot) {
+      float run = before;
+#pragma unroll
+      for (int gg = 0; gg < 3; ++gg)
+        if (gg < g) run += bsg[gg][ot];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        run += e[4 * ot + r];
+        const float cdf = run / S;
+        const int k = 16 * ot + 4 * g + r;
+        if (ok[4 * ot + r] && first == 64 && u < cdf) first = k;
+      }
+      before += T[ot];
+    }
+    int act_a = min(first, __shfl_xor(first, 16));
+    act_a = min(act_a, __shfl_xor(act_a, 32));
+    if (act_a == 64) {  // rounding left u >= CDF_44: last action with weight
+      int lastk = -1;
+#pragma unroll
+      for (int ot = 0; ot < 3; ++ot)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (ok[4 * ot + r] && e[4 * ot + r] > 0.0f) lastk = max(lastk, 16 * ot + 4 * g + r);
+      lastk = max(lastk, __shfl_xor(lastk, 16));
+      lastk = max(lastk, __shfl_xor(lastk, 32));
+      act_a = lastk >= 0 ? lastk : kActions - 1;
+    }
+    float la = -INFINITY;
+#pragma unroll
+    for (int ot = 0; ot < 3; ++ot)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * ot + 4 * g + r == act_a) la = l[4 * ot + r];
+    la = fmaxf(la, __shfl_xor(la, 16));
+    la = fmaxf(la, __shfl_xor(la, 32));
+    const float logp = (la - m) - logf(S);
+    bad |= __shfl_xor(bad, 16);
+    bad |= __shfl_xor(bad, 32);
+
+    // ---- step 6: portfolio (exposure fraction of equity, turnover cost) ---
+    const int xi = act_a / 9;
+    const int oi = (act_a % 9) / 3;
+    const int ui = act_a % 3;
+    const float ex = exposure_of(ep, xi);
+    const float cost = cost_of(ep, oi) * (1.0f + ep.urgency_mult * (float)ui);
+    const float ret = p1 / p0 - 1.0f;
+    const float pnl = ex * ret - cost * fabsf(ex - e_prev);
+    V = V * (1.0f + pnl);
+
+    // ---- step 7: triple barrier on raw prices ------------------------------
+    if (ex != 0.0f) {
+      const int sd = ex > 0.0f ? 1 : -1;
+      const int prev = e_prev > 0.0f ? 1 : (e_prev < 0.0f ? -1 : 0);
+      if (prev == 0 || prev != sd) {
+        armed = 1;
+        side = sd;
+        entry = p0;
+        t_open = t;
+      }
+    } else {
+      armed = 0;
+    }
+    int hit = 0, code = 0;
+    if (armed) {
+      if (side > 0) {
+        if (p1 >= entry * ep.up_pt) { hit = 1; code = 1; }
+        else if (p1 <= entry * ep.dn_sl) { hit = -1; code = 2; }
+      } else {
+        if (p1 <= entry * ep.dn_pt) { hit = 1; code = 1; }
+        else if (p1 >= entry * ep.up_sl) { hit = -1; code = 2; }
+      }
+      if (code == 0 && t + 1 - t_open >= ep.max_hold) code = 3;
+    }
+
+    // ---- step 8: diversity window, 3-class entropy in nats -----------------
+    const int cat = xi <= 1 ? 0 : (xi == 2 ? 1 : 2);
+    const int pos = pushed % ep.div_window;
+    if (pushed >= ep.div_window) {
+      const int old = (int)((ring >> (2 * pos)) & 3u);
+      cnt0 -= old == 0; cnt1 -= old == 1; cnt2 -= old == 2;
+    }
+    ring = (ring & ~(3ull << (2 * pos))) | ((uint64_t)cat << (2 * pos));
+    cnt0 += cat == 0; cnt1 += cat == 1; cnt2 += cat == 2;
+    ++pushed;
+    const float nn = (float)(cnt0 + cnt1 + cnt2);
+    float H = 0.0f;
+    if (cnt0 > 0) { const float p = (float)cnt0 / nn; H -= p * logf(p); }
+    if (cnt1 > 0) { const float p = (float)cnt1 / nn; H -= p * logf(p); }
+    if (cnt2 > 0) { const float p = (float)cnt2 / nn; H -= p * logf(p); }
+    const float div = H < ep.div_threshold ? ep.div_penalty : 0.0f;
+
+    // ---- steps 10-11: partial reward and stores ----------------------------
+    const float partial = pnl * (1.0f + ep.barrier_scale * (float)hit) + div;
+    const int done = code != 0;
+    if (valid) {
+      if (g == 0) {
+        a.actions[o] = act_a;
+        a.log_probs[o] = logp;
+        a.rewards[o] = partial;
+        a.dones[o] = (uint8_t)done;
+        a.barrier[o] = (uint8_t)code;
+        if (bad && a.counters) atomicAdd(a.counters, 1u);
+      }
+      if (a.logits) {
+        float* lrow = a.logits + o * kActions;
+#pragma unroll
+        for (int ot = 0; ot < 3; ++ot)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (ok[4 * ot + r]) lrow[16 * ot + 4 * g + r] = l[4 * ot + r];
+      }
+    }
+
+    // ---- step 12: reset on done; the bar pointer keeps advancing ------------
+    e_prev = ex;
+    if (done) {
+      V = 1.0f;
+      e_prev = 0.0f;
+      armed = 0;
+      cnt0 = cnt1 = cnt2 = 0;
+      pushed = 0;
+      ring = 0;
+    }
+#pragma unroll
+    for (int s = 0; s < kFirstSteps; ++s) fcur[s] = fnext[s];
+    p0 = p1;
+    p1 = p2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
+  if (a.N <= 0 || a.L <= 0) return hipSuccess;
+  constexpr int WPG = 2;
+  const int per_block = WPG * kRowsPerWave;
+  const unsigned blocks = (unsigned)((a.N + per_block - 1) / per_block);
+  hipLaunchKernelGGL((actor_rollout_kernel<WPG>), dim3(blocks), dim3(64 * WPG), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace rl

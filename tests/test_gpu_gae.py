@@ -1,0 +1,92 @@
+"""GPU parity of the standalone GAE scan (PPO CUDA Pipeline Design, Kernel
+Phases, Phase B) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import synthdata
+from parity import close_mask, gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
+
+
+def run(r, v, d, gamma=0.99, lam=0.95, last=None, offset=0):
+    import torch
+    import rl_experience_collection_amd as rx
+    L, N = r.shape
+
+    def dev(a):
+        if offset == 0:
+            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        # misaligned view: `offset` elements into a larger buffer
+        flat = torch.zeros(a.size + offset, dtype=torch.from_numpy(a[:0]).dtype, device="cuda")
+        flat[offset:] = torch.from_numpy(np.ascontiguousarray(a).ravel()).cuda()
+        return flat[offset:].view(a.shape)
+
+    R, V, D = dev(r), dev(v), dev(d)
+    A = torch.empty_like(R)
+    Rt = torch.empty_like(R)
+    lv = None if last is None else dev(last)
+    rx.gae_scan(R, V, D, lv, gamma, lam, A, Rt)
+    torch.cuda.synchronize()
+    return A.cpu().numpy(), Rt.cpu().numpy()
+
+
+def check(r, v, d, gamma=0.99, lam=0.95, last=None, offset=0):
+    A, R = run(r, v, d, gamma, lam, last, offset)
+    Ao, Ro = oracle.gae(r, v, d, gamma, lam, last_values=last)
+    assert close_mask(A, Ao).all(), np.abs(A - Ao).max()
+    assert close_mask(R, Ro).all(), np.abs(R - Ro).max()
+    assert np.array_equal(R, (A + v).astype(np.float32))
+    return A, R
+
+
+@pytest.mark.parametrize("L,N", [(1, 1), (2, 3), (17, 5), (16, 1024), (100, 16), (37, 1000),
+                                 (33, 2049), (500, 8192), (129, 4100)])
+def test_gae_matches_oracle(L, N):
+    r, v, d = synthdata.gae_inputs(N, L, seed=L * 7 + N)
+    check(r, v, d)
+
+
+def test_gae_full_size_4096x2048():
+    spec = synthdata.WORKLOADS["gae_n4096_l2048"]
+    r, v, d = synthdata.gae_inputs(spec["N"], spec["L"], spec["seed"])
+    check(r, v, d)
+
+
+@pytest.mark.parametrize("N", [6, 7, 1030])
+def test_gae_last_values_and_vector_widths(N):
+    L = 45
+    r, v, d = synthdata.gae_inputs(N, L, seed=N)
+    last = np.linspace(-1, 1, N).astype(np.float32)
+    check(r, v, d, last=last)
+
+
+@pytest.mark.parametrize("offset", [1, 2])
+def test_gae_misaligned_views(offset):
+    r, v, d = synthdata.gae_inputs(256, 40, seed=offset)
+    check(r, v, d, offset=offset)
+
+
+def test_gae_dense_dones_and_extreme_params():
+    r, v, d = synthdata.gae_inputs(300, 64, seed=9, p_done=0.5)
+    check(r, v, d, gamma=1.0, lam=1.0)
+    check(r, v, d, gamma=0.5, lam=0.0)
+    d1 = np.ones_like(d)
+    A, _ = check(r, v, d1)
+    assert np.array_equal(A, r - v)
+
+
+def test_gae_deterministic_across_calls():
+    r, v, d = synthdata.gae_inputs(4096, 512, seed=3)
+    A1, R1 = run(r, v, d)
+    A2, R2 = run(r, v, d)
+    assert np.array_equal(A1, A2) and np.array_equal(R1, R2)
+
+
+def test_gae_empty_is_noop():
+    import torch
+    import rl_experience_collection_amd as rx
+    z = torch.zeros((0, 5), device="cuda")
+    rx.gae_scan(z, z, torch.zeros((0, 5), dtype=torch.uint8, device="cuda"), None, 0.99, 0.95, z, z)

@@ -1,0 +1,134 @@
+"""GPU parity of the whole collection (rollout_collect) against the oracle,
+through the C ABI, on the seeded workloads and edge cases."""
+import numpy as np
+import pytest
+
+import oracle
+import synthdata
+from parity import compare_rollout, gpu_available, run_gpu, close_mask
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
+
+
+def _assert_parity(inp, gpu, orc, episodes=None, **kw):
+    rep = {}
+    fails = compare_rollout(inp, gpu, orc, episodes=episodes, report=rep, **kw)
+    print(f"near-tie flags: {len(rep['flagged'])} {rep['flagged'][:5]}")
+    assert not fails, "\n".join(fails[:20])
+    return rep
+
+
+def test_tiny_workload_n16_l100():
+    inp = synthdata.ppo_inputs("ppo_n16_l100")
+    _assert_parity(inp, run_gpu(inp), oracle.rollout(inp))
+
+
+def test_tiny_workload_with_random_biases():
+    inp = synthdata.ppo_inputs("ppo_n16_l100", bias_scale=0.2)
+    _assert_parity(inp, run_gpu(inp), oracle.rollout(inp))
+
+
+@pytest.mark.parametrize("N,L", [(1, 1), (1, 7), (19, 37), (33, 64), (47, 3)])
+def test_ragged_sizes(N, L):
+    spec = dict(N=N, L=L, n_bars=3000, seed=100 + N + L)
+    inp = synthdata.ppo_inputs(spec, bias_scale=0.1)
+    _assert_parity(inp, run_gpu(inp), oracle.rollout(inp))
+
+
+def test_default_workload_n128_l500():
+    inp = synthdata.ppo_inputs("ppo_n128_l500")
+    rep = _assert_parity(inp, run_gpu(inp), oracle.rollout(inp))
+    assert len(rep["flagged"]) <= 64
+
+
+def test_chip_workload_n8192_l500_sampled_episodes():
+    """Full-size launch; the oracle recomputes a spread of episodes."""
+    inp = synthdata.ppo_inputs("ppo_n8192_l500")
+    gpu = run_gpu(inp, logits=True)
+    sub = sorted(set(list(range(0, 8192, 331)) + [8191, 8190, 15, 16]))
+    orc = oracle.rollout(inp, subset=sub)
+    _assert_parity(inp, gpu, orc, episodes=sub)
+    # every (t, n): integer codes consistent, finite floats
+    assert np.array_equal(gpu["dones"], (gpu["barrier"] > 0).astype(np.uint8))
+    for k in ("values", "rewards", "advantages", "returns", "log_probs"):
+        assert np.isfinite(gpu[k]).all(), k
+    assert np.array_equal(gpu["returns"], (gpu["advantages"] + gpu["values"]).astype(np.float32))
+
+
+def test_gae_inside_collect_matches_oracle_gae_on_gpu_streams():
+    inp = synthdata.ppo_inputs("ppo_n128_l500")
+    gpu = run_gpu(inp, logits=False)
+    A, R = oracle.gae(gpu["rewards"], gpu["values"], gpu["dones"], 0.99, 0.95)
+    assert close_mask(gpu["advantages"], A).all()
+    assert close_mask(gpu["returns"], R).all()
+
+
+def test_deterministic_and_episode_independent():
+    inp = synthdata.ppo_inputs(dict(N=48, L=80, n_bars=5000, seed=7))
+    g1 = run_gpu(inp)
+    g2 = run_gpu(inp)
+    for k in g1:
+        if g1[k] is not None and k != "counters":
+            assert np.array_equal(g1[k], g2[k]), k
+    sub = dict(inp)
+    sub["N"] = 16
+    sub["starts"] = inp["starts"][:16]
+    g3 = run_gpu(sub)
+    for k in ("states", "actions", "log_probs", "values", "rewards", "dones", "barrier",
+              "advantages", "returns"):
+        assert np.array_equal(g3[k], g1[k][:, :16]), k
+
+
+def test_clamped_starts_are_counted_and_match_clamped_oracle():
+    inp = synthdata.ppo_inputs(dict(N=20, L=30, n_bars=400, seed=11))
+    bad = inp["starts"].copy()
+    bad[3] = -5
+    bad[7] = 400 - 30  # one past the last valid start
+    bad[8] = 10**6
+    gin = dict(inp)
+    gin["starts"] = bad
+    gpu = run_gpu(gin)
+    assert int(gpu["counters"][1]) == 3
+    fixed = dict(inp)
+    fixed["starts"] = np.clip(bad, 0, 400 - 30 - 1).astype(np.int32)
+    _assert_parity(fixed, gpu, oracle.rollout(fixed))
+
+
+def test_set_weights_takes_effect():
+    import torch
+    import rl_experience_collection_amd as rx
+    from parity import to_device
+    a = synthdata.ppo_inputs(dict(N=32, L=40, n_bars=3000, seed=21))
+    b = dict(a)
+    b["weights"] = synthdata.ppo_weights(99, bias_scale=0.1)
+    da, db = to_device(a), to_device(b)
+    col = rx.Collector(32, 40, da["weights"], da["features"], da["prices"], settings=a["settings"])
+    col.set_weights(db["weights"])
+    out = col.collect(da["starts"], a["sampler_seed"], logits=True)
+    torch.cuda.synchronize()
+    gpu = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+    col.close()
+    _assert_parity(b, gpu, oracle.rollout(b))
+
+
+def test_sampler_chi_square_on_gpu():
+    """1e6 GPU draws from one fixed logit vector (constant actor output)."""
+    from scipy import stats
+    inp = synthdata.ppo_inputs(dict(N=8192, L=123, n_bars=2000, seed=5))
+    w = inp["weights"]
+    g = np.random.default_rng(0)
+    logits = (g.standard_normal(45) * 1.5).astype(np.float32)
+    w["actor"][4] = np.zeros_like(w["actor"][4])
+    w["actor"][5] = logits
+    gpu = run_gpu(inp, logits=False)
+    n = gpu["actions"].size
+    counts = np.bincount(gpu["actions"].ravel(), minlength=45).astype(np.float64)
+    p = np.exp(logits.astype(np.float64) - logits.max())
+    p /= p.sum()
+    exp = p * n
+    small = exp < 5
+    obs = np.append(counts[~small], counts[small].sum()) if small.any() else counts
+    ex = np.append(exp[~small], exp[small].sum()) if small.any() else exp
+    chi2 = ((obs - ex) ** 2 / ex).sum()
+    assert chi2 < stats.chi2.ppf(1 - 1e-6, obs.size - 1)
