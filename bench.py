@@ -1,0 +1,234 @@
+"""Benchmark of fused PPO experience collection on one MI355X.
+
+One step = one rollout_collect: actor rollout over L steps, batched critic +
+curiosity + reward over the L*N stored states, GAE scan.  The headline
+workload is the chip-filling PPO collection (N=8192 episodes x L=500 steps,
+fp32); the pages' default N=128 x L=500 collection and the standalone GAE
+scan (N=4096 x L=2048) are measured in the same run and reported beside it.
+
+Prints ONE JSON line.  Every input is synthetic and seeded (synthdata), and
+resident in HBM before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA = 157.3e12   # MI355X dense fp32 matrix, FLOP/s
+PEAK_HBM = 8.0e12           # MI355X HBM3E, B/s
+METRIC = "experiences/sec at N=128,L=500 and N=8192; MFMA util %; GAE scan HBM GB/s"
+
+# algorithmic work per unit (2 flops per multiply-add; biases not counted)
+ACTOR_FLOP = 2 * (54 * 128 + 128 * 64 + 64 * 45)                                  # 35,968
+CRITIC_FLOP = 2 * (54 * 512 + 512 * 384 + 384 * 256 + 256 * 128 + 128 * 64 + 64)  # 727,168
+CURIOSITY_FLOP = 2 * (54 * 128 + 128 * 51) + 128                                  # 27,008
+VALUE_KERNEL_FLOP = CRITIC_FLOP + CURIOSITY_FLOP                                  # 754,176
+MLP_FLOP = ACTOR_FLOP + VALUE_KERNEL_FLOP                                         # 790,144
+GAE_BYTES = 17   # read r 4, V 4, d 1; write A 4, R 4
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, files):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_hash(files):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_collect(inp, steps, warmup, precision=0):
+    import torch
+    import numpy as np
+    import rl_experience_collection_amd as rx
+
+    N, L = inp["N"], inp["L"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    w = inp["weights"]
+    weights = dict(actor=[dev(x) for x in w["actor"]], critic=[dev(x) for x in w["critic"]],
+                   curiosity=[dev(x) for x in w["curiosity"]])
+    feats, prices, starts = dev(inp["features"]), dev(inp["prices"]), dev(inp["starts"])
+    col = rx.Collector(N, L, weights, feats, prices, settings=inp["settings"], precision=precision)
+    outs = rx.alloc_outputs(N, L, "cuda")
+    ev = rx.HipEvents(4 * steps)
+    seed = inp["sampler_seed"]
+    for i in range(warmup):
+        col.collect(starts, seed + i, outputs=outs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        col.collect(starts, seed + warmup + i, outputs=outs, phase_events=ev.handles[4 * i:4 * i + 4])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = np.array([[ev.elapsed_ms(4 * i + j, 4 * i + j + 1) for j in range(3)] for i in range(steps)])
+    per_step = np.array([ev.elapsed_ms(4 * i, 4 * i + 3) for i in range(steps)])
+    bad = int(outs["counters"][0].item())
+    ev.close()
+    col.close()
+    return dict(N=N, L=L, wall_s=wall, step_ms_events=per_step, phases_ms=ph.mean(axis=0),
+                nonfinite=bad)
+
+
+def time_gae(spec, reps):
+    """Cold: a 512 MiB read sweep evicts the 256 MB infinity cache with clean
+    lines before each timed launch.  Warm: back-to-back launches."""
+    import numpy as np
+    import torch
+    import synthdata
+    import rl_experience_collection_amd as rx
+
+    r, v, d = synthdata.gae_inputs(spec["N"], spec["L"], spec["seed"])
+    R, V, D = (torch.from_numpy(x).cuda() for x in (r, v, d))
+    A, Rt = torch.empty_like(R), torch.empty_like(R)
+    flush = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    ev = rx.HipEvents(2)
+    cold = []
+    for i in range(reps + 2):
+        flush.sum()
+        ev.record(0)
+        rx.gae_scan(R, V, D, None, 0.99, 0.95, A, Rt)
+        ev.record(1)
+        torch.cuda.synchronize()
+        if i >= 2:
+            cold.append(ev.elapsed_ms(0, 1))
+    rx.gae_scan(R, V, D, None, 0.99, 0.95, A, Rt)
+    ev.record(0)
+    for i in range(reps):
+        rx.gae_scan(R, V, D, None, 0.99, 0.95, A, Rt)
+    ev.record(1)
+    torch.cuda.synchronize()
+    warm = ev.elapsed_ms(0, 1) / reps
+    ev.close()
+    n = spec["N"] * spec["L"]
+    return dict(elements=n, cold_ms=float(np.median(cold)), warm_ms=float(warm))
+
+
+def cpu_baseline(inp, n_episodes):
+    """The oracle as it stands on a bounded episode subset of the same workload."""
+    import numpy as np
+    import oracle
+
+    sub = np.linspace(0, inp["N"] - 1, n_episodes).astype(np.int32)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    oracle.rollout(inp, subset=sub, n_threads=threads, with_logits=False)
+    dt = time.perf_counter() - t0
+    exp = n_episodes * inp["L"]
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=exp / dt, unit="experiences/s", cores=threads, kind="oracle",
+                sample=f"{n_episodes} of {inp['N']} episodes x {inp['L']} steps "
+                       f"({exp} experiences, {dt:.1f} s) of the N={inp['N']} L={inp['L']} "
+                       f"workload; episodes are independent; host CPU: {cpu}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-episodes", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the collection shards by episode and runs with no "
+              f"communication, so --gpus {args.gpus} is not supported in this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synthdata
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+
+    spec = dict(synthdata.WORKLOADS["ppo_n8192_l500"])
+    log("generating inputs ...")
+    big_inp = synthdata.ppo_inputs(spec)
+    log("timing N=8192 L=500 fp32 ...")
+    big = time_collect(big_inp, args.steps, args.warmup)
+    N, L = big["N"], big["L"]
+    ms = big["wall_s"] * 1000 / args.steps
+    exps = N * L * args.steps / big["wall_s"]
+    t_roll, t_val, t_gae = big["phases_ms"]
+    log("timing N=128 L=500 fp32 ...")
+    small = time_collect(synthdata.ppo_inputs("ppo_n128_l500"), args.steps, args.warmup)
+    log("timing GAE N=4096 L=2048 ...")
+    gae = time_gae(synthdata.WORKLOADS["gae_n4096_l2048"], max(args.steps, 20))
+
+    value_files = ["rl_experience_collection_amd/csrc/value.hip",
+                   "rl_experience_collection_amd/csrc/nets.hpp",
+                   "rl_experience_collection_amd/csrc/device.hpp"]
+    traffic = load_traffic("value_kernel_n8192_l500_traffic.txt", value_files)
+    achieved = VALUE_KERNEL_FLOP * N * L / (t_val * 1e-3)
+    roofline = dict(bound="mfma", achieved=achieved / 1e12, peak=PEAK_FP32_MFMA / 1e12,
+                    unit="TFLOP/s", frac=achieved / PEAK_FP32_MFMA, traffic=traffic,
+                    kernel="value_kernel (critic + curiosity, fp32 MFMA 16x16x4)",
+                    flop_per_launch=VALUE_KERNEL_FLOP * N * L, avg_launch_ms=t_val)
+    mlp_util = MLP_FLOP * N * L / ((t_roll + t_val) * 1e-3) / PEAK_FP32_MFMA
+    gae_in = 17 * N * L / (t_gae * 1e-3)
+
+    line = dict(
+        metric=METRIC, value=exps, unit="experiences/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="f32", data="synthetic",
+        config=dict(workload="ppo_collect_n8192_l500_fp32", episodes=N, steps_per_episode=L,
+                    bars=spec["n_bars"], experiences_per_step=N * L, precision="fp32"),
+        roofline=roofline,
+        phases_ms=dict(actor_rollout=t_roll, value_critic_curiosity=t_val, gae_scan=t_gae),
+        mlp_mfma_util=mlp_util,
+        gae_in_collect_GBps=gae_in / 1e9,
+        nonfinite_events=big["nonfinite"],
+        also=dict(
+            ppo_collect_n128_l500_fp32=dict(
+                value=128 * 500 * args.steps / small["wall_s"], unit="experiences/s",
+                ms_per_step=small["wall_s"] * 1000 / args.steps,
+                phases_ms=dict(zip(("actor_rollout", "value_critic_curiosity", "gae_scan"),
+                                   map(float, small["phases_ms"])))),
+            gae_scan_n4096_l2048=dict(
+                value=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / 1e9, unit="GB/s",
+                frac_of_hbm_peak=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / PEAK_HBM,
+                cold_ms=gae["cold_ms"], warm_ms=gae["warm_ms"],
+                warm_GBps=GAE_BYTES * gae["elements"] / (gae["warm_ms"] * 1e-3) / 1e9)),
+    )
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        line["cpu_baseline"] = cpu_baseline(big_inp, args.cpu_episodes)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -88,7 +88,7 @@ typedef struct {
 } rollout_config;
 
 /* Output buffers of one collection: DEVICE pointers, caller-owned, [L][N].
- * All are required except `logits` and `counters`. */
+ * All are required except `logits`, `counters` and `phase_events`. */
 typedef struct {
   float *states;      /* [L][N][54] f32 */
   int32_t *actions;   /* [L][N] i32, 0..44 */
@@ -101,8 +101,13 @@ typedef struct {
   float *returns;     /* [L][N] f32, advantages + values */
   float *logits;      /* [L][N][45] f32 or NULL (debug / parity only) */
   uint32_t *counters; /* [2] or NULL: reset then accumulated by this call:
-                         [0] steps whose logits, value or reward were not
-                         finite, [1] episodes whose start had to be clamped */
+                         [0] non-finite events (a step's logit vector, its
+                         value or its reward), [1] episodes whose start had
+                         to be clamped */
+  void *const *phase_events; /* NULL or [4] caller-created hipEvent_t (as
+                         void*), recorded on hip_stream before the rollout
+                         kernel, after it, after the value kernel and after
+                         the GAE scan, for per-phase timing */
 } rollout_outputs;
 
 /* Fill `cfg` with the default settings (the values in the comments above)

@@ -43,7 +43,7 @@ class RolloutConfig(C.Structure):
 class RolloutOutputs(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "states", "actions", "log_probs", "values", "rewards", "dones", "barrier",
-        "advantages", "returns", "logits", "counters")]
+        "advantages", "returns", "logits", "counters", "phase_events")]
 
 
 class RolloutError(RuntimeError):
@@ -188,7 +188,9 @@ def alloc_outputs(N: int, L: int, device="cuda", logits: bool = False, counters:
     return out
 
 
-def rollout_collect(handle: int, episode_starts, seed: int, outputs: dict, stream=None):
+def rollout_collect(handle: int, episode_starts, seed: int, outputs: dict, stream=None,
+                    phase_events=None):
+    """phase_events: None or a sequence of 4 hipEvent_t handles (ints)."""
     import torch
     L, N = outputs["actions"].shape
     o = RolloutOutputs()
@@ -203,6 +205,12 @@ def rollout_collect(handle: int, episode_starts, seed: int, outputs: dict, strea
     o.returns = _dev_ptr(outputs["returns"], torch.float32, (L, N), "returns")
     o.logits = _dev_ptr(outputs.get("logits"), torch.float32, (L, N, N_ACTIONS), "logits")
     o.counters = _dev_ptr(outputs.get("counters"), torch.int32, (2,), "counters")
+    ev = None
+    if phase_events is not None:
+        if len(phase_events) != 4:
+            raise ValueError("phase_events must hold 4 event handles")
+        ev = (C.c_void_p * 4)(*phase_events)
+        o.phase_events = C.cast(ev, C.c_void_p)
     s = _dev_ptr(episode_starts, torch.int32, (N,), "episode_starts")
     _check(load_library().rollout_collect(C.c_void_p(handle), s, C.c_uint64(seed), C.byref(o),
                                           _stream(stream)))
@@ -228,6 +236,39 @@ def rollout_destroy(handle: int):
         load_library().rollout_destroy(C.c_void_p(handle))
 
 
+class HipEvents:
+    """Timing events created through the HIP runtime (for phase_events)."""
+
+    def __init__(self, n: int):
+        self._hip = C.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self._hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            e = C.c_void_p()
+            if self._hip.hipEventCreate(C.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(e.value)
+
+    def record(self, i: int, stream=None):
+        if self._hip.hipEventRecord(C.c_void_p(self.handles[i]), _stream(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = C.c_float()
+        if self._hip.hipEventElapsedTime(C.byref(ms), C.c_void_p(self.handles[i]),
+                                         C.c_void_p(self.handles[j])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(C.c_void_p(h))
+        self.handles = []
+
+
 class Collector:
     """Owns one handle; weights as lists of [out, in] fp32 device tensors."""
 
@@ -244,10 +285,10 @@ class Collector:
                             weights["curiosity"], stream)
 
     def collect(self, episode_starts, seed: int, outputs: dict | None = None, logits=False,
-                stream=None) -> dict:
+                stream=None, phase_events=None) -> dict:
         if outputs is None:
             outputs = alloc_outputs(self.N, self.L, episode_starts.device, logits=logits)
-        rollout_collect(self.handle, episode_starts, seed, outputs, stream)
+        rollout_collect(self.handle, episode_starts, seed, outputs, stream, phase_events)
         return outputs
 
     def close(self):

@@ -52,8 +52,8 @@ struct GaeScratch {
 
 int gae_prepare(GaeScratch& s, const rl::GaeShape& shape, int32_t N, hipStream_t st,
                 rl::GaeScratchView* view) {
-  const size_t need = rl::gae_scratch_bytes(shape.nk, shape.nc, N);
-  bool relayout = (shape.nk != s.nk || shape.nc != s.nc || N != s.n);
+  const size_t need = rl::gae_scratch_bytes(shape.nk, N);
+  bool relayout = (shape.nk != s.nk || N != s.n);
   if (s.bytes < need) {
     if (s.mem) {
       hipError_t e = hipFree(s.mem);
@@ -72,10 +72,12 @@ int gae_prepare(GaeScratch& s, const rl::GaeShape& shape, int32_t N, hipStream_t
     s.ticket_base = 0;
     relayout = true;
   }
-  const size_t flag_bytes = ((size_t)shape.nk * shape.nc * 4 + 255) / 256 * 256;
-  const size_t agg_bytes = ((size_t)shape.nk * N * 8 + 255) / 256 * 256;
-  if (relayout || s.epoch >= (1u << 29)) {
-    RL_HIP(hipMemsetAsync(s.mem + 256, 0, flag_bytes, st), "hipMemsetAsync(gae flags)");
+  // The words are epoch-tagged; they are cleared only when their layout
+  // changes (or the epoch wraps), so that stale words never carry the
+  // current epoch.
+  if (relayout || s.epoch >= (1u << 28)) {
+    RL_HIP(hipMemsetAsync(s.mem + 256, 0, rl::gae_words_bytes(shape.nk, N), st),
+           "hipMemsetAsync(gae words)");
     s.epoch = 0;
     s.nk = shape.nk;
     s.nc = shape.nc;
@@ -84,9 +86,7 @@ int gae_prepare(GaeScratch& s, const rl::GaeShape& shape, int32_t N, hipStream_t
   s.epoch += 1;
   view->ticket = reinterpret_cast<uint32_t*>(s.mem);
   view->error = reinterpret_cast<uint32_t*>(s.mem + 4);
-  view->flags = reinterpret_cast<uint32_t*>(s.mem + 256);
-  view->agg = reinterpret_cast<uint64_t*>(s.mem + 256 + flag_bytes);
-  view->incl = reinterpret_cast<float*>(s.mem + 256 + flag_bytes + agg_bytes);
+  view->words = reinterpret_cast<uint64_t*>(s.mem + 256);
   view->ticket_base = s.ticket_base;
   view->epoch = s.epoch;
   return ROLLOUT_OK;
@@ -94,12 +94,7 @@ int gae_prepare(GaeScratch& s, const rl::GaeShape& shape, int32_t N, hipStream_t
 
 int gae_run(GaeScratch& s, const rl::GaeArgs& a, hipStream_t st) {
   if (a.L == 0 || a.N == 0) return ROLLOUT_OK;
-  auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) % m) == 0; };
-  const bool a16 = al(a.rewards, 16) && al(a.values, 16) && al(a.advantages, 16) &&
-                   al(a.returns, 16) && al(a.dones, 4);
-  const bool a8 = al(a.rewards, 8) && al(a.values, 8) && al(a.advantages, 8) && al(a.returns, 8) &&
-                  al(a.dones, 2);
-  const rl::GaeShape shape = rl::gae_shape(a.L, a.N, a16, a8);
+  const rl::GaeShape shape = rl::gae_shape(a.L, a.N);
   if (shape.tiles() >= (int64_t)1 << 31) return fail(ROLLOUT_EINVAL, "gae_scan: too many tiles");
   rl::GaeScratchView view;
   int rc = gae_prepare(s, shape, a.N, st, &view);
@@ -112,7 +107,7 @@ int gae_run(GaeScratch& s, const rl::GaeArgs& a, hipStream_t st) {
 
 // Reserve the scratch for the largest tile grid an (L, N) scan can use.
 int gae_reserve(GaeScratch& s, int32_t L, int32_t N, hipStream_t st) {
-  const rl::GaeShape shape = rl::gae_shape(L, N, false, false);
+  const rl::GaeShape shape = rl::gae_shape(L, N);
   rl::GaeScratchView view;
   const int rc = gae_prepare(s, shape, N, st, &view);
   s.epoch -= 1;  // nothing was launched with this epoch
@@ -316,7 +311,13 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
     return fail(ROLLOUT_EINVAL, "handle was created on device %d, current device is %d", h->device, dev);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const int32_t N = h->cfg.n_episodes, L = h->cfg.n_steps;
+  int rc = ROLLOUT_OK;
   if (out->counters) RL_HIP(hipMemsetAsync(out->counters, 0, 2 * sizeof(uint32_t), st), "counters");
+  auto mark = [&](int i) -> hipError_t {
+    if (!out->phase_events || !out->phase_events[i]) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(out->phase_events[i]), st);
+  };
+  RL_HIP(mark(0), "hipEventRecord(phase 0)");
 
   rl::RolloutArgs ra;
   ra.weights = h->weights;
@@ -338,6 +339,7 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   ra.logits = out->logits;
   ra.counters = out->counters;
   RL_HIP(rl::launch_actor_rollout(ra, st), "actor rollout launch");
+  RL_HIP(mark(1), "hipEventRecord(phase 1)");
 
   rl::ValueArgs va;
   va.weights = h->weights;
@@ -352,6 +354,7 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   va.rewards = out->rewards;
   va.counters = out->counters;
   RL_HIP(rl::launch_value(va, st), "value launch");
+  RL_HIP(mark(2), "hipEventRecord(phase 2)");
 
   rl::GaeArgs ga;
   ga.rewards = out->rewards;
@@ -364,7 +367,10 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   ga.lambda = h->cfg.lambda;
   ga.advantages = out->advantages;
   ga.returns = out->returns;
-  return gae_run(h->gae, ga, st);
+  rc = gae_run(h->gae, ga, st);
+  if (rc) return rc;
+  RL_HIP(mark(3), "hipEventRecord(phase 3)");
+  return ROLLOUT_OK;
 }
 
 int gae_scan(const float* rewards, const float* values, const uint8_t* dones,

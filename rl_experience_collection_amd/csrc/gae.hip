@@ -2,21 +2,30 @@
 // Design, Kernel Phases, Phase B), single pass at HBM speed.
 //
 // The recurrence A_t = delta_t + c_t A_{t+1} (c_t = gamma lambda (1 - d_t))
-// is affine in A_{t+1}, so a chunk of steps [t0, t1) maps A_{t1} to
-// A_{t0} = alpha + beta A_{t1}.  The grid is cut into tiles of
-// (256 * EPT episodes) x (TC steps).  Each workgroup
-//   1. takes the next tile in reverse-time order from an atomic ticket,
-//   2. loads its r, V, d once into registers (coalesced across episodes),
-//   3. publishes its chunk aggregate (alpha, beta) per episode,
-//   4. looks back at later-in-time tiles of the same episode columns until
-//      it finds one that has published its inclusive value A_{t0}, then
-//      folds the aggregates in between innermost-first, so the carry equals
-//      the sequential composition whatever the timing (bit-deterministic),
-//   5. publishes its own inclusive value, then writes A and R = A + V.
-// Every wait is on a tile holding an earlier ticket, i.e. a workgroup that
-// is already running, and the latest chunk never waits, so all waits end.
-// HBM traffic is the algorithmic 17 B per element plus 12 B per episode per
-// chunk of carry state.
+// is affine in A_{t+1}: a run of steps [t0, t1) maps A_{t1} to
+// A_{t0} = alpha + beta A_{t1}, with beta = 0 as soon as the run holds a done.
+//
+// Two levels:
+//  * a workgroup owns 64 episodes (one per lane) x a super-chunk of
+//    kGaeWaves * kGaeChunk steps; wave w loads its kGaeChunk steps once into
+//    registers (coalesced: one 256 B row of floats per step) and computes its
+//    (alpha_w, beta_w); the waves' maps are composed through LDS;
+//  * super-chunks of the same 64 episodes are chained across workgroups by a
+//    decoupled look-back: workgroups take super-chunks in reverse-time order
+//    from an atomic ticket, publish their aggregate alpha_S (or at once their
+//    inclusive value when the super-chunk holds a done or is the latest),
+//    look back to the nearest published inclusive value, fold the aggregates
+//    in between innermost-first and publish their own inclusive value
+//    alpha_S + beta_S * carry.
+// Every published value is one 64-bit word (value | epoch and status tag)
+// stored and polled with device-coherent relaxed atomics, so no fences are
+// needed.  A reader rebuilds the beta_S of an aggregate (no done inside) as
+// the same product of gl^kGaeChunk factors the owner formed, so every carry
+// is the same floating-point expression whatever the timing: results are
+// bit-deterministic.  Every wait is on a workgroup holding an earlier ticket
+// (already running) and the latest super-chunk never waits, so all waits
+// end.  HBM traffic is the algorithmic 17 B per element plus 8 B per episode
+// per super-chunk.
 #include "gae.hpp"
 
 #include <hip/hip_runtime.h>
@@ -27,247 +36,182 @@ namespace {
 
 constexpr uint32_t kAgg = 1u, kIncl = 2u;
 constexpr uint32_t kSpinLimit = 1u << 24;
+constexpr int kWalk = 8;   // aggregates held before waiting on an inclusive
+constexpr int kBatch = 4;  // later super-chunks read per look-back round
 
-__device__ __forceinline__ uint32_t flag_load(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void put_u64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t get_u64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void put_f32(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get_f32(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ uint64_t pack2(float a, float b) {
-  return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+__device__ __forceinline__ uint64_t pack_word(float value, uint32_t tag) {
+  return (uint64_t)__float_as_uint(value) | ((uint64_t)tag << 32);
 }
 
-template <int EPT>
-struct Vec;
-template <>
-struct Vec<1> {
-  typedef float F;
-  typedef uint8_t D;
-  static __device__ __forceinline__ float f(const F& v, int) { return v; }
-  static __device__ __forceinline__ float d(const D& v, int) { return (float)v; }
-  static __device__ __forceinline__ void set(F& v, int, float x) { v = x; }
-};
-template <>
-struct Vec<2> {
-  typedef float2 F;
-  typedef uint16_t D;
-  static __device__ __forceinline__ float f(const F& v, int e) { return e ? v.y : v.x; }
-  static __device__ __forceinline__ float d(const D& v, int e) { return (float)((v >> (8 * e)) & 0xFF); }
-  static __device__ __forceinline__ void set(F& v, int e, float x) { if (e) v.y = x; else v.x = x; }
-};
-template <>
-struct Vec<4> {
-  typedef float4 F;
-  typedef uint32_t D;
-  static __device__ __forceinline__ float f(const F& v, int e) {
-    return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
-  }
-  static __device__ __forceinline__ float d(const D& v, int e) { return (float)((v >> (8 * e)) & 0xFF); }
-  static __device__ __forceinline__ void set(F& v, int e, float x) {
-    if (e == 0) v.x = x; else if (e == 1) v.y = x; else if (e == 2) v.z = x; else v.w = x;
-  }
-};
-
-template <int EPT, int TC>
-__global__ __launch_bounds__(256) void gae_lookback_kernel(
+__global__ __launch_bounds__(64 * kGaeWaves) void gae_lookback_kernel(
     const float* __restrict__ rew, const float* __restrict__ val, const uint8_t* __restrict__ don,
     const float* __restrict__ last_values, int32_t L, int32_t N, float gamma, float gl,
     float* __restrict__ adv, float* __restrict__ ret, GaeScratchView sc, int32_t NC, int32_t NK) {
-  typedef Vec<EPT> V;
-  typedef typename V::F F;
-  typedef typename V::D D;
   __shared__ uint32_t s_tile;
-  __shared__ int32_t s_found;
+  __shared__ float s_a[kGaeWaves][64];
+  __shared__ float s_b[kGaeWaves][64];
+  __shared__ float s_carry[64];
 
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
   if (threadIdx.x == 0)
     s_tile = __hip_atomic_fetch_add(sc.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
              sc.ticket_base;
   __syncthreads();
   const uint32_t tile = s_tile;
-  if (tile >= (uint32_t)NC * (uint32_t)NK) return;  // stale ticket base: never expected
-  const int32_t k = NK - 1 - (int32_t)(tile / (uint32_t)NC);
+  if (tile >= (uint32_t)NC * (uint32_t)NK) return;  // stale ticket base: never expected (uniform)
+  const int32_t S = NK - 1 - (int32_t)(tile / (uint32_t)NC);
   const int32_t c = (int32_t)(tile % (uint32_t)NC);
-  const int32_t n0 = (c * 256 + (int32_t)threadIdx.x) * EPT;
-  const bool active = n0 < N;  // N is a multiple of EPT
-  const int32_t t0 = k * TC;
-  const int32_t cnt = min(TC, L - t0);
+  const int32_t n = c * 64 + lane;
+  const bool active = n < N;
+  const int32_t t0 = S * (kGaeWaves * kGaeChunk) + wv * kGaeChunk;
+  const int32_t cnt = active ? max(0, min(kGaeChunk, L - t0)) : 0;
 
-  // ---- load the chunk (one vector per step) -------------------------------
-  F r[TC], v[TC];
-  D d[TC];
-  F vnext;
+  // ---- load this wave's chunk --------------------------------------------
+  float r[kGaeChunk], v[kGaeChunk], d[kGaeChunk];
 #pragma unroll
-  for (int i = 0; i < TC; ++i) {
-    if (active && i < cnt) {
-      const int64_t o = (int64_t)(t0 + i) * N + n0;
-      r[i] = *reinterpret_cast<const F*>(rew + o);
-      v[i] = *reinterpret_cast<const F*>(val + o);
-      d[i] = *reinterpret_cast<const D*>(don + o);
-    }
-  }
-  if (active) {
-    if (t0 + cnt < L) {
-      vnext = *reinterpret_cast<const F*>(val + (int64_t)(t0 + cnt) * N + n0);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) V::set(vnext, e, last_values ? last_values[n0 + e] : 0.0f);
-    }
-  }
-
-  // ---- local pass: delta_t in place of r_t, chunk aggregate (alpha, beta) --
-  float alpha[EPT], beta[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    alpha[e] = 0.0f;
-    beta[e] = 1.0f;
-  }
-  if (active) {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      float vn = V::f(vnext, e), A = 0.0f, B = 1.0f;
-#pragma unroll
-      for (int i = TC - 1; i >= 0; --i) {
-        if (i < cnt) {
-          const float nd = 1.0f - V::d(d[i], e);
-          const float vi = V::f(v[i], e);
-          const float delta = V::f(r[i], e) + gamma * vn * nd - vi;
-          const float ci = gl * nd;
-          A = delta + ci * A;
-          B = ci * B;
-          V::set(r[i], e, delta);
-          vn = vi;
-        }
-      }
-      alpha[e] = A;
-      beta[e] = B;
-    }
-  }
-
-  const uint32_t tag = sc.epoch << 2;
-  uint32_t* flags = sc.flags + (int64_t)0;
-  float carry[EPT];
-  if (k == NK - 1) {
-    // latest chunk: A_L = 0, so its aggregate is already inclusive
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      carry[e] = 0.0f;
-      if (active) put_f32(sc.incl + (int64_t)k * N + n0 + e, alpha[e]);
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) flag_store(flags + (int64_t)k * NC + c, tag | kIncl);
-  } else {
-    if (active) {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        put_u64(sc.agg + (int64_t)k * N + n0 + e, pack2(alpha[e], beta[e]));
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      flag_store(flags + (int64_t)k * NC + c, tag | kAgg);
-      // find the nearest later tile with an inclusive value
-      int32_t j = k + 1;
-      uint32_t spins = 0;
-      for (;;) {
-        const uint32_t f = flag_load(flags + (int64_t)j * NC + c);
-        if ((f >> 2) == sc.epoch && (f & 3u) == kIncl) break;
-        if ((f >> 2) == sc.epoch && (f & 3u) == kAgg && j + 1 < NK) {
-          ++j;
-          continue;
-        }
-        if (++spins > kSpinLimit) {  // never expected: keeps the grid draining
-          __hip_atomic_fetch_add(sc.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      s_found = j;
-    }
-    __syncthreads();
-    const int32_t j = s_found;
-    if (active) {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        float x = get_f32(sc.incl + (int64_t)j * N + n0 + e);
-        for (int32_t i = j - 1; i > k; --i) {
-          const uint64_t ab = get_u64(sc.agg + (int64_t)i * N + n0 + e);
-          x = __uint_as_float((uint32_t)ab) + __uint_as_float((uint32_t)(ab >> 32)) * x;
-        }
-        carry[e] = x;
-        put_f32(sc.incl + (int64_t)k * N + n0 + e, alpha[e] + beta[e] * x);
-      }
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) flag_store(flags + (int64_t)k * NC + c, tag | kIncl);
-  }
-
-  // ---- fix-up: A_t from the carry, write A and R = A + V ------------------
-  if (!active) return;
-  float A[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) A[e] = carry[e];
-#pragma unroll
-  for (int i = TC - 1; i >= 0; --i) {
+  for (int i = 0; i < kGaeChunk; ++i) {
     if (i < cnt) {
-      F a_out, r_out;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const float nd = 1.0f - V::d(d[i], e);
-        A[e] = V::f(r[i], e) + (gl * nd) * A[e];
-        V::set(a_out, e, A[e]);
-        V::set(r_out, e, A[e] + V::f(v[i], e));
-      }
-      const int64_t o = (int64_t)(t0 + i) * N + n0;
-      *reinterpret_cast<F*>(adv + o) = a_out;
-      *reinterpret_cast<F*>(ret + o) = r_out;
+      const int64_t o = (int64_t)(t0 + i) * N + n;
+      r[i] = rew[o];
+      v[i] = val[o];
+      d[i] = (float)don[o];
     }
   }
-}
+  float vnext = 0.0f;
+  if (cnt > 0)
+    vnext = (t0 + cnt < L) ? val[(int64_t)(t0 + cnt) * N + n] : (last_values ? last_values[n] : 0.0f);
 
-template <int EPT, int TC>
-hipError_t launch(const GaeArgs& a, const GaeScratchView& sc, hipStream_t stream) {
-  const int32_t NC = cdiv_i(a.N, 256 * EPT), NK = cdiv_i(a.L, TC);
-  hipLaunchKernelGGL((gae_lookback_kernel<EPT, TC>), dim3((unsigned)(NC * NK)), dim3(256), 0, stream,
-                     a.rewards, a.values, a.dones, a.last_values, a.L, a.N, a.gamma,
-                     a.gamma * a.lambda, a.advantages, a.returns, sc, NC, NK);
-  return hipGetLastError();
+  // ---- chunk map: delta_t in place of r_t, A_t0 = alpha + beta A_t1 --------
+  float alpha = 0.0f, beta = 1.0f;
+  {
+    float vn = vnext;
+#pragma unroll
+    for (int i = kGaeChunk - 1; i >= 0; --i) {
+      if (i < cnt) {
+        const float nd = 1.0f - d[i];
+        const float delta = r[i] + gamma * vn * nd - v[i];
+        const float ci = gl * nd;
+        alpha = delta + ci * alpha;
+        beta = ci * beta;
+        r[i] = delta;
+        vn = v[i];
+      }
+    }
+  }
+  s_a[wv][lane] = alpha;
+  s_b[wv][lane] = beta;
+  __syncthreads();
+
+  // ---- super-chunk: compose, publish, look back (wave 0, lane = episode) --
+  if (wv == 0) {
+    float aS = 0.0f, bS = 1.0f;
+#pragma unroll
+    for (int w = kGaeWaves - 1; w >= 0; --w) {
+      aS = s_a[w][lane] + s_b[w][lane] * aS;
+      bS = s_b[w][lane] * bS;
+    }
+    const bool doneS = bS == 0.0f;
+    const uint32_t tag = sc.epoch << 3;
+    uint64_t* my = sc.words + (int64_t)S * N + n;
+    float carry = 0.0f;
+    if (active) {
+      const bool incl_now = (S == NK - 1) || doneS;
+      put_u64(my, pack_word(aS, tag | (incl_now ? kIncl : kAgg)));
+      if (S != NK - 1) {
+        // beta of a full super-chunk without dones, built like the owner's bS
+        float gl_c = 1.0f;
+#pragma unroll
+        for (int i = 0; i < kGaeChunk; ++i) gl_c = gl * gl_c;
+        float gl_s = 1.0f;
+#pragma unroll
+        for (int w = 0; w < kGaeWaves; ++w) gl_s = gl_c * gl_s;
+        float ag[kWalk];
+        int m = 0;
+        uint32_t spins = 0;
+        float x = 0.0f;
+        for (;;) {
+          uint64_t wd[kBatch];
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) {
+            const int32_t j = S + 1 + m + q;
+            wd[q] = j < NK ? get_u64(sc.words + (int64_t)j * N + n) : 0ull;
+          }
+          bool found = false, stop = false;
+          int got = 0;
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) {
+            if (stop) continue;
+            const uint32_t hi = (uint32_t)(wd[q] >> 32);
+            if (S + 1 + m + q >= NK || (hi >> 3) != sc.epoch) { stop = true; continue; }
+            if ((hi & 3u) == kIncl) {
+              x = __uint_as_float((uint32_t)wd[q]);
+              found = stop = true;
+              continue;
+            }
+            if (m + q >= kWalk) { stop = true; continue; }  // window full: wait here
+#pragma unroll
+            for (int z = 0; z < kWalk; ++z)
+              if (z == m + q) ag[z] = __uint_as_float((uint32_t)wd[q]);
+            ++got;
+          }
+          m += got;
+          if (found) break;
+          if (got == 0) {
+            if (++spins > kSpinLimit) {  // never expected: keeps the grid draining
+              __hip_atomic_fetch_add(sc.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+#pragma unroll
+        for (int z = kWalk - 1; z >= 0; --z)
+          if (z < m) x = ag[z] + gl_s * x;  // innermost first
+        carry = x;
+        if (!doneS) put_u64(my, pack_word(aS + bS * carry, tag | kIncl));
+      }
+    }
+    s_carry[lane] = carry;
+  }
+  __syncthreads();
+
+  // ---- carry of this wave's chunk, then A and R ---------------------------
+  if (cnt <= 0) return;
+  float A = s_carry[lane];
+  for (int w = kGaeWaves - 1; w > wv; --w) A = s_a[w][lane] + s_b[w][lane] * A;
+#pragma unroll
+  for (int i = kGaeChunk - 1; i >= 0; --i) {
+    if (i < cnt) {
+      A = r[i] + (gl * (1.0f - d[i])) * A;
+      const int64_t o = (int64_t)(t0 + i) * N + n;
+      adv[o] = A;
+      ret[o] = A + v[i];
+    }
+  }
 }
 
 }  // namespace
 
-GaeShape gae_shape(int32_t L, int32_t N, bool aligned16, bool aligned8) {
+GaeShape gae_shape(int32_t L, int32_t N) {
   GaeShape s;
-  s.ept = (N % 4 == 0 && aligned16) ? 4 : ((N % 2 == 0 && aligned8) ? 2 : 1);
-  s.tc = kGaeChunk;
-  s.nc = cdiv_i(N, 256 * s.ept);
-  s.nk = cdiv_i(L, s.tc);
+  s.nc = cdiv_i(N, 64);
+  s.nk = cdiv_i(L, kGaeWaves * kGaeChunk);
   return s;
 }
 
 hipError_t gae_launch(const GaeArgs& a, const GaeShape& shape, const GaeScratchView& sc,
                       hipStream_t stream) {
-  switch (shape.ept) {
-    case 4: return launch<4, kGaeChunk>(a, sc, stream);
-    case 2: return launch<2, kGaeChunk>(a, sc, stream);
-    default: return launch<1, kGaeChunk>(a, sc, stream);
-  }
+  hipLaunchKernelGGL(gae_lookback_kernel, dim3((unsigned)shape.tiles()), dim3(64 * kGaeWaves), 0,
+                     stream, a.rewards, a.values, a.dones, a.last_values, a.L, a.N, a.gamma,
+                     a.gamma * a.lambda, a.advantages, a.returns, sc, shape.nc, shape.nk);
+  return hipGetLastError();
 }
 
 }  // namespace rl

@@ -6,7 +6,8 @@
 
 namespace rl {
 
-constexpr int kGaeChunk = 16;  // steps per tile (registers: 16 x EPT x 3 words)
+constexpr int kGaeChunk = 16;  // steps per wave, held in registers (3 words each)
+constexpr int kGaeWaves = 16;  // waves per workgroup: a super-chunk is 256 steps
 
 inline int32_t cdiv_i(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
@@ -22,31 +23,25 @@ struct GaeArgs {
 };
 
 struct GaeShape {
-  int ept;  // episodes per thread (vector width of the loads)
-  int tc;   // steps per tile
-  int32_t nc, nk;  // tile columns and chunks
+  int32_t nc, nk;  // 64-episode columns and super-chunks
   int64_t tiles() const { return (int64_t)nc * nk; }
 };
 
 // Device view of the carry scratch of one stream/collector.
 struct GaeScratchView {
-  uint32_t* flags;     // [nk * nc], (epoch << 2) | status
-  uint64_t* agg;       // [nk * N] packed (alpha, beta)
-  float* incl;         // [nk * N]
+  uint64_t* words;     // [nk * N]: value | (epoch << 3 | has_done << 2 | status) << 32
   uint32_t* ticket;    // monotonically increasing ticket counter
   uint32_t* error;     // spin-limit events (never expected)
   uint32_t ticket_base;
-  uint32_t epoch;
+  uint32_t epoch;      // < 2^29
 };
 
-inline size_t gae_scratch_bytes(int32_t nk, int32_t nc, int32_t N) {
-  const size_t flags = (size_t)nk * nc * 4;
-  const size_t agg = (size_t)nk * N * 8;
-  const size_t incl = (size_t)nk * N * 4;
-  return 256 + ((flags + 255) / 256) * 256 + ((agg + 255) / 256) * 256 + ((incl + 255) / 256) * 256;
+inline size_t gae_words_bytes(int32_t nk, int32_t N) {
+  return ((size_t)nk * N * 8 + 255) / 256 * 256;
 }
+inline size_t gae_scratch_bytes(int32_t nk, int32_t N) { return 256 + gae_words_bytes(nk, N); }
 
-GaeShape gae_shape(int32_t L, int32_t N, bool aligned16, bool aligned8);
+GaeShape gae_shape(int32_t L, int32_t N);
 hipError_t gae_launch(const GaeArgs& a, const GaeShape& shape, const GaeScratchView& sc,
                       hipStream_t stream);
 

@@ -80,7 +80,8 @@ def market(n_bars: int, seed: int, rho: float = 0.9, sigma: float = 0.01, p0: fl
     g = _rng(seed, _STREAM_MARKET)
     eps = g.standard_normal((n_bars, N_FEATURES))
     eps[0] /= np.sqrt(1.0 - rho * rho)
-    feats = lfilter([1.0], [1.0, -rho], eps, axis=0).astype(np.float32)
+    # filter each feature's series along contiguous memory, then back to [bars, 51]
+    feats = lfilter([1.0], [1.0, -rho], np.ascontiguousarray(eps.T), axis=1).T.astype(np.float32)
     z = g.standard_normal(n_bars)
     z[0] = 0.0
     prices = (p0 * np.exp(sigma * np.cumsum(z))).astype(np.float32)
