@@ -54,18 +54,6 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Packed layout of one fp32 layer ("pk" arrays, built by the pack kernel):
-//   pk[((s * OG + og) * 64 + lane) * 4 + c] = W[o][i]
-//   o = 16 * (4 * og + c) + lane % 16,   i = kperm(s, lane / 16)
-// zero when o >= OUT or i >= IN.  S = k-steps, OG = ceil(ceil(OUT/16)/4).
-// First layer (state input):  kperm(s, g) = 14 g + s,        S = 14.
-// Chained layer:              kperm(s, g) = 16 (s/4) + 4 g + s%4, S = IN/4.
-// Bias: pb[16 * ot + j] = b[16 * ot + j] (zero padded to 16 * OT).
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
-__host__ __device__ constexpr int out_tiles(int out) { return cdiv(out, 16); }
-__host__ __device__ constexpr int out_groups(int out) { return cdiv(cdiv(out, 16), 4); }
-__host__ __device__ constexpr int packed_floats(int steps, int out) {
-  return steps * out_groups(out) * 64 * 4;
-}
 
 }  // namespace rl

@@ -7,22 +7,40 @@
 namespace rl {
 
 // ---------------------------------------------------------------------------
-// Packed weight block.  One device allocation holds every layer in the MFMA
-// operand order described in device.hpp; offsets are in floats and 64-float
-// aligned.  First layers (state input) use S = 16 k-steps, the 54 inputs
-// spread 14 per lane group with the last two steps zero.
+// Layers are evaluated by kSplit cooperating waves on the same 16 rows: wave
+// q computes output tiles [q*OTW, (q+1)*OTW) with OTW = OT / kSplit.  The
+// packed A operands of one layer are laid out so that each wave reads one
+// contiguous block per k-step:
+//   pk[((s * kSplit + q) * 64 + lane) * OTW + i] = W[o][k]
+//   o = 16 * (q * OTW + i) + lane % 16,   k = kperm(s, lane / 16)
+// (zero when o >= OUT or k >= IN).  First layers (state input) use 16
+// k-steps with kperm(s, g) = 14 g + s (s < 14; steps 14, 15 are zero);
+// chained layers use kperm(s, g) = 16 (s / 4) + 4 g + s % 4, S = IN / 4.
+// Bias: pb[16 * ot + j] = b[16 * ot + j], zero padded to 16 * OT.
 // ---------------------------------------------------------------------------
+constexpr int kSplit = 4;
+
 struct LayerDesc {
-  int in, out, steps, first;  // first: state-input k order, else chained order
+  int in, out, steps, first, ot;  // ot = out tiles (a multiple of kSplit)
 };
 
 // Actor: 54 -> 128 -> 64 -> 45 (PPO CUDA Pipeline Design, Weight Layout).
-constexpr LayerDesc kActor[3] = {{54, 128, 16, 1}, {128, 64, 32, 0}, {64, 45, 16, 0}};
+constexpr LayerDesc kActor[3] = {{54, 128, 16, 1, 8}, {128, 64, 32, 0, 4}, {64, 45, 16, 0, 4}};
 // Critic: 54 -> 512 -> 384 -> 256 -> 128 -> 64 (-> 1 handled on the VALU).
-constexpr LayerDesc kCritic[5] = {
-    {54, 512, 16, 1}, {512, 384, 128, 0}, {384, 256, 96, 0}, {256, 128, 64, 0}, {128, 64, 32, 0}};
+constexpr LayerDesc kCritic[5] = {{54, 512, 16, 1, 32},
+                                  {512, 384, 128, 0, 24},
+                                  {384, 256, 96, 0, 16},
+                                  {256, 128, 64, 0, 8},
+                                  {128, 64, 32, 0, 4}};
 // Curiosity forward model: 54 dense inputs (+45 one-hot, gathered) -> 128 -> 51.
-constexpr LayerDesc kCur[2] = {{54, 128, 16, 1}, {128, 51, 32, 0}};
+constexpr LayerDesc kCur[2] = {{54, 128, 16, 1, 8}, {128, 51, 32, 0, 4}};
+
+// Packed weights of a layer, plus kPrefetch zero k-steps so the prefetch of
+// the layer's last steps reads inside the block.
+constexpr int kPrefetch = 3;
+__host__ __device__ constexpr int64_t packed_layer_floats(const LayerDesc& d) {
+  return (int64_t)(d.steps + kPrefetch) * 64 * d.ot;
+}
 
 struct PackedOffsets {
   // actor block (contiguous, staged into LDS by the rollout kernel)
@@ -39,20 +57,20 @@ __host__ __device__ constexpr PackedOffsets packed_offsets() {
   int64_t off = 0;
   for (int l = 0; l < 3; ++l) {
     p.actor_w[l] = off;
-    off = align64(off + packed_floats(kActor[l].steps, kActor[l].out));
+    off = align64(off + packed_layer_floats(kActor[l]));
   }
   for (int l = 0; l < 3; ++l) {
     p.actor_b[l] = off;
-    off = align64(off + 16 * out_tiles(kActor[l].out));
+    off = align64(off + 16 * kActor[l].ot);
   }
   p.actor_end = off;
   for (int l = 0; l < 5; ++l) {
     p.critic_w[l] = off;
-    off = align64(off + packed_floats(kCritic[l].steps, kCritic[l].out));
+    off = align64(off + packed_layer_floats(kCritic[l]));
   }
   for (int l = 0; l < 5; ++l) {
     p.critic_b[l] = off;
-    off = align64(off + 16 * out_tiles(kCritic[l].out));
+    off = align64(off + 16 * kCritic[l].ot);
   }
   p.critic_w6 = off;
   off = align64(off + 64);
@@ -60,11 +78,11 @@ __host__ __device__ constexpr PackedOffsets packed_offsets() {
   off = align64(off + 1);
   for (int l = 0; l < 2; ++l) {
     p.cur_w[l] = off;
-    off = align64(off + packed_floats(kCur[l].steps, kCur[l].out));
+    off = align64(off + packed_layer_floats(kCur[l]));
   }
   for (int l = 0; l < 2; ++l) {
     p.cur_b[l] = off;
-    off = align64(off + 16 * out_tiles(kCur[l].out));
+    off = align64(off + 16 * kCur[l].ot);
   }
   p.cur_onehot = off;
   off = align64(off + 45 * 128);
@@ -91,56 +109,76 @@ __device__ __forceinline__ float cost_of(const EnvParams& p, int o) {
   return o == 0 ? p.cost0 : (o == 1 ? p.cost1 : p.cost2);
 }
 
+// OTW consecutive floats of a lane's packed block (OTW in 1, 2, 4, 6, 8).
+template <int OTW>
+__device__ __forceinline__ void load_operands(const float* p, float (&a)[OTW]) {
+  if constexpr (OTW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < OTW; i += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p + i);
+      a[i] = v[0]; a[i + 1] = v[1]; a[i + 2] = v[2]; a[i + 3] = v[3];
+    }
+  } else if constexpr (OTW % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < OTW; i += 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p + i);
+      a[i] = v.x; a[i + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < OTW; ++i) a[i] = p[i];
+  }
+}
+
 // ---------------------------------------------------------------------------
-// One MFMA layer for the 16 rows of a wave: acc[ot] = bias + W x, where the
-// lane's B operands for k-steps 4*kt .. 4*kt+3 sit in its own LDS slot
-// act[kt*64 + lane] (a float4).  Those slots are written by the same lane
-// (its D registers of the previous layer, or its state inputs), so the
-// buffer is lane-private and needs no barrier.  Weights are read with one
-// 16-byte load per 4 MFMAs and prefetched one k-step ahead.
+// This wave's share of one layer for the 16 rows of its row group:
+// acc[i] = bias + W x for output tile q*OTW + i.  The B operands of k-steps
+// 4*kt .. 4*kt+3 of lane l sit in buf[kt*64 + l], written by lane l of the
+// producing waves (the MFMA output layout of lane l is the next layer's
+// input layout of lane l).  Software pipeline: the weights of k-step s+3 are
+// loaded before the MFMAs of step s, into a 4-slot ring indexed by s % 4;
+// scheduling barriers keep that order (the compiler would otherwise move
+// each load next to its use), so three steps of loads are always in flight.
+// Addresses are a wave-uniform base plus one 32-bit lane offset.
 // ---------------------------------------------------------------------------
-template <int S, int OT>
-__device__ __forceinline__ void mfma_layer(const f32x4* __restrict__ pk, const float* __restrict__ pb,
-                                           const f32x4* act, f32x4 (&acc)[OT], int lane) {
-  constexpr int OG = (OT + 3) / 4;
+template <int S, int OTW>
+__device__ __forceinline__ void mfma_layer(const float* __restrict__ pk, const float* __restrict__ pb,
+                                           const f32x4* buf, f32x4 (&acc)[OTW], int q, int lane) {
+  static_assert(kPrefetch == 3, "the ring below holds kPrefetch + 1 = 4 steps");
   constexpr int KT = (S + 3) / 4;
+  constexpr int kStep = kSplit * 64 * OTW;  // floats per k-step
   const int g = lane >> 4;
+  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
 #pragma unroll
-  for (int ot = 0; ot < OT; ++ot) acc[ot] = *reinterpret_cast<const f32x4*>(pb + 16 * ot + 4 * g);
-  const f32x4* w = pk + lane;
-  f32x4 a_cur[OG], a_nxt[OG];
+  for (int i = 0; i < OTW; ++i)
+    acc[i] = *reinterpret_cast<const f32x4*>(pb + 16 * (q * OTW + i) + 4 * g);
+  float a[4][OTW];
 #pragma unroll
-  for (int og = 0; og < OG; ++og) a_cur[og] = w[og * 64];
+  for (int j = 0; j < 3; ++j) load_operands<OTW>(pk + j * kStep + lane_off, a[j]);
 #pragma unroll 1
   for (int kt = 0; kt < KT; ++kt) {
-    const f32x4 b = act[kt * 64 + lane];
+    const float* wk = pk + (4 * kt + 3) * kStep;  // step s + 3 of r = 0
+    const f32x4 b = buf[kt * 64 + lane];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int s = 4 * kt + r;
-      const int sn = (s + 1 < S) ? s + 1 : s;
+      load_operands<OTW>(wk + r * kStep + lane_off, a[(r + 3) & 3]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int og = 0; og < OG; ++og) a_nxt[og] = w[(sn * OG + og) * 64];
-#pragma unroll
-      for (int og = 0; og < OG; ++og) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (4 * og + c < OT) acc[4 * og + c] = mfma4(a_cur[og][c], b[r], acc[4 * og + c]);
-      }
-#pragma unroll
-      for (int og = 0; og < OG; ++og) a_cur[og] = a_nxt[og];
+      for (int i = 0; i < OTW; ++i) acc[i] = mfma4(a[r][i], b[r], acc[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-// ReLU the accumulators into the lane's LDS slots (next layer's B operands).
-template <int OT>
-__device__ __forceinline__ void relu_store(const f32x4 (&acc)[OT], f32x4* act, int lane) {
+// ReLU this wave's accumulators into its tiles of the shared buffer.
+template <int OTW>
+__device__ __forceinline__ void relu_store(const f32x4 (&acc)[OTW], f32x4* buf, int q, int lane) {
 #pragma unroll
-  for (int ot = 0; ot < OT; ++ot) {
-    f32x4 v = acc[ot];
+  for (int i = 0; i < OTW; ++i) {
+    f32x4 v = acc[i];
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = fmaxf(v[r], 0.0f);
-    act[ot * 64 + lane] = v;
+    buf[(q * OTW + i) * 64 + lane] = v;
   }
 }
 

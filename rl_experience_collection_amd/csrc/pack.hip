@@ -1,5 +1,5 @@
 // Weight repacking: caller-layout [out, in] fp32 tensors -> the MFMA operand
-// order of nets.hpp.  Runs on the device, stream-ordered, at create and at
+// order of nets.hpp (per k-step, one contiguous block per cooperating wave).  Runs on the device, stream-ordered, at create and at
 // every weight update.
 #include "pack.hpp"
 
@@ -7,31 +7,29 @@ namespace rl {
 
 namespace {
 
-// One thread per packed float: pk[((s*OG + og)*64 + lane)*4 + c].
+// One thread per packed float: pk[((s*kSplit + q)*64 + lane)*OTW + i].
 __global__ void pack_layer_kernel(const float* __restrict__ W, int in, int ld, int out, int steps,
-                                  int first, float* __restrict__ pk) {
-  const int og_n = out_groups(out);
-  const int64_t total = (int64_t)steps * og_n * 256;
+                                  int first, int otw, float* __restrict__ pk) {
+  const int64_t total = (int64_t)steps * kSplit * 64 * otw;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int c = (int)(idx & 3);
-  const int lane = (int)((idx >> 2) & 63);
-  const int64_t rest = idx >> 8;
-  const int og = (int)(rest % og_n);
-  const int s = (int)(rest / og_n);
-  const int o = 16 * (4 * og + c) + (lane & 15);
+  const int i = (int)(idx % otw);
+  const int lane = (int)((idx / otw) % 64);
+  const int q = (int)((idx / ((int64_t)otw * 64)) % kSplit);
+  const int s = (int)(idx / ((int64_t)otw * 64 * kSplit));
+  const int o = 16 * (q * otw + i) + (lane & 15);
   const int g = lane >> 4;
-  int i;
+  int k;
   bool ok;
   if (first) {
-    i = kFirstSteps * g + s;
+    k = kFirstSteps * g + s;
     ok = s < kFirstSteps;
   } else {
-    i = 16 * (s >> 2) + 4 * g + (s & 3);
+    k = 16 * (s >> 2) + 4 * g + (s & 3);
     ok = true;
   }
-  ok = ok && o < out && i < in;
-  pk[idx] = ok ? W[(int64_t)o * ld + i] : 0.0f;
+  ok = ok && o < out && k < in;
+  pk[idx] = ok ? W[(int64_t)o * ld + k] : 0.0f;
 }
 
 __global__ void pack_bias_kernel(const float* __restrict__ b, int out, int padded,
@@ -54,14 +52,15 @@ __global__ void copy_kernel(const float* __restrict__ src, int n, float* __restr
 }
 
 hipError_t pack_layer(const float* W, const LayerDesc& d, int ld, float* pk, hipStream_t st) {
-  const int64_t total = (int64_t)packed_floats(d.steps, d.out);
+  const int64_t total = packed_layer_floats(d);
   hipLaunchKernelGGL(pack_layer_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, W,
-                     d.in, ld, d.out, d.steps, d.first, pk);
+                     d.in, ld, d.out, d.steps, d.first, d.ot / kSplit, pk);
   return hipGetLastError();
 }
 
-hipError_t pack_bias(const float* b, int out, float* pb, hipStream_t st) {
-  const int padded = 16 * out_tiles(out);
+hipError_t pack_bias(const float* b, const LayerDesc& d, float* pb, hipStream_t st) {
+  const int out = d.out;
+  const int padded = 16 * d.ot;
   hipLaunchKernelGGL(pack_bias_kernel, dim3((padded + 255) / 256), dim3(256), 0, st, b, out, padded,
                      pb);
   return hipGetLastError();
@@ -80,20 +79,20 @@ hipError_t pack_weights(const float* const actor[6], const float* const critic[1
   } while (0)
   for (int l = 0; l < 3; ++l) {
     RL_TRY(pack_layer(actor[2 * l], kActor[l], kActor[l].in, block + P.actor_w[l], st));
-    RL_TRY(pack_bias(actor[2 * l + 1], kActor[l].out, block + P.actor_b[l], st));
+    RL_TRY(pack_bias(actor[2 * l + 1], kActor[l], block + P.actor_b[l], st));
   }
   for (int l = 0; l < 5; ++l) {
     RL_TRY(pack_layer(critic[2 * l], kCritic[l], kCritic[l].in, block + P.critic_w[l], st));
-    RL_TRY(pack_bias(critic[2 * l + 1], kCritic[l].out, block + P.critic_b[l], st));
+    RL_TRY(pack_bias(critic[2 * l + 1], kCritic[l], block + P.critic_b[l], st));
   }
   hipLaunchKernelGGL(copy_kernel, dim3(1), dim3(64), 0, st, critic[10], 64, block + P.critic_w6);
   RL_TRY(hipGetLastError());
   hipLaunchKernelGGL(copy_kernel, dim3(1), dim3(64), 0, st, critic[11], 1, block + P.critic_b6);
   RL_TRY(hipGetLastError());
   RL_TRY(pack_layer(cur[0], kCur[0], kState + kActions, block + P.cur_w[0], st));
-  RL_TRY(pack_bias(cur[1], kCur[0].out, block + P.cur_b[0], st));
+  RL_TRY(pack_bias(cur[1], kCur[0], block + P.cur_b[0], st));
   RL_TRY(pack_layer(cur[2], kCur[1], kCur[1].in, block + P.cur_w[1], st));
-  RL_TRY(pack_bias(cur[3], kCur[1].out, block + P.cur_b[1], st));
+  RL_TRY(pack_bias(cur[3], kCur[1], block + P.cur_b[1], st));
   hipLaunchKernelGGL(pack_onehot_kernel, dim3((kActions * 128 + 255) / 256), dim3(256), 0, st, cur[0],
                      block + P.cur_onehot);
   RL_TRY(hipGetLastError());

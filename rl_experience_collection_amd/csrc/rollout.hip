@@ -1,7 +1,8 @@
 // Sequential part of PPO experience collection (PPO CUDA Pipeline Design,
 // Kernel Phases, Phase A): the chain that each step's state depends on.
 //
-// A wave owns 16 episodes for all L steps.  Per step it
+// Four waves own 16 episodes for all L steps, each computing a quarter of
+// every actor layer's outputs (activations shared through LDS).  Per step
 //   - assembles the 54-wide state (51 features of the bar, V/V0 - 1, the
 //     exposure held, the spread) and stores it (steps 1-2, 11),
 //   - runs the actor 54 -> 128 -> 64 -> 45 on MFMA with the packed actor
@@ -17,9 +18,10 @@
 // in one batched pass over every stored state.
 //
 // MFMA output layout: lane l holds logits 16*ot + 4*(l/16) + r of episode
-// l%16, so each episode's 45 logits sit in the 4 lanes l%16 + 16*g.  All
-// per-episode scalars (draw, portfolio, barrier, window) are computed
-// redundantly by those 4 lanes.
+// l%16, so each episode's 45 logits sit in the 4 lanes l%16 + 16*g once the
+// three logit tiles are gathered from LDS.  All per-episode scalars (draw,
+// portfolio, barrier, window) are computed redundantly by those 4 lanes in
+// each of the 4 waves, so no broadcast is needed; wave 0 stores.
 #include "collect.hpp"
 
 #include <math.h>
@@ -30,7 +32,7 @@ namespace {
 
 constexpr PackedOffsets kP = packed_offsets();
 constexpr int kActorF4 = (int)(kP.actor_end / 4);
-constexpr int kActF4PerWave = 8 * 64;  // widest actor activation: 128 = 8 tiles
+constexpr int kBufF4 = 8 * 64;  // widest actor activation: 128 = 8 tiles
 
 __device__ __forceinline__ void load_features(const float* __restrict__ F, int64_t bar, int g,
                                               float (&f)[kFirstSteps]) {
@@ -39,24 +41,27 @@ __device__ __forceinline__ void load_features(const float* __restrict__ F, int64
   for (int s = 0; s < kFirstSteps; ++s) f[s] = (kFirstSteps * g + s < kFeatures) ? row[s] : 0.0f;
 }
 
-template <int WPG>
-__global__ __launch_bounds__(64 * WPG) void actor_rollout_kernel(RolloutArgs a) {
+template <int RG>
+__global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(RolloutArgs a) {
   __shared__ f32x4 s_w[kActorF4];
-  __shared__ f32x4 s_act[WPG][kActF4PerWave];
+  __shared__ f32x4 s_buf[RG][kBufF4];
+  __shared__ f32x4 s_state[RG][4 * 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int rg = wave / kSplit;
+  const int q = wave % kSplit;
   const int g = lane >> 4;
 
   {  // stage the packed actor into LDS
     const f32x4* src = reinterpret_cast<const f32x4*>(a.weights);
-    for (int i = threadIdx.x; i < kActorF4; i += 64 * WPG) s_w[i] = src[i];
+    for (int i = threadIdx.x; i < kActorF4; i += 64 * kSplit * RG) s_w[i] = src[i];
   }
-  __syncthreads();
 
-  const int32_t n_raw = (blockIdx.x * WPG + wave) * kRowsPerWave + (lane & 15);
+  const int32_t n_raw = (blockIdx.x * RG + rg) * kRowsPerWave + (lane & 15);
   const bool valid = n_raw < a.N;
   const int32_t n = valid ? n_raw : a.N - 1;
+  const bool writer = valid && q == 0;
   const EnvParams& ep = a.ep;
 
   // clamp the start so every read stays inside the market buffers
@@ -64,30 +69,27 @@ __global__ __launch_bounds__(64 * WPG) void actor_rollout_kernel(RolloutArgs a) 
   int64_t st = a.starts[n];
   const bool clamped = st < 0 || st > hi;
   st = st < 0 ? 0 : (st > hi ? hi : st);
-  if (valid && g == 0) {
+  if (writer && g == 0) {
     a.start_used[n] = (int32_t)st;
     if (clamped && a.counters) atomicAdd(a.counters + 1, 1u);
   }
 
   const float* sw = reinterpret_cast<const float*>(s_w);
-  const f32x4* w1 = s_w + kP.actor_w[0] / 4;
-  const f32x4* w2 = s_w + kP.actor_w[1] / 4;
-  const f32x4* w3 = s_w + kP.actor_w[2] / 4;
-  const float* b1 = sw + kP.actor_b[0];
-  const float* b2 = sw + kP.actor_b[1];
-  const float* b3 = sw + kP.actor_b[2];
-  f32x4* act = s_act[wave];
+  f32x4* buf = s_buf[rg];
+  f32x4* sbuf = s_state[rg];
 
   float fcur[kFirstSteps];
   load_features(a.features, st, g, fcur);
   float p0 = a.prices[st], p1 = a.prices[st + 1];
 
-  // episode state (PPO CUDA Pipeline Design, Phase A steps 6-8, 12)
+  // episode state (PPO CUDA Pipeline Design, Phase A steps 6-8, 12), held
+  // identically by the 4 lanes of the episode in each of the 4 waves
   float V = 1.0f, e_prev = 0.0f, entry = 0.0f;
   int armed = 0, side = 0, t_open = 0;
   int cnt0 = 0, cnt1 = 0, cnt2 = 0, pushed = 0;
   uint64_t ring = 0;  // 2 bits per window slot
   const float V0 = 1.0f;
+  __syncthreads();  // weights staged
 
   for (int32_t t = 0; t < a.L; ++t) {
     const int64_t bar = st + t;
@@ -106,17 +108,19 @@ __global__ __launch_bounds__(64 * WPG) void actor_rollout_kernel(RolloutArgs a) 
     }
     B[14] = 0.0f;
     B[15] = 0.0f;
+    if (q == 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 v;
-      v[0] = B[4 * q]; v[1] = B[4 * q + 1]; v[2] = B[4 * q + 2]; v[3] = B[4 * q + 3];
-      act[q * 64 + lane] = v;
-    }
-    if (valid) {
-      float* srow = a.states + o * kState + kFirstSteps * g;
+      for (int k4 = 0; k4 < 4; ++k4) {
+        f32x4 v;
+        v[0] = B[4 * k4]; v[1] = B[4 * k4 + 1]; v[2] = B[4 * k4 + 2]; v[3] = B[4 * k4 + 3];
+        sbuf[k4 * 64 + lane] = v;
+      }
+      if (valid) {
+        float* srow = a.states + o * kState + kFirstSteps * g;
 #pragma unroll
-      for (int s = 0; s < kFirstSteps; ++s)
-        if (kFirstSteps * g + s < kState) srow[s] = B[s];
+        for (int s = 0; s < kFirstSteps; ++s)
+          if (kFirstSteps * g + s < kState) srow[s] = B[s];
+      }
     }
 
     // prefetch the next bar (independent of this step's outcome)
@@ -125,35 +129,49 @@ __global__ __launch_bounds__(64 * WPG) void actor_rollout_kernel(RolloutArgs a) 
     if (t + 1 < a.L) {
       load_features(a.features, bar + 1, g, fnext);
       p2 = a.prices[bar + 2];
+    } else {
+#pragma unroll
+      for (int s = 0; s < kFirstSteps; ++s) fnext[s] = fcur[s];
     }
+    __syncthreads();  // state operands written
 
-    // ---- step 3: actor --------------------------------------------------
+    // ---- step 3: actor, a quarter of each layer per wave ------------------
     {
-      f32x4 h[8];
-      mfma_layer<16, 8>(w1, b1, act, h, lane);
-      relu_store<8>(h, act, lane);
+      f32x4 h[2];
+      mfma_layer<16, 2>(sw + kP.actor_w[0], sw + kP.actor_b[0], sbuf, h, q, lane);
+      relu_store<2>(h, buf, q, lane);  // buf is free: last read before the previous barrier
     }
+    __syncthreads();
     {
-      f32x4 h[4];
-      mfma_layer<32, 4>(w2, b2, act, h, lane);
-      relu_store<4>(h, act, lane);
+      f32x4 h[1];
+      mfma_layer<32, 1>(sw + kP.actor_w[1], sw + kP.actor_b[1], buf, h, q, lane);
+      __syncthreads();
+      relu_store<1>(h, buf, q, lane);
     }
-    f32x4 lg[3];
-    mfma_layer<16, 3>(w3, b3, act, lg, lane);
+    __syncthreads();
+    {
+      f32x4 h[1];
+      mfma_layer<16, 1>(sw + kP.actor_w[2], sw + kP.actor_b[2], buf, h, q, lane);
+      __syncthreads();
+      buf[q * 64 + lane] = h[0];  // raw logits (tile 3 is padding)
+    }
+    __syncthreads();
 
-    // ---- step 4: softmax, CDF, inverse-CDF draw, log-prob -------------------
+    // ---- step 4: softmax, CDF, inverse-CDF draw, log-prob (every wave) ----
     float l[12], e[12];
     bool ok[12];
     int bad = 0;
 #pragma unroll
-    for (int ot = 0; ot < 3; ++ot)
+    for (int ot = 0; ot < 3; ++ot) {
+      const f32x4 lv = buf[ot * 64 + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * ot + r;
         ok[i] = 16 * ot + 4 * g + r < kActions;
-        l[i] = lg[ot][r];
+        l[i] = lv[r];
         if (ok[i] && !isfinite(l[i])) bad = 1;
       }
+    }
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 12; ++i)
@@ -273,7 +291,7 @@ __global__ __launch_bounds__(64 * WPG) void actor_rollout_kernel(RolloutArgs a) 
     // ---- steps 10-11: partial reward and stores ----------------------------
     const float partial = pnl * (1.0f + ep.barrier_scale * (float)hit) + div;
     const int done = code != 0;
-    if (valid) {
+    if (writer) {
       if (g == 0) {
         a.actions[o] = act_a;
         a.log_probs[o] = logp;
@@ -313,10 +331,15 @@ __global__ __launch_bounds__(64 * WPG) void actor_rollout_kernel(RolloutArgs a) 
 
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
   if (a.N <= 0 || a.L <= 0) return hipSuccess;
-  constexpr int WPG = 2;
-  const int per_block = WPG * kRowsPerWave;
-  const unsigned blocks = (unsigned)((a.N + per_block - 1) / per_block);
-  hipLaunchKernelGGL((actor_rollout_kernel<WPG>), dim3(blocks), dim3(64 * WPG), 0, st, a);
+  // two 16-episode groups per workgroup once there are enough episodes to
+  // fill every CU with one workgroup; otherwise one group, spread wider
+  if (a.N >= 2 * 16 * 256) {
+    const unsigned blocks = (unsigned)((a.N + 31) / 32);
+    hipLaunchKernelGGL((actor_rollout_kernel<2>), dim3(blocks), dim3(64 * kSplit * 2), 0, st, a);
+  } else {
+    const unsigned blocks = (unsigned)((a.N + 15) / 16);
+    hipLaunchKernelGGL((actor_rollout_kernel<1>), dim3(blocks), dim3(64 * kSplit), 0, st, a);
+  }
   return hipGetLastError();
 }
 
