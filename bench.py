@@ -196,6 +196,9 @@ def main():
     achieved = VALUE_KERNEL_FLOP * N * L / (t_val * 1e-3)
     roofline = dict(bound="mfma", achieved=achieved / 1e12, peak=PEAK_FP32_MFMA / 1e12,
                     unit="TFLOP/s", frac=achieved / PEAK_FP32_MFMA, traffic=traffic,
+                    traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                 "copy-calibrated; null if the kernel changed since)",
+                    algorithmic_bytes_per_launch=4096000 * 436,
                     kernel="value_kernel (critic + curiosity, fp32 MFMA 16x16x4)",
                     flop_per_launch=VALUE_KERNEL_FLOP * N * L, avg_launch_ms=t_val)
     mlp_util = MLP_FLOP * N * L / ((t_roll + t_val) * 1e-3) / PEAK_FP32_MFMA

@@ -26,7 +26,10 @@ namespace rl {
 namespace {
 
 constexpr PackedOffsets kP = packed_offsets();
-constexpr int kRowGroups = 2;
+#ifndef RL_VALUE_ROW_GROUPS
+#define RL_VALUE_ROW_GROUPS 2
+#endif
+constexpr int kRowGroups = RL_VALUE_ROW_GROUPS;
 constexpr int kThreads = 64 * kSplit * kRowGroups;
 constexpr int kBufF4 = 32 * 64;  // widest activation: 512 = 32 tiles of 16
 
