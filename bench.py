@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA = 157.3e12   # MI355X dense fp32 matrix, FLOP/s
+PEAK_BF16_MFMA = 2.5e15     # MI355X dense bf16 matrix, FLOP/s
 PEAK_HBM = 8.0e12           # MI355X HBM3E, B/s
 METRIC = "experiences/sec at N=128,L=500 and N=8192; MFMA util %; GAE scan HBM GB/s"
 
@@ -161,7 +162,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-episodes", type=int, default=256)
+    ap.add_argument("--cpu-episodes", type=int, default=2560)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -184,6 +185,8 @@ def main():
     ms = big["wall_s"] * 1000 / args.steps
     exps = N * L * args.steps / big["wall_s"]
     t_roll, t_val, t_gae = big["phases_ms"]
+    log("timing N=8192 L=500 bf16 ...")
+    bfr = time_collect(big_inp, args.steps, args.warmup, precision=1)
     log("timing N=128 L=500 fp32 ...")
     small = time_collect(synthdata.ppo_inputs("ppo_n128_l500"), args.steps, args.warmup)
     log("timing GAE N=4096 L=2048 ...")
@@ -216,6 +219,14 @@ def main():
         gae_in_collect_GBps=gae_in / 1e9,
         nonfinite_events=big["nonfinite"],
         also=dict(
+            ppo_collect_n8192_l500_bf16=dict(
+                value=N * L * args.steps / bfr["wall_s"], unit="experiences/s",
+                ms_per_step=bfr["wall_s"] * 1000 / args.steps,
+                phases_ms=dict(zip(("actor_rollout", "value_critic_curiosity", "gae_scan"),
+                                   map(float, bfr["phases_ms"]))),
+                value_kernel_TFLOPs=VALUE_KERNEL_FLOP * N * L / (bfr["phases_ms"][1] * 1e-3) / 1e12,
+                value_kernel_frac_of_bf16_peak=VALUE_KERNEL_FLOP * N * L /
+                (bfr["phases_ms"][1] * 1e-3) / PEAK_BF16_MFMA),
             ppo_collect_n128_l500_fp32=dict(
                 value=128 * 500 * args.steps / small["wall_s"], unit="experiences/s",
                 ms_per_step=small["wall_s"] * 1000 / args.steps,

@@ -164,7 +164,6 @@ int check_config(const rollout_config* c) {
     if (c->cur_dims[i] != kCurDims[i]) return fail(ROLLOUT_EINVAL, "curiosity dims must be 99,128,51");
   if (c->precision != ROLLOUT_FP32 && c->precision != ROLLOUT_BF16)
     return fail(ROLLOUT_EINVAL, "unknown precision %d", c->precision);
-  if (c->precision == ROLLOUT_BF16) return fail(ROLLOUT_ENOTIMPL, "bf16 collection is not built yet");
   if (c->div_window < 1 || c->div_window > 32)
     return fail(ROLLOUT_EINVAL, "div_window must be in 1..32 (got %d)", c->div_window);
   if (c->max_hold < 1) return fail(ROLLOUT_EINVAL, "max_hold must be >= 1");
@@ -338,6 +337,7 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   ra.barrier = out->barrier;
   ra.logits = out->logits;
   ra.counters = out->counters;
+  ra.bf16 = h->cfg.precision == ROLLOUT_BF16;
   RL_HIP(rl::launch_actor_rollout(ra, st), "actor rollout launch");
   RL_HIP(mark(1), "hipEventRecord(phase 1)");
 
@@ -353,6 +353,7 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   va.values = out->values;
   va.rewards = out->rewards;
   va.counters = out->counters;
+  va.bf16 = h->cfg.precision == ROLLOUT_BF16;
   RL_HIP(rl::launch_value(va, st), "value launch");
   RL_HIP(mark(2), "hipEventRecord(phase 2)");
 

@@ -28,6 +28,7 @@ struct RolloutArgs {
   uint8_t* barrier;       // [L][N]
   float* logits;          // [L][N][45] or null
   uint32_t* counters;     // [2] or null
+  int bf16;               // bf16 weights and layer inputs, fp32 accumulation
 };
 
 // Batched part: critic value and curiosity bonus of every stored (t, n),
@@ -43,6 +44,7 @@ struct ValueArgs {
   float* values;
   float* rewards;  // in: partial reward, out: full reward
   uint32_t* counters;
+  int bf16;
 };
 
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st);

@@ -9,6 +9,7 @@
 namespace rl {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kFeatures = 51;
 constexpr int kState = 54;
@@ -52,6 +53,24 @@ __device__ __forceinline__ float draw_uniform(uint64_t seed, uint32_t episode, u
 // --------------------------------------------------------------------------
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8*(l/16) + j] and
+// B[8*(l/16) + j][l%16] for j = 0..7; D as for the fp32 form.
+__device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 with round-to-nearest-even (the hardware conversion).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float bf16_round(float x) {
+  return __builtin_bit_cast(float, bf16_bits(x) << 16);
 }
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }

@@ -35,18 +35,40 @@ constexpr LayerDesc kCritic[5] = {{54, 512, 16, 1, 32},
 // Curiosity forward model: 54 dense inputs (+45 one-hot, gathered) -> 128 -> 51.
 constexpr LayerDesc kCur[2] = {{54, 128, 16, 1, 8}, {128, 51, 32, 0, 4}};
 
+// bf16 forms (v_mfma_f32_16x16x32_bf16): a k-step covers 32 inputs, 8 per
+// lane group.  First layers: kperm(s, g, j) = 32 s + 8 g + j (54 -> 2 steps).
+// Chained layers: kperm(s, g, j) = 16 (2 s + j / 4) + 4 g + j % 4, i.e. the
+// output tiles 2s and 2s+1 of the previous layer form k-step s.
+constexpr LayerDesc kActorB[3] = {{54, 128, 2, 1, 8}, {128, 64, 4, 0, 4}, {64, 45, 2, 0, 4}};
+constexpr LayerDesc kCriticB[5] = {{54, 512, 2, 1, 32},
+                                   {512, 384, 16, 0, 24},
+                                   {384, 256, 12, 0, 16},
+                                   {256, 128, 8, 0, 8},
+                                   {128, 64, 4, 0, 4}};
+constexpr LayerDesc kCurB[2] = {{54, 128, 2, 1, 8}, {128, 51, 4, 0, 4}};
+
 // Packed weights of a layer, plus kPrefetch zero k-steps so the prefetch of
 // the layer's last steps reads inside the block.
 constexpr int kPrefetch = 3;
 __host__ __device__ constexpr int64_t packed_layer_floats(const LayerDesc& d) {
   return (int64_t)(d.steps + kPrefetch) * 64 * d.ot;
 }
+// bf16 layer: 8 bf16 (16 bytes, 4 float slots) per lane, tile and k-step.
+__host__ __device__ constexpr int64_t packed_layer_floats_bf16(const LayerDesc& d) {
+  return (int64_t)(d.steps + kPrefetch) * 64 * d.ot * 4;
+}
 
 struct PackedOffsets {
-  // actor block (contiguous, staged into LDS by the rollout kernel)
+  // fp32 actor block (contiguous, staged into LDS by the rollout kernel)
   int64_t actor_w[3], actor_b[3], actor_end;
   int64_t critic_w[5], critic_b[5], critic_w6, critic_b6;
   int64_t cur_w[2], cur_b[2], cur_onehot;
+  // bf16 forms: a contiguous actor block [bact_begin, bact_end) with its own
+  // copy of the biases, the bf16 critic and curiosity layers (biases shared
+  // with the fp32 block), and bf16-rounded copies (as fp32) of the critic's
+  // 64 -> 1 row and of the curiosity one-hot columns
+  int64_t bact_begin, bact_w[3], bact_b[3], bact_end;
+  int64_t bcritic_w[5], bcur_w[2], bcritic_w6, bcur_onehot;
   int64_t total;
 };
 
@@ -86,8 +108,38 @@ __host__ __device__ constexpr PackedOffsets packed_offsets() {
   }
   p.cur_onehot = off;
   off = align64(off + 45 * 128);
+  p.bact_begin = off;
+  for (int l = 0; l < 3; ++l) {
+    p.bact_w[l] = off;
+    off = align64(off + packed_layer_floats_bf16(kActorB[l]));
+  }
+  for (int l = 0; l < 3; ++l) {
+    p.bact_b[l] = off;
+    off = align64(off + 16 * kActorB[l].ot);
+  }
+  p.bact_end = off;
+  for (int l = 0; l < 5; ++l) {
+    p.bcritic_w[l] = off;
+    off = align64(off + packed_layer_floats_bf16(kCriticB[l]));
+  }
+  for (int l = 0; l < 2; ++l) {
+    p.bcur_w[l] = off;
+    off = align64(off + packed_layer_floats_bf16(kCurB[l]));
+  }
+  p.bcritic_w6 = off;
+  off = align64(off + 64);
+  p.bcur_onehot = off;
+  off = align64(off + 45 * 128);
   p.total = off;
   return p;
+}
+
+// State element held by lane group g at first-layer k-step slot s (16 slots
+// per lane): fp32 form k = 14 g + s (s < 14), bf16 form k = 32 (s / 8) + 8 g
+// + s % 8.  Values for k >= 54 are zero.
+template <bool BF16>
+__host__ __device__ constexpr int state_k(int g, int s) {
+  return BF16 ? 32 * (s / 8) + 8 * g + (s % 8) : (s < 14 ? 14 * g + s : 1 << 20);
 }
 
 // Scalar constants of the environment step, computed once on the host.
@@ -179,6 +231,97 @@ __device__ __forceinline__ void relu_store(const f32x4 (&acc)[OTW], f32x4* buf, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = fmaxf(v[r], 0.0f);
     buf[(q * OTW + i) * 64 + lane] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 form of mfma_layer: k-step s consumes 8 bf16 B operands per lane from
+// bufb[s*64 + l] and 8 bf16 weights per output tile; accumulation is fp32.
+// The same 4-slot prefetch ring as the fp32 form.
+// ---------------------------------------------------------------------------
+template <int S, int OTW>
+__device__ __forceinline__ void mfma_layer_bf16(const uint4* __restrict__ pk,
+                                                const float* __restrict__ pb, const uint4* bufb,
+                                                f32x4 (&acc)[OTW], int q, int lane) {
+  static_assert(kPrefetch == 3, "the ring below holds kPrefetch + 1 = 4 steps");
+  constexpr int KT = S / 4;
+  constexpr int TAIL = S % 4;
+  constexpr int kStep = kSplit * 64 * OTW;  // uint4 per k-step
+  const int g = lane >> 4;
+  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
+#pragma unroll
+  for (int i = 0; i < OTW; ++i)
+    acc[i] = *reinterpret_cast<const f32x4*>(pb + 16 * (q * OTW + i) + 4 * g);
+  uint4 a[4][OTW];
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int i = 0; i < OTW; ++i) a[j][i] = pk[j * kStep + lane_off + i];
+#pragma unroll 1
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint4* wk = pk + (4 * kt + 3) * kStep;
+    uint4 b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = bufb[(4 * kt + r) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) a[(r + 3) & 3][i] = wk[r * kStep + lane_off + i];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) acc[i] = mfma_bf16(a[r][i], b[r], acc[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // remaining steps (S % 4): their operands are already in slots 0 .. TAIL-1
+#pragma unroll
+  for (int r = 0; r < TAIL; ++r) {
+    const uint4 b = bufb[(4 * KT + r) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < OTW; ++i) acc[i] = mfma_bf16(a[r][i], b, acc[i]);
+  }
+}
+
+// ReLU, round to bf16 and store this wave's tiles as the next layer's k-step
+// operands: tile t lands in half t % 2 of k-step t / 2.
+template <int OTW>
+__device__ __forceinline__ void relu_store_bf16(const f32x4 (&acc)[OTW], uint4* bufb, int q,
+                                                int lane) {
+  uint2* half = reinterpret_cast<uint2*>(bufb);
+#pragma unroll
+  for (int i = 0; i < OTW; ++i) {
+    const int t = q * OTW + i;
+    const f32x4 v = acc[i];
+    uint2 w;
+    w.x = pack_bf16x2(fmaxf(v[0], 0.0f), fmaxf(v[1], 0.0f));
+    w.y = pack_bf16x2(fmaxf(v[2], 0.0f), fmaxf(v[3], 0.0f));
+    half[((t >> 1) * 64 + lane) * 2 + (t & 1)] = w;
+  }
+}
+
+// The 16 first-layer operands of a lane (state_k order) as LDS operands:
+// fp32: four float4 (k-steps 4 q4 .. 4 q4 + 3); bf16: two k-steps of 8.
+template <bool BF16>
+__device__ __forceinline__ void store_state_operands(const float (&B)[16], void* buf, int lane) {
+  if constexpr (BF16) {
+    uint4* b = reinterpret_cast<uint4*>(buf);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint4 w;
+      w.x = pack_bf16x2(B[8 * s + 0], B[8 * s + 1]);
+      w.y = pack_bf16x2(B[8 * s + 2], B[8 * s + 3]);
+      w.z = pack_bf16x2(B[8 * s + 4], B[8 * s + 5]);
+      w.w = pack_bf16x2(B[8 * s + 6], B[8 * s + 7]);
+      b[s * 64 + lane] = w;
+    }
+  } else {
+    f32x4* b = reinterpret_cast<f32x4*>(buf);
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      f32x4 v;
+      v[0] = B[4 * k4]; v[1] = B[4 * k4 + 1]; v[2] = B[4 * k4 + 2]; v[3] = B[4 * k4 + 3];
+      b[k4 * 64 + lane] = v;
+    }
   }
 }
 

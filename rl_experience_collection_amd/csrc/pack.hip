@@ -10,7 +10,7 @@ namespace {
 // One thread per packed float: pk[((s*kSplit + q)*64 + lane)*OTW + i].
 __global__ void pack_layer_kernel(const float* __restrict__ W, int in, int ld, int out, int steps,
                                   int first, int otw, float* __restrict__ pk) {
-  const int64_t total = (int64_t)steps * kSplit * 64 * otw;
+  const int64_t total = (int64_t)(steps + kPrefetch) * kSplit * 64 * otw;  // incl. zero padding
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int i = (int)(idx % otw);
@@ -30,6 +30,38 @@ __global__ void pack_layer_kernel(const float* __restrict__ W, int in, int ld, i
   }
   ok = ok && o < out && k < in;
   pk[idx] = ok ? W[(int64_t)o * ld + k] : 0.0f;
+}
+
+// bf16 form: pk[(((s*kSplit + q)*64 + lane)*OTW + i)*8 + j], 8 bf16 per
+// (k-step, lane, tile), k = kperm(s, lane / 16, j) of nets.hpp.
+__global__ void pack_layer_bf16_kernel(const float* __restrict__ W, int in, int ld, int out,
+                                       int steps, int first, int otw, uint16_t* __restrict__ pk) {
+  const int64_t total = (int64_t)(steps + kPrefetch) * kSplit * 64 * otw * 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int j = (int)(idx % 8);
+  const int i = (int)((idx / 8) % otw);
+  const int lane = (int)((idx / (8 * (int64_t)otw)) % 64);
+  const int q = (int)((idx / (8 * (int64_t)otw * 64)) % kSplit);
+  const int s = (int)(idx / (8 * (int64_t)otw * 64 * kSplit));
+  const int o = 16 * (q * otw + i) + (lane & 15);
+  const int g = lane >> 4;
+  const int k = first ? 32 * s + 8 * g + j : 16 * (2 * s + j / 4) + 4 * g + (j % 4);
+  const bool ok = s < steps && o < out && k < in;
+  pk[idx] = ok ? (uint16_t)bf16_bits(W[(int64_t)o * ld + k]) : (uint16_t)0;
+}
+
+// bf16-rounded copies (kept as fp32) of a plain array and of the curiosity
+// one-hot columns.
+__global__ void round_copy_kernel(const float* __restrict__ src, int n, float* __restrict__ dst) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < n) dst[j] = bf16_round(src[j]);
+}
+__global__ void pack_onehot_bf16_kernel(const float* __restrict__ W, float* __restrict__ oh) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= kActions * 128) return;
+  const int a = idx / 128, o = idx % 128;
+  oh[idx] = bf16_round(W[(int64_t)o * (kState + kActions) + kState + a]);
 }
 
 __global__ void pack_bias_kernel(const float* __restrict__ b, int out, int padded,
@@ -55,6 +87,14 @@ hipError_t pack_layer(const float* W, const LayerDesc& d, int ld, float* pk, hip
   const int64_t total = packed_layer_floats(d);
   hipLaunchKernelGGL(pack_layer_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, W,
                      d.in, ld, d.out, d.steps, d.first, d.ot / kSplit, pk);
+  return hipGetLastError();
+}
+
+hipError_t pack_layer_bf16(const float* W, const LayerDesc& d, int ld, float* pk, hipStream_t st) {
+  const int64_t total = packed_layer_floats_bf16(d) * 2;  // bf16 elements
+  hipLaunchKernelGGL(pack_layer_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     W, d.in, ld, d.out, d.steps, d.first, d.ot / kSplit,
+                     reinterpret_cast<uint16_t*>(pk));
   return hipGetLastError();
 }
 
@@ -95,6 +135,20 @@ hipError_t pack_weights(const float* const actor[6], const float* const critic[1
   RL_TRY(pack_bias(cur[3], kCur[1], block + P.cur_b[1], st));
   hipLaunchKernelGGL(pack_onehot_kernel, dim3((kActions * 128 + 255) / 256), dim3(256), 0, st, cur[0],
                      block + P.cur_onehot);
+  RL_TRY(hipGetLastError());
+  // bf16 forms
+  for (int l = 0; l < 3; ++l) {
+    RL_TRY(pack_layer_bf16(actor[2 * l], kActorB[l], kActorB[l].in, block + P.bact_w[l], st));
+    RL_TRY(pack_bias(actor[2 * l + 1], kActorB[l], block + P.bact_b[l], st));
+  }
+  for (int l = 0; l < 5; ++l)
+    RL_TRY(pack_layer_bf16(critic[2 * l], kCriticB[l], kCriticB[l].in, block + P.bcritic_w[l], st));
+  RL_TRY(pack_layer_bf16(cur[0], kCurB[0], kState + kActions, block + P.bcur_w[0], st));
+  RL_TRY(pack_layer_bf16(cur[2], kCurB[1], kCurB[1].in, block + P.bcur_w[1], st));
+  hipLaunchKernelGGL(round_copy_kernel, dim3(1), dim3(64), 0, st, critic[10], 64, block + P.bcritic_w6);
+  RL_TRY(hipGetLastError());
+  hipLaunchKernelGGL(pack_onehot_bf16_kernel, dim3((kActions * 128 + 255) / 256), dim3(256), 0, st,
+                     cur[0], block + P.bcur_onehot);
   RL_TRY(hipGetLastError());
 #undef RL_TRY
   return hipSuccess;

@@ -5,8 +5,9 @@
 // every actor layer's outputs (activations shared through LDS).  Per step
 //   - assembles the 54-wide state (51 features of the bar, V/V0 - 1, the
 //     exposure held, the spread) and stores it (steps 1-2, 11),
-//   - runs the actor 54 -> 128 -> 64 -> 45 on MFMA with the packed actor
-//     weights resident in LDS for the whole kernel (step 3),
+//   - runs the actor 54 -> 128 -> 64 -> 45 on MFMA (fp32, or bf16 weights and
+//     layer inputs with fp32 accumulation) with the packed actor resident in
+//     LDS for the whole kernel (step 3),
 //   - takes a max-shifted softmax, its CDF and the inverse-CDF draw
 //     a = min{k : u < CDF_k} with u from the counter-based generator, and
 //     log p(a) = (l_a - max) - ln S (step 4),
@@ -31,17 +32,24 @@ namespace rl {
 namespace {
 
 constexpr PackedOffsets kP = packed_offsets();
-constexpr int kActorF4 = (int)(kP.actor_end / 4);
+constexpr int64_t kActorF32 = kP.actor_end;                  // fp32 actor block (floats)
+constexpr int64_t kActorBF16 = kP.bact_end - kP.bact_begin;  // bf16 actor block (floats)
+constexpr int kActorF4 = (int)((kActorF32 > kActorBF16 ? kActorF32 : kActorBF16) / 4);
 constexpr int kBufF4 = 8 * 64;  // widest actor activation: 128 = 8 tiles
 
+// The features a lane feeds to the first layer (its 16 state slots).
+template <bool BF16>
 __device__ __forceinline__ void load_features(const float* __restrict__ F, int64_t bar, int g,
-                                              float (&f)[kFirstSteps]) {
-  const float* row = F + bar * kFeatures + kFirstSteps * g;
+                                              float (&f)[16]) {
+  const float* row = F + bar * kFeatures;
 #pragma unroll
-  for (int s = 0; s < kFirstSteps; ++s) f[s] = (kFirstSteps * g + s < kFeatures) ? row[s] : 0.0f;
+  for (int s = 0; s < 16; ++s) {
+    const int k = state_k<BF16>(g, s);
+    f[s] = k < kFeatures ? row[k] : 0.0f;
+  }
 }
 
-template <int RG>
+template <int RG, bool BF16>
 __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(RolloutArgs a) {
   __shared__ f32x4 s_w[kActorF4];
   __shared__ f32x4 s_buf[RG][kBufF4];
@@ -53,9 +61,11 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
   const int q = wave % kSplit;
   const int g = lane >> 4;
 
-  {  // stage the packed actor into LDS
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.weights);
-    for (int i = threadIdx.x; i < kActorF4; i += 64 * kSplit * RG) s_w[i] = src[i];
+  {  // stage the packed actor (fp32 or bf16 block) into LDS
+    const int64_t begin = BF16 ? kP.bact_begin : 0;
+    const int n4 = (int)((BF16 ? kActorBF16 : kActorF32) / 4);
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.weights + begin);
+    for (int i = threadIdx.x; i < n4; i += 64 * kSplit * RG) s_w[i] = src[i];
   }
 
   const int32_t n_raw = (blockIdx.x * RG + rg) * kRowsPerWave + (lane & 15);
@@ -78,8 +88,8 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
   f32x4* buf = s_buf[rg];
   f32x4* sbuf = s_state[rg];
 
-  float fcur[kFirstSteps];
-  load_features(a.features, st, g, fcur);
+  float fcur[16];
+  load_features<BF16>(a.features, st, g, fcur);
   float p0 = a.prices[st], p1 = a.prices[st + 1];
 
   // episode state (PPO CUDA Pipeline Design, Phase A steps 6-8, 12), held
@@ -95,65 +105,79 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
     const int64_t bar = st + t;
     const int64_t o = (int64_t)t * a.N + n;
 
-    // ---- steps 1-2: state, as this lane's 16 first-layer k-steps --------
+    // ---- steps 1-2: state, as this lane's 16 first-layer slots -----------
+    // features k < 51, then V/V0 - 1, the exposure held and the spread
+    const float vn = V / V0 - 1.0f;
     float B[16];
 #pragma unroll
-    for (int s = 0; s < kFirstSteps; ++s) B[s] = fcur[s];
-    if (g == 3) {  // k = 42 + s: features up to 50, then the portfolio features
-      B[9] = V / V0 - 1.0f;
-      B[10] = e_prev;
-      B[11] = ep.spread;
-      B[12] = 0.0f;
-      B[13] = 0.0f;
+    for (int s = 0; s < 16; ++s) {
+      const int k = state_k<BF16>(g, s);
+      B[s] = k < kFeatures ? fcur[s]
+                           : (k == 51 ? vn : (k == 52 ? e_prev : (k == 53 ? ep.spread : 0.0f)));
     }
-    B[14] = 0.0f;
-    B[15] = 0.0f;
     if (q == 0) {
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        f32x4 v;
-        v[0] = B[4 * k4]; v[1] = B[4 * k4 + 1]; v[2] = B[4 * k4 + 2]; v[3] = B[4 * k4 + 3];
-        sbuf[k4 * 64 + lane] = v;
-      }
+      store_state_operands<BF16>(B, sbuf, lane);
       if (valid) {
-        float* srow = a.states + o * kState + kFirstSteps * g;
+        float* srow = a.states + o * kState;
 #pragma unroll
-        for (int s = 0; s < kFirstSteps; ++s)
-          if (kFirstSteps * g + s < kState) srow[s] = B[s];
+        for (int s = 0; s < 16; ++s) {
+          const int k = state_k<BF16>(g, s);
+          if (k < kState) srow[k] = B[s];
+        }
       }
     }
 
     // prefetch the next bar (independent of this step's outcome)
-    float fnext[kFirstSteps];
+    float fnext[16];
     float p2 = p1;
     if (t + 1 < a.L) {
-      load_features(a.features, bar + 1, g, fnext);
+      load_features<BF16>(a.features, bar + 1, g, fnext);
       p2 = a.prices[bar + 2];
     } else {
 #pragma unroll
-      for (int s = 0; s < kFirstSteps; ++s) fnext[s] = fcur[s];
+      for (int s = 0; s < 16; ++s) fnext[s] = fcur[s];
     }
     __syncthreads();  // state operands written
 
     // ---- step 3: actor, a quarter of each layer per wave ------------------
     {
       f32x4 h[2];
-      mfma_layer<16, 2>(sw + kP.actor_w[0], sw + kP.actor_b[0], sbuf, h, q, lane);
-      relu_store<2>(h, buf, q, lane);  // buf is free: last read before the previous barrier
+      if constexpr (BF16) {
+        mfma_layer_bf16<2, 2>(reinterpret_cast<const uint4*>(sw + kP.bact_w[0] - kP.bact_begin),
+                              sw + kP.bact_b[0] - kP.bact_begin,
+                              reinterpret_cast<const uint4*>(sbuf), h, q, lane);
+        relu_store_bf16<2>(h, reinterpret_cast<uint4*>(buf), q, lane);
+      } else {
+        mfma_layer<16, 2>(sw + kP.actor_w[0], sw + kP.actor_b[0], sbuf, h, q, lane);
+        relu_store<2>(h, buf, q, lane);  // buf is free: last read before the previous barrier
+      }
     }
     __syncthreads();
     {
       f32x4 h[1];
-      mfma_layer<32, 1>(sw + kP.actor_w[1], sw + kP.actor_b[1], buf, h, q, lane);
-      __syncthreads();
-      relu_store<1>(h, buf, q, lane);
+      if constexpr (BF16) {
+        mfma_layer_bf16<4, 1>(reinterpret_cast<const uint4*>(sw + kP.bact_w[1] - kP.bact_begin),
+                              sw + kP.bact_b[1] - kP.bact_begin,
+                              reinterpret_cast<const uint4*>(buf), h, q, lane);
+        __syncthreads();
+        relu_store_bf16<1>(h, reinterpret_cast<uint4*>(buf), q, lane);
+      } else {
+        mfma_layer<32, 1>(sw + kP.actor_w[1], sw + kP.actor_b[1], buf, h, q, lane);
+        __syncthreads();
+        relu_store<1>(h, buf, q, lane);
+      }
     }
     __syncthreads();
     {
       f32x4 h[1];
-      mfma_layer<16, 1>(sw + kP.actor_w[2], sw + kP.actor_b[2], buf, h, q, lane);
+      if constexpr (BF16)
+        mfma_layer_bf16<2, 1>(reinterpret_cast<const uint4*>(sw + kP.bact_w[2] - kP.bact_begin),
+                              sw + kP.bact_b[2] - kP.bact_begin,
+                              reinterpret_cast<const uint4*>(buf), h, q, lane);
+      else
+        mfma_layer<16, 1>(sw + kP.actor_w[2], sw + kP.actor_b[2], buf, h, q, lane);
       __syncthreads();
-      buf[q * 64 + lane] = h[0];  // raw logits (tile 3 is padding)
+      buf[q * 64 + lane] = h[0];  // raw logits, fp32 (tile 3 is padding)
     }
     __syncthreads();
 
@@ -321,7 +345,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
       ring = 0;
     }
 #pragma unroll
-    for (int s = 0; s < kFirstSteps; ++s) fcur[s] = fnext[s];
+    for (int s = 0; s < 16; ++s) fcur[s] = fnext[s];
     p0 = p1;
     p1 = p2;
   }
@@ -333,13 +357,17 @@ hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
   if (a.N <= 0 || a.L <= 0) return hipSuccess;
   // two 16-episode groups per workgroup once there are enough episodes to
   // fill every CU with one workgroup; otherwise one group, spread wider
-  if (a.N >= 2 * 16 * 256) {
-    const unsigned blocks = (unsigned)((a.N + 31) / 32);
-    hipLaunchKernelGGL((actor_rollout_kernel<2>), dim3(blocks), dim3(64 * kSplit * 2), 0, st, a);
-  } else {
-    const unsigned blocks = (unsigned)((a.N + 15) / 16);
-    hipLaunchKernelGGL((actor_rollout_kernel<1>), dim3(blocks), dim3(64 * kSplit), 0, st, a);
-  }
+  const bool two = a.N >= 2 * 16 * 256;
+  const unsigned blocks = (unsigned)(two ? (a.N + 31) / 32 : (a.N + 15) / 16);
+  const dim3 block(64 * kSplit * (two ? 2 : 1));
+  if (two && a.bf16)
+    hipLaunchKernelGGL((actor_rollout_kernel<2, true>), dim3(blocks), block, 0, st, a);
+  else if (two)
+    hipLaunchKernelGGL((actor_rollout_kernel<2, false>), dim3(blocks), block, 0, st, a);
+  else if (a.bf16)
+    hipLaunchKernelGGL((actor_rollout_kernel<1, true>), dim3(blocks), block, 0, st, a);
+  else
+    hipLaunchKernelGGL((actor_rollout_kernel<1, false>), dim3(blocks), block, 0, st, a);
   return hipGetLastError();
 }
 

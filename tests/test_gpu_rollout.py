@@ -132,3 +132,55 @@ def test_sampler_chi_square_on_gpu():
     ex = np.append(exp[~small], exp[small].sum()) if small.any() else exp
     chi2 = ((obs - ex) ** 2 / ex).sum()
     assert chi2 < stats.chi2.ppf(1 - 1e-6, obs.size - 1)
+
+
+# --------------------------------------------------------------------------- bf16
+BF16_RTOL, BF16_ATOL = 2e-2, 1e-5
+
+
+def _bf16_compare(inp, episodes=None):
+    """GPU bf16 collection vs the oracle's bf16 mode with the GPU's actions
+    teacher-forced: integers bit-exact; floats within 1e-5 + 2e-2 * scale,
+    where the scale is max(|o|, rms of that output over the compared set) (for
+    logits the row's largest |logit|): a bf16 result is a sum whose terms are
+    rounded to 8 bits, so a one-ulp flip of an activation near a rounding
+    boundary (different fp32 summation order) moves it by an amount that
+    follows the terms' size, not a cancelled sum.  Element-wise-relative
+    outliers are counted and reported."""
+    gpu = run_gpu(inp, precision=1)
+    free = oracle.rollout(inp, precision=oracle.BF16, subset=episodes)
+    cols = list(range(inp["N"])) if episodes is None else list(episodes)
+    agree = float((free["actions"][:, cols] == gpu["actions"][:, cols]).mean())
+    forced = oracle.rollout(inp, precision=oracle.BF16, forced_actions=gpu["actions"], subset=episodes)
+    for k in ("dones", "barrier"):
+        assert np.array_equal(gpu[k][:, cols], forced[k][:, cols]), k
+    worst = {}
+    for k, ko in (("states", "states"), ("logits", "logits"), ("log_probs", "log_probs"),
+                  ("values", "values"), ("rewards", "rewards"), ("advantages", "adv"),
+                  ("returns", "ret")):
+        g, o = gpu[k][:, cols].astype(np.float64), forced[ko][:, cols].astype(np.float64)
+        rms = float(np.sqrt((o * o).mean()))
+        if k == "logits":
+            # a logit vector is one dot product per action: relative to the row's scale
+            scale = np.broadcast_to(np.abs(o).max(axis=-1, keepdims=True), o.shape)
+        else:
+            scale = np.maximum(np.abs(o), rms)
+        err = np.abs(g - o) - (BF16_ATOL + BF16_RTOL * scale)
+        outl = np.abs(g - o) > BF16_ATOL + BF16_RTOL * np.abs(o)
+        worst[k] = (float(err.max()), int((err > 0).sum()), int(outl.sum()), g.size)
+    print(f"bf16: free-running action agreement {agree:.4f}; per output (worst excess, "
+          f"beyond tolerance, element-wise-relative outliers, count): {worst}")
+    for k, (mx, nbad, _, n) in worst.items():
+        assert nbad == 0, f"{k}: {nbad} of {n} beyond tolerance (worst excess {mx:.3g})"
+    return agree
+
+
+def test_bf16_tiny_teacher_forced():
+    inp = synthdata.ppo_inputs("ppo_n16_l100", bias_scale=0.1)
+    assert _bf16_compare(inp) > 0.5
+
+
+def test_bf16_chip_workload_sampled_episodes():
+    inp = synthdata.ppo_inputs("ppo_n8192_l500")
+    sub = sorted(set(list(range(0, 8192, 397)) + [8191]))
+    _bf16_compare(inp, episodes=sub)
