@@ -73,6 +73,33 @@ __device__ __forceinline__ float bf16_round(float x) {
   return __builtin_bit_cast(float, bf16_bits(x) << 16);
 }
 
+// Value held by lane l ^ 16 / l ^ 32 (gfx950 lane-swap instructions: no LDS
+// round trip).  permlane16_swap exchanges rows 1, 3 of its first operand with
+// rows 0, 2 of its second; permlane32_swap the upper half of the first with
+// the lower half of the second.
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t v, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (lane & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t v, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (lane & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float lane_xor16f(float v, int lane) {
+  return __uint_as_float(lane_xor16(__float_as_uint(v), lane));
+}
+__device__ __forceinline__ float lane_xor32f(float v, int lane) {
+  return __uint_as_float(lane_xor32(__float_as_uint(v), lane));
+}
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations
+// (not its outstanding global loads and stores, which __syncthreads() would
+// also drain), then s_barrier.  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace rl

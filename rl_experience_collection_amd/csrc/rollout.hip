@@ -54,6 +54,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
   __shared__ f32x4 s_w[kActorF4];
   __shared__ f32x4 s_buf[RG][kBufF4];
   __shared__ f32x4 s_state[RG][4 * 64];
+  __shared__ float s_ln[33];  // ln k for window counts k = 0..32 (ln 0 unused: times 0)
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -61,6 +62,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
   const int q = wave % kSplit;
   const int g = lane >> 4;
 
+  if (threadIdx.x <= 32) s_ln[threadIdx.x] = threadIdx.x == 0 ? 0.0f : logf((float)threadIdx.x);
   {  // stage the packed actor (fp32 or bf16 block) into LDS
     const int64_t begin = BF16 ? kP.bact_begin : 0;
     const int n4 = (int)((BF16 ? kActorBF16 : kActorF32) / 4);
@@ -96,10 +98,10 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
   // identically by the 4 lanes of the episode in each of the 4 waves
   float V = 1.0f, e_prev = 0.0f, entry = 0.0f;
   int armed = 0, side = 0, t_open = 0;
-  int cnt0 = 0, cnt1 = 0, cnt2 = 0, pushed = 0;
+  int cnt0 = 0, cnt1 = 0, cnt2 = 0, pushed = 0, pos = 0;
   uint64_t ring = 0;  // 2 bits per window slot
   const float V0 = 1.0f;
-  __syncthreads();  // weights staged
+  lds_barrier();  // weights staged
 
   for (int32_t t = 0; t < a.L; ++t) {
     const int64_t bar = st + t;
@@ -137,7 +139,10 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
 #pragma unroll
       for (int s = 0; s < 16; ++s) fnext[s] = fcur[s];
     }
-    __syncthreads();  // state operands written
+    lds_barrier();  // state operands written
+
+    // the step's draw depends only on (seed, episode, step)
+    const float u = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 0u);
 
     // ---- step 3: actor, a quarter of each layer per wave ------------------
     {
@@ -152,22 +157,22 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
         relu_store<2>(h, buf, q, lane);  // buf is free: last read before the previous barrier
       }
     }
-    __syncthreads();
+    lds_barrier();
     {
       f32x4 h[1];
       if constexpr (BF16) {
         mfma_layer_bf16<4, 1>(reinterpret_cast<const uint4*>(sw + kP.bact_w[1] - kP.bact_begin),
                               sw + kP.bact_b[1] - kP.bact_begin,
                               reinterpret_cast<const uint4*>(buf), h, q, lane);
-        __syncthreads();
+        lds_barrier();
         relu_store_bf16<1>(h, reinterpret_cast<uint4*>(buf), q, lane);
       } else {
         mfma_layer<32, 1>(sw + kP.actor_w[1], sw + kP.actor_b[1], buf, h, q, lane);
-        __syncthreads();
+        lds_barrier();
         relu_store<1>(h, buf, q, lane);
       }
     }
-    __syncthreads();
+    lds_barrier();
     {
       f32x4 h[1];
       if constexpr (BF16)
@@ -176,12 +181,16 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
                               reinterpret_cast<const uint4*>(buf), h, q, lane);
       else
         mfma_layer<16, 1>(sw + kP.actor_w[2], sw + kP.actor_b[2], buf, h, q, lane);
-      __syncthreads();
+      lds_barrier();
       buf[q * 64 + lane] = h[0];  // raw logits, fp32 (tile 3 is padding)
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- step 4: softmax, CDF, inverse-CDF draw, log-prob (every wave) ----
+    // The 4 lanes of an episode hold logit tiles ot = 0..2 as groups g:
+    // index k = 16 ot + 4 g + r.  Cross-lane steps use lane swaps; sums over
+    // the 4 lanes are butterflies (b_g + b_g^1) + (b_g^2 + b_g^3), the same
+    // bits in every lane.
     float l[12], e[12];
     bool ok[12];
     int bad = 0;
@@ -200,43 +209,42 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
 #pragma unroll
     for (int i = 0; i < 12; ++i)
       if (ok[i]) m = fmaxf(m, l[i]);
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = fmaxf(m, lane_xor16f(m, lane));
+    m = fmaxf(m, lane_xor32f(m, lane));
 #pragma unroll
     for (int i = 0; i < 12; ++i) e[i] = ok[i] ? expf(l[i] - m) : 0.0f;
-    float bs[3];
+    // block sums of the 4 groups of each tile, by absolute group index
+    float T[3], pre[3];
 #pragma unroll
-    for (int ot = 0; ot < 3; ++ot) bs[ot] = ((e[4 * ot] + e[4 * ot + 1]) + e[4 * ot + 2]) + e[4 * ot + 3];
-    float bsg[4][3];
-    const int base = lane & 15;
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-      for (int ot = 0; ot < 3; ++ot) bsg[gg][ot] = __shfl(bs[ot], base + 16 * gg);
-    float T[3];
-#pragma unroll
-    for (int ot = 0; ot < 3; ++ot) T[ot] = ((bsg[0][ot] + bsg[1][ot]) + bsg[2][ot]) + bsg[3][ot];
+    for (int ot = 0; ot < 3; ++ot) {
+      const float bs = ((e[4 * ot] + e[4 * ot + 1]) + e[4 * ot + 2]) + e[4 * ot + 3];
+      const float p16 = lane_xor16f(bs, lane);  // group g ^ 1
+      const float p32 = lane_xor32f(bs, lane);  // group g ^ 2
+      const float p48 = lane_xor16f(p32, lane); // group g ^ 3
+      T[ot] = (bs + p16) + (p32 + p48);
+      const float b0 = g == 0 ? bs : (g == 1 ? p16 : (g == 2 ? p32 : p48));
+      const float b1 = g == 1 ? bs : (g == 0 ? p16 : (g == 3 ? p32 : p48));
+      const float b2 = g == 2 ? bs : (g == 3 ? p16 : (g == 0 ? p32 : p48));
+      pre[ot] = g == 0 ? 0.0f : (g == 1 ? b0 : (g == 2 ? b0 + b1 : (b0 + b1) + b2));
+    }
     const float S = (T[0] + T[1]) + T[2];
-    const float u = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 0u);
+    // first k with u < CDF_k, as u * S < (sum of e up to k)
+    const float uS = u * S;
     int first = 64;
     float before = 0.0f;
 #pragma unroll
     for (int ot = 0; ot < 3; ++ot) {
-      float run = before;
-#pragma unroll
-      for (int gg = 0; gg < 3; ++gg)
-        if (gg < g) run += bsg[gg][ot];
+      float run = before + pre[ot];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         run += e[4 * ot + r];
-        const float cdf = run / S;
         const int k = 16 * ot + 4 * g + r;
-        if (ok[4 * ot + r] && first == 64 && u < cdf) first = k;
+        if (ok[4 * ot + r] && first == 64 && uS < run) first = k;
       }
       before += T[ot];
     }
-    int act_a = min(first, __shfl_xor(first, 16));
-    act_a = min(act_a, __shfl_xor(act_a, 32));
+    int act_a = min(first, (int)lane_xor16((uint32_t)first, lane));
+    act_a = min(act_a, (int)lane_xor32((uint32_t)act_a, lane));
     if (act_a == 64) {  // rounding left u >= CDF_44: last action with weight
       int lastk = -1;
 #pragma unroll
@@ -244,8 +252,8 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (ok[4 * ot + r] && e[4 * ot + r] > 0.0f) lastk = max(lastk, 16 * ot + 4 * g + r);
-      lastk = max(lastk, __shfl_xor(lastk, 16));
-      lastk = max(lastk, __shfl_xor(lastk, 32));
+      lastk = max(lastk, (int)lane_xor16((uint32_t)lastk, lane));
+      lastk = max(lastk, (int)lane_xor32((uint32_t)lastk, lane));
       act_a = lastk >= 0 ? lastk : kActions - 1;
     }
     float la = -INFINITY;
@@ -254,11 +262,11 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (16 * ot + 4 * g + r == act_a) la = l[4 * ot + r];
-    la = fmaxf(la, __shfl_xor(la, 16));
-    la = fmaxf(la, __shfl_xor(la, 32));
+    la = fmaxf(la, lane_xor16f(la, lane));
+    la = fmaxf(la, lane_xor32f(la, lane));
     const float logp = (la - m) - logf(S);
-    bad |= __shfl_xor(bad, 16);
-    bad |= __shfl_xor(bad, 32);
+    bad |= (int)lane_xor16((uint32_t)bad, lane);
+    bad |= (int)lane_xor32((uint32_t)bad, lane);
 
     // ---- step 6: portfolio (exposure fraction of equity, turnover cost) ---
     const int xi = act_a / 9;
@@ -296,8 +304,9 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
     }
 
     // ---- step 8: diversity window, 3-class entropy in nats -----------------
+    // H = ln n - (sum_c n_c ln n_c) / n, compared as n ln n - sum n_c ln n_c
+    // < threshold * n; ln of the counts 0..32 comes from an LDS table
     const int cat = xi <= 1 ? 0 : (xi == 2 ? 1 : 2);
-    const int pos = pushed % ep.div_window;
     if (pushed >= ep.div_window) {
       const int old = (int)((ring >> (2 * pos)) & 3u);
       cnt0 -= old == 0; cnt1 -= old == 1; cnt2 -= old == 2;
@@ -305,12 +314,11 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
     ring = (ring & ~(3ull << (2 * pos))) | ((uint64_t)cat << (2 * pos));
     cnt0 += cat == 0; cnt1 += cat == 1; cnt2 += cat == 2;
     ++pushed;
-    const float nn = (float)(cnt0 + cnt1 + cnt2);
-    float H = 0.0f;
-    if (cnt0 > 0) { const float p = (float)cnt0 / nn; H -= p * logf(p); }
-    if (cnt1 > 0) { const float p = (float)cnt1 / nn; H -= p * logf(p); }
-    if (cnt2 > 0) { const float p = (float)cnt2 / nn; H -= p * logf(p); }
-    const float div = H < ep.div_threshold ? ep.div_penalty : 0.0f;
+    pos = pos + 1 == ep.div_window ? 0 : pos + 1;
+    const int nn = cnt0 + cnt1 + cnt2;
+    const float hn = (float)nn * s_ln[nn] -
+                     (((float)cnt0 * s_ln[cnt0] + (float)cnt1 * s_ln[cnt1]) + (float)cnt2 * s_ln[cnt2]);
+    const float div = hn < ep.div_threshold * (float)nn ? ep.div_penalty : 0.0f;
 
     // ---- steps 10-11: partial reward and stores ----------------------------
     const float partial = pnl * (1.0f + ep.barrier_scale * (float)hit) + div;
@@ -342,6 +350,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
       armed = 0;
       cnt0 = cnt1 = cnt2 = 0;
       pushed = 0;
+      pos = 0;
       ring = 0;
     }
 #pragma unroll

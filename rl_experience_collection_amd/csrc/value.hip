@@ -47,12 +47,12 @@ __device__ __forceinline__ void layer(const float* W, int64_t w32, int64_t wb, i
                              reinterpret_cast<const uint4*>(buf), acc, q, lane);
   else
     mfma_layer<S32, OTW>(W + w32, W + b_off, reinterpret_cast<const f32x4*>(buf), acc, q, lane);
-  __syncthreads();  // every wave has read the input
+  lds_barrier();  // every wave has read the input
   if constexpr (BF16)
     relu_store_bf16<OTW>(acc, reinterpret_cast<uint4*>(buf), q, lane);
   else
     relu_store<OTW>(acc, reinterpret_cast<f32x4*>(buf), q, lane);
-  __syncthreads();  // the output is complete
+  lds_barrier();  // the output is complete
 }
 
 // This wave's share of a layer whose output is not stored (accumulators).
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void value_kernel(ValueArgs a) {
     store_state_operands<BF16>(B, s_state[rg], lane);
     store_state_operands<BF16>(B, buf, lane);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- critic -----------------------------------------------------------
   layer<BF16, 16, 2, 32>(W, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], buf, q, lane);
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void value_kernel(ValueArgs a) {
     part += __shfl_xor(part, 32);
     if (g == 0) s_part[rg][q][lane] = part;
   }
-  __syncthreads();  // critic input no longer needed; partial sums visible
+  lds_barrier();  // critic input no longer needed; partial sums visible
   float value = 0.0f;
   if (q == 0)
     value = W[kP.critic_b6] + ((s_part[rg][0][lane & 15] + s_part[rg][1][lane & 15]) +
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void value_kernel(ValueArgs a) {
     else
       relu_store<2>(c, reinterpret_cast<f32x4*>(buf), q, lane);
   }
-  __syncthreads();
+  lds_barrier();
   float bonus = 0.0f;
   {
     f32x4 pr[1];
@@ -161,9 +161,9 @@ __global__ __launch_bounds__(kThreads) void value_kernel(ValueArgs a) {
     }
     se += __shfl_xor(se, 16);
     se += __shfl_xor(se, 32);
-    __syncthreads();  // value partials read by wave 0 before they are reused
+    lds_barrier();  // value partials read by wave 0 before they are reused
     if (g == 0) s_part[rg][q][lane] = se;
-    __syncthreads();
+    lds_barrier();
     if (q == 0) {
       const float sum = (s_part[rg][0][lane & 15] + s_part[rg][1][lane & 15]) +
                         (s_part[rg][2][lane & 15] + s_part[rg][3][lane & 15]);
