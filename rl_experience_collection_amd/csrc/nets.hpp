@@ -2,6 +2,8 @@
 // evaluator shared by the actor-rollout and value kernels.
 #pragma once
 
+#include <type_traits>
+
 #include "device.hpp"
 
 namespace rl {
@@ -297,6 +299,156 @@ __device__ __forceinline__ void relu_store_bf16(const f32x4 (&acc)[OTW], uint4* 
     w.y = pack_bf16x2(fmaxf(v[2], 0.0f), fmaxf(v[3], 0.0f));
     half[((t >> 1) * 64 + lane) * 2 + (t & 1)] = w;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Weight stream of one layer for a wave that evaluates RT row tiles (16 rows
+// each) at once: every A operand loaded from global memory feeds RT MFMAs,
+// which divides the weight traffic per flop by RT.  stream_begin loads the
+// bias tiles and the first kPrefetch k-steps; callers issue it for layer
+// j + 1 before the barriers and stores that end layer j, so those loads are
+// in flight while the waves synchronise.  stream_layer then runs the 4-slot
+// ring of mfma_layer; B operands (activations in LDS, row tile rt at
+// buf + rt * tile_stride) are read one step ahead.
+// ---------------------------------------------------------------------------
+template <bool BF16, int OTW>
+struct WeightStream {
+  using Op = typename std::conditional<BF16, uint4, float>::type;
+  static constexpr int kStep = kSplit * 64 * OTW;  // Op elements per k-step
+  Op a[4][OTW];
+  f32x4 bias[OTW];
+};
+
+template <bool BF16, int OTW>
+__device__ __forceinline__ void stream_begin(WeightStream<BF16, OTW>& st, const float* pk,
+                                             const float* pb, int q, int lane) {
+  constexpr int kStep = WeightStream<BF16, OTW>::kStep;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < OTW; ++i)
+    st.bias[i] = *reinterpret_cast<const f32x4*>(pb + 16 * (q * OTW + i) + 4 * g);
+  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
+  if constexpr (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(pk);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) st.a[j][i] = p[j * kStep + lane_off + i];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) load_operands<OTW>(pk + j * kStep + lane_off, st.a[j]);
+  }
+}
+
+// fp32: S k-steps of 4 (S % 4 == 0); one f32x4 of B per row tile covers 4 steps.
+template <int S, int OTW, int RT>
+__device__ __forceinline__ void stream_layer(WeightStream<false, OTW>& st,
+                                             const float* __restrict__ pk, const f32x4* buf,
+                                             int tile_stride, f32x4 (&acc)[RT][OTW], int q,
+                                             int lane) {
+  static_assert(kPrefetch == 3 && S % 4 == 0, "4-slot ring over whole groups of 4 steps");
+  constexpr int KT = S / 4;
+  constexpr int kStep = WeightStream<false, OTW>::kStep;
+  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < OTW; ++i) acc[rt][i] = st.bias[i];
+  f32x4 b[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) b[rt] = buf[rt * tile_stride + lane];
+#pragma unroll 1
+  for (int kt = 0; kt < KT; ++kt) {
+    const float* wk = pk + (4 * kt + 3) * kStep;
+    const int kn = kt + 1 < KT ? kt + 1 : kt;
+    f32x4 bn[RT];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      load_operands<OTW>(wk + r * kStep + lane_off, st.a[(r + 3) & 3]);
+      if (r == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) bn[rt] = buf[rt * tile_stride + kn * 64 + lane];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < OTW; ++i) acc[rt][i] = mfma4(st.a[r][i], b[rt][r], acc[rt][i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) b[rt] = bn[rt];
+  }
+}
+
+// bf16: S k-steps of 32; one uint4 of B per row tile and step.
+template <int S, int OTW, int RT>
+__device__ __forceinline__ void stream_layer(WeightStream<true, OTW>& st,
+                                             const float* __restrict__ pkf, const uint4* buf,
+                                             int tile_stride, f32x4 (&acc)[RT][OTW], int q,
+                                             int lane) {
+  static_assert(kPrefetch == 3, "the ring holds kPrefetch + 1 = 4 steps");
+  constexpr int KT = S / 4;
+  constexpr int TAIL = S % 4;
+  constexpr int kStep = WeightStream<true, OTW>::kStep;
+  const uint4* pk = reinterpret_cast<const uint4*>(pkf);
+  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < OTW; ++i) acc[rt][i] = st.bias[i];
+  uint4 b[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) b[rt] = buf[rt * tile_stride + lane];
+#pragma unroll 1
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint4* wk = pk + (4 * kt + 3) * kStep;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sn = 4 * kt + r + 1 < S ? 4 * kt + r + 1 : S - 1;
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) st.a[(r + 3) & 3][i] = wk[r * kStep + lane_off + i];
+      uint4 bn[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) bn[rt] = buf[rt * tile_stride + sn * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < OTW; ++i) acc[rt][i] = mfma_bf16(st.a[r][i], b[rt], acc[rt][i]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) b[rt] = bn[rt];
+    }
+  }
+  // remaining steps (S % 4): their operands are already in slots 0 .. TAIL-1
+#pragma unroll
+  for (int r = 0; r < TAIL; ++r) {
+    const int sn = 4 * KT + r + 1 < S ? 4 * KT + r + 1 : S - 1;
+    uint4 bn[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) bn[rt] = buf[rt * tile_stride + sn * 64 + lane];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) acc[rt][i] = mfma_bf16(st.a[r][i], b[rt], acc[rt][i]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) b[rt] = bn[rt];
+  }
+}
+
+// ReLU store of RT row tiles (row tile rt at buf + rt * tile_stride).
+template <int OTW, int RT>
+__device__ __forceinline__ void relu_store_tiles(const f32x4 (&acc)[RT][OTW], f32x4* buf,
+                                                 int tile_stride, int q, int lane) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) relu_store<OTW>(acc[rt], buf + rt * tile_stride, q, lane);
+}
+template <int OTW, int RT>
+__device__ __forceinline__ void relu_store_tiles_bf16(const f32x4 (&acc)[RT][OTW], uint4* buf,
+                                                      int tile_stride, int q, int lane) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) relu_store_bf16<OTW>(acc[rt], buf + rt * tile_stride, q, lane);
 }
 
 // The 16 first-layer operands of a lane (state_k order) as LDS operands:
