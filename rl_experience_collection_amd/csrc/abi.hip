@@ -193,6 +193,7 @@ struct rollout_s {
   int64_t n_bars = 0;
   float* weights = nullptr;      // packed block
   int32_t* start_used = nullptr; // [N]
+  unsigned long long* value_sched = nullptr;  // work counter of the value kernel
   GaeScratch gae;
 };
 
@@ -271,6 +272,12 @@ int rollout_create(const rollout_config* cfg, const float* const actor[6],
     return fail(ROLLOUT_ENOMEM, "cannot allocate start buffer");
   }
   h->start_used = static_cast<int32_t*>(p);
+  if (hipMalloc(&p, 256) != hipSuccess) {
+    (void)hipGetLastError();
+    rollout_destroy(h);
+    return fail(ROLLOUT_ENOMEM, "cannot allocate scheduler counter");
+  }
+  h->value_sched = static_cast<unsigned long long*>(p);
   rc = gae_reserve(h->gae, cfg->n_steps, cfg->n_episodes, st);
   if (rc) {
     rollout_destroy(h);
@@ -353,6 +360,7 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   va.values = out->values;
   va.rewards = out->rewards;
   va.counters = out->counters;
+  va.sched = h->value_sched;
   va.bf16 = h->cfg.precision == ROLLOUT_BF16;
   RL_HIP(rl::launch_value(va, st), "value launch");
   RL_HIP(mark(2), "hipEventRecord(phase 2)");
@@ -394,6 +402,7 @@ void rollout_destroy(rollout_handle h) {
   if (!h) return;
   if (h->weights) (void)hipFree(h->weights);
   if (h->start_used) (void)hipFree(h->start_used);
+  if (h->value_sched) (void)hipFree(h->value_sched);
   if (h->gae.mem) (void)hipFree(h->gae.mem);
   delete h;
 }

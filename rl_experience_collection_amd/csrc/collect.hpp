@@ -44,6 +44,7 @@ struct ValueArgs {
   float* values;
   float* rewards;  // in: partial reward, out: full reward
   uint32_t* counters;
+  unsigned long long* sched;  // [1] work counter of the persistent grid (zeroed per launch)
   int bf16;
 };
 

@@ -24,40 +24,50 @@ constexpr int kSplit = 4;
 
 struct LayerDesc {
   int in, out, steps, first, ot;  // ot = out tiles (a multiple of kSplit)
+  int pad;                         // zero k-steps after the layer (ring prefetch reach)
 };
 
+// Weight-ring slots of a streamed layer (value kernel): layers with few
+// output tiles per wave issue little MFMA work per k-step, so they keep more
+// steps in flight (fp32: the whole layer for one tile per wave; bf16: up to
+// 8 steps of 16-byte operands).  Streamed layers need no zero padding.
+__host__ __device__ constexpr int ring_depth(bool bf16, int otw) {
+  return otw >= 4 ? (bf16 ? 3 : 4) : (bf16 ? 8 : (otw == 2 ? 16 : 32));
+}
+
 // Actor: 54 -> 128 -> 64 -> 45 (PPO CUDA Pipeline Design, Weight Layout).
-constexpr LayerDesc kActor[3] = {{54, 128, 16, 1, 8}, {128, 64, 32, 0, 4}, {64, 45, 16, 0, 4}};
+constexpr LayerDesc kActor[3] = {{54, 128, 16, 1, 8, 3}, {128, 64, 32, 0, 4, 3}, {64, 45, 16, 0, 4, 3}};
 // Critic: 54 -> 512 -> 384 -> 256 -> 128 -> 64 (-> 1 handled on the VALU).
-constexpr LayerDesc kCritic[5] = {{54, 512, 16, 1, 32},
-                                  {512, 384, 128, 0, 24},
-                                  {384, 256, 96, 0, 16},
-                                  {256, 128, 64, 0, 8},
-                                  {128, 64, 32, 0, 4}};
+constexpr LayerDesc kCritic[5] = {{54, 512, 16, 1, 32, 0},
+                                  {512, 384, 128, 0, 24, 0},
+                                  {384, 256, 96, 0, 16, 0},
+                                  {256, 128, 64, 0, 8, 0},
+                                  {128, 64, 32, 0, 4, 0}};
 // Curiosity forward model: 54 dense inputs (+45 one-hot, gathered) -> 128 -> 51.
-constexpr LayerDesc kCur[2] = {{54, 128, 16, 1, 8}, {128, 51, 32, 0, 4}};
+constexpr LayerDesc kCur[2] = {{54, 128, 16, 1, 8, 0}, {128, 51, 32, 0, 4, 0}};
 
 // bf16 forms (v_mfma_f32_16x16x32_bf16): a k-step covers 32 inputs, 8 per
 // lane group.  First layers: kperm(s, g, j) = 32 s + 8 g + j (54 -> 2 steps).
 // Chained layers: kperm(s, g, j) = 16 (2 s + j / 4) + 4 g + j % 4, i.e. the
 // output tiles 2s and 2s+1 of the previous layer form k-step s.
-constexpr LayerDesc kActorB[3] = {{54, 128, 2, 1, 8}, {128, 64, 4, 0, 4}, {64, 45, 2, 0, 4}};
-constexpr LayerDesc kCriticB[5] = {{54, 512, 2, 1, 32},
-                                   {512, 384, 16, 0, 24},
-                                   {384, 256, 12, 0, 16},
-                                   {256, 128, 8, 0, 8},
-                                   {128, 64, 4, 0, 4}};
-constexpr LayerDesc kCurB[2] = {{54, 128, 2, 1, 8}, {128, 51, 4, 0, 4}};
+constexpr LayerDesc kActorB[3] = {{54, 128, 2, 1, 8, 3}, {128, 64, 4, 0, 4, 3}, {64, 45, 2, 0, 4, 3}};
+constexpr LayerDesc kCriticB[5] = {{54, 512, 2, 1, 32, 0},
+                                   {512, 384, 16, 0, 24, 0},
+                                   {384, 256, 12, 0, 16, 0},
+                                   {256, 128, 8, 0, 8, 0},
+                                   {128, 64, 4, 0, 4, 0}};
+constexpr LayerDesc kCurB[2] = {{54, 128, 2, 1, 8, 0}, {128, 51, 4, 0, 4, 0}};
 
-// Packed weights of a layer, plus kPrefetch zero k-steps so the prefetch of
-// the layer's last steps reads inside the block.
+// Packed weights of a layer, plus d.pad zero k-steps so the prefetch of the
+// layer's last steps reads inside the block.  The actor's layers (read from
+// LDS through a 4-slot ring) carry kPrefetch = 3.
 constexpr int kPrefetch = 3;
 __host__ __device__ constexpr int64_t packed_layer_floats(const LayerDesc& d) {
-  return (int64_t)(d.steps + kPrefetch) * 64 * d.ot;
+  return (int64_t)(d.steps + d.pad) * 64 * d.ot;
 }
 // bf16 layer: 8 bf16 (16 bytes, 4 float slots) per lane, tile and k-step.
 __host__ __device__ constexpr int64_t packed_layer_floats_bf16(const LayerDesc& d) {
-  return (int64_t)(d.steps + kPrefetch) * 64 * d.ot * 4;
+  return (int64_t)(d.steps + d.pad) * 64 * d.ot * 4;
 }
 
 struct PackedOffsets {
@@ -304,137 +314,196 @@ __device__ __forceinline__ void relu_store_bf16(const f32x4 (&acc)[OTW], uint4* 
 // ---------------------------------------------------------------------------
 // Weight stream of one layer for a wave that evaluates RT row tiles (16 rows
 // each) at once: every A operand loaded from global memory feeds RT MFMAs,
-// which divides the weight traffic per flop by RT.  stream_begin loads the
-// bias tiles and the first kPrefetch k-steps; callers issue it for layer
+// which divides the weight traffic per flop by RT.  The ring has D slots
+// (k-step s in slot s % D) and runs D - 1 steps ahead; the last group of D
+// steps is peeled so no load reaches past the layer.  stream_begin loads the
+// bias tiles and the first min(D - 1, S) k-steps; callers issue it for layer
 // j + 1 before the barriers and stores that end layer j, so those loads are
-// in flight while the waves synchronise.  stream_layer then runs the 4-slot
-// ring of mfma_layer; B operands (activations in LDS, row tile rt at
-// buf + rt * tile_stride) are read one step ahead.
+// in flight while the waves synchronise.  B operands come from a loader
+// (LDS operand layout, or the raw state rows for first layers) and are read
+// one group of steps ahead.
 // ---------------------------------------------------------------------------
-template <bool BF16, int OTW>
+template <bool BF16, int OTW, int D>
 struct WeightStream {
   using Op = typename std::conditional<BF16, uint4, float>::type;
   static constexpr int kStep = kSplit * 64 * OTW;  // Op elements per k-step
-  Op a[4][OTW];
+  Op a[D][OTW];
   f32x4 bias[OTW];
 };
 
 template <bool BF16, int OTW>
-__device__ __forceinline__ void stream_begin(WeightStream<BF16, OTW>& st, const float* pk,
-                                             const float* pb, int q, int lane) {
-  constexpr int kStep = WeightStream<BF16, OTW>::kStep;
+using Stream = WeightStream<BF16, OTW, ring_depth(BF16, OTW)>;
+
+// Weight loads through a buffer resource over the packed block: a 32-bit
+// per-lane byte offset (one VGPR per layer) plus a wave-uniform byte offset
+// (SGPR) for the k-step and tile, so the streams need no 64-bit addresses.
+using BufRsrc = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ BufRsrc weights_rsrc(const float* block, uint32_t bytes) {
+  // raw buffer (stride 0), 32-bit dword format word of the gfx9 family
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(block), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload_u4(BufRsrc r, uint32_t vo, uint32_t so) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int OTW>
+__device__ __forceinline__ void bload_operands(BufRsrc r, uint32_t vo, uint32_t so,
+                                               float (&a)[OTW]) {
+  if constexpr (OTW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < OTW; i += 4) {
+      const uint4 v = bload_u4(r, vo, so + 4u * i);
+      a[i] = __uint_as_float(v.x); a[i + 1] = __uint_as_float(v.y);
+      a[i + 2] = __uint_as_float(v.z); a[i + 3] = __uint_as_float(v.w);
+    }
+  } else if constexpr (OTW % 2 == 0) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < OTW; i += 2) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so + 4u * i, 0);
+      a[i] = __uint_as_float(v.x); a[i + 1] = __uint_as_float(v.y);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < OTW; ++i)
+      a[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, vo, so + 4u * i, 0));
+  }
+}
+
+// pk_b: byte offset of the layer's packed weights in the block; pb: biases.
+template <int S, bool BF16, int OTW, int D>
+__device__ __forceinline__ void stream_begin(WeightStream<BF16, OTW, D>& st, BufRsrc rs,
+                                             uint32_t pk_b, const float* pb, int q, int lane) {
+  constexpr uint32_t kStepB = WeightStream<BF16, OTW, D>::kStep * (BF16 ? 16u : 4u);
+  constexpr int kFirst = D - 1 < S ? D - 1 : S;
   const int g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < OTW; ++i)
     st.bias[i] = *reinterpret_cast<const f32x4*>(pb + 16 * (q * OTW + i) + 4 * g);
-  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
-  if constexpr (BF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(pk);
+  const uint32_t lane_b = (uint32_t)((q * 64 + lane) * OTW) * (BF16 ? 16u : 4u);
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+  for (int j = 0; j < kFirst; ++j) {
+    if constexpr (BF16) {
 #pragma unroll
-      for (int i = 0; i < OTW; ++i) st.a[j][i] = p[j * kStep + lane_off + i];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 3; ++j) load_operands<OTW>(pk + j * kStep + lane_off, st.a[j]);
+      for (int i = 0; i < OTW; ++i) st.a[j][i] = bload_u4(rs, lane_b, pk_b + j * kStepB + 16u * i);
+    } else {
+      bload_operands<OTW>(rs, lane_b, pk_b + j * kStepB, st.a[j]);
+    }
   }
 }
 
-// fp32: S k-steps of 4 (S % 4 == 0); one f32x4 of B per row tile covers 4 steps.
-template <int S, int OTW, int RT>
-__device__ __forceinline__ void stream_layer(WeightStream<false, OTW>& st,
-                                             const float* __restrict__ pk, const f32x4* buf,
-                                             int tile_stride, f32x4 (&acc)[RT][OTW], int q,
-                                             int lane) {
-  static_assert(kPrefetch == 3 && S % 4 == 0, "4-slot ring over whole groups of 4 steps");
-  constexpr int KT = S / 4;
-  constexpr int kStep = WeightStream<false, OTW>::kStep;
-  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
+// B operands in the LDS operand layout: fp32 group of 4 k-steps / bf16 k-step
+// grp of row tile rt at buf[rt * tile_stride + grp * 64 + lane].
+struct LdsOperands {
+  const f32x4* buf;
+  int tile_stride;
+  __device__ __forceinline__ f32x4 f32(int rt, int grp, int lane) const {
+    return buf[rt * tile_stride + grp * 64 + lane];
+  }
+  __device__ __forceinline__ uint4 bf16(int rt, int grp, int lane) const {
+    return reinterpret_cast<const uint4*>(buf)[rt * tile_stride + grp * 64 + lane];
+  }
+};
+
+// fp32: S k-steps of 4 inputs (S % D == 0); a row tile's f32x4 B operand
+// covers a group of 4 steps, read one group ahead.
+template <int S, int OTW, int D, int RT, class BL>
+__device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D>& st, BufRsrc rs,
+                                             uint32_t pk_b, const BL& bl, f32x4 (&acc)[RT][OTW],
+                                             int q, int lane) {
+  static_assert(D % 4 == 0 && S % D == 0, "whole groups of D steps");
+  constexpr int KT = S / D;
+  constexpr int G = S / 4;
+  constexpr uint32_t kStepB = WeightStream<false, OTW, D>::kStep * 4u;
+  const uint32_t lane_b = (uint32_t)((q * 64 + lane) * OTW) * 4u;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < OTW; ++i) acc[rt][i] = st.bias[i];
-  f32x4 b[RT];
+  f32x4 b[RT], bn[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) b[rt] = buf[rt * tile_stride + lane];
-#pragma unroll 1
-  for (int kt = 0; kt < KT; ++kt) {
-    const float* wk = pk + (4 * kt + 3) * kStep;
-    const int kn = kt + 1 < KT ? kt + 1 : kt;
-    f32x4 bn[RT];
+  for (int rt = 0; rt < RT; ++rt) b[rt] = bl.f32(rt, 0, lane);
+  auto group = [&](int kt, auto last) {
+    constexpr bool LAST = decltype(last)::value;
+    const uint32_t wk = pk_b + (uint32_t)(D * kt + D - 1) * kStepB;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      load_operands<OTW>(wk + r * kStep + lane_off, st.a[(r + 3) & 3]);
-      if (r == 0) {
+    for (int r = 0; r < D; ++r) {
+      if (!LAST || r == 0) bload_operands<OTW>(rs, lane_b, wk + r * kStepB, st.a[(r + D - 1) % D]);
+      if (r % 4 == 0 && !(LAST && r / 4 == D / 4 - 1)) {
+        const int gn = kt * (D / 4) + r / 4 + 1;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) bn[rt] = buf[rt * tile_stride + kn * 64 + lane];
+        for (int rt = 0; rt < RT; ++rt) bn[rt] = bl.f32(rt, gn < G ? gn : G - 1, lane);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < OTW; ++i) acc[rt][i] = mfma4(st.a[r][i], b[rt][r], acc[rt][i]);
+        for (int i = 0; i < OTW; ++i)
+          acc[rt][i] = mfma4(st.a[r][i], b[rt][r % 4], acc[rt][i]);
       __builtin_amdgcn_sched_barrier(0);
-    }
+      if (r % 4 == 3) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) b[rt] = bn[rt];
-  }
+        for (int rt = 0; rt < RT; ++rt) b[rt] = bn[rt];
+      }
+    }
+  };
+#pragma unroll 1
+  for (int kt = 0; kt < KT - 1; ++kt) group(kt, std::false_type{});
+  group(KT - 1, std::true_type{});
 }
 
-// bf16: S k-steps of 32; one uint4 of B per row tile and step.
-template <int S, int OTW, int RT>
-__device__ __forceinline__ void stream_layer(WeightStream<true, OTW>& st,
-                                             const float* __restrict__ pkf, const uint4* buf,
-                                             int tile_stride, f32x4 (&acc)[RT][OTW], int q,
-                                             int lane) {
-  static_assert(kPrefetch == 3, "the ring holds kPrefetch + 1 = 4 steps");
-  constexpr int KT = S / 4;
-  constexpr int TAIL = S % 4;
-  constexpr int kStep = WeightStream<true, OTW>::kStep;
-  const uint4* pk = reinterpret_cast<const uint4*>(pkf);
-  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
+// bf16: S k-steps of 32 inputs; one uint4 of B per row tile and step.
+template <int S, int OTW, int D, int RT, class BL>
+__device__ __forceinline__ void stream_layer(WeightStream<true, OTW, D>& st, BufRsrc rs,
+                                             uint32_t pk_b, const BL& bl, f32x4 (&acc)[RT][OTW],
+                                             int q, int lane) {
+  constexpr int KT = S / D;
+  constexpr int TAIL = S % D;
+  constexpr uint32_t kStepB = WeightStream<true, OTW, D>::kStep * 16u;
+  const uint32_t lane_b = (uint32_t)((q * 64 + lane) * OTW) * 16u;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < OTW; ++i) acc[rt][i] = st.bias[i];
-  uint4 b[RT];
+  uint4 b[RT], bn[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) b[rt] = buf[rt * tile_stride + lane];
-#pragma unroll 1
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint4* wk = pk + (4 * kt + 3) * kStep;
+  for (int rt = 0; rt < RT; ++rt) b[rt] = bl.bf16(rt, 0, lane);
+  // one step: weights of step s + D - 1 (when inside the layer), B of step
+  // s + 1, then the MFMAs of step s from slot `slot`
+  auto step = [&](int s, int slot, uint32_t wsrc, bool load_w, bool load_b) {
+    if (load_w) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int sn = 4 * kt + r + 1 < S ? 4 * kt + r + 1 : S - 1;
-#pragma unroll
-      for (int i = 0; i < OTW; ++i) st.a[(r + 3) & 3][i] = wk[r * kStep + lane_off + i];
-      uint4 bn[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) bn[rt] = buf[rt * tile_stride + sn * 64 + lane];
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < OTW; ++i) acc[rt][i] = mfma_bf16(st.a[r][i], b[rt], acc[rt][i]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) b[rt] = bn[rt];
+      for (int i = 0; i < OTW; ++i) st.a[(slot + D - 1) % D][i] = bload_u4(rs, lane_b, wsrc + 16u * i);
     }
-  }
-  // remaining steps (S % 4): their operands are already in slots 0 .. TAIL-1
+    if (load_b) {
 #pragma unroll
-  for (int r = 0; r < TAIL; ++r) {
-    const int sn = 4 * KT + r + 1 < S ? 4 * KT + r + 1 : S - 1;
-    uint4 bn[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) bn[rt] = buf[rt * tile_stride + sn * 64 + lane];
+      for (int rt = 0; rt < RT; ++rt) bn[rt] = bl.bf16(rt, s + 1, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < OTW; ++i) acc[rt][i] = mfma_bf16(st.a[r][i], b[rt], acc[rt][i]);
+      for (int i = 0; i < OTW; ++i) acc[rt][i] = mfma_bf16(st.a[slot][i], b[rt], acc[rt][i]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) b[rt] = bn[rt];
+  };
+  if constexpr (KT > 0) {
+#pragma unroll 1
+    for (int kt = 0; kt < KT - 1; ++kt) {
+      const uint32_t wk = pk_b + (uint32_t)(D * kt + D - 1) * kStepB;
+#pragma unroll
+      for (int r = 0; r < D; ++r) step(D * kt + r, r, wk + r * kStepB, true, true);
+    }
+    const uint32_t wk = pk_b + (uint32_t)(D * (KT - 1) + D - 1) * kStepB;
+#pragma unroll
+    for (int r = 0; r < D; ++r)
+      step(D * (KT - 1) + r, r, wk + r * kStepB, r <= TAIL, D * (KT - 1) + r + 1 < S);
   }
+  // remaining steps (S % D): already in slots 0 .. TAIL-1
+#pragma unroll
+  for (int r = 0; r < TAIL; ++r) step(D * KT + r, r, pk_b, false, D * KT + r + 1 < S);
 }
 
 // ReLU store of RT row tiles (row tile rt at buf + rt * tile_stride).

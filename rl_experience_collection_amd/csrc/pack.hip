@@ -9,8 +9,8 @@ namespace {
 
 // One thread per packed float: pk[((s*kSplit + q)*64 + lane)*OTW + i].
 __global__ void pack_layer_kernel(const float* __restrict__ W, int in, int ld, int out, int steps,
-                                  int first, int otw, float* __restrict__ pk) {
-  const int64_t total = (int64_t)(steps + kPrefetch) * kSplit * 64 * otw;  // incl. zero padding
+                                  int pad, int first, int otw, float* __restrict__ pk) {
+  const int64_t total = (int64_t)(steps + pad) * kSplit * 64 * otw;  // incl. zero padding
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int i = (int)(idx % otw);
@@ -26,7 +26,7 @@ __global__ void pack_layer_kernel(const float* __restrict__ W, int in, int ld, i
     ok = s < kFirstSteps;
   } else {
     k = 16 * (s >> 2) + 4 * g + (s & 3);
-    ok = true;
+    ok = s < steps;
   }
   ok = ok && o < out && k < in;
   pk[idx] = ok ? W[(int64_t)o * ld + k] : 0.0f;
@@ -35,8 +35,9 @@ __global__ void pack_layer_kernel(const float* __restrict__ W, int in, int ld, i
 // bf16 form: pk[(((s*kSplit + q)*64 + lane)*OTW + i)*8 + j], 8 bf16 per
 // (k-step, lane, tile), k = kperm(s, lane / 16, j) of nets.hpp.
 __global__ void pack_layer_bf16_kernel(const float* __restrict__ W, int in, int ld, int out,
-                                       int steps, int first, int otw, uint16_t* __restrict__ pk) {
-  const int64_t total = (int64_t)(steps + kPrefetch) * kSplit * 64 * otw * 8;
+                                       int steps, int pad, int first, int otw,
+                                       uint16_t* __restrict__ pk) {
+  const int64_t total = (int64_t)(steps + pad) * kSplit * 64 * otw * 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int j = (int)(idx % 8);
@@ -86,14 +87,14 @@ __global__ void copy_kernel(const float* __restrict__ src, int n, float* __restr
 hipError_t pack_layer(const float* W, const LayerDesc& d, int ld, float* pk, hipStream_t st) {
   const int64_t total = packed_layer_floats(d);
   hipLaunchKernelGGL(pack_layer_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, W,
-                     d.in, ld, d.out, d.steps, d.first, d.ot / kSplit, pk);
+                     d.in, ld, d.out, d.steps, d.pad, d.first, d.ot / kSplit, pk);
   return hipGetLastError();
 }
 
 hipError_t pack_layer_bf16(const float* W, const LayerDesc& d, int ld, float* pk, hipStream_t st) {
   const int64_t total = packed_layer_floats_bf16(d) * 2;  // bf16 elements
   hipLaunchKernelGGL(pack_layer_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     W, d.in, ld, d.out, d.steps, d.first, d.ot / kSplit,
+                     W, d.in, ld, d.out, d.steps, d.pad, d.first, d.ot / kSplit,
                      reinterpret_cast<uint16_t*>(pk));
   return hipGetLastError();
 }

@@ -40,28 +40,72 @@ constexpr int kThreads = 64 * kSplit;
 template <bool BF16>
 struct ValueShape {
   static constexpr int RT = BF16 ? RL_VALUE_RT_BF16 : RL_VALUE_RT_F32;
-  // 16-byte LDS operands per row tile: the widest activation (512) and the
-  // first-layer state operands
+  // 16-byte LDS operands per row tile of the widest activation (512)
   static constexpr int kTile = BF16 ? 16 * 64 : 32 * 64;
-  static constexpr int kStateTile = BF16 ? 2 * 64 : 4 * 64;
-  static_assert(RT >= 1 && RT <= kSplit, "one wave loads each row tile's states");
+  // the workgroup's state rows as stored, plus slack read (and masked) by
+  // the operand loader past the last row
+  static constexpr int kRaw = RT * kRowsPerWave * kState + 16;
+  static_assert(RT >= 1 && RT <= kSplit, "every row tile's result has a writing wave");
 };
 
-template <bool BF16, int OTW>
-__device__ __forceinline__ void begin(WeightStream<BF16, OTW>& st, const float* W, int64_t w32,
+// First-layer B operands read from the state rows staged in LDS (row-major
+// [16 RT][54]): lane (n = lane % 16, g = lane / 16) of row tile rt takes
+// state_k(g, s) of row 16 rt + n, zero where the k-permutation points past
+// the 54 inputs (the packed weights are zero there as well).
+struct RawStates {
+  const float* raw;
+  __device__ __forceinline__ f32x4 f32(int rt, int grp, int lane) const {
+    const int n = lane & 15, g = lane >> 4;
+    const int k0 = kFirstSteps * g + 4 * grp;
+    const float* p = raw + (rt * kRowsPerWave + n) * kState + k0;
+    const float2 lo = *reinterpret_cast<const float2*>(p);
+    const float2 hi = *reinterpret_cast<const float2*>(p + 2);
+    f32x4 v = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 4 * grp + j;
+      v[j] = (s < kFirstSteps && k0 + j < kState) ? v[j] : 0.0f;
+    }
+    return v;
+  }
+  __device__ __forceinline__ uint4 bf16(int rt, int step, int lane) const {
+    const int n = lane & 15, g = lane >> 4;
+    const int k0 = 32 * step + 8 * g;
+    const float* p = raw + (rt * kRowsPerWave + n) * kState + k0;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p + j);
+      x[j] = k0 + j < kState ? v.x : 0.0f;
+      x[j + 1] = k0 + j + 1 < kState ? v.y : 0.0f;
+    }
+    uint4 w;
+    w.x = pack_bf16x2(x[0], x[1]);
+    w.y = pack_bf16x2(x[2], x[3]);
+    w.z = pack_bf16x2(x[4], x[5]);
+    w.w = pack_bf16x2(x[6], x[7]);
+    return w;
+  }
+};
+
+// The packed block as a buffer resource plus its base pointer (biases and
+// small tables are read through the pointer).
+struct Weights {
+  BufRsrc rs;
+  const float* W;
+};
+
+template <int S, bool BF16, int OTW, int D>
+__device__ __forceinline__ void begin(WeightStream<BF16, OTW, D>& st, const Weights& w, int64_t w32,
                                       int64_t wb, int64_t b_off, int q, int lane) {
-  stream_begin<BF16, OTW>(st, W + (BF16 ? wb : w32), W + b_off, q, lane);
+  stream_begin<S>(st, w.rs, (uint32_t)(4 * (BF16 ? wb : w32)), w.W + b_off, q, lane);
 }
 
-template <bool BF16, int S, int OTW, int RT>
-__device__ __forceinline__ void run(WeightStream<BF16, OTW>& st, const float* W, int64_t w32,
-                                    int64_t wb, const f32x4* buf, int tile_stride,
-                                    f32x4 (&acc)[RT][OTW], int q, int lane) {
-  if constexpr (BF16)
-    stream_layer<S, OTW, RT>(st, W + wb, reinterpret_cast<const uint4*>(buf), tile_stride, acc, q,
-                             lane);
-  else
-    stream_layer<S, OTW, RT>(st, W + w32, buf, tile_stride, acc, q, lane);
+template <int S, bool BF16, int OTW, int D, int RT, class BL>
+__device__ __forceinline__ void run(WeightStream<BF16, OTW, D>& st, const Weights& w, int64_t w32,
+                                    int64_t wb, const BL& bl, f32x4 (&acc)[RT][OTW], int q,
+                                    int lane) {
+  stream_layer<S, OTW, D, RT>(st, w.rs, (uint32_t)(4 * (BF16 ? wb : w32)), bl, acc, q, lane);
 }
 
 template <bool BF16, int OTW, int RT>
@@ -78,7 +122,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   using Sh = ValueShape<BF16>;
   constexpr int RT = Sh::RT;
   constexpr int TS = Sh::kTile;
-  constexpr int SS = Sh::kStateTile;
   // layer k-steps (fp32 / bf16 forms differ) and per-wave output tiles
   constexpr int S1 = BF16 ? kCriticB[0].steps : kCritic[0].steps;
   constexpr int S2 = BF16 ? kCriticB[1].steps : kCritic[1].steps;
@@ -88,72 +131,169 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int SC1 = BF16 ? kCurB[0].steps : kCur[0].steps;
   constexpr int SC2 = BF16 ? kCurB[1].steps : kCur[1].steps;
   __shared__ f32x4 s_buf[RT * TS];
-  __shared__ f32x4 s_state[RT * SS];
+  __shared__ float s_raw[Sh::kRaw];
   __shared__ float s_part[2][RT][kSplit][16];
 
-  const int lane = threadIdx.x & 63;
-  const int q = threadIdx.x >> 6;
-  const int g = lane >> 4;
   const int64_t rows = (int64_t)a.L * a.N;
-  const int64_t tile0 = (int64_t)blockIdx.x * RT;
-  const float* W = a.weights;
+  const int64_t groups = ((rows + kRowsPerWave - 1) / kRowsPerWave + RT - 1) / RT;
 
-  WeightStream<BF16, 8> w1;
-  begin(w1, W, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], q, lane);
+  // Persistent workgroups: the grid is the resident capacity; a workgroup
+  // starts on group blockIdx.x and takes its next group from a work counter
+  // (gridDim.x + ticket), so faster workgroups take more groups.  Across
+  // iterations every LDS buffer's last read and next write are separated by
+  // at least one of the body's barriers, so the loop adds none.
+  __shared__ unsigned long long s_next;
+  // The state rows of a group are loaded into registers one iteration ahead
+  // (once the next group is known) and stored to LDS at the top of the
+  // iteration that uses them.
+  constexpr int kPer = (Sh::kRaw + kThreads - 1) / kThreads;
+  // floats of a group's state rows present in [L][N][54] (the rest read 0)
+  auto avail_of = [&](int64_t g_) -> int {
+    const int64_t av = (rows - g_ * RT * kRowsPerWave) * kState;
+    return av < Sh::kRaw ? (int)av : Sh::kRaw;
+  };
+  auto load_states = [&](int64_t g_, int tid_, float (&v)[kPer]) {
+    const float* base = a.states + g_ * RT * kRowsPerWave * kState;
+    const int avail = avail_of(g_);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {  // clamped, so the loads are unconditional
+      const int e = i * kThreads + tid_;
+      v[i] = base[e < avail ? e : avail - 1];
+    }
+  };
+  float v_states[kPer];
+  int64_t grp = blockIdx.x;
+  if (grp < groups) load_states(grp, (int)threadIdx.x, v_states);
+#pragma unroll 1
+  while (grp < groups) {
+  const int64_t tile0 = grp * RT;
+  // the weight loads are the same every iteration; an opaque zero offset on
+  // the pointer and an opaque copy of the thread index keep the compiler
+  // from hoisting them (and the registers they would hold) out of the loop
+  int32_t opaque0 = 0;  // (an offset, so W keeps the global address space)
+  asm volatile("" : "+s"(opaque0));
+  const float* W = a.weights + opaque0;
+  const Weights wt{weights_rsrc(W, (uint32_t)(4 * kP.total)), W};
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int q = tid >> 6;
+  const int g = lane >> 4;
 
-  // ---- state operands: wave q < RT loads row tile q ----------------------
   const int64_t my_raw = (tile0 + q) * kRowsPerWave + (lane & 15);
   const int64_t my_row = my_raw < rows ? my_raw : rows - 1;  // tail rows recompute the last row
-  if (q < RT) {
-    const float* srow = a.states + my_row * kState;
-    float B[16];
+  // (t, n) of the workgroup's first row; a row tile's rows are row0 + off
+  const int64_t row0 = tile0 * kRowsPerWave;
+  const uint64_t t_base = (uint64_t)(row0 / a.N);
+  const uint32_t n_base = (uint32_t)(row0 - (int64_t)t_base * a.N);
+
+  // ---- the workgroup's 16 RT state rows, contiguous in [L][N][54] (loaded
+  // in v_states): staged in LDS, rows past the end as 0 ------------------
+  // ticket for the next group, taken before the loads below and published
+  // after the first layer (when it has long arrived)
+  unsigned long long ticket = 0;
+  if (tid == 0) ticket = atomicAdd(a.sched, 1ull);
+  Stream<BF16, 8> w1;
+  begin<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], q, lane);
+  {
+    const int avail = avail_of(grp);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int k = state_k<BF16>(g, s);
-      B[s] = k < kState ? srow[k] : 0.0f;
+    for (int i = 0; i < kPer; ++i) {
+      const int e = i * kThreads + tid;
+      if (e < Sh::kRaw) s_raw[e] = e < avail ? v_states[i] : 0.0f;
     }
-    store_state_operands<BF16>(B, s_state + q * SS, lane);
-    store_state_operands<BF16>(B, s_buf + q * TS, lane);
   }
+  const RawStates states_in{s_raw};
+  const LdsOperands acts{s_buf, TS};
   lds_barrier();
 
   // ---- critic -----------------------------------------------------------
-  f32x4 h1[RT][8];
-  run<BF16, S1, 8, RT>(w1, W, kP.critic_w[0], kP.bcritic_w[0], s_buf, TS, h1, q, lane);
-  WeightStream<BF16, 6> w2;
-  begin(w2, W, kP.critic_w[1], kP.bcritic_w[1], kP.critic_b[1], q, lane);
-  lds_barrier();  // every wave has read the input
-  store<BF16, 8, RT>(h1, s_buf, TS, q, lane);
+  // the first layer reads the staged states, so s_buf is free for its output
+  Stream<BF16, 6> w2;
+  if constexpr (BF16 && RT % 2 == 0) {
+    // all k-steps of the bf16 first layer sit in the ring: two passes of
+    // RT / 2 row tiles over the same weight registers halve the accumulators
+    static_assert(S1 < ring_depth(true, 8), "first layer fully prefetched");
+    constexpr int H = RT / 2;
+    f32x4 h1[H][8];
+    run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], states_in, h1, q, lane);
+    store<BF16, 8, H>(h1, s_buf, TS, q, lane);
+    run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], RawStates{s_raw + H * kRowsPerWave * kState},
+            h1, q, lane);
+    begin<S2>(w2, wt, kP.critic_w[1], kP.bcritic_w[1], kP.critic_b[1], q, lane);
+    store<BF16, 8, H>(h1, s_buf + H * TS, TS, q, lane);
+  } else {
+    f32x4 h1[RT][8];
+    run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], states_in, h1, q, lane);
+    begin<S2>(w2, wt, kP.critic_w[1], kP.bcritic_w[1], kP.critic_b[1], q, lane);
+    store<BF16, 8, RT>(h1, s_buf, TS, q, lane);
+  }
+  // every wave read the previous s_next before the barrier above
+  if (tid == 0) s_next = gridDim.x + ticket;
   lds_barrier();  // the output is complete
 
   f32x4 h2[RT][6];
-  run<BF16, S2, 6, RT>(w2, W, kP.critic_w[1], kP.bcritic_w[1], s_buf, TS, h2, q, lane);
-  WeightStream<BF16, 4> w3;
-  begin(w3, W, kP.critic_w[2], kP.bcritic_w[2], kP.critic_b[2], q, lane);
+  run<S2>(w2, wt, kP.critic_w[1], kP.bcritic_w[1], acts, h2, q, lane);
+  Stream<BF16, 4> w3;
+  begin<S3>(w3, wt, kP.critic_w[2], kP.bcritic_w[2], kP.critic_b[2], q, lane);
   lds_barrier();
   store<BF16, 6, RT>(h2, s_buf, TS, q, lane);
   lds_barrier();
 
   f32x4 h3[RT][4];
-  run<BF16, S3, 4, RT>(w3, W, kP.critic_w[2], kP.bcritic_w[2], s_buf, TS, h3, q, lane);
-  WeightStream<BF16, 2> w4;
-  begin(w4, W, kP.critic_w[3], kP.bcritic_w[3], kP.critic_b[3], q, lane);
+  run<S3>(w3, wt, kP.critic_w[2], kP.bcritic_w[2], acts, h3, q, lane);
+  Stream<BF16, 2> w4;
+  begin<S4>(w4, wt, kP.critic_w[3], kP.bcritic_w[3], kP.critic_b[3], q, lane);
+  // what the curiosity and reward epilogue reads, loaded past the register
+  // peak of the wide layers so it arrives during the rest: row (t, n) of
+  // every row tile, its action, its start bar and this wave's partial reward
+  int act[RT];
+  int32_t t_of[RT], start_of[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const uint32_t x = n_base + (uint32_t)(rt * kRowsPerWave + (lane & 15));
+    const uint32_t dt = x / (uint32_t)a.N;
+    int32_t n = (int32_t)(x - dt * (uint32_t)a.N);
+    int32_t t = (int32_t)(t_base + dt);
+    if (t_base + dt >= (uint64_t)a.L) {  // rows past the end: the last row
+      t = a.L - 1;
+      n = a.N - 1;
+    }
+    const int v = a.actions[(int64_t)t * a.N + n];
+    act[rt] = v < 0 ? 0 : (v >= kActions ? kActions - 1 : v);
+    t_of[rt] = t;
+    start_of[rt] = a.start_used[n];
+  }
+  const float partial = q < RT ? a.rewards[my_row] : 0.0f;
   lds_barrier();
   store<BF16, 4, RT>(h3, s_buf, TS, q, lane);
   lds_barrier();
 
   f32x4 h4[RT][2];
-  run<BF16, S4, 2, RT>(w4, W, kP.critic_w[3], kP.bcritic_w[3], s_buf, TS, h4, q, lane);
-  WeightStream<BF16, 1> w5;
-  begin(w5, W, kP.critic_w[4], kP.bcritic_w[4], kP.critic_b[4], q, lane);
+  run<S4>(w4, wt, kP.critic_w[3], kP.bcritic_w[3], acts, h4, q, lane);
+  Stream<BF16, 1> w5;
+  begin<S5>(w5, wt, kP.critic_w[4], kP.bcritic_w[4], kP.critic_b[4], q, lane);
+  // next-bar features of every row tile for the curiosity MSE: lane holds
+  // features 16q + 4g + r
+  f32x4 feat[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float* fn = a.features + ((int64_t)start_of[rt] + t_of[rt] + 1) * kFeatures;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * q + 4 * g + r;  // unconditional load, masked after
+      const float v = fn[j < kFeatures ? j : kFeatures - 1];
+      feat[rt][r] = j < kFeatures ? v : 0.0f;
+    }
+  }
   lds_barrier();
   store<BF16, 2, RT>(h4, s_buf, TS, q, lane);
   lds_barrier();
 
   f32x4 h5[RT][1];
-  run<BF16, S5, 1, RT>(w5, W, kP.critic_w[4], kP.bcritic_w[4], s_buf, TS, h5, q, lane);
-  WeightStream<BF16, 2> c1;
-  begin(c1, W, kP.cur_w[0], kP.bcur_w[0], kP.cur_b[0], q, lane);
+  run<S5>(w5, wt, kP.critic_w[4], kP.bcritic_w[4], acts, h5, q, lane);
+  Stream<BF16, 2> c1;
+  begin<SC1>(c1, wt, kP.cur_w[0], kP.bcur_w[0], kP.cur_b[0], q, lane);
   {
     // 64 -> 1 on the VALU: this wave holds hidden units 16q .. 16q+15
     const float* w6 = W + (BF16 ? kP.bcritic_w6 : kP.critic_w6) + 16 * q + 4 * g;
@@ -172,18 +312,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
 
-  // ---- curiosity layer 1 (reads the state operands, not s_buf) ----------
-  int act[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int64_t raw = (tile0 + rt) * kRowsPerWave + (lane & 15);
-    int v = a.actions[raw < rows ? raw : rows - 1];
-    act[rt] = v < 0 ? 0 : (v >= kActions ? kActions - 1 : v);
-  }
+  // ---- curiosity layer 1 (reads the staged states, not s_buf) -----------
   f32x4 c[RT][2];
-  run<BF16, SC1, 2, RT>(c1, W, kP.cur_w[0], kP.bcur_w[0], s_state, SS, c, q, lane);
-  WeightStream<BF16, 1> c2;
-  begin(c2, W, kP.cur_w[1], kP.bcur_w[1], kP.cur_b[1], q, lane);
+  run<SC1>(c1, wt, kP.cur_w[0], kP.bcur_w[0], states_in, c, q, lane);
+  Stream<BF16, 1> c2;
+  begin<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], kP.cur_b[1], q, lane);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float* oh = W + (BF16 ? kP.bcur_onehot : kP.cur_onehot) + act[rt] * 128 + 4 * g;
@@ -191,6 +324,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int i = 0; i < 2; ++i) c[rt][i] += *reinterpret_cast<const f32x4*>(oh + 16 * (2 * q + i));
   }
   lds_barrier();  // critic input no longer read; value partials visible
+  // the next group (written after this iteration's first barrier): its
+  // state rows load now, during the curiosity layers
+  const int64_t grp_next = (int64_t)s_next;
+  {
+    int tid2 = tid;  // an opaque copy: nothing computed for the staging above is kept live
+    asm volatile("" : "+v"(tid2));
+    // unconditional (clamped group): a conditional load would keep the old
+    // values live through the body
+    load_states(grp_next < groups ? grp_next : groups - 1, tid2, v_states);
+  }
   float value = 0.0f;
   if (q < RT)
     value = W[kP.critic_b6] + ((s_part[0][q][0][lane & 15] + s_part[0][q][1][lane & 15]) +
@@ -200,21 +343,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // ---- curiosity layer 2, MSE against the next bar's features -------------
   f32x4 pr[RT][1];
-  run<BF16, SC2, 1, RT>(c2, W, kP.cur_w[1], kP.bcur_w[1], s_buf, TS, pr, q, lane);
+  run<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], acts, pr, q, lane);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int64_t raw = (tile0 + rt) * kRowsPerWave + (lane & 15);
-    const int64_t row = raw < rows ? raw : rows - 1;
-    const int32_t t = (int32_t)(row / a.N);
-    const int32_t n = (int32_t)(row % a.N);
-    const int64_t bar = (int64_t)a.start_used[n] + t;
-    const float* fn = a.features + (bar + 1) * kFeatures;
     float se = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = 16 * q + 4 * g + r;
       if (j < kFeatures) {
-        const float d = pr[rt][0][r] - fn[j];
+        const float d = pr[rt][0][r] - feat[rt][r];
         se += d * d;
       }
     }
@@ -229,14 +366,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const float sum = (s_part[1][q][0][lane] + s_part[1][q][1][lane]) +
                       (s_part[1][q][2][lane] + s_part[1][q][3][lane]);
     const float bonus = a.ep.curiosity_coef * (sum / (float)kFeatures);
-    int my_act = a.actions[my_row];
-    my_act = my_act < 0 ? 0 : (my_act >= kActions ? kActions - 1 : my_act);
+    int my_act = act[0];
+#pragma unroll
+    for (int rt = 1; rt < RT; ++rt) my_act = q == rt ? act[rt] : my_act;
     const float ex = exposure_of(a.ep, my_act / 9);
-    const float reward = (a.rewards[my_row] + bonus) - a.ep.risk_coef * fabsf(ex);
+    const float reward = (partial + bonus) - a.ep.risk_coef * fabsf(ex);
     a.values[my_row] = value;
     a.rewards[my_row] = reward;
     if (a.counters && (!isfinite(value) || !isfinite(reward))) atomicAdd(a.counters, 1u);
   }
+  // the same value in every lane: keep the loop control scalar
+  grp = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)grp_next) |
+        ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(grp_next >> 32)) << 32);
+  }  // row-tile groups
+}
+
+__global__ void zero_u64_kernel(unsigned long long* p) { p[threadIdx.x] = 0ull; }
+
+// Resident workgroups of a value kernel on the current device (all CUs at
+// the kernel's occupancy), cached per device.
+template <bool BF16>
+int resident_groups() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, value_kernel<BF16>, kThreads, 0) !=
+          hipSuccess)
+    return 0;
+  cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
+  return cache[dev];
 }
 
 }  // namespace
@@ -245,15 +406,17 @@ hipError_t launch_value(const ValueArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.L * a.N;
   if (rows <= 0) return hipSuccess;
   const int64_t tiles = (rows + kRowsPerWave - 1) / kRowsPerWave;
-  if (a.bf16) {
-    constexpr int RT = ValueShape<true>::RT;
-    hipLaunchKernelGGL(value_kernel<true>, dim3((unsigned)((tiles + RT - 1) / RT)), dim3(kThreads),
-                       0, st, a);
-  } else {
-    constexpr int RT = ValueShape<false>::RT;
-    hipLaunchKernelGGL(value_kernel<false>, dim3((unsigned)((tiles + RT - 1) / RT)), dim3(kThreads),
-                       0, st, a);
-  }
+  const int RT = a.bf16 ? ValueShape<true>::RT : ValueShape<false>::RT;
+  const int64_t groups = (tiles + RT - 1) / RT;
+  const int resident = a.bf16 ? resident_groups<true>() : resident_groups<false>();
+  if (resident <= 0) return hipErrorInvalidDevice;
+  const unsigned grid = (unsigned)(groups < resident ? groups : resident);
+  if (!a.sched) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, st, a.sched);
+  if (a.bf16)
+    hipLaunchKernelGGL(value_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(value_kernel<false>, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
