@@ -63,6 +63,13 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run __graft_entry__.build() "
                           "(or python rl_experience_collection_amd/build.py)")
+    # torch's HIP runtime has the same soname as the system one: load it
+    # first, so this library binds to the runtime torch's tensors and streams
+    # live in (loaded first, it would bind torch to the system copy instead)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = C.CDLL(path)
     vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
     L.rollout_config_default.argtypes = [C.POINTER(RolloutConfig), i32, i32]

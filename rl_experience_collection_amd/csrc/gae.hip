@@ -74,19 +74,27 @@ __global__ __launch_bounds__(64 * kGaeWaves) void gae_lookback_kernel(
   const int32_t cnt = active ? max(0, min(kGaeChunk, L - t0)) : 0;
 
   // ---- load this wave's chunk --------------------------------------------
+  // Every load is issued before any is waited on: indices are clamped into
+  // the buffers (steps past the chunk and idle lanes read a valid element
+  // that is never used), so no load sits behind a branch.
   float r[kGaeChunk], v[kGaeChunk], d[kGaeChunk];
+  uint32_t db[kGaeChunk];
+  const int32_t nl = active ? n : N - 1;
 #pragma unroll
   for (int i = 0; i < kGaeChunk; ++i) {
-    if (i < cnt) {
-      const int64_t o = (int64_t)(t0 + i) * N + n;
-      r[i] = rew[o];
-      v[i] = val[o];
-      d[i] = (float)don[o];
-    }
+    const int32_t t = min(t0 + i, L - 1);
+    const int64_t o = (int64_t)t * N + nl;
+    r[i] = rew[o];
+    v[i] = val[o];
+    db[i] = don[o];
   }
+  const int32_t tn = min(t0 + cnt, L - 1);
+  const float v_after = val[(int64_t)tn * N + nl];
+  const float v_last = last_values ? last_values[nl] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < kGaeChunk; ++i) d[i] = (float)db[i];
   float vnext = 0.0f;
-  if (cnt > 0)
-    vnext = (t0 + cnt < L) ? val[(int64_t)(t0 + cnt) * N + n] : (last_values ? last_values[n] : 0.0f);
+  if (cnt > 0) vnext = (t0 + cnt < L) ? v_after : v_last;
 
   // ---- chunk map: delta_t in place of r_t, A_t0 = alpha + beta A_t1 --------
   float alpha = 0.0f, beta = 1.0f;

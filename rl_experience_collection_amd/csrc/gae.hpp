@@ -6,8 +6,14 @@
 
 namespace rl {
 
-constexpr int kGaeChunk = 16;  // steps per wave, held in registers (3 words each)
-constexpr int kGaeWaves = 16;  // waves per workgroup: a super-chunk is 256 steps
+#ifndef RL_GAE_CHUNK
+#define RL_GAE_CHUNK 16
+#endif
+#ifndef RL_GAE_WAVES
+#define RL_GAE_WAVES 16
+#endif
+constexpr int kGaeChunk = RL_GAE_CHUNK;  // steps per wave, held in registers (3 words each)
+constexpr int kGaeWaves = RL_GAE_WAVES;  // waves per workgroup: a super-chunk is 256 steps
 
 inline int32_t cdiv_i(int32_t a, int32_t b) { return (a + b - 1) / b; }
 

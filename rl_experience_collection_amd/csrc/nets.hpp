@@ -166,11 +166,19 @@ struct EnvParams {
   float barrier_scale, spread, risk_coef, curiosity_coef;
 };
 
-__device__ __forceinline__ float exposure_of(const EnvParams& p, int x) {
-  return x == 0 ? p.ex0 : (x == 1 ? p.ex1 : (x == 2 ? p.ex2 : (x == 3 ? p.ex3 : p.ex4)));
-}
-__device__ __forceinline__ float cost_of(const EnvParams& p, int o) {
-  return o == 0 ? p.cost0 : (o == 1 ? p.cost1 : p.cost2);
+// The exposure and cost-rate tables as a small LDS array (exposure of a/9
+// at [0, 5), cost rate of (a%9)/3 at [5, 8)).  Selected with a runtime index
+// from the kernel argument they would become a load from kernel-argument
+// memory, whose wait also drains every outstanding load and store.
+constexpr int kEnvTable = 8;
+__device__ __forceinline__ void fill_env_table(const EnvParams& p, float* t, int tid) {
+  if (tid < kEnvTable) {
+    const float v[kEnvTable] = {p.ex0, p.ex1, p.ex2, p.ex3, p.ex4, p.cost0, p.cost1, p.cost2};
+    float x = v[0];
+#pragma unroll
+    for (int i = 1; i < kEnvTable; ++i) x = tid == i ? v[i] : x;
+    t[tid] = x;
+  }
 }
 
 // OTW consecutive floats of a lane's packed block (OTW in 1, 2, 4, 6, 8).

@@ -133,6 +133,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ f32x4 s_buf[RT * TS];
   __shared__ float s_raw[Sh::kRaw];
   __shared__ float s_part[2][RT][kSplit][16];
+  __shared__ float s_env[kEnvTable];
+  fill_env_table(a.ep, s_env, (int)threadIdx.x);  // read after the loop's first barrier
 
   const int64_t rows = (int64_t)a.L * a.N;
   const int64_t groups = ((rows + kRowsPerWave - 1) / kRowsPerWave + RT - 1) / RT;
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int my_act = act[0];
 #pragma unroll
     for (int rt = 1; rt < RT; ++rt) my_act = q == rt ? act[rt] : my_act;
-    const float ex = exposure_of(a.ep, my_act / 9);
+    const float ex = s_env[my_act / 9];
     const float reward = (partial + bonus) - a.ep.risk_coef * fabsf(ex);
     a.values[my_row] = value;
     a.rewards[my_row] = reward;
