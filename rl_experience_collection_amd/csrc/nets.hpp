@@ -16,8 +16,9 @@ namespace rl {
 //   pk[((s * kSplit + q) * 64 + lane) * OTW + i] = W[o][k]
 //   o = 16 * (q * OTW + i) + lane % 16,   k = kperm(s, lane / 16)
 // (zero when o >= OUT or k >= IN).  First layers (state input) use 16
-// k-steps with kperm(s, g) = 14 g + s (s < 14; steps 14, 15 are zero);
-// chained layers use kperm(s, g) = 16 (s / 4) + 4 g + s % 4, S = IN / 4.
+// k-steps with kperm(s, g) = 14 g + s (s < 14; steps 14, 15 are zero), the
+// actor's with kperm(s, g) = 4 s + g; chained layers use
+// kperm(s, g) = 16 (s / 4) + 4 g + s % 4, S = IN / 4.
 // Bias: pb[16 * ot + j] = b[16 * ot + j], zero padded to 16 * OT.
 // ---------------------------------------------------------------------------
 constexpr int kSplit = 4;
@@ -36,7 +37,9 @@ __host__ __device__ constexpr int ring_depth(bool bf16, int otw) {
 }
 
 // Actor: 54 -> 128 -> 64 -> 45 (PPO CUDA Pipeline Design, Weight Layout).
-constexpr LayerDesc kActor[3] = {{54, 128, 16, 1, 8, 3}, {128, 64, 32, 0, 4, 3}, {64, 45, 16, 0, 4, 3}};
+// Its first layer takes the state in natural order (first = 2: k = 4 s + g),
+// so the portfolio inputs k >= 48 sit in k-steps 12 and 13 only.
+constexpr LayerDesc kActor[3] = {{54, 128, 16, 2, 8, 3}, {128, 64, 32, 0, 4, 3}, {64, 45, 16, 0, 4, 3}};
 // Critic: 54 -> 512 -> 384 -> 256 -> 128 -> 64 (-> 1 handled on the VALU).
 constexpr LayerDesc kCritic[5] = {{54, 512, 16, 1, 32, 0},
                                   {512, 384, 128, 0, 24, 0},
@@ -379,9 +382,33 @@ __device__ __forceinline__ void bload_operands(BufRsrc r, uint32_t vo, uint32_t 
   }
 }
 
+// Weight sources of a streamed layer: byte offsets (lane part + wave-uniform
+// step part) into the packed block, either in global memory through the
+// buffer resource or staged in LDS.
+struct GlobalWeights {
+  BufRsrc rs;
+  template <int OTW>
+  __device__ __forceinline__ void f32(uint32_t lane_b, uint32_t step_b, float (&a)[OTW]) const {
+    bload_operands<OTW>(rs, lane_b, step_b, a);
+  }
+  __device__ __forceinline__ uint4 u4(uint32_t lane_b, uint32_t step_b) const {
+    return bload_u4(rs, lane_b, step_b);
+  }
+};
+struct LdsWeights {
+  const char* base;
+  template <int OTW>
+  __device__ __forceinline__ void f32(uint32_t lane_b, uint32_t step_b, float (&a)[OTW]) const {
+    load_operands<OTW>(reinterpret_cast<const float*>(base + step_b + lane_b), a);
+  }
+  __device__ __forceinline__ uint4 u4(uint32_t lane_b, uint32_t step_b) const {
+    return *reinterpret_cast<const uint4*>(base + step_b + lane_b);
+  }
+};
+
 // pk_b: byte offset of the layer's packed weights in the block; pb: biases.
-template <int S, bool BF16, int OTW, int D>
-__device__ __forceinline__ void stream_begin(WeightStream<BF16, OTW, D>& st, BufRsrc rs,
+template <int S, bool BF16, int OTW, int D, class WS>
+__device__ __forceinline__ void stream_begin(WeightStream<BF16, OTW, D>& st, const WS& ws,
                                              uint32_t pk_b, const float* pb, int q, int lane) {
   constexpr uint32_t kStepB = WeightStream<BF16, OTW, D>::kStep * (BF16 ? 16u : 4u);
   constexpr int kFirst = D - 1 < S ? D - 1 : S;
@@ -394,9 +421,9 @@ __device__ __forceinline__ void stream_begin(WeightStream<BF16, OTW, D>& st, Buf
   for (int j = 0; j < kFirst; ++j) {
     if constexpr (BF16) {
 #pragma unroll
-      for (int i = 0; i < OTW; ++i) st.a[j][i] = bload_u4(rs, lane_b, pk_b + j * kStepB + 16u * i);
+      for (int i = 0; i < OTW; ++i) st.a[j][i] = ws.u4(lane_b, pk_b + j * kStepB + 16u * i);
     } else {
-      bload_operands<OTW>(rs, lane_b, pk_b + j * kStepB, st.a[j]);
+      ws.template f32<OTW>(lane_b, pk_b + j * kStepB, st.a[j]);
     }
   }
 }
@@ -416,8 +443,8 @@ struct LdsOperands {
 
 // fp32: S k-steps of 4 inputs (S % D == 0); a row tile's f32x4 B operand
 // covers a group of 4 steps, read one group ahead.
-template <int S, int OTW, int D, int RT, class BL>
-__device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D>& st, BufRsrc rs,
+template <int S, int OTW, int D, int RT, class WS, class BL>
+__device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D>& st, const WS& ws,
                                              uint32_t pk_b, const BL& bl, f32x4 (&acc)[RT][OTW],
                                              int q, int lane) {
   static_assert(D % 4 == 0 && S % D == 0, "whole groups of D steps");
@@ -437,7 +464,7 @@ __device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D>& st, Bu
     const uint32_t wk = pk_b + (uint32_t)(D * kt + D - 1) * kStepB;
 #pragma unroll
     for (int r = 0; r < D; ++r) {
-      if (!LAST || r == 0) bload_operands<OTW>(rs, lane_b, wk + r * kStepB, st.a[(r + D - 1) % D]);
+      if (!LAST || r == 0) ws.template f32<OTW>(lane_b, wk + r * kStepB, st.a[(r + D - 1) % D]);
       if (r % 4 == 0 && !(LAST && r / 4 == D / 4 - 1)) {
         const int gn = kt * (D / 4) + r / 4 + 1;
 #pragma unroll
@@ -462,8 +489,8 @@ __device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D>& st, Bu
 }
 
 // bf16: S k-steps of 32 inputs; one uint4 of B per row tile and step.
-template <int S, int OTW, int D, int RT, class BL>
-__device__ __forceinline__ void stream_layer(WeightStream<true, OTW, D>& st, BufRsrc rs,
+template <int S, int OTW, int D, int RT, class WS, class BL>
+__device__ __forceinline__ void stream_layer(WeightStream<true, OTW, D>& st, const WS& ws,
                                              uint32_t pk_b, const BL& bl, f32x4 (&acc)[RT][OTW],
                                              int q, int lane) {
   constexpr int KT = S / D;
@@ -482,7 +509,7 @@ __device__ __forceinline__ void stream_layer(WeightStream<true, OTW, D>& st, Buf
   auto step = [&](int s, int slot, uint32_t wsrc, bool load_w, bool load_b) {
     if (load_w) {
 #pragma unroll
-      for (int i = 0; i < OTW; ++i) st.a[(slot + D - 1) % D][i] = bload_u4(rs, lane_b, wsrc + 16u * i);
+      for (int i = 0; i < OTW; ++i) st.a[(slot + D - 1) % D][i] = ws.u4(lane_b, wsrc + 16u * i);
     }
     if (load_b) {
 #pragma unroll

@@ -21,7 +21,10 @@ __global__ void pack_layer_kernel(const float* __restrict__ W, int in, int ld, i
   const int g = lane >> 4;
   int k;
   bool ok;
-  if (first) {
+  if (first == 2) {  // natural order: k = 4 s + g
+    k = 4 * s + g;
+    ok = s < steps;
+  } else if (first) {
     k = kFirstSteps * g + s;
     ok = s < kFirstSteps;
   } else {

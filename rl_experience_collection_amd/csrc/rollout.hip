@@ -34,9 +34,6 @@ namespace rl {
 namespace {
 
 constexpr PackedOffsets kP = packed_offsets();
-constexpr int64_t kActorF32 = kP.actor_end;                  // fp32 actor block (floats)
-constexpr int64_t kActorBF16 = kP.bact_end - kP.bact_begin;  // bf16 actor block (floats)
-constexpr int kActorF4 = (int)((kActorF32 > kActorBF16 ? kActorF32 : kActorBF16) / 4);
 constexpr int kBufA = 8 * 64;  // first-layer output (128 = 8 tiles), then the logits
 constexpr int kBufB = 4 * 64;  // second-layer output (64 = 4 tiles)
 
@@ -84,15 +81,15 @@ __device__ __forceinline__ float row_scan(float x) {
   return x + dpp_f<0x118>(x);  // row_shr:8
 }
 
-// Position of state element k of row-group episode e in the first-layer
-// operand buffer: fp32 as a float index (k = 14 g + s, slot s of lane
-// e + 16 g), bf16 as a 16-bit index (k = 32 s' + 8 g + j).
+// Position of state element k of episode e in the first-layer operand
+// buffer (natural order k = 4 s + g for fp32, k = 32 s + 8 g + j for bf16):
+// fp32 as a float index (slot s of lane e + 16 g), bf16 as a 16-bit index.
 template <bool BF16>
 __device__ __forceinline__ int state_slot(int e, int k) {
   if constexpr (BF16) {
     return ((k >> 5) * 64 + e + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
   } else {
-    const int g = k / kFirstSteps, s = k - kFirstSteps * g;
+    const int s = k >> 2, g = k & 3;
     return ((s >> 2) * 64 + e + 16 * g) * 4 + (s & 3);
   }
 }
@@ -117,38 +114,136 @@ __device__ __forceinline__ void load_features(const float* __restrict__ F, int64
   }
 }
 
-template <int RG, bool BF16>
-__global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(RolloutArgs a) {
-  __shared__ f32x4 s_w[kActorF4];
-  __shared__ f32x4 s_bufA[RG][kBufA];
-  __shared__ f32x4 s_bufB[RG][kBufB];
-  __shared__ f32x4 s_state[RG][4 * 64];
+// Wave q's share of an actor layer, held in registers for the whole kernel:
+// the A operands of its OTW output tiles for k-steps 0..S-1, and its bias.
+template <bool BF16, int S, int OTW>
+struct RegLayer {
+  using Op = typename std::conditional<BF16, uint4, float>::type;
+  Op a[S][OTW];
+  f32x4 bias[OTW];
+};
+
+template <bool BF16, int S, int OTW>
+__device__ __forceinline__ void load_reg_layer(RegLayer<BF16, S, OTW>& L, const float* pk,
+                                               const float* pb, int q, int lane) {
+  constexpr int kStep = kSplit * 64 * OTW;  // packed operands per k-step
+  const int g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < OTW; ++i)
+    L.bias[i] = *reinterpret_cast<const f32x4*>(pb + 16 * (q * OTW + i) + 4 * g);
+  const int lane_off = (q * 64 + lane) * OTW;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) L.a[s][i] = reinterpret_cast<const uint4*>(pk)[s * kStep + lane_off + i];
+    } else {
+      load_operands<OTW>(pk + s * kStep + lane_off, L.a[s]);
+    }
+  }
+}
+
+// acc += sum over k-steps [S0, S1) of A_s B_s, B from the LDS operand layout
+// (fp32: one f32x4 per group of 4 steps; bf16: one uint4 per step), all
+// B reads issued before the first MFMA.
+template <int S0, int S1, bool BF16, int S, int OTW>
+__device__ __forceinline__ void reg_mfma(const RegLayer<BF16, S, OTW>& L, const f32x4* buf,
+                                         f32x4 (&acc)[OTW], int lane) {
+  if constexpr (BF16) {
+    const uint4* bb = reinterpret_cast<const uint4*>(buf);
+    uint4 b[S1 - S0];
+#pragma unroll
+    for (int s = S0; s < S1; ++s) b[s - S0] = bb[s * 64 + lane];
+#pragma unroll
+    for (int s = S0; s < S1; ++s)
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) acc[i] = mfma_bf16(L.a[s][i], b[s - S0], acc[i]);
+  } else {
+    constexpr int G0 = S0 / 4, G1 = (S1 + 3) / 4;
+    f32x4 b[G1 - G0];
+#pragma unroll
+    for (int gr = G0; gr < G1; ++gr) b[gr - G0] = buf[gr * 64 + lane];
+#pragma unroll
+    for (int s = S0; s < S1; ++s)
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) acc[i] = mfma4(L.a[s][i], b[s / 4 - G0][s % 4], acc[i]);
+  }
+}
+
+// The first-layer feature part, one k-step at a time: step<p>() issues the
+// MFMAs of k-step p (the whole part for bf16, where it is one k-step) with
+// scheduling fences on both sides, so callers can place them between
+// independent VALU work.  The B operands are read once, at construction.
+template <bool BF16, int S, int TAIL>
+struct PreStepper {
+  const RegLayer<BF16, S, 2>& L;
+  typename std::conditional<BF16, uint4, f32x4>::type b[BF16 ? TAIL : (TAIL + 3) / 4];
+  __device__ __forceinline__ PreStepper(const RegLayer<BF16, S, 2>& layer, const f32x4* buf, int lane)
+      : L(layer) {
+#pragma unroll
+    for (int i = 0; i < (BF16 ? TAIL : (TAIL + 3) / 4); ++i) {
+      if constexpr (BF16)
+        b[i] = reinterpret_cast<const uint4*>(buf)[i * 64 + lane];
+      else
+        b[i] = buf[i * 64 + lane];
+    }
+  }
+  template <int P>
+  __device__ __forceinline__ void step(f32x4 (&acc)[2]) const {
+    if constexpr (P < TAIL) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (BF16)
+          acc[i] = mfma_bf16(L.a[P][i], b[P], acc[i]);
+        else
+          acc[i] = mfma4(L.a[P][i], b[P / 4][P % 4], acc[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs a) {
+  __shared__ f32x4 s_bufA[kBufA];
+  __shared__ f32x4 s_bufB[kBufB];
+  __shared__ f32x4 s_state[4 * 64];
   __shared__ float s_ln[33];  // ln k for window counts k = 0..32 (ln 0 unused: times 0)
   __shared__ float s_env[kEnvTable];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int rg = wave / kSplit;
-  const int q = wave % kSplit;
+  const int q = threadIdx.x >> 6;
 
   if (threadIdx.x <= 32) s_ln[threadIdx.x] = threadIdx.x == 0 ? 0.0f : logf((float)threadIdx.x);
   fill_env_table(a.ep, s_env, (int)threadIdx.x);
-  {  // stage the packed actor (fp32 or bf16 block) into LDS
-    const int64_t begin = BF16 ? kP.bact_begin : 0;
-    const int n4 = (int)((BF16 ? kActorBF16 : kActorF32) / 4);
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.weights + begin);
-    for (int i = threadIdx.x; i < n4; i += 64 * kSplit * RG) s_w[i] = src[i];
-  }
   // state operands start at zero: the padding slots stay zero
-  for (int i = threadIdx.x; i < RG * 4 * 64; i += 64 * kSplit * RG)
-    (&s_state[0][0])[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  s_state[threadIdx.x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Draw and environment layout: wave q owns episodes 4q .. 4q+3 of its
-  // row group, one row of 16 lanes (j = lane % 16) per episode; a row holds
-  // the episode's portfolio state identically in all 16 lanes.
-  const int e = 4 * q + (lane >> 4);  // episode within the row group
+  // this wave's output tiles of the three layers, in registers throughout
+  // (fp32 first layer: k-steps 14 and 15 only carry zero padding)
+  constexpr int kS1 = BF16 ? kActorB[0].steps : 14;
+  constexpr int kS2 = BF16 ? kActorB[1].steps : kActor[1].steps;
+  constexpr int kS3 = BF16 ? kActorB[2].steps : kActor[2].steps;
+  // first k-step holding a portfolio input (k = 48 .. 53): the steps before
+  // it depend only on market features, known a step ahead
+  constexpr int kTail = BF16 ? 1 : 12;
+  RegLayer<BF16, kS1, 2> w1;
+  RegLayer<BF16, kS2, 1> w2;
+  RegLayer<BF16, kS3, 1> w3;
+  load_reg_layer(w1, a.weights + (BF16 ? kP.bact_w[0] : kP.actor_w[0]),
+                 a.weights + (BF16 ? kP.bact_b[0] : kP.actor_b[0]), q, lane);
+  load_reg_layer(w2, a.weights + (BF16 ? kP.bact_w[1] : kP.actor_w[1]),
+                 a.weights + (BF16 ? kP.bact_b[1] : kP.actor_b[1]), q, lane);
+  load_reg_layer(w3, a.weights + (BF16 ? kP.bact_w[2] : kP.actor_w[2]),
+                 a.weights + (BF16 ? kP.bact_b[2] : kP.actor_b[2]), q, lane);
+
+  // Draw and environment layout: wave q owns episodes 4q .. 4q+3 of the
+  // workgroup's 16, one row of 16 lanes (j = lane % 16) per episode; a row
+  // holds the episode's portfolio state identically in all 16 lanes.
+  const int e = 4 * q + (lane >> 4);
   const int j = lane & 15;
-  const int32_t n_raw = (blockIdx.x * RG + rg) * kRowsPerWave + e;
+  const int32_t n_raw = blockIdx.x * kRowsPerWave + e;
   const bool valid = n_raw < a.N;
   const int32_t n = valid ? n_raw : a.N - 1;
   const EnvParams& ep = a.ep;
@@ -163,13 +258,14 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
     if (clamped && a.counters) atomicAdd(a.counters + 1, 1u);
   }
 
-  const float* sw = reinterpret_cast<const float*>(s_w);
-  f32x4* bufA = s_bufA[rg];
-  f32x4* bufB = s_bufB[rg];
-  f32x4* sbuf = s_state[rg];
+  f32x4* bufA = s_bufA;
+  f32x4* bufB = s_bufB;
+  f32x4* sbuf = s_state;
 
-  float fcur[4];
-  load_features(a.features, st, j, fcur);
+  // features of steps t and t+1 (bars st + t, st + t + 1)
+  float f0[4], f1[4];
+  load_features(a.features, st, j, f0);
+  load_features(a.features, st + 1, j, f1);
   float p0 = a.prices[st], p1 = a.prices[st + 1];
 
   // episode state (PPO CUDA Pipeline Design, Phase A steps 6-8, 12)
@@ -178,81 +274,86 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
   int cnt0 = 0, cnt1 = 0, cnt2 = 0, pushed = 0, pos = 0;
   uint64_t ring = 0;  // 2 bits per window slot
   const float V0 = 1.0f;
-  lds_barrier();  // weights staged, operand buffer cleared
+  lds_barrier();  // operand buffer cleared
   if (j == 2) put_state<BF16>(sbuf, e, 53, ep.spread);  // constant element
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    if (j + 16 * h < kFeatures) put_state<BF16>(sbuf, e, j + 16 * h, f0[h]);
+  lds_barrier();
+  // first-layer feature part of step 0
+  f32x4 pre[2];
+  pre[0] = w1.bias[0];
+  pre[1] = w1.bias[1];
+  reg_mfma<0, kTail>(w1, sbuf, pre, lane);
 
   for (int32_t t = 0; t < a.L; ++t) {
     const int64_t bar = st + t;
     const int64_t o = (int64_t)t * a.N + n;
 
-    // prefetch the next bar (independent of this step's outcome), issued
-    // before this step's stores so that no wait in the step covers them; on
-    // the last step the bar is still inside the buffers and goes unused
-    float fnext[4];
-    load_features(a.features, bar + 1, j, fnext);
+    // prefetch two bars ahead (independent of the outcomes), issued before
+    // this step's stores so that no wait in the step covers them
+    float f2[4];
+    load_features(a.features, bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1, j, f2);
     const float p2 = a.prices[bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1];
 
     // ---- steps 1-2: state = 51 features, V/V0 - 1, exposure held, spread --
+    // (the features are already in the operand buffer)
     const float vn = V / V0 - 1.0f;
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      if (j + 16 * h < kFeatures) put_state<BF16>(sbuf, e, j + 16 * h, fcur[h]);
     if (j == 0) put_state<BF16>(sbuf, e, 51, vn);
     if (j == 1) put_state<BF16>(sbuf, e, 52, e_prev);
     if (valid) {
       float* srow = a.states + o * kState;
 #pragma unroll
       for (int h = 0; h < 4; ++h)
-        if (j + 16 * h < kFeatures) srow[j + 16 * h] = fcur[h];
+        if (j + 16 * h < kFeatures) srow[j + 16 * h] = f0[h];
       if (j < 3) srow[kFeatures + j] = j == 0 ? vn : (j == 1 ? e_prev : ep.spread);
     }
-    lds_barrier();  // state operands written; last step's logits read
+    lds_barrier();  // state operands complete; last step's logits read
 
     // the step's draw depends only on (seed, episode, step)
     const float u = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 0u);
 
     // ---- step 3: actor, a quarter of each layer per wave ------------------
-    // (MFMA layout: lane l computes rows l % 16 of the row group)
+    // (MFMA layout: lane l computes rows l % 16 of the workgroup)
     {
-      f32x4 h[2];
-      if constexpr (BF16) {
-        mfma_layer_bf16<2, 2>(reinterpret_cast<const uint4*>(sw + kP.bact_w[0] - kP.bact_begin),
-                              sw + kP.bact_b[0] - kP.bact_begin,
-                              reinterpret_cast<const uint4*>(sbuf), h, q, lane);
-        relu_store_bf16<2>(h, reinterpret_cast<uint4*>(bufA), q, lane);
-      } else {
-        mfma_layer<16, 2>(sw + kP.actor_w[0], sw + kP.actor_b[0], sbuf, h, q, lane);
-        relu_store<2>(h, bufA, q, lane);
-      }
-    }
-    lds_barrier();
-    {
-      f32x4 h[1];
-      if constexpr (BF16) {
-        mfma_layer_bf16<4, 1>(reinterpret_cast<const uint4*>(sw + kP.bact_w[1] - kP.bact_begin),
-                              sw + kP.bact_b[1] - kP.bact_begin,
-                              reinterpret_cast<const uint4*>(bufA), h, q, lane);
-        relu_store_bf16<1>(h, reinterpret_cast<uint4*>(bufB), q, lane);
-      } else {
-        mfma_layer<32, 1>(sw + kP.actor_w[1], sw + kP.actor_b[1], bufA, h, q, lane);
-        relu_store<1>(h, bufB, q, lane);
-      }
-    }
-    lds_barrier();
-    {
-      f32x4 h[1];
+      f32x4 h[2] = {pre[0], pre[1]};
+      reg_mfma<kTail, kS1>(w1, sbuf, h, lane);
       if constexpr (BF16)
-        mfma_layer_bf16<2, 1>(reinterpret_cast<const uint4*>(sw + kP.bact_w[2] - kP.bact_begin),
-                              sw + kP.bact_b[2] - kP.bact_begin,
-                              reinterpret_cast<const uint4*>(bufB), h, q, lane);
+        relu_store_bf16<2>(h, reinterpret_cast<uint4*>(bufA), q, lane);
       else
-        mfma_layer<16, 1>(sw + kP.actor_w[2], sw + kP.actor_b[2], bufB, h, q, lane);
+        relu_store<2>(h, bufA, q, lane);
+    }
+    lds_barrier();
+    // next step's features into the operand buffer (this step's state has
+    // been read); the next feature part reads them after the next barrier
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      if (j + 16 * h < kFeatures) put_state<BF16>(sbuf, e, j + 16 * h, f1[h]);
+    {
+      f32x4 h[1] = {w2.bias[0]};
+      reg_mfma<0, kS2>(w2, bufA, h, lane);
+      if constexpr (BF16)
+        relu_store_bf16<1>(h, reinterpret_cast<uint4*>(bufB), q, lane);
+      else
+        relu_store<1>(h, bufB, q, lane);
+    }
+    lds_barrier();
+    {
+      f32x4 h[1] = {w3.bias[0]};
+      reg_mfma<0, kS3>(w3, bufB, h, lane);
       // raw logits, fp32 (tile 3 is padding), over the first-layer output,
       // which every wave finished reading before the previous barrier:
       // logit k of row e at bufA[(k / 16) * 64 + e + 16 * (k % 16 / 4)][k % 4]
       bufA[q * 64 + lane] = h[0];
     }
     lds_barrier();
+
+    // first-layer feature part of the next step: its k-steps are spread
+    // over the draw and environment below (one k-step per point, pinned by
+    // scheduling fences), so the MFMAs run while the VALU works
+    pre[0] = w1.bias[0];
+    pre[1] = w1.bias[1];
+    PreStepper<BF16, kS1, kTail> ps(w1, sbuf, lane);
 
     // ---- step 4: softmax, CDF, inverse-CDF draw, log-prob -----------------
     // lane j of the episode's row holds logits k = j + 16 h, h = 0..2
@@ -264,6 +365,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
       ok[h] = j + 16 * h < kActions;
       l[h] = lg[(h * 64 + e + 16 * (j >> 2)) * 4 + (j & 3)];
     }
+    ps.template step<0>(pre);
     int bad = 0;
     float m = -INFINITY;
 #pragma unroll
@@ -273,8 +375,10 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
         m = fmaxf(m, l[h]);
       }
     m = row_max(m);
+    ps.template step<1>(pre);
 #pragma unroll
     for (int h = 0; h < 3; ++h) ex[h] = ok[h] ? expf(l[h] - m) : 0.0f;
+    ps.template step<2>(pre);
     // CDF_k = (totals of the earlier blocks h) + (prefix within block h)
     float T[3], run[3];
 #pragma unroll
@@ -283,6 +387,8 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
       run[h] = row_scan(ex[h]);
     }
     run[1] = T[0] + run[1];
+    ps.template step<3>(pre);
+
     run[2] = (T[0] + T[1]) + run[2];
     const float S = (T[0] + T[1]) + T[2];
     // first k with u < CDF_k, as u * S < (sum of e up to k)
@@ -292,6 +398,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
     for (int h = 2; h >= 0; --h)
       if (ok[h] && uS < run[h]) cand = j + 16 * h;
     int act_a = row_min_i(cand);
+    ps.template step<4>(pre);
     if (act_a == 64) {  // rounding left u >= CDF_44: last action with weight
       int lastk = -1;
 #pragma unroll
@@ -306,6 +413,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
       if (j + 16 * h == act_a) la = l[h];
     la = row_max(la);
     const float logp = (la - m) - logf(S);
+    ps.template step<5>(pre);
     bad = row_max_i(bad);
 
     // ---- step 6: portfolio (exposure fraction of equity, turnover cost) ---
@@ -317,6 +425,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
     const float ret = p1 / p0 - 1.0f;
     const float pnl = exq * ret - cost * fabsf(exq - e_prev);
     V = V * (1.0f + pnl);
+    ps.template step<6>(pre);
 
     // ---- step 7: triple barrier on raw prices ------------------------------
     if (exq != 0.0f) {
@@ -332,6 +441,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
       armed = 0;
     }
     int hit = 0, code = 0;
+    ps.template step<7>(pre);
     if (armed) {
       if (side > 0) {
         if (p1 >= entry * ep.up_pt) { hit = 1; code = 1; }
@@ -347,6 +457,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
     // H = ln n - (sum_c n_c ln n_c) / n, compared as n ln n - sum n_c ln n_c
     // < threshold * n; ln of the counts 0..32 comes from an LDS table
     const int cat = xi <= 1 ? 0 : (xi == 2 ? 1 : 2);
+    ps.template step<8>(pre);
     if (pushed >= ep.div_window) {
       const int old = (int)((ring >> (2 * pos)) & 3u);
       cnt0 -= old == 0; cnt1 -= old == 1; cnt2 -= old == 2;
@@ -356,12 +467,14 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
     ++pushed;
     pos = pos + 1 == ep.div_window ? 0 : pos + 1;
     const int nn = cnt0 + cnt1 + cnt2;
+    ps.template step<9>(pre);
     const float hn = (float)nn * s_ln[nn] -
                      (((float)cnt0 * s_ln[cnt0] + (float)cnt1 * s_ln[cnt1]) + (float)cnt2 * s_ln[cnt2]);
     const float div = hn < ep.div_threshold * (float)nn ? ep.div_penalty : 0.0f;
 
     // ---- steps 10-11: partial reward and stores (lane 0 of the row) -------
     const float partial = pnl * (1.0f + ep.barrier_scale * (float)hit) + div;
+    ps.template step<10>(pre);
     const int done = code != 0;
     if (valid) {
       if (j == 0) {
@@ -381,6 +494,7 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
     }
 
     // ---- step 12: reset on done; the bar pointer keeps advancing ------------
+    ps.template step<11>(pre);
     e_prev = exq;
     if (done) {
       V = 1.0f;
@@ -392,7 +506,10 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
       ring = 0;
     }
 #pragma unroll
-    for (int h = 0; h < 4; ++h) fcur[h] = fnext[h];
+    for (int h = 0; h < 4; ++h) {
+      f0[h] = f1[h];
+      f1[h] = f2[h];
+    }
     p0 = p1;
     p1 = p2;
   }
@@ -402,19 +519,11 @@ __global__ __launch_bounds__(64 * kSplit * RG) void actor_rollout_kernel(Rollout
 
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
   if (a.N <= 0 || a.L <= 0) return hipSuccess;
-  // two 16-episode groups per workgroup once there are enough episodes to
-  // fill every CU with one workgroup; otherwise one group, spread wider
-  const bool two = a.N >= 2 * 16 * 256;
-  const unsigned blocks = (unsigned)(two ? (a.N + 31) / 32 : (a.N + 15) / 16);
-  const dim3 block(64 * kSplit * (two ? 2 : 1));
-  if (two && a.bf16)
-    hipLaunchKernelGGL((actor_rollout_kernel<2, true>), dim3(blocks), block, 0, st, a);
-  else if (two)
-    hipLaunchKernelGGL((actor_rollout_kernel<2, false>), dim3(blocks), block, 0, st, a);
-  else if (a.bf16)
-    hipLaunchKernelGGL((actor_rollout_kernel<1, true>), dim3(blocks), block, 0, st, a);
+  const unsigned blocks = (unsigned)((a.N + kRowsPerWave - 1) / kRowsPerWave);
+  if (a.bf16)
+    hipLaunchKernelGGL(actor_rollout_kernel<true>, dim3(blocks), dim3(64 * kSplit), 0, st, a);
   else
-    hipLaunchKernelGGL((actor_rollout_kernel<1, false>), dim3(blocks), block, 0, st, a);
+    hipLaunchKernelGGL(actor_rollout_kernel<false>, dim3(blocks), dim3(64 * kSplit), 0, st, a);
   return hipGetLastError();
 }
 

@@ -91,21 +91,21 @@ struct RawStates {
 // The packed block as a buffer resource plus its base pointer (biases and
 // small tables are read through the pointer).
 struct Weights {
-  BufRsrc rs;
+  GlobalWeights gw;
   const float* W;
 };
 
 template <int S, bool BF16, int OTW, int D>
 __device__ __forceinline__ void begin(WeightStream<BF16, OTW, D>& st, const Weights& w, int64_t w32,
                                       int64_t wb, int64_t b_off, int q, int lane) {
-  stream_begin<S>(st, w.rs, (uint32_t)(4 * (BF16 ? wb : w32)), w.W + b_off, q, lane);
+  stream_begin<S>(st, w.gw, (uint32_t)(4 * (BF16 ? wb : w32)), w.W + b_off, q, lane);
 }
 
 template <int S, bool BF16, int OTW, int D, int RT, class BL>
 __device__ __forceinline__ void run(WeightStream<BF16, OTW, D>& st, const Weights& w, int64_t w32,
                                     int64_t wb, const BL& bl, f32x4 (&acc)[RT][OTW], int q,
                                     int lane) {
-  stream_layer<S, OTW, D, RT>(st, w.rs, (uint32_t)(4 * (BF16 ? wb : w32)), bl, acc, q, lane);
+  stream_layer<S, OTW, D, RT>(st, w.gw, (uint32_t)(4 * (BF16 ? wb : w32)), bl, acc, q, lane);
 }
 
 template <bool BF16, int OTW, int RT>
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   int32_t opaque0 = 0;  // (an offset, so W keeps the global address space)
   asm volatile("" : "+s"(opaque0));
   const float* W = a.weights + opaque0;
-  const Weights wt{weights_rsrc(W, (uint32_t)(4 * kP.total)), W};
+  const Weights wt{GlobalWeights{weights_rsrc(W, (uint32_t)(4 * kP.total))}, W};
   int tid = (int)threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
