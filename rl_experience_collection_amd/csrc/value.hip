@@ -42,50 +42,11 @@ struct ValueShape {
   static constexpr int RT = BF16 ? RL_VALUE_RT_BF16 : RL_VALUE_RT_F32;
   // 16-byte LDS operands per row tile of the widest activation (512)
   static constexpr int kTile = BF16 ? 16 * 64 : 32 * 64;
-  // the workgroup's state rows as stored, plus slack read (and masked) by
-  // the operand loader past the last row
-  static constexpr int kRaw = RT * kRowsPerWave * kState + 16;
+  // floats of the workgroup's state rows, and 16-byte first-layer operands
+  // per row tile (bf16: 2 k-steps, fp32: 4 groups of 4 k-steps, x 64 lanes)
+  static constexpr int kRaw = RT * kRowsPerWave * kState;
+  static constexpr int kOpTile = BF16 ? 2 * 64 : 4 * 64;
   static_assert(RT >= 1 && RT <= kSplit, "every row tile's result has a writing wave");
-};
-
-// First-layer B operands read from the state rows staged in LDS (row-major
-// [16 RT][54]): lane (n = lane % 16, g = lane / 16) of row tile rt takes
-// state_k(g, s) of row 16 rt + n, zero where the k-permutation points past
-// the 54 inputs (the packed weights are zero there as well).
-struct RawStates {
-  const float* raw;
-  __device__ __forceinline__ f32x4 f32(int rt, int grp, int lane) const {
-    const int n = lane & 15, g = lane >> 4;
-    const int k0 = kFirstSteps * g + 4 * grp;
-    const float* p = raw + (rt * kRowsPerWave + n) * kState + k0;
-    const float2 lo = *reinterpret_cast<const float2*>(p);
-    const float2 hi = *reinterpret_cast<const float2*>(p + 2);
-    f32x4 v = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = 4 * grp + j;
-      v[j] = (s < kFirstSteps && k0 + j < kState) ? v[j] : 0.0f;
-    }
-    return v;
-  }
-  __device__ __forceinline__ uint4 bf16(int rt, int step, int lane) const {
-    const int n = lane & 15, g = lane >> 4;
-    const int k0 = 32 * step + 8 * g;
-    const float* p = raw + (rt * kRowsPerWave + n) * kState + k0;
-    float x[8];
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      const float2 v = *reinterpret_cast<const float2*>(p + j);
-      x[j] = k0 + j < kState ? v.x : 0.0f;
-      x[j + 1] = k0 + j + 1 < kState ? v.y : 0.0f;
-    }
-    uint4 w;
-    w.x = pack_bf16x2(x[0], x[1]);
-    w.y = pack_bf16x2(x[2], x[3]);
-    w.z = pack_bf16x2(x[4], x[5]);
-    w.w = pack_bf16x2(x[6], x[7]);
-    return w;
-  }
 };
 
 // The packed block as a buffer resource plus its base pointer (biases and
@@ -131,7 +92,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int SC1 = BF16 ? kCurB[0].steps : kCur[0].steps;
   constexpr int SC2 = BF16 ? kCurB[1].steps : kCur[1].steps;
   __shared__ f32x4 s_buf[RT * TS];
-  __shared__ float s_raw[Sh::kRaw];
+  __shared__ f32x4 s_opnd[RT * Sh::kOpTile];
   __shared__ float s_part[2][RT][kSplit][16];
   __shared__ float s_env[kEnvTable];
   fill_env_table(a.ep, s_env, (int)threadIdx.x);  // read after the loop's first barrier
@@ -145,27 +106,88 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // iterations every LDS buffer's last read and next write are separated by
   // at least one of the body's barriers, so the loop adds none.
   __shared__ unsigned long long s_next;
-  // The state rows of a group are loaded into registers one iteration ahead
-  // (once the next group is known) and stored to LDS at the top of the
-  // iteration that uses them.
-  constexpr int kPer = (Sh::kRaw + kThreads - 1) / kThreads;
-  // floats of a group's state rows present in [L][N][54] (the rest read 0)
+  // The state rows of the next group are loaded into registers during an
+  // iteration (once that group is known) and written to the first-layer
+  // operand layout as soon as this group's curiosity layer has read it.
+  // Thread tid handles the 16-byte operand chunks c = i * kThreads + tid:
+  // chunk c of the operand buffer is (row tile, k-group, lane) = (c / (64 G),
+  // c / 64 % G, c % 64), i.e. the inputs k0 .. k0 + kCF - 1 of row
+  // 16 rt + lane % 16 for lane group lane / 16; they are consecutive floats
+  // of the state row, and the chunk store is one 16-byte LDS write.
+  constexpr int kG = BF16 ? 2 : 4;          // k-groups per row tile
+  constexpr int kCF = BF16 ? 8 : 4;         // floats per chunk
+  constexpr int kCPT = RT * Sh::kOpTile / kThreads;
+  static_assert(RT * Sh::kOpTile % kThreads == 0, "whole chunks per thread");
+  // floats of a group's state rows present in [L][N][54]
   auto avail_of = [&](int64_t g_) -> int {
     const int64_t av = (rows - g_ * RT * kRowsPerWave) * kState;
     return av < Sh::kRaw ? (int)av : Sh::kRaw;
   };
-  auto load_states = [&](int64_t g_, int tid_, float (&v)[kPer]) {
-    const float* base = a.states + g_ * RT * kRowsPerWave * kState;
-    const int avail = avail_of(g_);
+  auto chunk_k0 = [](int c) {
+    const int gg = (c & 63) >> 4, grp = (c >> 6) & (kG - 1);
+    return BF16 ? 32 * grp + 8 * gg : kFirstSteps * gg + 4 * grp;
+  };
+  // the group's rows through a buffer resource whose extent ends at the last
+  // row present (reads past it return 0: the rows past the end)
+  auto load_states = [&](int64_t g_, int tid_, float (&v)[kCPT][kCF]) {
+    const BufRsrc rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.states + g_ * RT * kRowsPerWave * kState), 0, 4 * avail_of(g_),
+        0x00020000);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {  // clamped, so the loads are unconditional
-      const int e = i * kThreads + tid_;
-      v[i] = base[e < avail ? e : avail - 1];
+    for (int i = 0; i < kCPT; ++i) {
+      const int c = i * kThreads + tid_;
+      const int row = (c >> 6) / kG * kRowsPerWave + (c & 15);
+      const uint32_t off = 4u * (uint32_t)(row * kState + chunk_k0(c));
+#pragma unroll
+      for (int j = 0; j < kCF; j += 2) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs, off + 4u * j, 0, 0);
+        v[i][j] = __uint_as_float(w.x);
+        v[i][j + 1] = __uint_as_float(w.y);
+      }
     }
   };
-  float v_states[kPer];
+  // zero where the k-permutation points past the 54 inputs, then one
+  // 16-byte store per chunk
+  auto scatter_states = [&](int tid_, const float (&v)[kCPT][kCF]) {
+#pragma unroll
+    for (int i = 0; i < kCPT; ++i) {
+      const int c = i * kThreads + tid_;
+      const int k0 = chunk_k0(c);
+      float x[kCF];
+#pragma unroll
+      for (int j = 0; j < kCF; ++j) {
+        const bool ok = BF16 ? k0 + j < kState
+                             : (((c >> 6) & (kG - 1)) * 4 + j < kFirstSteps && k0 + j < kState);
+        x[j] = ok ? v[i][j] : 0.0f;
+      }
+      if constexpr (BF16) {
+        uint4 w;
+        w.x = pack_bf16x2(x[0], x[1]);
+        w.y = pack_bf16x2(x[2], x[3]);
+        w.z = pack_bf16x2(x[4], x[5]);
+        w.w = pack_bf16x2(x[6], x[7]);
+        reinterpret_cast<uint4*>(s_opnd)[c] = w;
+      } else {
+        s_opnd[c] = f32x4{x[0], x[1], x[2], x[3]};
+      }
+    }
+  };
+  // bf16: the first layer (two k-steps, all prefetched) loads at the end of
+  // the previous iteration, so its short MFMA run does not wait on L2
+  Stream<BF16, 8> w1;
+  if constexpr (BF16) {
+    const Weights wt0{GlobalWeights{weights_rsrc(a.weights, (uint32_t)(4 * kP.total))}, a.weights};
+    begin<S1>(w1, wt0, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], (int)threadIdx.x >> 6,
+              (int)threadIdx.x & 63);
+  }
   int64_t grp = blockIdx.x;
-  if (grp < groups) load_states(grp, (int)threadIdx.x, v_states);
+  if (grp < groups) {
+    float v0[kCPT][kCF];
+    load_states(grp, (int)threadIdx.x, v0);
+    scatter_states((int)threadIdx.x, v0);
+  }
+  __syncthreads();
 #pragma unroll 1
   while (grp < groups) {
   const int64_t tile0 = grp * RT;
@@ -189,28 +211,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const uint64_t t_base = (uint64_t)(row0 / a.N);
   const uint32_t n_base = (uint32_t)(row0 - (int64_t)t_base * a.N);
 
-  // ---- the workgroup's 16 RT state rows, contiguous in [L][N][54] (loaded
-  // in v_states): staged in LDS, rows past the end as 0 ------------------
   // ticket for the next group, taken before the loads below and published
   // after the first layer (when it has long arrived)
   unsigned long long ticket = 0;
   if (tid == 0) ticket = atomicAdd(a.sched, 1ull);
-  Stream<BF16, 8> w1;
-  begin<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], q, lane);
-  {
-    const int avail = avail_of(grp);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = i * kThreads + tid;
-      if (e < Sh::kRaw) s_raw[e] = e < avail ? v_states[i] : 0.0f;
-    }
-  }
-  const RawStates states_in{s_raw};
+  if constexpr (!BF16) begin<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], q, lane);
+  // (this group's operands were scattered before the previous barrier)
+  const LdsOperands states_in{s_opnd, Sh::kOpTile};
   const LdsOperands acts{s_buf, TS};
-  lds_barrier();
 
   // ---- critic -----------------------------------------------------------
-  // the first layer reads the staged states, so s_buf is free for its output
+  // the first layer reads the state operands, so s_buf is free for its output
   Stream<BF16, 6> w2;
   if constexpr (BF16 && RT % 2 == 0) {
     // all k-steps of the bf16 first layer sit in the ring: two passes of
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     f32x4 h1[H][8];
     run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], states_in, h1, q, lane);
     store<BF16, 8, H>(h1, s_buf, TS, q, lane);
-    run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], RawStates{s_raw + H * kRowsPerWave * kState},
+    run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], LdsOperands{s_opnd + H * Sh::kOpTile, Sh::kOpTile},
             h1, q, lane);
     begin<S2>(w2, wt, kP.critic_w[1], kP.bcritic_w[1], kP.critic_b[1], q, lane);
     store<BF16, 8, H>(h1, s_buf + H * TS, TS, q, lane);
@@ -238,6 +249,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   run<S2>(w2, wt, kP.critic_w[1], kP.bcritic_w[1], acts, h2, q, lane);
   Stream<BF16, 4> w3;
   begin<S3>(w3, wt, kP.critic_w[2], kP.bcritic_w[2], kP.critic_b[2], q, lane);
+  // the next group (published after the first layer): its state rows load
+  // past the register peak of the wide layers (fp32 here, bf16 two layers
+  // later), in flight until the scatter below; unconditional (clamped
+  // group), since a conditional load would keep the old values live
+  const int64_t grp_next = (int64_t)s_next;
+  float v_states[kCPT][kCF];
+  auto prefetch_next = [&]() {
+    int tid2 = tid;  // an opaque copy: nothing computed for the scatter is kept live
+    asm volatile("" : "+v"(tid2));
+    load_states(grp_next < groups ? grp_next : groups - 1, tid2, v_states);
+  };
+  if constexpr (!BF16) prefetch_next();
   lds_barrier();
   store<BF16, 6, RT>(h2, s_buf, TS, q, lane);
   lds_barrier();
@@ -275,6 +298,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   run<S4>(w4, wt, kP.critic_w[3], kP.bcritic_w[3], acts, h4, q, lane);
   Stream<BF16, 1> w5;
   begin<S5>(w5, wt, kP.critic_w[4], kP.bcritic_w[4], kP.critic_b[4], q, lane);
+  if constexpr (BF16) prefetch_next();
   // next-bar features of every row tile for the curiosity MSE: lane holds
   // features 16q + 4g + r
   f32x4 feat[RT];
@@ -314,7 +338,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
 
-  // ---- curiosity layer 1 (reads the staged states, not s_buf) -----------
+  // ---- curiosity layer 1 (reads the state operands, not s_buf) ----------
   f32x4 c[RT][2];
   run<SC1>(c1, wt, kP.cur_w[0], kP.bcur_w[0], states_in, c, q, lane);
   Stream<BF16, 1> c2;
@@ -326,16 +350,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int i = 0; i < 2; ++i) c[rt][i] += *reinterpret_cast<const f32x4*>(oh + 16 * (2 * q + i));
   }
   lds_barrier();  // critic input no longer read; value partials visible
-  // the next group (written after this iteration's first barrier): its
-  // state rows load now, during the curiosity layers
-  const int64_t grp_next = (int64_t)s_next;
-  {
-    int tid2 = tid;  // an opaque copy: nothing computed for the staging above is kept live
-    asm volatile("" : "+v"(tid2));
-    // unconditional (clamped group): a conditional load would keep the old
-    // values live through the body
-    load_states(grp_next < groups ? grp_next : groups - 1, tid2, v_states);
-  }
+  // the next group's state operands (the last reader of this group's was
+  // the curiosity layer above); the final barrier makes them visible
+  if (grp_next < groups) scatter_states(tid, v_states);
   float value = 0.0f;
   if (q < RT)
     value = W[kP.critic_b6] + ((s_part[0][q][0][lane & 15] + s_part[0][q][1][lane & 15]) +
@@ -346,6 +363,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // ---- curiosity layer 2, MSE against the next bar's features -------------
   f32x4 pr[RT][1];
   run<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], acts, pr, q, lane);
+  if constexpr (BF16) begin<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], q, lane);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     float se = 0.0f;
