@@ -157,6 +157,28 @@ def cpu_baseline(inp, n_episodes):
                        f"workload; episodes are independent; host CPU: {cpu}")
 
 
+def run_single(name, steps, warmup):
+    """One workload, for profiler counter passes."""
+    import torch
+    import synthdata
+    if name.startswith("collect"):
+        inp = synthdata.ppo_inputs("ppo_n128_l500" if name == "collect_n128_fp32" else "ppo_n8192_l500")
+        r = time_collect(inp, steps, warmup, precision=1 if name.endswith("bf16") else 0)
+        return dict(workload=name, ms_per_step=r["wall_s"] * 1000 / steps,
+                    phases_ms=[float(x) for x in r["phases_ms"]])
+    if name.startswith("gae"):
+        spec = (synthdata.WORKLOADS["gae_n4096_l2048"] if name == "gae_n4096_l2048"
+                else dict(N=8192, L=500, seed=synthdata.WORKLOADS["ppo_n8192_l500"]["seed"]))
+        r = time_gae(spec, steps)
+        return dict(workload=name, cold_ms=r["cold_ms"], warm_ms=r["warm_ms"])
+    a = torch.ones(1 << 28, device="cuda")  # copy_1gib: 1 GiB read + 1 GiB written per copy
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return dict(workload=name, copies=steps, bytes_each_way=1 << 30)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +186,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-episodes", type=int, default=2560)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="all",
+                    choices=("all", "collect_n8192_fp32", "collect_n8192_bf16", "collect_n128_fp32",
+                             "gae_n4096_l2048", "gae_n8192_l500", "copy_1gib"),
+                    help="one workload only (for profiler counter passes); prints its own "
+                         "JSON line instead of the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the collection shards by episode and runs with no "
@@ -175,6 +202,10 @@ def main():
     import torch
     import synthdata
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+
+    if args.workload != "all":
+        print(json.dumps(run_single(args.workload, args.steps, args.warmup)), flush=True)
+        return
 
     spec = dict(synthdata.WORKLOADS["ppo_n8192_l500"])
     log("generating inputs ...")
@@ -189,8 +220,9 @@ def main():
     bfr = time_collect(big_inp, args.steps, args.warmup, precision=1)
     log("timing N=128 L=500 fp32 ...")
     small = time_collect(synthdata.ppo_inputs("ppo_n128_l500"), args.steps, args.warmup)
-    log("timing GAE N=4096 L=2048 ...")
+    log("timing GAE N=4096 L=2048 and N=8192 L=500 ...")
     gae = time_gae(synthdata.WORKLOADS["gae_n4096_l2048"], max(args.steps, 20))
+    gae_c = time_gae(dict(N=N, L=L, seed=spec["seed"]), max(args.steps, 20))
 
     value_files = ["rl_experience_collection_amd/csrc/value.hip",
                    "rl_experience_collection_amd/csrc/nets.hpp",
@@ -236,7 +268,14 @@ def main():
                 value=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / 1e9, unit="GB/s",
                 frac_of_hbm_peak=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / PEAK_HBM,
                 cold_ms=gae["cold_ms"], warm_ms=gae["warm_ms"],
-                warm_GBps=GAE_BYTES * gae["elements"] / (gae["warm_ms"] * 1e-3) / 1e9)),
+                warm_GBps=GAE_BYTES * gae["elements"] / (gae["warm_ms"] * 1e-3) / 1e9),
+            gae_scan_n8192_l500=dict(
+                value=GAE_BYTES * gae_c["elements"] / (gae_c["cold_ms"] * 1e-3) / 1e9, unit="GB/s",
+                frac_of_hbm_peak=GAE_BYTES * gae_c["elements"] / (gae_c["cold_ms"] * 1e-3) / PEAK_HBM,
+                cold_ms=gae_c["cold_ms"], warm_ms=gae_c["warm_ms"],
+                warm_GBps=GAE_BYTES * gae_c["elements"] / (gae_c["warm_ms"] * 1e-3) / 1e9,
+                warm_frac_of_hbm_peak=GAE_BYTES * gae_c["elements"] / (gae_c["warm_ms"] * 1e-3)
+                / PEAK_HBM)),
     )
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
