@@ -101,7 +101,7 @@ int gae_run(GaeScratch& s, const rl::GaeArgs& a, hipStream_t st) {
   if (rc) return rc;
   hipError_t e = rl::gae_launch(a, shape, view, st);
   if (e != hipSuccess) return hip_fail(e, "gae_scan launch");
-  s.ticket_base += (uint32_t)shape.tiles();
+  if (shape.nk > 1) s.ticket_base += (uint32_t)shape.tiles();  // tickets are taken only then
   return ROLLOUT_OK;
 }
 

@@ -12,8 +12,12 @@ namespace rl {
 #ifndef RL_GAE_WAVES
 #define RL_GAE_WAVES 16
 #endif
-constexpr int kGaeChunk = RL_GAE_CHUNK;  // steps per wave, held in registers (3 words each)
-constexpr int kGaeWaves = RL_GAE_WAVES;  // waves per workgroup: a super-chunk is 256 steps
+constexpr int kGaeChunk = RL_GAE_CHUNK;  // steps per thread, held in registers (3 words each)
+constexpr int kGaeWaves = RL_GAE_WAVES;  // waves per workgroup
+// A column is 32 or 64 episodes: 2 or 1 time slots per wave, super-chunks of
+// 512 or 256 steps.
+constexpr int gae_slots(int cols) { return kGaeWaves * 64 / cols; }
+constexpr int gae_super(int cols) { return gae_slots(cols) * kGaeChunk; }
 
 inline int32_t cdiv_i(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
@@ -29,7 +33,8 @@ struct GaeArgs {
 };
 
 struct GaeShape {
-  int32_t nc, nk;  // 64-episode columns and super-chunks
+  int32_t cols;    // episodes per column (32 or 64)
+  int32_t nc, nk;  // columns and super-chunks
   int64_t tiles() const { return (int64_t)nc * nk; }
 };
 

@@ -43,7 +43,8 @@ def check(r, v, d, gamma=0.99, lam=0.95, last=None, offset=0):
 
 
 @pytest.mark.parametrize("L,N", [(1, 1), (2, 3), (17, 5), (16, 1024), (100, 16), (37, 1000),
-                                 (33, 2049), (500, 8192), (129, 4100)])
+                                 (33, 2049), (500, 8192), (129, 4100), (512, 96), (513, 31),
+                                 (700, 33), (1025, 100), (1537, 40)])
 def test_gae_matches_oracle(L, N):
     r, v, d = synthdata.gae_inputs(N, L, seed=L * 7 + N)
     check(r, v, d)
@@ -78,11 +79,20 @@ def test_gae_dense_dones_and_extreme_params():
     assert np.array_equal(A, r - v)
 
 
-def test_gae_deterministic_across_calls():
-    r, v, d = synthdata.gae_inputs(4096, 512, seed=3)
+@pytest.mark.parametrize("L,N", [(512, 4096), (2048, 1024)])
+def test_gae_deterministic_across_calls(L, N):
+    r, v, d = synthdata.gae_inputs(N, L, seed=3)
     A1, R1 = run(r, v, d)
     A2, R2 = run(r, v, d)
     assert np.array_equal(A1, A2) and np.array_equal(R1, R2)
+
+
+@pytest.mark.parametrize("p_done", [0.0, 0.0005])
+def test_gae_long_chains(p_done):
+    """Rollouts of many super-chunks: carries cross more super-chunks than a
+    reader folds before it waits on an inclusive value."""
+    r, v, d = synthdata.gae_inputs(64, 5000, seed=11, p_done=p_done)
+    check(r, v, d)
 
 
 def test_gae_empty_is_noop():
