@@ -98,9 +98,24 @@ def time_collect(inp, steps, warmup, precision=0):
                 nonfinite=bad)
 
 
-def time_gae(spec, reps):
+def probe_lib():
+    """Measurement kernels (weight-stream and GAE-traffic ceilings), built
+    beside the collection library."""
+    import ctypes as C
+    import torch  # noqa: F401  (the HIP runtime must be loaded through torch first)
+    lib = C.CDLL(os.path.join(ROOT, "rl_experience_collection_amd", "libbenchprobes.so"))
+    P = C.c_void_p
+    lib.bench_value_stream_shape.argtypes = [C.c_int, C.POINTER(C.c_longlong), C.POINTER(C.c_int)]
+    lib.bench_weight_stream.argtypes = [P, C.c_longlong, C.c_longlong, P, P]
+    lib.bench_gae_traffic.argtypes = [P, P, P, P, P, C.c_longlong, P]
+    return lib
+
+
+def time_gae(spec, reps, traffic_only=False):
     """Cold: a 512 MiB read sweep evicts the 256 MB infinity cache with clean
-    lines before each timed launch.  Warm: back-to-back launches."""
+    lines before each timed launch.  Warm: back-to-back launches.  With
+    traffic_only, the element-wise kernel that moves the same bytes is timed
+    instead of the scan (the copy ceiling at this size)."""
     import numpy as np
     import torch
     import synthdata
@@ -110,26 +125,71 @@ def time_gae(spec, reps):
     R, V, D = (torch.from_numpy(x).cuda() for x in (r, v, d))
     A, Rt = torch.empty_like(R), torch.empty_like(R)
     flush = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    if traffic_only:
+        lib, st = probe_lib(), torch.cuda.current_stream().cuda_stream
+
+        def launch():
+            rc = lib.bench_gae_traffic(R.data_ptr(), V.data_ptr(), D.data_ptr(), A.data_ptr(),
+                                       Rt.data_ptr(), R.numel(), st)
+            if rc:
+                raise RuntimeError(f"bench_gae_traffic: {rc}")
+    else:
+        def launch():
+            rx.gae_scan(R, V, D, None, 0.99, 0.95, A, Rt)
     ev = rx.HipEvents(2)
     cold = []
     for i in range(reps + 2):
         flush.sum()
         ev.record(0)
-        rx.gae_scan(R, V, D, None, 0.99, 0.95, A, Rt)
+        launch()
         ev.record(1)
         torch.cuda.synchronize()
         if i >= 2:
             cold.append(ev.elapsed_ms(0, 1))
-    rx.gae_scan(R, V, D, None, 0.99, 0.95, A, Rt)
+    launch()
     ev.record(0)
     for i in range(reps):
-        rx.gae_scan(R, V, D, None, 0.99, 0.95, A, Rt)
+        launch()
     ev.record(1)
     torch.cuda.synchronize()
     warm = ev.elapsed_ms(0, 1) / reps
     ev.close()
     n = spec["N"] * spec["L"]
     return dict(elements=n, cold_ms=float(np.median(cold)), warm_ms=float(warm))
+
+
+def time_weight_stream(rows, bf16, reps):
+    """The value kernel's weight stream alone (no arithmetic) for `rows`
+    stored states: the L2-to-register bound of that kernel."""
+    import ctypes as C
+    import torch
+    import rl_experience_collection_amd as rx
+    lib = probe_lib()
+    nbytes, per = C.c_longlong(), C.c_int()
+    if lib.bench_value_stream_shape(int(bf16), C.byref(nbytes), C.byref(per)):
+        raise RuntimeError("bench_value_stream_shape failed")
+    groups = -(-rows // per.value)
+    blob = torch.randn(nbytes.value // 4, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = lib.bench_weight_stream(blob.data_ptr(), nbytes.value, groups, sink.data_ptr(), st)
+        if rc:
+            raise RuntimeError(f"bench_weight_stream: {rc}")
+    for _ in range(2):
+        launch()
+    ev = rx.HipEvents(2)
+    ev.record(0)
+    for _ in range(reps):
+        launch()
+    ev.record(1)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / reps
+    ev.close()
+    total = nbytes.value * groups
+    return dict(ms=ms, block_bytes=nbytes.value, rows_per_item=per.value, items=groups,
+                bytes_per_launch=total, TBps=total / (ms * 1e-3) / 1e12)
 
 
 def cpu_baseline(inp, n_episodes):
@@ -167,10 +227,12 @@ def run_single(name, steps, warmup):
         return dict(workload=name, ms_per_step=r["wall_s"] * 1000 / steps,
                     phases_ms=[float(x) for x in r["phases_ms"]])
     if name.startswith("gae"):
-        spec = (synthdata.WORKLOADS["gae_n4096_l2048"] if name == "gae_n4096_l2048"
+        spec = (synthdata.WORKLOADS["gae_n4096_l2048"] if name.endswith("n4096_l2048")
                 else dict(N=8192, L=500, seed=synthdata.WORKLOADS["ppo_n8192_l500"]["seed"]))
-        r = time_gae(spec, steps)
+        r = time_gae(spec, steps, traffic_only=name.startswith("gae_traffic"))
         return dict(workload=name, cold_ms=r["cold_ms"], warm_ms=r["warm_ms"])
+    if name.startswith("weight_stream"):
+        return dict(workload=name, **time_weight_stream(8192 * 500, name.endswith("bf16"), steps))
     a = torch.ones(1 << 28, device="cuda")  # copy_1gib: 1 GiB read + 1 GiB written per copy
     b = torch.empty_like(a)
     for _ in range(steps):
@@ -188,7 +250,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="all",
                     choices=("all", "collect_n8192_fp32", "collect_n8192_bf16", "collect_n128_fp32",
-                             "gae_n4096_l2048", "gae_n8192_l500", "copy_1gib"),
+                             "gae_n4096_l2048", "gae_n8192_l500", "gae_traffic_n4096_l2048",
+                             "gae_traffic_n8192_l500", "weight_stream_fp32", "weight_stream_bf16",
+                             "copy_1gib"),
                     help="one workload only (for profiler counter passes); prints its own "
                          "JSON line instead of the benchmark line")
     args = ap.parse_args()
@@ -223,6 +287,11 @@ def main():
     log("timing GAE N=4096 L=2048 and N=8192 L=500 ...")
     gae = time_gae(synthdata.WORKLOADS["gae_n4096_l2048"], max(args.steps, 20))
     gae_c = time_gae(dict(N=N, L=L, seed=spec["seed"]), max(args.steps, 20))
+    log("timing the ceilings: GAE traffic element-wise, value-kernel weight stream ...")
+    gae_x = time_gae(synthdata.WORKLOADS["gae_n4096_l2048"], max(args.steps, 20), traffic_only=True)
+    gae_cx = time_gae(dict(N=N, L=L, seed=spec["seed"]), max(args.steps, 20), traffic_only=True)
+    ws_f = time_weight_stream(N * L, False, 5)
+    ws_b = time_weight_stream(N * L, True, 5)
 
     value_files = ["rl_experience_collection_amd/csrc/value.hip",
                    "rl_experience_collection_amd/csrc/nets.hpp",
@@ -235,7 +304,9 @@ def main():
                                  "copy-calibrated; null if the kernel changed since)",
                     algorithmic_bytes_per_launch=4096000 * 436,
                     kernel="value_kernel (critic + curiosity, fp32 MFMA 16x16x4)",
-                    flop_per_launch=VALUE_KERNEL_FLOP * N * L, avg_launch_ms=t_val)
+                    flop_per_launch=VALUE_KERNEL_FLOP * N * L, avg_launch_ms=t_val,
+                    weight_stream_bound=dict(ms=ws_f["ms"], TBps=ws_f["TBps"],
+                                             bytes_per_launch=ws_f["bytes_per_launch"]))
     mlp_util = MLP_FLOP * N * L / ((t_roll + t_val) * 1e-3) / PEAK_FP32_MFMA
     gae_in = 17 * N * L / (t_gae * 1e-3)
 
@@ -258,7 +329,13 @@ def main():
                                    map(float, bfr["phases_ms"]))),
                 value_kernel_TFLOPs=VALUE_KERNEL_FLOP * N * L / (bfr["phases_ms"][1] * 1e-3) / 1e12,
                 value_kernel_frac_of_bf16_peak=VALUE_KERNEL_FLOP * N * L /
-                (bfr["phases_ms"][1] * 1e-3) / PEAK_BF16_MFMA),
+                (bfr["phases_ms"][1] * 1e-3) / PEAK_BF16_MFMA,
+                # the value kernel streams its weights from L2 once per work item:
+                # the bound is the slower of the MFMA peak and that stream alone
+                weight_stream_bound_ms=ws_b["ms"], weight_stream_TBps=ws_b["TBps"],
+                weight_stream_bytes_per_launch=ws_b["bytes_per_launch"],
+                value_kernel_frac_of_bound=max(ws_b["ms"], VALUE_KERNEL_FLOP * N * L /
+                                               PEAK_BF16_MFMA * 1e3) / float(bfr["phases_ms"][1])),
             ppo_collect_n128_l500_fp32=dict(
                 value=128 * 500 * args.steps / small["wall_s"], unit="experiences/s",
                 ms_per_step=small["wall_s"] * 1000 / args.steps,
@@ -268,14 +345,18 @@ def main():
                 value=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / 1e9, unit="GB/s",
                 frac_of_hbm_peak=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / PEAK_HBM,
                 cold_ms=gae["cold_ms"], warm_ms=gae["warm_ms"],
-                warm_GBps=GAE_BYTES * gae["elements"] / (gae["warm_ms"] * 1e-3) / 1e9),
+                warm_GBps=GAE_BYTES * gae["elements"] / (gae["warm_ms"] * 1e-3) / 1e9,
+                copy_ceiling_cold_ms=gae_x["cold_ms"], copy_ceiling_warm_ms=gae_x["warm_ms"],
+                frac_of_copy_ceiling_cold=gae_x["cold_ms"] / gae["cold_ms"]),
             gae_scan_n8192_l500=dict(
                 value=GAE_BYTES * gae_c["elements"] / (gae_c["cold_ms"] * 1e-3) / 1e9, unit="GB/s",
                 frac_of_hbm_peak=GAE_BYTES * gae_c["elements"] / (gae_c["cold_ms"] * 1e-3) / PEAK_HBM,
                 cold_ms=gae_c["cold_ms"], warm_ms=gae_c["warm_ms"],
                 warm_GBps=GAE_BYTES * gae_c["elements"] / (gae_c["warm_ms"] * 1e-3) / 1e9,
                 warm_frac_of_hbm_peak=GAE_BYTES * gae_c["elements"] / (gae_c["warm_ms"] * 1e-3)
-                / PEAK_HBM)),
+                / PEAK_HBM,
+                copy_ceiling_cold_ms=gae_cx["cold_ms"], copy_ceiling_warm_ms=gae_cx["warm_ms"],
+                frac_of_copy_ceiling_cold=gae_cx["cold_ms"] / gae_c["cold_ms"])),
     )
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")

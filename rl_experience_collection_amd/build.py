@@ -9,6 +9,9 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(os.path.dirname(PKG), "_build", "rollout")
 LIB = os.path.join(PKG, "librollout.so")
 SOURCES = ["abi.hip", "pack.hip", "rollout.hip", "value.hip", "gae.hip"]
+# measurement kernels used by bench.py only, in a library of their own
+PROBE_LIB = os.path.join(PKG, "libbenchprobes.so")
+PROBE_SOURCES = ["bench_probes.hip"]
 ARCH = os.environ.get("ROLLOUT_OFFLOAD_ARCH", "gfx950")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -30,20 +33,26 @@ def _compile(src):
     return obj, err
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for _, err in results:
-        if verbose and err.strip():
-            print(err)
-    objs = [o for o, _ in results]
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        results = list(ex.map(_compile, srcs))
+    for _, err in results:
+        if verbose and err.strip():
+            print(err)
+    objs = [o for o, _ in results]
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 

@@ -28,6 +28,19 @@ struct LayerDesc {
   int pad;                         // zero k-steps after the layer (ring prefetch reach)
 };
 
+// Row tiles of 16 rows per value-kernel work item: every work item streams
+// the whole critic and curiosity weight block once, so rows per work item
+// set the weight-stream bytes per row.
+#ifndef RL_VALUE_RT_F32
+#define RL_VALUE_RT_F32 2
+#endif
+#ifndef RL_VALUE_RT_BF16
+#define RL_VALUE_RT_BF16 4
+#endif
+__host__ __device__ constexpr int value_row_tiles(bool bf16) {
+  return bf16 ? RL_VALUE_RT_BF16 : RL_VALUE_RT_F32;
+}
+
 // Weight-ring slots of a streamed layer (value kernel): layers with few
 // output tiles per wave issue little MFMA work per k-step, so they keep more
 // steps in flight (fp32: the whole layer for one tile per wave; bf16: up to

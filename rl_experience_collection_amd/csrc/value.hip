@@ -29,17 +29,11 @@ namespace rl {
 namespace {
 
 constexpr PackedOffsets kP = packed_offsets();
-#ifndef RL_VALUE_RT_F32
-#define RL_VALUE_RT_F32 2
-#endif
-#ifndef RL_VALUE_RT_BF16
-#define RL_VALUE_RT_BF16 4
-#endif
 constexpr int kThreads = 64 * kSplit;
 
 template <bool BF16>
 struct ValueShape {
-  static constexpr int RT = BF16 ? RL_VALUE_RT_BF16 : RL_VALUE_RT_F32;
+  static constexpr int RT = value_row_tiles(BF16);
   // 16-byte LDS operands per row tile of the widest activation (512)
   static constexpr int kTile = BF16 ? 16 * 64 : 32 * 64;
   // floats of the workgroup's state rows, and 16-byte first-layer operands
