@@ -49,6 +49,25 @@ class Outputs(C.Structure):
         "rewards", "dones", "barrier", "adv", "ret")]
 
 
+class QNet(C.Structure):
+    _fields_ = [("w", C.c_void_p * 6), ("b", C.c_void_p * 6)]
+
+
+class DqnNets(C.Structure):
+    _fields_ = [("online", QNet), ("target", QNet),
+                ("cw", C.c_void_p * 2), ("cb", C.c_void_p * 2)]
+
+
+class DqnParams(C.Structure):
+    _fields_ = [("epsilon", C.c_float), ("alpha", C.c_float)]
+
+
+class DqnOutputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "states", "next_states", "q_values", "actions", "explored", "q_gap", "q_taken",
+        "q_next_max", "rewards", "dones", "barrier", "td", "priority")]
+
+
 class Episode(C.Structure):
     _fields_ = [
         ("V", C.c_float), ("e_prev", C.c_float),
@@ -99,6 +118,15 @@ def lib():
         L.orc_rollout.argtypes = [C.POINTER(Params), C.POINTER(Nets), vp, vp, C.c_int64, vp,
                                   C.c_uint64, vp, vp, i32, C.POINTER(Outputs), i32]
         L.orc_rollout.restype = C.c_int
+        L.orc_dueling_q.argtypes = [C.POINTER(QNet), vp, C.c_int, vp]
+        L.orc_argmax_first.argtypes = [vp, C.c_int]
+        L.orc_argmax_first.restype = C.c_int
+        L.orc_random_action.argtypes = [f32]
+        L.orc_random_action.restype = C.c_int
+        L.orc_dqn_rollout.argtypes = [C.POINTER(Params), C.POINTER(DqnParams), C.POINTER(DqnNets),
+                                      vp, vp, C.c_int64, vp, C.c_uint64, vp, vp, i32,
+                                      C.POINTER(DqnOutputs), i32]
+        L.orc_dqn_rollout.restype = C.c_int
         _lib = L
     return _lib
 
@@ -272,4 +300,82 @@ def rollout(inputs: dict, precision: int = FP32, forced_actions=None, subset=Non
                            0 if sub is None else sub.size, C.byref(o), n_threads)
     if rc != 0:
         raise ValueError("oracle rollout rejected its arguments")
+    return out
+
+
+# -------------------------------------------------------------------------- DQN
+def _qnet(arrays, keep):
+    """QNet struct over 12 [out, in] arrays (trunk 1, trunk 2, value 1, value 2,
+    advantage 1, advantage 2; weight then bias)."""
+    net = QNet()
+    for i in range(6):
+        w, b = _f32(arrays[2 * i]), _f32(arrays[2 * i + 1])
+        keep += [w, b]
+        net.w[i], net.b[i] = w.ctypes.data, b.ctypes.data
+    return net
+
+
+def dueling_q(arrays, s, precision: int = FP32) -> np.ndarray:
+    keep = []
+    net = _qnet(arrays, keep)
+    x = _f32(s)
+    q = np.zeros(N_ACTIONS, np.float32)
+    lib().orc_dueling_q(C.byref(net), _p(x), precision, _p(q))
+    return q
+
+
+def argmax_first(x) -> int:
+    x = _f32(x)
+    return lib().orc_argmax_first(_p(x), x.size)
+
+
+def random_action(u: float) -> int:
+    return lib().orc_random_action(float(u))
+
+
+def dqn_rollout(inputs: dict, precision: int = FP32, forced_actions=None, subset=None,
+                n_threads: int = 0, with_q: bool = True, with_next: bool = True) -> dict:
+    """Run the DQN oracle on host arrays from synthdata.dqn_inputs(); [L][N] arrays."""
+    N, L = inputs["N"], inputs["L"]
+    p = make_params(inputs["settings"], N, L, precision)
+    p.gamma = inputs["dqn"]["gamma"]
+    dq = DqnParams()
+    dq.epsilon, dq.alpha = inputs["dqn"]["epsilon"], inputs["dqn"]["alpha"]
+    w = inputs["weights"]
+    keep = []
+    nets = DqnNets()
+    nets.online = _qnet(w["online"], keep)
+    nets.target = _qnet(w["target"], keep)
+    for i in range(2):
+        cw, cb = _f32(w["curiosity"][2 * i]), _f32(w["curiosity"][2 * i + 1])
+        keep += [cw, cb]
+        nets.cw[i], nets.cb[i] = cw.ctypes.data, cb.ctypes.data
+    feats, prices = _f32(inputs["features"]), _f32(inputs["prices"])
+    starts = np.ascontiguousarray(inputs["starts"], np.int32)
+    out = dict(
+        states=np.zeros((L, N, STATE_DIM), np.float32),
+        next_states=np.zeros((L, N, STATE_DIM), np.float32) if with_next else None,
+        q_values=np.zeros((L, N, N_ACTIONS), np.float32) if with_q else None,
+        actions=np.zeros((L, N), np.int32),
+        explored=np.zeros((L, N), np.uint8),
+        q_gap=np.zeros((L, N), np.float32),
+        q_taken=np.zeros((L, N), np.float32),
+        q_next_max=np.zeros((L, N), np.float32),
+        rewards=np.zeros((L, N), np.float32),
+        dones=np.zeros((L, N), np.uint8),
+        barrier=np.zeros((L, N), np.uint8),
+        td=np.zeros((L, N), np.float32),
+        priority=np.zeros((L, N), np.float32),
+    )
+    o = DqnOutputs()
+    for k, arr in out.items():
+        setattr(o, k, None if arr is None else arr.ctypes.data)
+    fa = None if forced_actions is None else np.ascontiguousarray(forced_actions, np.int32)
+    sub = None if subset is None else np.ascontiguousarray(subset, np.int32)
+    rc = lib().orc_dqn_rollout(C.byref(p), C.byref(dq), C.byref(nets), _p(feats), _p(prices),
+                               feats.shape[0], _p(starts), C.c_uint64(inputs["sampler_seed"]),
+                               _p(fa), _p(sub), 0 if sub is None else sub.size, C.byref(o),
+                               n_threads)
+    if rc != 0:
+        raise ValueError("oracle DQN rollout rejected its arguments")
     return out

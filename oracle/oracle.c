@@ -471,3 +471,159 @@ int orc_rollout(const orc_params *p, const orc_nets *nets_in, const float *featu
   for (int i = 0; i < n_owned; ++i) free(owned[i]);
   return (failed || rc) ? -1 : 0;
 }
+
+/* ======================================================================== */
+/* DQN collection ([DQN] Data Flow steps 1-15, Kernel Components 1, 7, 8).   */
+/* ======================================================================== */
+void orc_dueling_q(const orc_qnet *net, const float *s, int precision, float *q) {
+  float h1[256], h2[128], v1[64], a1[64], v, a[ORC_N_ACTIONS];
+  orc_linear(net->w[0], net->b[0], s, ORC_STATE_DIM, 256, 1, precision, h1);
+  orc_linear(net->w[1], net->b[1], h1, 256, 128, 1, precision, h2);
+  orc_linear(net->w[2], net->b[2], h2, 128, 64, 1, precision, v1);
+  orc_linear(net->w[3], net->b[3], v1, 64, 1, 0, precision, &v);
+  orc_linear(net->w[4], net->b[4], h2, 128, 64, 1, precision, a1);
+  orc_linear(net->w[5], net->b[5], a1, 64, ORC_N_ACTIONS, 0, precision, a);
+  float sum = 0.0f;
+  for (int i = 0; i < ORC_N_ACTIONS; ++i) sum += a[i];
+  const float mean = sum / (float)ORC_N_ACTIONS;
+  for (int i = 0; i < ORC_N_ACTIONS; ++i) q[i] = v + (a[i] - mean);
+}
+
+int orc_argmax_first(const float *x, int n) {
+  int best = 0;
+  for (int i = 1; i < n; ++i)
+    if (x[i] > x[best]) best = i;
+  return best;
+}
+
+int orc_random_action(float u) {
+  /* u = m * 2^-24 with m < 2^24, so floor(45 u) = (45 m) >> 24 exactly */
+  const uint32_t m = (uint32_t)(u * 16777216.0f);
+  return (int)(((uint64_t)m * (uint64_t)ORC_N_ACTIONS) >> 24);
+}
+
+static int collect_dqn_episode(const orc_params *p, const orc_dqn_params *dq,
+                               const orc_dqn_nets *nets, const float *features,
+                               const float *prices, const int32_t *starts, uint64_t seed,
+                               const int32_t *forced, int32_t n, const orc_dqn_outputs *out) {
+  const int32_t N = p->n_episodes, L = p->n_steps;
+  const int prec = p->precision;
+  float s[ORC_STATE_DIM], sn[ORC_STATE_DIM], q[ORC_N_ACTIONS], qt[ORC_N_ACTIONS];
+  float cin[ORC_STATE_DIM + ORC_N_ACTIONS], ch[128], pred[ORC_N_FEATURES];
+  orc_episode ep;
+  orc_episode_reset(&ep);
+  const float V0 = 1.0f;
+
+  for (int32_t t = 0; t < L; ++t) {
+    const int64_t bar = (int64_t)starts[n] + t;
+    const int64_t o = (int64_t)t * N + n;
+    /* 1-3. state = 51 market features + normalised value, position, spread */
+    const float *f = features + bar * ORC_N_FEATURES;
+    for (int i = 0; i < ORC_N_FEATURES; ++i) s[i] = f[i];
+    s[51] = ep.V / V0 - 1.0f;
+    s[52] = ep.e_prev;
+    s[53] = p->spread;
+    memcpy(out->states + o * ORC_STATE_DIM, s, sizeof(s));
+
+    /* 4. online dueling Q of the state */
+    orc_dueling_q(&nets->online, s, prec, q);
+    if (out->q_values) memcpy(out->q_values + o * ORC_N_ACTIONS, q, sizeof(q));
+
+    /* 5. epsilon-greedy: stream 1 decides, stream 2 picks the random action */
+    const float u_explore = orc_uniform(seed, (uint32_t)n, (uint32_t)t, 1u);
+    const int explore = u_explore < dq->epsilon;
+    const int greedy = orc_argmax_first(q, ORC_N_ACTIONS);
+    int a = explore ? orc_random_action(orc_uniform(seed, (uint32_t)n, (uint32_t)t, 2u)) : greedy;
+    if (forced) {
+      a = forced[o];
+      if (a < 0 || a >= ORC_N_ACTIONS) return -1;
+    }
+    if (out->explored) out->explored[o] = (uint8_t)explore;
+    if (out->q_gap) {
+      float second = -INFINITY;
+      for (int i = 0; i < ORC_N_ACTIONS; ++i)
+        if (i != greedy && q[i] > second) second = q[i];
+      out->q_gap[o] = q[greedy] - second;
+    }
+    const float q_taken = q[a];
+
+    /* 6-8. portfolio, barrier, diversity */
+    float pnl, div, e;
+    int hit, code;
+    const int done = orc_env_step(p, &ep, a, t, prices[bar], prices[bar + 1], &pnl, &hit, &code,
+                                  &div, &e);
+
+    /* 9. curiosity on [state, one-hot(action)] against the next bar */
+    for (int i = 0; i < ORC_STATE_DIM; ++i) cin[i] = s[i];
+    for (int i = 0; i < ORC_N_ACTIONS; ++i) cin[ORC_STATE_DIM + i] = (i == a) ? 1.0f : 0.0f;
+    orc_linear(nets->cw[0], nets->cb[0], cin, ORC_STATE_DIM + ORC_N_ACTIONS, 128, 1, prec, ch);
+    orc_linear(nets->cw[1], nets->cb[1], ch, 128, ORC_N_FEATURES, 0, prec, pred);
+    const float *fn = features + (bar + 1) * ORC_N_FEATURES;
+    float se = 0.0f;
+    for (int j = 0; j < ORC_N_FEATURES; ++j) {
+      const float dj = pred[j] - fn[j];
+      se += dj * dj;
+    }
+    const float bonus = p->curiosity_coef * (se / (float)ORC_N_FEATURES);
+
+    /* 13. reward, as in the PPO collection */
+    const float reward =
+        pnl * (1.0f + p->barrier_scale * (float)hit) + div + bonus - p->risk_coef * fabsf(e);
+
+    /* 10-12. next state (after the trade, before any reset), target Q, TD */
+    for (int i = 0; i < ORC_N_FEATURES; ++i) sn[i] = fn[i];
+    sn[51] = ep.V / V0 - 1.0f;
+    sn[52] = ep.e_prev;
+    sn[53] = p->spread;
+    if (out->next_states) memcpy(out->next_states + o * ORC_STATE_DIM, sn, sizeof(sn));
+    orc_dueling_q(&nets->target, sn, prec, qt);
+    float qmax = qt[0];
+    for (int i = 1; i < ORC_N_ACTIONS; ++i) qmax = qt[i] > qmax ? qt[i] : qmax;
+    const float td = reward + p->gamma * qmax * (float)(1 - done) - q_taken;
+
+    /* 14. store */
+    out->actions[o] = a;
+    out->q_taken[o] = q_taken;
+    out->q_next_max[o] = qmax;
+    out->rewards[o] = reward;
+    out->dones[o] = (uint8_t)done;
+    out->barrier[o] = (uint8_t)code;
+    out->td[o] = td;
+    out->priority[o] = powf(fabsf(td), dq->alpha);
+
+    /* 15. reset on done; the bar pointer keeps advancing */
+    if (done) orc_episode_reset(&ep);
+  }
+  return 0;
+}
+
+int orc_dqn_rollout(const orc_params *p, const orc_dqn_params *dq, const orc_dqn_nets *nets,
+                    const float *features, const float *prices, int64_t n_bars,
+                    const int32_t *starts, uint64_t seed, const int32_t *forced_actions,
+                    const int32_t *subset, int32_t n_subset, const orc_dqn_outputs *out,
+                    int32_t n_threads) {
+  if (!p || !dq || !nets || !features || !prices || !starts || !out) return -1;
+  if (p->n_episodes <= 0 || p->n_steps <= 0) return -1;
+  if (p->precision != ORC_FP32 && p->precision != ORC_FP64) return -1;
+  if (p->div_window <= 0 || p->div_window > ORC_MAX_WINDOW) return -1;
+  if (!out->states || !out->actions || !out->q_taken || !out->q_next_max || !out->rewards ||
+      !out->dones || !out->barrier || !out->td || !out->priority)
+    return -1;
+  const int32_t N = p->n_episodes, L = p->n_steps;
+  for (int32_t n = 0; n < N; ++n)
+    if (starts[n] < 0 || (int64_t)starts[n] + L >= n_bars) return -1;
+  int rc = 0;
+  const int32_t count = subset ? n_subset : N;
+#ifdef _OPENMP
+  const int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : rc)
+#endif
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t n = subset ? subset[i] : i;
+    if (n < 0 || n >= N) { rc |= 1; continue; }
+    if (collect_dqn_episode(p, dq, nets, features, prices, starts, seed, forced_actions, n, out))
+      rc |= 1;
+  }
+  (void)n_threads;
+  return rc ? -1 : 0;
+}

@@ -15,6 +15,12 @@
  *           portfolio, barrier, diversity entropy, reward, TD error, RNG).
  *   [FUSED] "Fused CUDA Training Kernel - Implementation Plan": Task 1 step 3
  *           (45-action factorisation exp = a/9, ord = (a%9)/3, urg = a%3).
+ *   The DQN variant of the collection ([DQN] Data Flow, Kernel Components
+ *           1, 7 and 8): dueling Q online on the state, epsilon-greedy,
+ *           the same environment step and reward, target Q on the next
+ *           state and the TD error; priority = |TD|^alpha as in the
+ *           priority update of "GPU-Resident Prioritized Experience
+ *           Replay" (Sampling Kernels).
  *   Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
  *           Easy as 1, 2, 3", SC'11 (the pages' LCG is replaced by this
  *           counter-based generator keyed by (seed, episode, step, stream)).
@@ -145,6 +151,63 @@ int orc_rollout(const orc_params *p, const orc_nets *nets, const float *features
                 const float *prices, int64_t n_bars, const int32_t *starts, uint64_t seed,
                 const int32_t *forced_actions, const int32_t *subset, int32_t n_subset,
                 const orc_outputs *out, int32_t n_threads);
+
+/* --- DQN collection -------------------------------------------------------- */
+/* Dueling Q-network ([DQN] Kernel Components 1, with the configured widths):
+ * h = ReLU(W2 ReLU(W1 s + b1) + b2)            trunk 54 -> 256 -> 128
+ * V = Wv2 ReLU(Wv1 h + bv1) + bv2              value head 128 -> 64 -> 1
+ * A = Wa2 ReLU(Wa1 h + ba1) + ba2              advantage head 128 -> 64 -> 45
+ * Q_i = V + (A_i - mean(A)), mean = (sum of A left to right) / 45.
+ * w/b order: trunk 1, trunk 2, value 1, value 2, advantage 1, advantage 2;
+ * [out, in] row-major. */
+typedef struct {
+  const float *w[6], *b[6];
+} orc_qnet;
+
+typedef struct {
+  orc_qnet online, target;
+  const float *cw[2], *cb[2];    /* curiosity: (54+45)->128->51 */
+} orc_dqn_nets;
+
+typedef struct {
+  float epsilon;                 /* exploration probability */
+  float alpha;                   /* priority = |td|^alpha */
+} orc_dqn_params;
+
+/* Outputs, host pointers, [L][N] (states/next_states [L][N][54], q_values
+ * [L][N][45]).  Nullable: next_states, q_values, explored, q_gap. */
+typedef struct {
+  float *states;
+  float *next_states;  /* the state after the step, before any reset */
+  float *q_values;     /* online Q of the state */
+  int32_t *actions;
+  uint8_t *explored;   /* 1 when the action is the random one */
+  float *q_gap;        /* largest minus second-largest online Q */
+  float *q_taken;      /* online Q of the action */
+  float *q_next_max;   /* max over actions of the target Q of next_state */
+  float *rewards;
+  uint8_t *dones;
+  uint8_t *barrier;
+  float *td;           /* r + gamma (1 - done) q_next_max - q_taken */
+  float *priority;     /* |td|^alpha */
+} orc_dqn_outputs;
+
+void orc_dueling_q(const orc_qnet *net, const float *s, int precision, float *q);
+/* index of the largest element, the lowest index among equal maxima */
+int orc_argmax_first(const float *x, int n);
+/* the uniformly random action of a draw u in [0, 1): floor(45 u), exact */
+int orc_random_action(float u);
+/* One DQN collection: for each step the online Q of the state, the action
+ * (random with probability epsilon: stream 1 decides, stream 2 picks), the
+ * environment step and reward of the PPO collection, the next state before
+ * any reset, its target Q, the TD error and the priority; then the reset on
+ * done.  Precision ORC_FP32 or ORC_FP64.  Same argument rules as
+ * orc_rollout; returns 0, or -1 on bad arguments. */
+int orc_dqn_rollout(const orc_params *p, const orc_dqn_params *dq, const orc_dqn_nets *nets,
+                    const float *features, const float *prices, int64_t n_bars,
+                    const int32_t *starts, uint64_t seed, const int32_t *forced_actions,
+                    const int32_t *subset, int32_t n_subset, const orc_dqn_outputs *out,
+                    int32_t n_threads);
 
 #ifdef __cplusplus
 }

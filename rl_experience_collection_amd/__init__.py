@@ -8,7 +8,10 @@ fails to load, importing the functions raises.
 The functions carry the C names:
     rollout_config_default, rollout_create, rollout_set_weights,
     rollout_collect, gae_scan, rollout_destroy, rollout_last_error
-plus two helpers, `alloc_outputs` and the `Collector` convenience class.
+    (include/rollout.h), and dqn_config_default, dqn_create,
+    dqn_set_weights, dqn_collect, dqn_destroy (include/dqn.h),
+plus helpers: `alloc_outputs`, `alloc_dqn_outputs` and the `Collector` and
+`DqnCollector` convenience classes.
 """
 from __future__ import annotations
 
@@ -22,7 +25,8 @@ ROLLOUT_OK, ROLLOUT_EINVAL, ROLLOUT_ENOMEM, ROLLOUT_EHIP, ROLLOUT_ENOTIMPL = 0, 
 ROLLOUT_FP32, ROLLOUT_BF16 = 0, 1
 STATE_DIM, N_ACTIONS, N_FEATURES = 54, 45, 51
 EXPORTED = ("rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
-            "gae_scan", "rollout_destroy", "rollout_last_error")
+            "gae_scan", "rollout_destroy", "rollout_last_error",
+            "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_collect", "dqn_destroy")
 
 
 class RolloutConfig(C.Structure):
@@ -44,6 +48,27 @@ class RolloutOutputs(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "states", "actions", "log_probs", "values", "rewards", "dones", "barrier",
         "advantages", "returns", "logits", "counters", "phase_events")]
+
+
+class DqnConfig(C.Structure):
+    _fields_ = [
+        ("n_episodes", C.c_int32), ("n_steps", C.c_int32),
+        ("n_features", C.c_int32), ("state_dim", C.c_int32), ("n_actions", C.c_int32),
+        ("trunk_dims", C.c_int32 * 3), ("value_dims", C.c_int32 * 3),
+        ("advantage_dims", C.c_int32 * 3), ("cur_dims", C.c_int32 * 3),
+        ("epsilon", C.c_float), ("gamma", C.c_float), ("priority_alpha", C.c_float),
+        ("profit_take", C.c_float), ("stop_loss", C.c_float), ("max_hold", C.c_int32),
+        ("div_window", C.c_int32), ("div_threshold", C.c_float), ("div_penalty", C.c_float),
+        ("curiosity_coef", C.c_float), ("risk_coef", C.c_float), ("spread", C.c_float),
+        ("barrier_scale", C.c_float),
+        ("exposure", C.c_float * 5), ("cost", C.c_float * 3), ("urgency_mult", C.c_float),
+    ]
+
+
+class DqnOutputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "states", "next_states", "q_values", "actions", "explored", "q_taken", "q_next_max",
+        "rewards", "dones", "barrier", "td", "priorities", "counters", "phase_events")]
 
 
 class RolloutError(RuntimeError):
@@ -82,8 +107,16 @@ def load_library(path: str = LIB_PATH):
     L.rollout_destroy.restype = None
     L.rollout_last_error.argtypes = []
     L.rollout_last_error.restype = C.c_char_p
+    L.dqn_config_default.argtypes = [C.POINTER(DqnConfig), i32, i32]
+    L.dqn_create.argtypes = [C.POINTER(DqnConfig), C.POINTER(vp), C.POINTER(vp), C.POINTER(vp),
+                             vp, vp, i64, vp, C.POINTER(vp)]
+    L.dqn_set_weights.argtypes = [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp]
+    L.dqn_collect.argtypes = [vp, vp, C.c_uint64, C.POINTER(DqnOutputs), vp]
+    L.dqn_destroy.argtypes = [vp]
+    L.dqn_destroy.restype = None
     for name in ("rollout_config_default", "rollout_create", "rollout_set_weights",
-                 "rollout_collect", "gae_scan"):
+                 "rollout_collect", "gae_scan", "dqn_config_default", "dqn_create",
+                 "dqn_set_weights", "dqn_collect"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -301,6 +334,145 @@ class Collector:
     def close(self):
         if self.handle:
             rollout_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# --------------------------------------------------------------------------- DQN
+Q_NET_SHAPES = [(256, 54), (256,), (128, 256), (128,), (64, 128), (64,), (1, 64), (1,),
+                (64, 128), (64,), (45, 64), (45,)]
+
+
+def dqn_config_default(n_episodes: int, n_steps: int, settings: dict | None = None,
+                       dqn: dict | None = None) -> DqnConfig:
+    """settings: environment scalars (as for rollout_config_default); dqn:
+    {'epsilon', 'gamma', 'alpha'}."""
+    cfg = DqnConfig()
+    _check(load_library().dqn_config_default(C.byref(cfg), n_episodes, n_steps))
+    for k, v in (settings or {}).items():
+        if k in ("gamma", "lam", "lambda"):
+            continue  # GAE settings of the PPO collection
+        if k in ("exposure", "cost"):
+            setattr(cfg, k, (C.c_float * len(v))(*v))
+        else:
+            setattr(cfg, k, v)
+    for k, v in (dqn or {}).items():
+        setattr(cfg, "priority_alpha" if k == "alpha" else k, v)
+    return cfg
+
+
+def _nullable_array(tensors, shapes, name):
+    return None if tensors is None else _ptr_array(tensors, shapes, name)
+
+
+def dqn_create(cfg: DqnConfig, online, target, curiosity, features, prices, stream=None):
+    """Returns an opaque handle (int).  The market tensors are borrowed."""
+    import torch
+    o = _ptr_array(online, Q_NET_SHAPES, "online")
+    t = _ptr_array(target, Q_NET_SHAPES, "target")
+    u = _ptr_array(curiosity, CURIOSITY_SHAPES, "curiosity")
+    if features.dim() != 2 or features.shape[1] != N_FEATURES:
+        raise ValueError("features must be [n_bars, 51]")
+    f = _dev_ptr(features, torch.float32, name="features")
+    p = _dev_ptr(prices, torch.float32, (features.shape[0],), "prices")
+    h = C.c_void_p()
+    _check(load_library().dqn_create(C.byref(cfg), o, t, u, f, p, features.shape[0],
+                                     _stream(stream), C.byref(h)))
+    return h.value
+
+
+def dqn_set_weights(handle: int, online=None, target=None, curiosity=None, stream=None):
+    """None keeps that network."""
+    _check(load_library().dqn_set_weights(
+        C.c_void_p(handle), _nullable_array(online, Q_NET_SHAPES, "online"),
+        _nullable_array(target, Q_NET_SHAPES, "target"),
+        _nullable_array(curiosity, CURIOSITY_SHAPES, "curiosity"), _stream(stream)))
+
+
+def alloc_dqn_outputs(N: int, L: int, device="cuda", next_states: bool = True,
+                      q_values: bool = False, explored: bool = True, counters: bool = True):
+    import torch
+    f32 = dict(dtype=torch.float32, device=device)
+    u8 = dict(dtype=torch.uint8, device=device)
+    return dict(
+        states=torch.empty((L, N, STATE_DIM), **f32),
+        next_states=torch.empty((L, N, STATE_DIM), **f32) if next_states else None,
+        q_values=torch.empty((L, N, N_ACTIONS), **f32) if q_values else None,
+        actions=torch.empty((L, N), dtype=torch.int32, device=device),
+        explored=torch.empty((L, N), **u8) if explored else None,
+        q_taken=torch.empty((L, N), **f32),
+        q_next_max=torch.empty((L, N), **f32),
+        rewards=torch.empty((L, N), **f32),
+        dones=torch.empty((L, N), **u8),
+        barrier=torch.empty((L, N), **u8),
+        td=torch.empty((L, N), **f32),
+        priorities=torch.empty((L, N), **f32),
+        counters=torch.zeros(2, dtype=torch.int32, device=device) if counters else None,
+    )
+
+
+def dqn_collect(handle: int, episode_starts, seed: int, outputs: dict, stream=None,
+                phase_events=None):
+    """phase_events: None or a sequence of 2 hipEvent_t handles (ints)."""
+    import torch
+    L, N = outputs["actions"].shape
+    o = DqnOutputs()
+    o.states = _dev_ptr(outputs["states"], torch.float32, (L, N, STATE_DIM), "states")
+    o.next_states = _dev_ptr(outputs.get("next_states"), torch.float32, (L, N, STATE_DIM),
+                             "next_states")
+    o.q_values = _dev_ptr(outputs.get("q_values"), torch.float32, (L, N, N_ACTIONS), "q_values")
+    o.actions = _dev_ptr(outputs["actions"], torch.int32, (L, N), "actions")
+    o.explored = _dev_ptr(outputs.get("explored"), torch.uint8, (L, N), "explored")
+    for k in ("q_taken", "q_next_max", "rewards", "td", "priorities"):
+        setattr(o, k, _dev_ptr(outputs[k], torch.float32, (L, N), k))
+    o.dones = _dev_ptr(outputs["dones"], torch.uint8, (L, N), "dones")
+    o.barrier = _dev_ptr(outputs["barrier"], torch.uint8, (L, N), "barrier")
+    o.counters = _dev_ptr(outputs.get("counters"), torch.int32, (2,), "counters")
+    ev = None
+    if phase_events is not None:
+        if len(phase_events) != 2:
+            raise ValueError("phase_events must hold 2 event handles")
+        ev = (C.c_void_p * 2)(*phase_events)
+        o.phase_events = C.cast(ev, C.c_void_p)
+    s = _dev_ptr(episode_starts, torch.int32, (N,), "episode_starts")
+    _check(load_library().dqn_collect(C.c_void_p(handle), s, C.c_uint64(seed), C.byref(o),
+                                      _stream(stream)))
+
+
+def dqn_destroy(handle: int):
+    if handle:
+        load_library().dqn_destroy(C.c_void_p(handle))
+
+
+class DqnCollector:
+    """Owns one DQN handle; weights as lists of [out, in] fp32 device tensors."""
+
+    def __init__(self, n_episodes: int, n_steps: int, weights: dict, features, prices,
+                 settings: dict | None = None, dqn: dict | None = None, stream=None):
+        self.N, self.L = n_episodes, n_steps
+        self.cfg = dqn_config_default(n_episodes, n_steps, settings, dqn)
+        self.features, self.prices = features, prices  # borrowed by the library
+        self.handle = dqn_create(self.cfg, weights["online"], weights["target"],
+                                 weights["curiosity"], features, prices, stream)
+
+    def set_weights(self, online=None, target=None, curiosity=None, stream=None):
+        dqn_set_weights(self.handle, online, target, curiosity, stream)
+
+    def collect(self, episode_starts, seed: int, outputs: dict | None = None, q_values=False,
+                stream=None, phase_events=None) -> dict:
+        if outputs is None:
+            outputs = alloc_dqn_outputs(self.N, self.L, episode_starts.device, q_values=q_values)
+        dqn_collect(self.handle, episode_starts, seed, outputs, stream, phase_events)
+        return outputs
+
+    def close(self):
+        if self.handle:
+            dqn_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -12,6 +12,7 @@
 #include <string>
 #include <utility>
 
+#include "../../include/dqn.h"
 #include "../../include/rollout.h"
 #include "collect.hpp"
 #include "gae.hpp"
@@ -124,7 +125,8 @@ const int32_t kActorDims[4] = {54, 128, 64, 45};
 const int32_t kCriticDims[7] = {54, 512, 384, 256, 128, 64, 1};
 const int32_t kCurDims[3] = {99, 128, 51};
 
-rl::EnvParams env_params(const rollout_config& c) {
+template <class Config>
+rl::EnvParams env_params(const Config& c) {
   rl::EnvParams p;
   p.ex0 = c.exposure[0]; p.ex1 = c.exposure[1]; p.ex2 = c.exposure[2];
   p.ex3 = c.exposure[3]; p.ex4 = c.exposure[4];
@@ -182,7 +184,53 @@ int check_weights(const float* const actor[6], const float* const critic[12],
   return ROLLOUT_OK;
 }
 
+const int32_t kTrunkDims[3] = {54, 256, 128};
+const int32_t kValueDims[3] = {128, 64, 1};
+const int32_t kAdvDims[3] = {128, 64, 45};
+
+int check_dqn_config(const dqn_config* c) {
+  if (!c) return fail(ROLLOUT_EINVAL, "config is NULL");
+  if (c->n_episodes < 1 || c->n_steps < 1)
+    return fail(ROLLOUT_EINVAL, "n_episodes and n_steps must be >= 1 (got %d, %d)", c->n_episodes,
+                c->n_steps);
+  if ((int64_t)c->n_episodes * c->n_steps >= (int64_t)1 << 40)
+    return fail(ROLLOUT_EINVAL, "n_episodes * n_steps too large");
+  if (c->n_features != 51 || c->state_dim != 54 || c->n_actions != 45)
+    return fail(ROLLOUT_EINVAL, "features/state/actions must be 51/54/45");
+  for (int i = 0; i < 3; ++i) {
+    if (c->trunk_dims[i] != kTrunkDims[i]) return fail(ROLLOUT_EINVAL, "trunk dims must be 54,256,128");
+    if (c->value_dims[i] != kValueDims[i]) return fail(ROLLOUT_EINVAL, "value head dims must be 128,64,1");
+    if (c->advantage_dims[i] != kAdvDims[i])
+      return fail(ROLLOUT_EINVAL, "advantage head dims must be 128,64,45");
+    if (c->cur_dims[i] != kCurDims[i]) return fail(ROLLOUT_EINVAL, "curiosity dims must be 99,128,51");
+  }
+  if (!(c->epsilon >= 0.0f && c->epsilon <= 1.0f))
+    return fail(ROLLOUT_EINVAL, "epsilon must be in [0, 1]");
+  if (c->div_window < 1 || c->div_window > 32)
+    return fail(ROLLOUT_EINVAL, "div_window must be in 1..32 (got %d)", c->div_window);
+  if (c->max_hold < 1) return fail(ROLLOUT_EINVAL, "max_hold must be >= 1");
+  return ROLLOUT_OK;
+}
+
+int check_tensors(const float* const* w, int count, const char* what) {
+  if (!w) return ROLLOUT_OK;
+  for (int i = 0; i < count; ++i)
+    if (!w[i]) return fail(ROLLOUT_EINVAL, "%s tensor %d is NULL", what, i);
+  return ROLLOUT_OK;
+}
+
 }  // namespace
+
+struct dqn_s {
+  int device = 0;
+  dqn_config cfg;
+  rl::EnvParams ep;
+  const float* features = nullptr;
+  const float* prices = nullptr;
+  int64_t n_bars = 0;
+  float* weights = nullptr;  // packed block (dqn_packed_offsets layout)
+  float* heads = nullptr;    // assembly scratch of the head layers
+};
 
 struct rollout_s {
   int device = 0;
@@ -408,5 +456,158 @@ void rollout_destroy(rollout_handle h) {
 }
 
 const char* rollout_last_error(void) { return g_last_error.c_str(); }
+
+int dqn_config_default(dqn_config* cfg, int32_t n_episodes, int32_t n_steps) {
+  if (!cfg) return fail(ROLLOUT_EINVAL, "config is NULL");
+  rollout_config base;
+  rollout_config_default(&base, n_episodes, n_steps);
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->n_episodes = n_episodes;
+  cfg->n_steps = n_steps;
+  cfg->n_features = 51;
+  cfg->state_dim = 54;
+  cfg->n_actions = 45;
+  std::memcpy(cfg->trunk_dims, kTrunkDims, sizeof(kTrunkDims));
+  std::memcpy(cfg->value_dims, kValueDims, sizeof(kValueDims));
+  std::memcpy(cfg->advantage_dims, kAdvDims, sizeof(kAdvDims));
+  std::memcpy(cfg->cur_dims, kCurDims, sizeof(kCurDims));
+  cfg->epsilon = 0.1f;
+  cfg->gamma = 0.99f;
+  cfg->priority_alpha = 0.6f;
+  cfg->profit_take = base.profit_take;
+  cfg->stop_loss = base.stop_loss;
+  cfg->max_hold = base.max_hold;
+  cfg->div_window = base.div_window;
+  cfg->div_threshold = base.div_threshold;
+  cfg->div_penalty = base.div_penalty;
+  cfg->curiosity_coef = base.curiosity_coef;
+  cfg->risk_coef = base.risk_coef;
+  cfg->spread = base.spread;
+  cfg->barrier_scale = base.barrier_scale;
+  std::memcpy(cfg->exposure, base.exposure, sizeof(base.exposure));
+  std::memcpy(cfg->cost, base.cost, sizeof(base.cost));
+  cfg->urgency_mult = base.urgency_mult;
+  return ROLLOUT_OK;
+}
+
+int dqn_create(const dqn_config* cfg, const float* const online[12], const float* const target[12],
+               const float* const curiosity[4], const float* features, const float* prices,
+               int64_t n_bars, void* hip_stream, dqn_handle* out) {
+  if (!out) return fail(ROLLOUT_EINVAL, "out handle pointer is NULL");
+  *out = nullptr;
+  int rc = check_dqn_config(cfg);
+  if (rc) return rc;
+  if (!online || !target || !curiosity) return fail(ROLLOUT_EINVAL, "weight array is NULL");
+  if ((rc = check_tensors(online, 12, "online")) || (rc = check_tensors(target, 12, "target")) ||
+      (rc = check_tensors(curiosity, 4, "curiosity")))
+    return rc;
+  if (!features || !prices) return fail(ROLLOUT_EINVAL, "features/prices are NULL");
+  if (n_bars < (int64_t)cfg->n_steps + 1)
+    return fail(ROLLOUT_EINVAL, "n_bars (%lld) must be >= n_steps + 1", (long long)n_bars);
+  if (n_bars > ((int64_t)1 << 31) - 2) return fail(ROLLOUT_EINVAL, "n_bars too large");
+  auto* h = new (std::nothrow) dqn_s();
+  if (!h) return fail(ROLLOUT_ENOMEM, "host allocation failed");
+  h->cfg = *cfg;
+  h->ep = env_params(*cfg);
+  h->features = features;
+  h->prices = prices;
+  h->n_bars = n_bars;
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "hipGetDevice");
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, (size_t)rl::dqn_packed_offsets().total * sizeof(float)) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return fail(ROLLOUT_ENOMEM, "cannot allocate packed weights");
+  }
+  h->weights = static_cast<float*>(p);
+  if (hipMalloc(&p, rl::dqn_pack_scratch_floats() * sizeof(float)) != hipSuccess) {
+    (void)hipGetLastError();
+    dqn_destroy(h);
+    return fail(ROLLOUT_ENOMEM, "cannot allocate head scratch");
+  }
+  h->heads = static_cast<float*>(p);
+  e = rl::pack_dqn_weights(online, target, curiosity, h->weights, h->heads,
+                           static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) {
+    dqn_destroy(h);
+    return hip_fail(e, "weight packing");
+  }
+  *out = h;
+  return ROLLOUT_OK;
+}
+
+int dqn_set_weights(dqn_handle h, const float* const online[12], const float* const target[12],
+                    const float* const curiosity[4], void* hip_stream) {
+  if (!h) return fail(ROLLOUT_EINVAL, "handle is NULL");
+  int rc;
+  if ((rc = check_tensors(online, 12, "online")) || (rc = check_tensors(target, 12, "target")) ||
+      (rc = check_tensors(curiosity, 4, "curiosity")))
+    return rc;
+  hipError_t e = rl::pack_dqn_weights(online, target, curiosity, h->weights, h->heads,
+                                      static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "weight packing");
+  return ROLLOUT_OK;
+}
+
+int dqn_collect(dqn_handle h, const int32_t* episode_starts, uint64_t seed, const dqn_outputs* out,
+                void* hip_stream) {
+  if (!h) return fail(ROLLOUT_EINVAL, "handle is NULL");
+  if (!episode_starts) return fail(ROLLOUT_EINVAL, "episode_starts is NULL");
+  if (!out) return fail(ROLLOUT_EINVAL, "outputs struct is NULL");
+  if (!out->states || !out->actions || !out->q_taken || !out->q_next_max || !out->rewards ||
+      !out->dones || !out->barrier || !out->td || !out->priorities)
+    return fail(ROLLOUT_EINVAL, "a required output buffer is NULL");
+  int dev = -1;
+  RL_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev != h->device)
+    return fail(ROLLOUT_EINVAL, "handle was created on device %d, current device is %d", h->device, dev);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (out->counters) RL_HIP(hipMemsetAsync(out->counters, 0, 2 * sizeof(uint32_t), st), "counters");
+  auto mark = [&](int i) -> hipError_t {
+    if (!out->phase_events || !out->phase_events[i]) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(out->phase_events[i]), st);
+  };
+  RL_HIP(mark(0), "hipEventRecord(phase 0)");
+  rl::DqnArgs da;
+  da.weights = h->weights;
+  da.features = h->features;
+  da.prices = h->prices;
+  da.n_bars = h->n_bars;
+  da.starts = episode_starts;
+  da.seed = seed;
+  da.N = h->cfg.n_episodes;
+  da.L = h->cfg.n_steps;
+  da.ep = h->ep;
+  da.epsilon = h->cfg.epsilon;
+  da.gamma = h->cfg.gamma;
+  da.alpha = h->cfg.priority_alpha;
+  da.states = out->states;
+  da.next_states = out->next_states;
+  da.q_values = out->q_values;
+  da.actions = out->actions;
+  da.explored = out->explored;
+  da.q_taken = out->q_taken;
+  da.q_next_max = out->q_next_max;
+  da.rewards = out->rewards;
+  da.dones = out->dones;
+  da.barrier = out->barrier;
+  da.td = out->td;
+  da.priority = out->priorities;
+  da.counters = out->counters;
+  RL_HIP(rl::launch_dqn(da, st), "dqn launch");
+  RL_HIP(mark(1), "hipEventRecord(phase 1)");
+  return ROLLOUT_OK;
+}
+
+void dqn_destroy(dqn_handle h) {
+  if (!h) return;
+  if (h->weights) (void)hipFree(h->weights);
+  if (h->heads) (void)hipFree(h->heads);
+  delete h;
+}
 
 }  // extern "C"

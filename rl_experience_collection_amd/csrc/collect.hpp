@@ -48,7 +48,34 @@ struct ValueArgs {
   int bf16;
 };
 
+// DQN collection: every step of every episode in one sequential kernel.
+struct DqnArgs {
+  const float* weights;   // packed block (dqn_packed_offsets layout)
+  const float* features;  // [n_bars][51]
+  const float* prices;    // [n_bars]
+  int64_t n_bars;
+  const int32_t* starts;  // [N]
+  uint64_t seed;
+  int32_t N, L;
+  EnvParams ep;
+  float epsilon, gamma, alpha;
+  float* states;          // [L][N][54]
+  float* next_states;     // [L][N][54] or null
+  float* q_values;        // [L][N][45] or null
+  int32_t* actions;       // [L][N]
+  uint8_t* explored;      // [L][N] or null
+  float* q_taken;         // [L][N]
+  float* q_next_max;      // [L][N]
+  float* rewards;         // [L][N]
+  uint8_t* dones;         // [L][N]
+  uint8_t* barrier;       // [L][N]
+  float* td;              // [L][N]
+  float* priority;        // [L][N]
+  uint32_t* counters;     // [2] or null
+};
+
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st);
+hipError_t launch_dqn(const DqnArgs& a, hipStream_t st);
 hipError_t launch_value(const ValueArgs& a, hipStream_t st);
 
 }  // namespace rl

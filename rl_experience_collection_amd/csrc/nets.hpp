@@ -162,6 +162,64 @@ __host__ __device__ constexpr PackedOffsets packed_offsets() {
   return p;
 }
 
+// ---------------------------------------------------------------------------
+// DQN collection ("GPU Pipeline Phase 2b", Kernel Components 1, with the
+// configured widths): a dueling Q-network, online and target copies, and the
+// curiosity forward model, all fp32.  The two heads share their input, so
+// each network is four streamed layers:
+//   Q1  54 -> 256 (ReLU)   state operands in natural order (first = 2),
+//                          14 k-steps packed plus 2 zero steps so the
+//                          stream runs whole groups of 4
+//   Q2  256 -> 128 (ReLU)
+//   QH1 128 -> 128 (ReLU)  [value head 1 (outputs 0..63); advantage head 1
+//                          (outputs 64..127)]
+//   QH2 128 -> 64          outputs 0..44 the advantages (from inputs
+//                          64..127), output 45 the value (from inputs
+//                          0..63), 46..63 zero
+// and the curiosity model is the dense state part of its first layer plus a
+// column gather of the action's one-hot weights, then 128 -> 51.
+constexpr LayerDesc kQ1 = {54, 256, 14, 2, 16, 2};
+constexpr LayerDesc kQ2 = {256, 128, 64, 0, 8, 0};
+constexpr LayerDesc kQH1 = {128, 128, 32, 0, 8, 0};
+constexpr LayerDesc kQH2 = {128, 64, 32, 0, 4, 0};
+constexpr LayerDesc kQC1 = {54, 128, 14, 2, 8, 2};
+constexpr LayerDesc kQC2 = {128, 51, 32, 0, 4, 0};
+constexpr int kQValueRow = 45;  // QH2 output holding the value
+
+struct DqnOffsets {
+  int64_t w[2][4], b[2][4];  // [online, target][Q1, Q2, QH1, QH2]
+  int64_t cw[2], cb[2], c_onehot;
+  int64_t total;
+};
+
+__host__ __device__ constexpr DqnOffsets dqn_packed_offsets() {
+  DqnOffsets p{};
+  const LayerDesc ls[4] = {kQ1, kQ2, kQH1, kQH2};
+  int64_t off = 0;
+  for (int net = 0; net < 2; ++net) {
+    for (int l = 0; l < 4; ++l) {
+      p.w[net][l] = off;
+      off = align64(off + packed_layer_floats(ls[l]));
+    }
+    for (int l = 0; l < 4; ++l) {
+      p.b[net][l] = off;
+      off = align64(off + 16 * ls[l].ot);
+    }
+  }
+  p.cw[0] = off;
+  off = align64(off + packed_layer_floats(kQC1));
+  p.cw[1] = off;
+  off = align64(off + packed_layer_floats(kQC2));
+  p.cb[0] = off;
+  off = align64(off + 16 * kQC1.ot);
+  p.cb[1] = off;
+  off = align64(off + 16 * kQC2.ot);
+  p.c_onehot = off;
+  off = align64(off + 45 * 128);
+  p.total = off;
+  return p;
+}
+
 // State element held by lane group g at first-layer k-step slot s (16 slots
 // per lane): fp32 form k = 14 g + s (s < 14), bf16 form k = 32 (s / 8) + 8 g
 // + s % 8.  Values for k >= 54 are zero.

@@ -110,7 +110,83 @@ hipError_t pack_bias(const float* b, const LayerDesc& d, float* pb, hipStream_t 
   return hipGetLastError();
 }
 
+// The two head layers of a dueling Q-network as dense [out, in] matrices (see
+// kQH1 / kQH2): h1 = [Wv1; Wa1] (128 x 128), h2 (64 x 128) with the
+// advantage rows 0..44 over inputs 64..127 and the value row 45 over inputs
+// 0..63.  Layout of `dst`: h1 weights, h1 bias (128), h2 weights, h2 bias (64).
+constexpr int kHeadFloats = 128 * 128 + 128 + 64 * 128 + 64;
+__global__ void assemble_heads_kernel(const float* __restrict__ wv1, const float* __restrict__ bv1,
+                                      const float* __restrict__ wv2, const float* __restrict__ bv2,
+                                      const float* __restrict__ wa1, const float* __restrict__ ba1,
+                                      const float* __restrict__ wa2, const float* __restrict__ ba2,
+                                      float* __restrict__ dst) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= kHeadFloats) return;
+  float v = 0.0f;
+  if (idx < 128 * 128) {
+    const int o = idx / 128, k = idx % 128;
+    v = o < 64 ? wv1[o * 128 + k] : wa1[(o - 64) * 128 + k];
+  } else if (idx < 128 * 128 + 128) {
+    const int o = idx - 128 * 128;
+    v = o < 64 ? bv1[o] : ba1[o - 64];
+  } else if (idx < 128 * 128 + 128 + 64 * 128) {
+    const int r = idx - (128 * 128 + 128);
+    const int o = r / 128, k = r % 128;
+    if (o < kActions && k >= 64) v = wa2[o * 64 + (k - 64)];
+    else if (o == kQValueRow && k < 64) v = wv2[k];
+  } else {
+    const int o = idx - (128 * 128 + 128 + 64 * 128);
+    v = o < kActions ? ba2[o] : (o == kQValueRow ? bv2[0] : 0.0f);
+  }
+  dst[idx] = v;
+}
+
 }  // namespace
+
+size_t dqn_pack_scratch_floats() { return 2 * (size_t)kHeadFloats; }
+
+hipError_t pack_dqn_weights(const float* const online[12], const float* const target[12],
+                            const float* const cur[4], float* block, float* scratch,
+                            hipStream_t st) {
+  const DqnOffsets P = dqn_packed_offsets();
+  hipError_t e = hipSuccess;
+#define RL_TRY(x)           \
+  do {                      \
+    e = (x);                \
+    if (e != hipSuccess) return e; \
+  } while (0)
+  for (int net = 0; net < 2; ++net) {
+    const float* const* w = net == 0 ? online : target;
+    if (!w) continue;  // keep the packed copy of this network
+    float* heads = scratch + net * kHeadFloats;
+    hipLaunchKernelGGL(assemble_heads_kernel, dim3((kHeadFloats + 255) / 256), dim3(256), 0, st,
+                       w[4], w[5], w[6], w[7], w[8], w[9], w[10], w[11], heads);
+    RL_TRY(hipGetLastError());
+    const float* h1w = heads;
+    const float* h1b = heads + 128 * 128;
+    const float* h2w = h1b + 128;
+    const float* h2b = h2w + 64 * 128;
+    RL_TRY(pack_layer(w[0], kQ1, kQ1.in, block + P.w[net][0], st));
+    RL_TRY(pack_bias(w[1], kQ1, block + P.b[net][0], st));
+    RL_TRY(pack_layer(w[2], kQ2, kQ2.in, block + P.w[net][1], st));
+    RL_TRY(pack_bias(w[3], kQ2, block + P.b[net][1], st));
+    RL_TRY(pack_layer(h1w, kQH1, 128, block + P.w[net][2], st));
+    RL_TRY(pack_bias(h1b, kQH1, block + P.b[net][2], st));
+    RL_TRY(pack_layer(h2w, kQH2, 128, block + P.w[net][3], st));
+    RL_TRY(pack_bias(h2b, kQH2, block + P.b[net][3], st));
+  }
+  if (cur) {
+    RL_TRY(pack_layer(cur[0], kQC1, kState + kActions, block + P.cw[0], st));
+    RL_TRY(pack_bias(cur[1], kQC1, block + P.cb[0], st));
+    RL_TRY(pack_layer(cur[2], kQC2, kQC2.in, block + P.cw[1], st));
+    RL_TRY(pack_bias(cur[3], kQC2, block + P.cb[1], st));
+    hipLaunchKernelGGL(pack_onehot_kernel, dim3((kActions * 128 + 255) / 256), dim3(256), 0, st,
+                       cur[0], block + P.c_onehot);
+    RL_TRY(hipGetLastError());
+  }
+#undef RL_TRY
+  return hipSuccess;
+}
 
 hipError_t pack_weights(const float* const actor[6], const float* const critic[12],
                         const float* const cur[4], float* block, hipStream_t st) {

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for PPO experience collection.
+"""Seeded synthetic inputs for PPO and DQN experience collection.
 
 This module only *generates inputs*: market features and prices, network
 weights, episode start bars, GAE test streams and the scalar settings of a
@@ -34,6 +34,10 @@ N_ACTIONS = 45
 ACTOR_DIMS = (54, 128, 64, 45)
 CRITIC_DIMS = (54, 512, 384, 256, 128, 64, 1)
 CURIOSITY_DIMS = (STATE_DIM + N_ACTIONS, 128, N_FEATURES)
+# dueling Q-network of the DQN collection: trunk, value head, advantage head
+Q_TRUNK_DIMS = (54, 256, 128)
+Q_VALUE_DIMS = (128, 64, 1)
+Q_ADV_DIMS = (128, 64, 45)
 
 # Named workloads: sizes and master seeds.
 WORKLOADS = {
@@ -41,6 +45,7 @@ WORKLOADS = {
     "ppo_n128_l500": dict(N=128, L=500, n_bars=200_000, seed=1),
     "gae_n4096_l2048": dict(N=4096, L=2048, seed=2),
     "ppo_n8192_l500": dict(N=8192, L=500, n_bars=1_000_000, seed=3),
+    "dqn_n16384_l500": dict(N=16384, L=500, n_bars=1_000_000, seed=4),
 }
 
 _STREAM_MARKET = 1
@@ -115,6 +120,27 @@ def ppo_weights(seed: int, bias_scale: float = 0.0) -> dict:
     )
 
 
+def q_net_weights(g, bias_scale: float) -> list:
+    """12 arrays: trunk 1, trunk 2, value 1, value 2, advantage 1, advantage 2
+    (weight [out, in], then bias)."""
+    return (_mlp(g, Q_TRUNK_DIMS, bias_scale) + _mlp(g, Q_VALUE_DIMS, bias_scale)
+            + _mlp(g, Q_ADV_DIMS, bias_scale))
+
+
+def dqn_weights(seed: int, bias_scale: float = 0.0) -> dict:
+    """{'online': [12], 'target': [12], 'curiosity': [4]}: online and target
+    nets initialised independently."""
+    g = _rng(seed, _STREAM_WEIGHTS)
+    return dict(online=q_net_weights(g, bias_scale), target=q_net_weights(g, bias_scale),
+                curiosity=_mlp(g, CURIOSITY_DIMS, bias_scale))
+
+
+def dqn_settings() -> dict:
+    """Scalars of the DQN collection: exploration rate, TD discount, priority
+    exponent."""
+    return dict(epsilon=0.1, gamma=0.99, alpha=0.6)
+
+
 def episode_starts(N: int, L: int, n_bars: int, seed: int) -> np.ndarray:
     g = _rng(seed, _STREAM_STARTS)
     return g.integers(0, n_bars - L, size=N, dtype=np.int64).astype(np.int32)
@@ -147,4 +173,23 @@ def ppo_inputs(name_or_spec, bias_scale: float = 0.0) -> dict:
         starts=episode_starts(N, L, nb, seed),
         sampler_seed=sampler_seed(seed),
         settings=settings(),
+    )
+
+
+def dqn_inputs(name_or_spec, bias_scale: float = 0.0, epsilon: float | None = None) -> dict:
+    """Everything one DQN collection needs, for a named workload or a spec dict."""
+    spec = WORKLOADS[name_or_spec] if isinstance(name_or_spec, str) else dict(name_or_spec)
+    N, L, nb, seed = spec["N"], spec["L"], spec["n_bars"], spec["seed"]
+    feats, prices = market(nb, seed)
+    dq = dqn_settings()
+    if epsilon is not None:
+        dq["epsilon"] = epsilon
+    return dict(
+        N=N, L=L, n_bars=nb, seed=seed,
+        features=feats, prices=prices,
+        weights=dqn_weights(seed, bias_scale),
+        starts=episode_starts(N, L, nb, seed),
+        sampler_seed=sampler_seed(seed),
+        settings=settings(),
+        dqn=dq,
     )

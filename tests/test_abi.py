@@ -1,5 +1,5 @@
-"""The C-ABI library loads and exports every symbol include/rollout.h
-declares; host-side argument checks answer without touching a GPU."""
+"""The C-ABI library loads and exports every symbol include/*.h declares;
+host-side argument checks answer without touching a GPU."""
 import ctypes as C
 import os
 import re
@@ -7,13 +7,16 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rollout.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rollout.h", "dqn.h")]
 
 
 def declared_functions():
-    txt = open(HEADER).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    names = re.findall(r"^\s*(?:int|void|const char \*)\s*\*?\s*(\w+)\s*\(", txt, flags=re.M)
+    names = []
+    for header in HEADERS:
+        txt = open(header).read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        names += re.findall(r"^\s*(?:int|void|const char \*)\s*\*?\s*(\w+)\s*\(", txt,
+                            flags=re.M)
     return sorted(set(names))
 
 
@@ -27,7 +30,8 @@ def rx():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
-         "gae_scan", "rollout_destroy", "rollout_last_error"])
+         "gae_scan", "rollout_destroy", "rollout_last_error",
+         "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_collect", "dqn_destroy"])
 
 
 def test_library_exports_every_declared_symbol(rx):
@@ -80,3 +84,41 @@ def test_host_side_errors_without_gpu(rx):
     assert lib.gae_scan(None, None, None, None, 3, 5, 0.99, 0.95, None, None, None) == rx.ROLLOUT_EINVAL
     assert lib.gae_scan(None, None, None, None, -1, 5, 0.99, 0.95, None, None, None) == rx.ROLLOUT_EINVAL
     lib.rollout_destroy(None)
+
+
+def test_dqn_config_default_values(rx):
+    cfg = rx.dqn_config_default(16384, 500)
+    assert (cfg.n_episodes, cfg.n_steps, cfg.n_features, cfg.state_dim, cfg.n_actions) == \
+        (16384, 500, 51, 54, 45)
+    assert list(cfg.trunk_dims) == [54, 256, 128]
+    assert list(cfg.value_dims) == [128, 64, 1]
+    assert list(cfg.advantage_dims) == [128, 64, 45]
+    assert list(cfg.cur_dims) == [99, 128, 51]
+    assert abs(cfg.epsilon - 0.1) < 1e-7 and abs(cfg.gamma - 0.99) < 1e-7
+    assert abs(cfg.priority_alpha - 0.6) < 1e-7
+    assert cfg.max_hold == 50 and cfg.div_window == 20
+
+
+def test_dqn_config_struct_size_matches_header(rx):
+    # 5 ints, 4 x 3 dims, 3 floats, 2 floats, 2 ints, 2 + 4 floats, 5 + 3 + 1 floats
+    assert C.sizeof(rx.DqnConfig) == 4 * (5 + 12 + 3 + 2 + 2 + 6 + 9)
+    assert C.sizeof(rx.DqnOutputs) == 8 * 14
+
+
+def test_dqn_host_side_errors_without_gpu(rx):
+    lib = rx.load_library()
+    h = C.c_void_p()
+    assert lib.dqn_create(None, None, None, None, None, None, 0, None, C.byref(h)) == rx.ROLLOUT_EINVAL
+    assert "config" in rx.rollout_last_error()
+    cfg = rx.dqn_config_default(16, 10)
+    cfg.epsilon = 1.5
+    assert lib.dqn_create(C.byref(cfg), None, None, None, None, None, 0, None, C.byref(h)) == \
+        rx.ROLLOUT_EINVAL
+    assert "epsilon" in rx.rollout_last_error()
+    cfg = rx.dqn_config_default(16, 10)
+    cfg.trunk_dims[1] = 512
+    assert lib.dqn_create(C.byref(cfg), None, None, None, None, None, 0, None, C.byref(h)) == \
+        rx.ROLLOUT_EINVAL
+    assert "trunk" in rx.rollout_last_error()
+    assert lib.dqn_collect(None, None, 0, None, None) == rx.ROLLOUT_EINVAL
+    lib.dqn_destroy(None)
