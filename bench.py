@@ -32,6 +32,10 @@ CRITIC_FLOP = 2 * (54 * 512 + 512 * 384 + 384 * 256 + 256 * 128 + 128 * 64 + 64)
 CURIOSITY_FLOP = 2 * (54 * 128 + 128 * 51) + 128                                  # 27,008
 VALUE_KERNEL_FLOP = CRITIC_FLOP + CURIOSITY_FLOP                                  # 754,176
 MLP_FLOP = ACTOR_FLOP + VALUE_KERNEL_FLOP                                         # 790,144
+# DQN collection: online and target dueling nets (trunk 54-256-128, value
+# head 128-64-1, advantage head 128-64-45) and the curiosity model
+Q_NET_FLOP = 2 * (54 * 256 + 256 * 128 + 128 * 64 + 64 * 1 + 128 * 64 + 64 * 45)   # 131,840
+DQN_FLOP = 2 * Q_NET_FLOP + CURIOSITY_FLOP                                          # 290,688
 GAE_BYTES = 17   # read r 4, V 4, d 1; write A 4, R 4
 
 
@@ -96,6 +100,36 @@ def time_collect(inp, steps, warmup, precision=0):
     col.close()
     return dict(N=N, L=L, wall_s=wall, step_ms_events=per_step, phases_ms=ph.mean(axis=0),
                 nonfinite=bad)
+
+
+def time_dqn(inp, steps, warmup):
+    """DQN collections at the input's size; events around each launch."""
+    import torch
+    import numpy as np
+    import rl_experience_collection_amd as rx
+
+    N, L = inp["N"], inp["L"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    w = inp["weights"]
+    weights = {k: [dev(x) for x in w[k]] for k in ("online", "target", "curiosity")}
+    feats, prices, starts = dev(inp["features"]), dev(inp["prices"]), dev(inp["starts"])
+    col = rx.DqnCollector(N, L, weights, feats, prices, settings=inp["settings"], dqn=inp["dqn"])
+    outs = rx.alloc_dqn_outputs(N, L, "cuda")
+    ev = rx.HipEvents(2 * steps)
+    seed = inp["sampler_seed"]
+    for i in range(warmup):
+        col.collect(starts, seed + i, outputs=outs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        col.collect(starts, seed + warmup + i, outputs=outs, phase_events=ev.handles[2 * i:2 * i + 2])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)])
+    bad = int(outs["counters"][0].item())
+    ev.close()
+    col.close()
+    return dict(N=N, L=L, wall_s=wall, kernel_ms=float(per.mean()), nonfinite=bad)
 
 
 def probe_lib():
@@ -231,6 +265,12 @@ def run_single(name, steps, warmup):
                 else dict(N=8192, L=500, seed=synthdata.WORKLOADS["ppo_n8192_l500"]["seed"]))
         r = time_gae(spec, steps, traffic_only=name.startswith("gae_traffic"))
         return dict(workload=name, cold_ms=r["cold_ms"], warm_ms=r["warm_ms"])
+    if name.startswith("dqn"):
+        r = time_dqn(synthdata.dqn_inputs("dqn_n16384_l500"), steps, warmup)
+        return dict(workload=name, ms_per_step=r["wall_s"] * 1000 / steps, kernel_ms=r["kernel_ms"],
+                    exp_per_s=r["N"] * r["L"] * steps / r["wall_s"],
+                    TFLOPs=DQN_FLOP * r["N"] * r["L"] / (r["kernel_ms"] * 1e-3) / 1e12,
+                    nonfinite=r["nonfinite"])
     if name.startswith("weight_stream"):
         return dict(workload=name, **time_weight_stream(8192 * 500, name.endswith("bf16"), steps))
     a = torch.ones(1 << 28, device="cuda")  # copy_1gib: 1 GiB read + 1 GiB written per copy
@@ -252,6 +292,7 @@ def main():
                     choices=("all", "collect_n8192_fp32", "collect_n8192_bf16", "collect_n128_fp32",
                              "gae_n4096_l2048", "gae_n8192_l500", "gae_traffic_n4096_l2048",
                              "gae_traffic_n8192_l500", "weight_stream_fp32", "weight_stream_bf16",
+                             "dqn_n16384_l500",
                              "copy_1gib"),
                     help="one workload only (for profiler counter passes); prints its own "
                          "JSON line instead of the benchmark line")
