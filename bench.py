@@ -333,6 +333,9 @@ def main():
     gae_cx = time_gae(dict(N=N, L=L, seed=spec["seed"]), max(args.steps, 20), traffic_only=True)
     ws_f = time_weight_stream(N * L, False, 5)
     ws_b = time_weight_stream(N * L, True, 5)
+    log("timing the DQN collection N=16384 L=500 ...")
+    dq = time_dqn(synthdata.dqn_inputs("dqn_n16384_l500"), args.steps, args.warmup)
+    dq_exp = dq["N"] * dq["L"]
 
     value_files = ["rl_experience_collection_amd/csrc/value.hip",
                    "rl_experience_collection_amd/csrc/nets.hpp",
@@ -377,6 +380,13 @@ def main():
                 weight_stream_bytes_per_launch=ws_b["bytes_per_launch"],
                 value_kernel_frac_of_bound=max(ws_b["ms"], VALUE_KERNEL_FLOP * N * L /
                                                PEAK_BF16_MFMA * 1e3) / float(bfr["phases_ms"][1])),
+            dqn_collect_n16384_l500_fp32=dict(
+                value=dq_exp * args.steps / dq["wall_s"], unit="experiences/s",
+                ms_per_step=dq["wall_s"] * 1000 / args.steps, kernel_ms=dq["kernel_ms"],
+                flop_per_experience=DQN_FLOP,
+                TFLOPs=DQN_FLOP * dq_exp / (dq["kernel_ms"] * 1e-3) / 1e12,
+                frac_of_fp32_peak=DQN_FLOP * dq_exp / (dq["kernel_ms"] * 1e-3) / PEAK_FP32_MFMA,
+                nonfinite_events=dq["nonfinite"]),
             ppo_collect_n128_l500_fp32=dict(
                 value=128 * 500 * args.steps / small["wall_s"], unit="experiences/s",
                 ms_per_step=small["wall_s"] * 1000 / args.steps,

@@ -58,32 +58,46 @@ __device__ __forceinline__ void dense(const GlobalWeights& gw, uint32_t pk_b, co
 
 // Dueling Q-network `net` (0 online, 1 target) on the state operands `in`:
 // the head layer's raw outputs (advantages 0..44, value 45) end in bufB.
-// Entry: `in` complete, bufA and bufB free; exit: before any barrier.
+// Entry: `in` complete, bufA and bufB free; exit: before any barrier.  Each
+// layer's weight stream starts before the store and barrier that end the
+// previous layer, so its first loads are in flight while the waves meet.
+// The head layer skips its zero blocks: output tiles 0-1 (advantages 0..31)
+// read only inputs 64..127 (k-steps 16..31), tile 2 (advantages 32..44 and
+// the value) reads all, and tile 3 holds only padding.
 __device__ __forceinline__ void q_network(const GlobalWeights& gw, const float* W, int net,
                                           const f32x4* in, f32x4* bufA, f32x4* bufB, int q,
                                           int lane) {
-  {
-    f32x4 h[1][4];
-    dense<16, 4>(gw, 4u * (uint32_t)kD.w[net][0], W + kD.b[net][0], in, h, q, lane);
-    relu_store_tiles<4, 1>(h, bufA, 0, q, lane);
-  }
+  constexpr uint32_t kHeadStepB = kSplit * 64 * 4;  // bytes per k-step, one tile per wave
+  const uint32_t w0 = 4u * (uint32_t)kD.w[net][0], w1 = 4u * (uint32_t)kD.w[net][1];
+  const uint32_t w2 = 4u * (uint32_t)kD.w[net][2], w3 = 4u * (uint32_t)kD.w[net][3];
+  WeightStream<false, 4, 4> s0;
+  stream_begin<16>(s0, gw, w0, W + kD.b[net][0], q, lane);
+  f32x4 h0[1][4];
+  stream_layer<16, 4, 4, 1>(s0, gw, w0, LdsOperands{in, 0}, h0, q, lane);
+  WeightStream<false, 2, 8> s1;
+  stream_begin<64>(s1, gw, w1, W + kD.b[net][1], q, lane);
+  relu_store_tiles<4, 1>(h0, bufA, 0, q, lane);
   lds_barrier();
-  {
-    f32x4 h[1][2];
-    dense<64, 2>(gw, 4u * (uint32_t)kD.w[net][1], W + kD.b[net][1], bufA, h, q, lane);
-    relu_store_tiles<2, 1>(h, bufB, 0, q, lane);
-  }
+  f32x4 h1[1][2];
+  stream_layer<64, 2, 8, 1>(s1, gw, w1, LdsOperands{bufA, 0}, h1, q, lane);
+  WeightStream<false, 2, 8> s2;
+  stream_begin<32>(s2, gw, w2, W + kD.b[net][2], q, lane);
+  relu_store_tiles<2, 1>(h1, bufB, 0, q, lane);
   lds_barrier();
-  {
-    f32x4 h[1][2];
-    dense<32, 2>(gw, 4u * (uint32_t)kD.w[net][2], W + kD.b[net][2], bufB, h, q, lane);
-    relu_store_tiles<2, 1>(h, bufA, 0, q, lane);
-  }
+  f32x4 h2[1][2];
+  stream_layer<32, 2, 8, 1>(s2, gw, w2, LdsOperands{bufB, 0}, h2, q, lane);
+  WeightStream<false, 1, 8> s3;
+  const uint32_t w3q = q < 2 ? w3 + 16u * kHeadStepB : w3;
+  stream_begin<16>(s3, gw, w3q, W + kD.b[net][3], q, lane);
+  relu_store_tiles<2, 1>(h2, bufA, 0, q, lane);
   lds_barrier();
-  {
-    f32x4 h[1][1];
-    dense<32, 1>(gw, 4u * (uint32_t)kD.w[net][3], W + kD.b[net][3], bufA, h, q, lane);
-    bufB[q * 64 + lane] = h[0][0];  // raw: no ReLU on the head outputs
+  f32x4 h3[1][1];
+  if (q < 2) {
+    stream_layer<16, 1, 8, 1>(s3, gw, w3q, LdsOperands{bufA + 4 * 64, 0}, h3, q, lane);
+    bufB[q * 64 + lane] = h3[0][0];
+  } else if (q == 2) {
+    stream_layer<32, 1, 8, 1>(s3, gw, w3, LdsOperands{bufA, 0}, h3, q, lane);
+    bufB[q * 64 + lane] = h3[0][0];  // raw: no ReLU on the head outputs
   }
 }
 
