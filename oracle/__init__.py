@@ -127,6 +127,12 @@ def lib():
                                       vp, vp, C.c_int64, vp, C.c_uint64, vp, vp, i32,
                                       C.POINTER(DqnOutputs), i32]
         L.orc_dqn_rollout.restype = C.c_int
+        L.orc_per_uniform.argtypes = [C.c_uint64, C.c_uint32]
+        L.orc_per_uniform.restype = C.c_double
+        L.orc_per_sample.argtypes = [vp, C.c_int64, i32, C.c_uint64, f32, vp, vp, vp]
+        L.orc_per_sample.restype = C.c_int
+        L.orc_per_update.argtypes = [vp, C.c_int64, vp, vp, i32, f32, f32, f32]
+        L.orc_per_update.restype = C.c_int
         _lib = L
     return _lib
 
@@ -379,3 +385,33 @@ def dqn_rollout(inputs: dict, precision: int = FP32, forced_actions=None, subset
     if rc != 0:
         raise ValueError("oracle DQN rollout rejected its arguments")
     return out
+
+
+# ---------------------------------------------------------------- prioritized replay
+def per_uniform(seed: int, draw: int) -> float:
+    return lib().orc_per_uniform(C.c_uint64(seed), draw)
+
+
+def per_sample(priorities, batch: int, seed: int, beta: float):
+    """(indices [B] i32, weights [B] f32, gap [B] f64) by proportional sampling."""
+    p = _f32(priorities).ravel()
+    idx = np.zeros(batch, np.int32)
+    w = np.zeros(batch, np.float32)
+    gap = np.zeros(batch, np.float64)
+    rc = lib().orc_per_sample(_p(p), p.size, batch, C.c_uint64(seed), float(beta), _p(idx), _p(w),
+                              _p(gap))
+    if rc != 0:
+        raise ValueError("oracle PER sample rejected its arguments")
+    return idx, w, gap
+
+
+def per_update(priorities, indices, td, alpha: float, epsilon: float, max_priority: float):
+    """A new priority array after the batch's update (the input is not modified)."""
+    p = _f32(priorities).ravel().copy()
+    idx = np.ascontiguousarray(indices, np.int32)
+    t = _f32(td)
+    rc = lib().orc_per_update(_p(p), p.size, _p(idx), _p(t), idx.size, float(alpha),
+                              float(epsilon), float(max_priority))
+    if rc != 0:
+        raise ValueError("oracle PER update rejected its arguments")
+    return p

@@ -627,3 +627,79 @@ int orc_dqn_rollout(const orc_params *p, const orc_dqn_params *dq, const orc_dqn
   (void)n_threads;
   return rc ? -1 : 0;
 }
+
+/* ======================================================================== */
+/* Prioritized replay ("GPU-Resident Prioritized Experience Replay",         */
+/* Sampling Kernels: proportional sampling, IS weights, priority update).    */
+/* ======================================================================== */
+double orc_per_uniform(uint64_t seed, uint32_t draw) {
+  /* counter (draw, 0, 4, 0): 53 bits from the first two output words */
+  const uint32_t ctr[4] = {draw, 0u, 4u, 0u};
+  const uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  const uint64_t m = ((uint64_t)out[0] << 21) | (uint64_t)(out[1] >> 11);
+  return (double)m * (1.0 / 9007199254740992.0);
+}
+
+static double per_value(float p) { return (p > 0.0f) ? (double)p : 0.0; } /* NaN, <0 -> 0 */
+
+int orc_per_sample(const float *priorities, int64_t n, int32_t batch, uint64_t seed, float beta,
+                   int32_t *indices, float *weights, double *gap) {
+  if (!priorities || !indices || !weights || n <= 0 || batch < 0) return -1;
+  double *C = (double *)malloc((size_t)n * sizeof(double));
+  double *w = (double *)malloc((size_t)(batch > 0 ? batch : 1) * sizeof(double));
+  if (!C || !w) { free(C); free(w); return -1; }
+  double run = 0.0;
+  for (int64_t k = 0; k < n; ++k) {
+    run += per_value(priorities[k]);
+    C[k] = run;
+  }
+  const double T = run;
+  const int uniform = !(T > 0.0) || isinf(T);
+  double wmax = 0.0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const double u = orc_per_uniform(seed, (uint32_t)b);
+    int64_t k;
+    if (uniform) {
+      k = (int64_t)(u * (double)n);
+      if (k >= n) k = n - 1;
+      w[b] = 1.0;
+      if (gap) gap[b] = 1.0;
+    } else {
+      const double target = u * T;
+      int64_t lo = 0, hi = n - 1; /* first k with C[k] > target; C[n-1] = T > target */
+      while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (C[mid] > target) hi = mid; else lo = mid + 1;
+      }
+      k = lo;
+      w[b] = pow((double)n * per_value(priorities[k]) / T, -(double)beta);
+      if (gap) {
+        const double below = k > 0 ? target - C[k - 1] : target;
+        const double above = C[k] - target;
+        gap[b] = (below < above ? below : above) / T;
+      }
+    }
+    indices[b] = (int32_t)k;
+    if (w[b] > wmax) wmax = w[b];
+  }
+  for (int32_t b = 0; b < batch; ++b) weights[b] = (float)(w[b] / wmax);
+  free(C);
+  free(w);
+  return 0;
+}
+
+int orc_per_update(float *priorities, int64_t n, const int32_t *indices, const float *td,
+                   int32_t batch, float alpha, float epsilon, float max_priority) {
+  if (!priorities || !indices || !td || batch < 0) return -1;
+  for (int32_t b = 0; b < batch; ++b)
+    if (indices[b] < 0 || (int64_t)indices[b] >= n) return -1;
+  for (int32_t b = 0; b < batch; ++b) {
+    float v = powf(fabsf(td[b]), alpha) + epsilon;
+    if (!(v >= epsilon)) v = epsilon; /* NaN */
+    if (v > max_priority) v = max_priority;
+    priorities[indices[b]] = v;
+  }
+  return 0;
+}

@@ -209,6 +209,29 @@ int orc_dqn_rollout(const orc_params *p, const orc_dqn_params *dq, const orc_dqn
                     const int32_t *subset, int32_t n_subset, const orc_dqn_outputs *out,
                     int32_t n_threads);
 
+/* --- prioritized replay: sampling and priority update ----------------------
+ * "GPU-Resident Prioritized Experience Replay", Sampling Kernels
+ * (proportional) and Error Handling:
+ *  - draw b uses the 53-bit uniform u_b of orc_per_uniform;
+ *  - with C_k the inclusive prefix sums of the priorities (fp64, left to
+ *    right; negative and NaN priorities count as 0) and T = C_{n-1}, the
+ *    sample is the first k with C_k > u_b T;
+ *  - its importance weight is (n p_k / T)^(-beta), divided by the largest
+ *    weight of the batch (fp64, rounded to float at the end);
+ *  - if T is not positive and finite the draw is uniform, k = floor(u_b n),
+ *    with weight 1.
+ * gap (nullable) receives, per draw, the distance from u_b T to the nearest
+ * of C_{k-1}, C_k, divided by T (near-tie screening). */
+double orc_per_uniform(uint64_t seed, uint32_t draw);
+int orc_per_sample(const float *priorities, int64_t n, int32_t batch, uint64_t seed, float beta,
+                   int32_t *indices, float *weights, double *gap);
+/* Priority update in batch order (a repeated index keeps the last value):
+ * priority[i_b] = clamp(|td_b|^alpha + epsilon, epsilon, max_priority), with
+ * NaN giving epsilon.  Returns -1 (nothing written) if an index is out of
+ * range. */
+int orc_per_update(float *priorities, int64_t n, const int32_t *indices, const float *td,
+                   int32_t batch, float alpha, float epsilon, float max_priority);
+
 #ifdef __cplusplus
 }
 #endif
