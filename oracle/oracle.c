@@ -674,6 +674,9 @@ int orc_per_sample(const float *priorities, int64_t n, int32_t batch, uint64_t s
         if (C[mid] > target) hi = mid; else lo = mid + 1;
       }
       k = lo;
+      /* only if rounding put u T at T itself: the last priority with weight */
+      if (!(C[k] > target))
+        while (k > 0 && per_value(priorities[k]) == 0.0) --k;
       w[b] = pow((double)n * per_value(priorities[k]) / T, -(double)beta);
       if (gap) {
         const double below = k > 0 ? target - C[k - 1] : target;

@@ -8,10 +8,12 @@ fails to load, importing the functions raises.
 The functions carry the C names:
     rollout_config_default, rollout_create, rollout_set_weights,
     rollout_collect, gae_scan, rollout_destroy, rollout_last_error
-    (include/rollout.h), and dqn_config_default, dqn_create,
-    dqn_set_weights, dqn_collect, dqn_destroy (include/dqn.h),
+    (include/rollout.h), dqn_config_default, dqn_create,
+    dqn_set_weights, dqn_collect, dqn_destroy (include/dqn.h), and
+    per_create, per_sample, per_gather, per_update, per_destroy
+    (include/per.h),
 plus helpers: `alloc_outputs`, `alloc_dqn_outputs` and the `Collector` and
-`DqnCollector` convenience classes.
+`DqnCollector` and `PerSampler` convenience classes.
 """
 from __future__ import annotations
 
@@ -26,7 +28,8 @@ ROLLOUT_FP32, ROLLOUT_BF16 = 0, 1
 STATE_DIM, N_ACTIONS, N_FEATURES = 54, 45, 51
 EXPORTED = ("rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
             "gae_scan", "rollout_destroy", "rollout_last_error",
-            "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_collect", "dqn_destroy")
+            "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_collect", "dqn_destroy",
+            "per_create", "per_sample", "per_gather", "per_update", "per_destroy")
 
 
 class RolloutConfig(C.Structure):
@@ -114,9 +117,17 @@ def load_library(path: str = LIB_PATH):
     L.dqn_collect.argtypes = [vp, vp, C.c_uint64, C.POINTER(DqnOutputs), vp]
     L.dqn_destroy.argtypes = [vp]
     L.dqn_destroy.restype = None
+    f32 = C.c_float
+    L.per_create.argtypes = [i64, i32, C.POINTER(vp)]
+    L.per_sample.argtypes = [vp, vp, i64, i32, C.c_uint64, f32, vp, vp, vp]
+    L.per_gather.argtypes = [vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.per_update.argtypes = [vp, i64, vp, vp, i32, f32, f32, f32, vp]
+    L.per_destroy.argtypes = [vp]
+    L.per_destroy.restype = None
     for name in ("rollout_config_default", "rollout_create", "rollout_set_weights",
                  "rollout_collect", "gae_scan", "dqn_config_default", "dqn_create",
-                 "dqn_set_weights", "dqn_collect"):
+                 "dqn_set_weights", "dqn_collect", "per_create", "per_sample", "per_gather",
+                 "per_update"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -473,6 +484,90 @@ class DqnCollector:
     def close(self):
         if self.handle:
             dqn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------- prioritized replay
+def per_create(capacity: int, max_batch: int) -> int:
+    h = C.c_void_p()
+    _check(load_library().per_create(capacity, max_batch, C.byref(h)))
+    return h.value
+
+
+def per_sample(handle: int, priorities, batch: int, seed: int, beta: float, indices, weights,
+               stream=None):
+    import torch
+    n = priorities.numel()
+    _check(load_library().per_sample(
+        C.c_void_p(handle), _dev_ptr(priorities, torch.float32, (n,), "priorities"), n, batch,
+        C.c_uint64(seed), beta, _dev_ptr(indices, torch.int32, (batch,), "indices"),
+        _dev_ptr(weights, torch.float32, (batch,), "weights"), _stream(stream)))
+
+
+def per_gather(indices, n: int, states=None, next_states=None, actions=None, rewards=None,
+               dones=None, out: dict | None = None, stream=None) -> dict:
+    """Sources are flat [n(, 54)] views (a [L][N] collection output reshaped);
+    returns the batch arrays (allocated when `out` is None)."""
+    import torch
+    B = indices.numel()
+    dev = indices.device
+    src = dict(states=states, next_states=next_states, actions=actions, rewards=rewards, dones=dones)
+    if out is None:
+        mk = dict(states=lambda: torch.empty((B, STATE_DIM), dtype=torch.float32, device=dev),
+                  next_states=lambda: torch.empty((B, STATE_DIM), dtype=torch.float32, device=dev),
+                  actions=lambda: torch.empty(B, dtype=torch.int32, device=dev),
+                  rewards=lambda: torch.empty(B, dtype=torch.float32, device=dev),
+                  dones=lambda: torch.empty(B, dtype=torch.uint8, device=dev))
+        out = {k: (mk[k]() if v is not None else None) for k, v in src.items()}
+    types = dict(states=torch.float32, next_states=torch.float32, actions=torch.int32,
+                 rewards=torch.float32, dones=torch.uint8)
+    shp = lambda k, m: (m, STATE_DIM) if k in ("states", "next_states") else (m,)
+    ps = [_dev_ptr(src[k], types[k], shp(k, n), k) for k in src]
+    po = [_dev_ptr(out[k], types[k], shp(k, B), "out_" + k) if out.get(k) is not None else None
+          for k in src]
+    _check(load_library().per_gather(_dev_ptr(indices, torch.int32, (B,), "indices"), B, n, *ps,
+                                     *po, _stream(stream)))
+    return out
+
+
+def per_update(priorities, indices, td, alpha: float, epsilon: float, max_priority: float,
+               stream=None):
+    import torch
+    n, B = priorities.numel(), indices.numel()
+    _check(load_library().per_update(
+        _dev_ptr(priorities, torch.float32, (n,), "priorities"), n,
+        _dev_ptr(indices, torch.int32, (B,), "indices"), _dev_ptr(td, torch.float32, (B,), "td"),
+        B, alpha, epsilon, max_priority, _stream(stream)))
+
+
+def per_destroy(handle: int):
+    if handle:
+        load_library().per_destroy(C.c_void_p(handle))
+
+
+class PerSampler:
+    """Owns one sampler handle."""
+
+    def __init__(self, capacity: int, max_batch: int):
+        self.capacity, self.max_batch = capacity, max_batch
+        self.handle = per_create(capacity, max_batch)
+
+    def sample(self, priorities, batch: int, seed: int, beta: float, stream=None):
+        import torch
+        idx = torch.empty(batch, dtype=torch.int32, device=priorities.device)
+        w = torch.empty(batch, dtype=torch.float32, device=priorities.device)
+        per_sample(self.handle, priorities, batch, seed, beta, idx, w, stream)
+        return idx, w
+
+    def close(self):
+        if self.handle:
+            per_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

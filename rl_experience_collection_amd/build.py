@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(os.path.dirname(PKG), "_build", "rollout")
 LIB = os.path.join(PKG, "librollout.so")
-SOURCES = ["abi.hip", "pack.hip", "rollout.hip", "value.hip", "gae.hip", "dqn.hip"]
+SOURCES = ["abi.hip", "pack.hip", "rollout.hip", "value.hip", "gae.hip", "dqn.hip", "per.hip"]
 # measurement kernels used by bench.py only, in a library of their own
 PROBE_LIB = os.path.join(PKG, "libbenchprobes.so")
 PROBE_SOURCES = ["bench_probes.hip"]

@@ -13,8 +13,10 @@
 #include <utility>
 
 #include "../../include/dqn.h"
+#include "../../include/per.h"
 #include "../../include/rollout.h"
 #include "collect.hpp"
+#include "per.hpp"
 #include "gae.hpp"
 #include "pack.hpp"
 
@@ -220,6 +222,14 @@ int check_tensors(const float* const* w, int count, const char* what) {
 }
 
 }  // namespace
+
+struct per_s {
+  int device = 0;
+  int64_t capacity = 0;
+  int32_t max_batch = 0;
+  double* prefix = nullptr;  // block prefix sums, per_blocks(capacity)
+  double* raw = nullptr;     // unnormalised weights, max_batch
+};
 
 struct dqn_s {
   int device = 0;
@@ -601,6 +611,96 @@ int dqn_collect(dqn_handle h, const int32_t* episode_starts, uint64_t seed, cons
   RL_HIP(rl::launch_dqn(da, st), "dqn launch");
   RL_HIP(mark(1), "hipEventRecord(phase 1)");
   return ROLLOUT_OK;
+}
+
+constexpr int32_t kPerMaxBatch = 1 << 20;
+
+int per_create(int64_t capacity, int32_t max_batch, per_handle* out) {
+  if (!out) return fail(ROLLOUT_EINVAL, "out handle pointer is NULL");
+  *out = nullptr;
+  if (capacity < 1 || capacity > ((int64_t)1 << 31) - 1)
+    return fail(ROLLOUT_EINVAL, "capacity must be in 1 .. 2^31 - 1 (got %lld)", (long long)capacity);
+  if (max_batch < 1 || max_batch > kPerMaxBatch)
+    return fail(ROLLOUT_EINVAL, "max_batch must be in 1 .. %d (got %d)", kPerMaxBatch, max_batch);
+  auto* h = new (std::nothrow) per_s();
+  if (!h) return fail(ROLLOUT_ENOMEM, "host allocation failed");
+  h->capacity = capacity;
+  h->max_batch = max_batch;
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "hipGetDevice");
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, (size_t)rl::per_blocks(capacity) * sizeof(double)) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return fail(ROLLOUT_ENOMEM, "cannot allocate block prefixes");
+  }
+  h->prefix = static_cast<double*>(p);
+  if (hipMalloc(&p, (size_t)max_batch * sizeof(double)) != hipSuccess) {
+    (void)hipGetLastError();
+    per_destroy(h);
+    return fail(ROLLOUT_ENOMEM, "cannot allocate weight scratch");
+  }
+  h->raw = static_cast<double*>(p);
+  *out = h;
+  return ROLLOUT_OK;
+}
+
+int per_sample(per_handle h, const float* priorities, int64_t n, int32_t batch, uint64_t seed,
+               float beta, int32_t* indices, float* weights, void* hip_stream) {
+  if (!h) return fail(ROLLOUT_EINVAL, "handle is NULL");
+  if (!priorities || (batch > 0 && (!indices || !weights)))
+    return fail(ROLLOUT_EINVAL, "per_sample: NULL buffer");
+  if (n < 1 || n > h->capacity)
+    return fail(ROLLOUT_EINVAL, "per_sample: n must be in 1 .. capacity (%lld), got %lld",
+                (long long)h->capacity, (long long)n);
+  if (batch < 0 || batch > h->max_batch)
+    return fail(ROLLOUT_EINVAL, "per_sample: batch must be in 0 .. %d, got %d", h->max_batch, batch);
+  int dev = -1;
+  RL_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev != h->device)
+    return fail(ROLLOUT_EINVAL, "handle was created on device %d, current device is %d", h->device, dev);
+  RL_HIP(rl::per_sample_launch(priorities, n, batch, seed, beta, indices, weights, h->prefix, h->raw,
+                               static_cast<hipStream_t>(hip_stream)),
+         "per_sample launch");
+  return ROLLOUT_OK;
+}
+
+int per_gather(const int32_t* indices, int32_t batch, int64_t n, const float* states,
+               const float* next_states, const int32_t* actions, const float* rewards,
+               const uint8_t* dones, float* out_states, float* out_next_states,
+               int32_t* out_actions, float* out_rewards, uint8_t* out_dones, void* hip_stream) {
+  if (batch < 0 || batch > kPerMaxBatch) return fail(ROLLOUT_EINVAL, "per_gather: bad batch %d", batch);
+  if (batch == 0) return ROLLOUT_OK;
+  if (!indices || n < 1) return fail(ROLLOUT_EINVAL, "per_gather: NULL indices or n < 1");
+  if ((states && !out_states) || (next_states && !out_next_states) || (actions && !out_actions) ||
+      (rewards && !out_rewards) || (dones && !out_dones))
+    return fail(ROLLOUT_EINVAL, "per_gather: a source without its output buffer");
+  rl::PerGatherArgs a{indices, batch, n, states, next_states, actions, rewards, dones,
+                      out_states, out_next_states, out_actions, out_rewards, out_dones};
+  RL_HIP(rl::per_gather_launch(a, static_cast<hipStream_t>(hip_stream)), "per_gather launch");
+  return ROLLOUT_OK;
+}
+
+int per_update(float* priorities, int64_t n, const int32_t* indices, const float* td, int32_t batch,
+               float alpha, float epsilon, float max_priority, void* hip_stream) {
+  if (batch < 0 || batch > kPerMaxBatch) return fail(ROLLOUT_EINVAL, "per_update: bad batch %d", batch);
+  if (batch == 0) return ROLLOUT_OK;
+  if (!priorities || !indices || !td) return fail(ROLLOUT_EINVAL, "per_update: NULL buffer");
+  if (!(epsilon <= max_priority)) return fail(ROLLOUT_EINVAL, "per_update: epsilon > max_priority");
+  RL_HIP(rl::per_update_launch(priorities, n, indices, td, batch, alpha, epsilon, max_priority,
+                               static_cast<hipStream_t>(hip_stream)),
+         "per_update launch");
+  return ROLLOUT_OK;
+}
+
+void per_destroy(per_handle h) {
+  if (!h) return;
+  if (h->prefix) (void)hipFree(h->prefix);
+  if (h->raw) (void)hipFree(h->raw);
+  delete h;
 }
 
 void dqn_destroy(dqn_handle h) {

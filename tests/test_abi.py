@@ -7,7 +7,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("rollout.h", "dqn.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rollout.h", "dqn.h", "per.h")]
 
 
 def declared_functions():
@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
          "gae_scan", "rollout_destroy", "rollout_last_error",
-         "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_collect", "dqn_destroy"])
+         "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_collect", "dqn_destroy",
+         "per_create", "per_sample", "per_gather", "per_update", "per_destroy"])
 
 
 def test_library_exports_every_declared_symbol(rx):
@@ -122,3 +123,17 @@ def test_dqn_host_side_errors_without_gpu(rx):
     assert "trunk" in rx.rollout_last_error()
     assert lib.dqn_collect(None, None, 0, None, None) == rx.ROLLOUT_EINVAL
     lib.dqn_destroy(None)
+
+
+def test_per_host_side_errors_without_gpu(rx):
+    lib = rx.load_library()
+    h = C.c_void_p()
+    assert lib.per_create(0, 16, C.byref(h)) == rx.ROLLOUT_EINVAL
+    assert "capacity" in rx.rollout_last_error()
+    assert lib.per_create(100, 0, C.byref(h)) == rx.ROLLOUT_EINVAL
+    assert lib.per_sample(None, None, 10, 1, 0, 0.4, None, None, None) == rx.ROLLOUT_EINVAL
+    assert lib.per_update(None, 10, None, None, 1, 0.6, 0.01, 1.0, None) == rx.ROLLOUT_EINVAL
+    assert lib.per_update(None, 10, None, None, 0, 0.6, 0.01, 1.0, None) == rx.ROLLOUT_OK
+    assert lib.per_gather(None, 2, 10, None, None, None, None, None, None, None, None, None, None,
+                          None) == rx.ROLLOUT_EINVAL
+    lib.per_destroy(None)

@@ -1,0 +1,189 @@
+"""GPU parity of the prioritized-replay kernels (per_sample, per_gather,
+per_update) against the oracle, through the C ABI ("GPU-Resident Prioritized
+Experience Replay", Sampling Kernels).
+
+Indices are compared bit-exactly; a draw whose target u T lies within 1e-12 T
+of one of the oracle's prefix sums is a near tie (the GPU forms its fp64 sums
+in another order) and must then pick the oracle's index or its neighbour with
+weight.  Weights within 1e-6 relative; gathered rows bit-exact; updated
+priorities within 2 ulp of the oracle's (powf rounding).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synthdata
+from parity import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
+
+TIE = 1e-12
+
+
+def priorities(n, seed, holes=True):
+    g = np.random.default_rng(seed)
+    p = g.exponential(1.0, n).astype(np.float32)
+    if holes and n > 8:
+        k = max(1, n // 50)
+        p[g.integers(0, n, k)] = 0.0
+        p[g.integers(0, n, k)] = -1.0
+        p[g.integers(0, n, max(1, k // 4))] = np.nan
+    return p
+
+
+def gpu_sample(p, batch, seed, beta, capacity=None, max_batch=None):
+    import torch
+    import rl_experience_collection_amd as rx
+    s = rx.PerSampler(capacity or p.size, max_batch or max(batch, 1))
+    idx, w = s.sample(torch.from_numpy(p).cuda(), batch, seed, beta)
+    torch.cuda.synchronize()
+    out = idx.cpu().numpy(), w.cpu().numpy()
+    s.close()
+    return out
+
+
+def check_sample(p, batch, seed, beta=0.4):
+    gi, gw = gpu_sample(p, batch, seed, beta)
+    oi, ow, gap = oracle.per_sample(p, batch, seed, beta)
+    mism = np.nonzero(gi != oi)[0]
+    for b in mism:
+        assert gap[b] < TIE, f"draw {b}: gpu {gi[b]} oracle {oi[b]} gap {gap[b]:.3g}"
+        assert abs(int(gi[b]) - int(oi[b])) <= 2048, b
+        assert p[gi[b]] > 0, b
+    ok = np.setdiff1d(np.arange(batch), mism)
+    assert np.allclose(gw[ok], ow[ok], rtol=1e-6, atol=0), np.abs(gw - ow).max()
+    if batch:
+        assert gw.max() == np.float32(1.0)
+    return gi, gw, len(mism)
+
+
+@pytest.mark.parametrize("n,batch", [(1, 5), (7, 64), (2047, 300), (2048, 300), (2049, 300),
+                                     (100_003, 1000), (150_001, 2000), (1_000_000, 4096),
+                                     (4_200_000, 2048)])
+def test_sample_matches_oracle(n, batch):
+    check_sample(priorities(n, n), batch, seed=n + 11)
+
+
+def test_sample_at_the_dqn_workload_size():
+    """8,192,000 priorities (one N=16384 L=500 collection), batch 4096."""
+    n = 16384 * 500
+    _, _, flags = check_sample(priorities(n, 5), 4096, seed=77)
+    assert flags <= 2
+
+
+def test_sample_degenerate_and_beta_zero():
+    p = np.zeros(5000, np.float32)
+    gi, gw = gpu_sample(p, 200, 3, 0.4)
+    oi, ow, _ = oracle.per_sample(p, 200, 3, 0.4)
+    assert np.array_equal(gi, oi) and np.all(gw == 1.0)
+    _, w0, _ = check_sample(priorities(5000, 2), 100, 4, beta=0.0)
+    assert np.all(w0 == 1.0)
+
+
+def test_sample_empty_batch_and_reuse():
+    import torch
+    import rl_experience_collection_amd as rx
+    s = rx.PerSampler(10_000, 512)
+    p = torch.from_numpy(priorities(10_000, 1)).cuda()
+    s.sample(p, 0, 1, 0.4)
+    a = s.sample(p, 512, 9, 0.4)
+    small = torch.from_numpy(priorities(300, 2)).cuda()
+    b = s.sample(small, 17, 9, 0.4)  # a smaller array on the same handle
+    c = s.sample(p, 512, 9, 0.4)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+    oi, _, _ = oracle.per_sample(priorities(300, 2), 17, 9, 0.4)
+    assert np.array_equal(b[0].cpu().numpy(), oi)
+    s.close()
+
+
+def test_gather_rows_of_a_collection():
+    import torch
+    import rl_experience_collection_amd as rx
+    L, N = 9, 40
+    g = np.random.default_rng(0)
+    st = g.standard_normal((L, N, 54)).astype(np.float32)
+    nx = g.standard_normal((L, N, 54)).astype(np.float32)
+    ac = g.integers(0, 45, (L, N)).astype(np.int32)
+    rw = g.standard_normal((L, N)).astype(np.float32)
+    dn = (g.random((L, N)) < 0.1).astype(np.uint8)
+    idx = g.integers(0, L * N, 257).astype(np.int32)
+    d = lambda a: torch.from_numpy(a).cuda()
+    out = rx.per_gather(d(idx), L * N, d(st).view(-1, 54), d(nx).view(-1, 54), d(ac).view(-1),
+                        d(rw).view(-1), d(dn).view(-1))
+    torch.cuda.synchronize()
+    assert np.array_equal(out["states"].cpu().numpy(), st.reshape(-1, 54)[idx])
+    assert np.array_equal(out["next_states"].cpu().numpy(), nx.reshape(-1, 54)[idx])
+    assert np.array_equal(out["actions"].cpu().numpy(), ac.reshape(-1)[idx])
+    assert np.array_equal(out["rewards"].cpu().numpy(), rw.reshape(-1)[idx])
+    assert np.array_equal(out["dones"].cpu().numpy(), dn.reshape(-1)[idx])
+    part = rx.per_gather(d(idx), L * N, actions=d(ac).view(-1))
+    assert part["states"] is None
+    assert np.array_equal(part["actions"].cpu().numpy(), ac.reshape(-1)[idx])
+
+
+def ulp_close(a, b, ulps=2):
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    return np.abs(a.view(np.int32).astype(np.int64) - b.view(np.int32).astype(np.int64)) <= ulps
+
+
+@pytest.mark.parametrize("batch", [1, 255, 256, 3000])
+def test_update_matches_oracle(batch):
+    import torch
+    import rl_experience_collection_amd as rx
+    n = 50_000
+    g = np.random.default_rng(batch)
+    p = priorities(n, 8, holes=False)
+    idx = g.integers(0, n, batch).astype(np.int32)
+    if batch > 10:
+        idx[5] = idx[2]          # a repeat: the later entry wins
+        idx[batch - 1] = idx[0]
+    td = (g.standard_normal(batch) * 3).astype(np.float32)
+    if batch > 10:
+        td[3], td[4], td[6] = np.nan, np.inf, -np.inf
+    pd = torch.from_numpy(p).cuda()
+    rx.per_update(pd, torch.from_numpy(idx).cuda(), torch.from_numpy(td).cuda(), 0.6, 0.01, 20.0)
+    torch.cuda.synchronize()
+    want = oracle.per_update(p, idx, td, 0.6, 0.01, 20.0)
+    got = pd.cpu().numpy()
+    assert ulp_close(got, want).all(), np.abs(got - want).max()
+
+
+def test_update_skips_out_of_range():
+    import torch
+    import rl_experience_collection_amd as rx
+    p = np.ones(100, np.float32)
+    idx = np.array([3, -1, 100, 7], np.int32)
+    td = np.array([2.0, 5.0, 5.0, 0.5], np.float32)
+    pd = torch.from_numpy(p).cuda()
+    rx.per_update(pd, torch.from_numpy(idx).cuda(), torch.from_numpy(td).cuda(), 0.6, 0.01, 10.0)
+    want = oracle.per_update(p, idx[[0, 3]], td[[0, 3]], 0.6, 0.01, 10.0)
+    assert ulp_close(pd.cpu().numpy(), want).all()
+
+
+def test_collection_priorities_sample_gather_update():
+    """The DQN collection's priorities feed the sampler; the sampled rows are
+    the collection's own; the update writes back."""
+    import torch
+    import rl_experience_collection_amd as rx
+    from test_gpu_dqn import run_gpu
+    inp = synthdata.dqn_inputs(dict(N=64, L=50, n_bars=3000, seed=21), bias_scale=0.1)
+    col = run_gpu(inp, q_values=False)
+    pr = col["priorities"].reshape(-1)
+    gi, gw = gpu_sample(pr, 256, 5, 0.4)
+    oi, ow, gap = oracle.per_sample(pr, 256, 5, 0.4)
+    assert np.array_equal(gi, oi) or (gap[gi != oi] < TIE).all()
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = rx.per_gather(d(gi), pr.size, d(col["states"]).view(-1, 54),
+                        d(col["next_states"]).view(-1, 54), d(col["actions"]).view(-1),
+                        d(col["rewards"]).view(-1), d(col["dones"]).view(-1))
+    t, n = gi // 64, gi % 64
+    assert np.array_equal(out["states"].cpu().numpy(), col["states"][t, n])
+    assert np.array_equal(out["rewards"].cpu().numpy(), col["rewards"][t, n])
+    new_td = np.linspace(-2, 2, 256).astype(np.float32)
+    pd = d(pr.copy())
+    rx.per_update(pd, d(gi), d(new_td), 0.6, 1e-3, 50.0)
+    assert ulp_close(pd.cpu().numpy(), oracle.per_update(pr, gi, new_td, 0.6, 1e-3, 50.0)).all()
