@@ -132,6 +132,50 @@ def time_dqn(inp, steps, warmup):
     return dict(N=N, L=L, wall_s=wall, kernel_ms=float(per.mean()), nonfinite=bad)
 
 
+def time_per(n, batch, reps):
+    """Prioritized replay on n priorities: per_sample (batch draws), the
+    gather of the drawn rows of a replay of n transitions, per_update.
+    Priorities ~ Exp(1) with 2% zeros (synthetic)."""
+    import numpy as np
+    import torch
+    import rl_experience_collection_amd as rx
+    g = np.random.default_rng(9)
+    p = g.exponential(1.0, n).astype(np.float32)
+    p[g.integers(0, n, n // 50)] = 0.0
+    pd = torch.from_numpy(p).cuda()
+    states = torch.randn((n, 54), device="cuda")
+    acts = torch.zeros(n, dtype=torch.int32, device="cuda")
+    rew = torch.randn(n, device="cuda")
+    dn = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    td = torch.randn(batch, device="cuda")
+    s = rx.PerSampler(n, batch)
+    idx = torch.empty(batch, dtype=torch.int32, device="cuda")
+    w = torch.empty(batch, dtype=torch.float32, device="cuda")
+    out = dict(states=torch.empty((batch, 54), device="cuda"),
+               next_states=torch.empty((batch, 54), device="cuda"),
+               actions=torch.empty(batch, dtype=torch.int32, device="cuda"),
+               rewards=torch.empty(batch, device="cuda"),
+               dones=torch.empty(batch, dtype=torch.uint8, device="cuda"))
+    ev = rx.HipEvents(4)
+    t = np.zeros(3)
+    for r in range(reps + 2):
+        ev.record(0)
+        rx.per_sample(s.handle, pd, batch, 1000 + r, 0.4, idx, w)
+        ev.record(1)
+        rx.per_gather(idx, n, states, states, acts, rew, dn, out=out)
+        ev.record(2)
+        rx.per_update(pd, idx, td, 0.6, 1e-3, 100.0)
+        ev.record(3)
+        torch.cuda.synchronize()
+        if r >= 2:
+            t += [ev.elapsed_ms(0, 1), ev.elapsed_ms(1, 2), ev.elapsed_ms(2, 3)]
+    ev.close()
+    s.close()
+    t = t / reps
+    return dict(n=n, batch=batch, sample_ms=float(t[0]), gather_ms=float(t[1]),
+                update_ms=float(t[2]))
+
+
 def probe_lib():
     """Measurement kernels (weight-stream and GAE-traffic ceilings), built
     beside the collection library."""
@@ -271,6 +315,8 @@ def run_single(name, steps, warmup):
                     exp_per_s=r["N"] * r["L"] * steps / r["wall_s"],
                     TFLOPs=DQN_FLOP * r["N"] * r["L"] / (r["kernel_ms"] * 1e-3) / 1e12,
                     nonfinite=r["nonfinite"])
+    if name.startswith("per"):
+        return dict(workload=name, **time_per(16384 * 500, 4096, steps))
     if name.startswith("weight_stream"):
         return dict(workload=name, **time_weight_stream(8192 * 500, name.endswith("bf16"), steps))
     a = torch.ones(1 << 28, device="cuda")  # copy_1gib: 1 GiB read + 1 GiB written per copy
@@ -292,7 +338,7 @@ def main():
                     choices=("all", "collect_n8192_fp32", "collect_n8192_bf16", "collect_n128_fp32",
                              "gae_n4096_l2048", "gae_n8192_l500", "gae_traffic_n4096_l2048",
                              "gae_traffic_n8192_l500", "weight_stream_fp32", "weight_stream_bf16",
-                             "dqn_n16384_l500",
+                             "dqn_n16384_l500", "per_n8192000_b4096",
                              "copy_1gib"),
                     help="one workload only (for profiler counter passes); prints its own "
                          "JSON line instead of the benchmark line")
@@ -336,6 +382,9 @@ def main():
     log("timing the DQN collection N=16384 L=500 ...")
     dq = time_dqn(synthdata.dqn_inputs("dqn_n16384_l500"), args.steps, args.warmup)
     dq_exp = dq["N"] * dq["L"]
+    log("timing prioritized replay on 8,192,000 priorities ...")
+    per = time_per(dq_exp, 4096, max(args.steps, 20))
+    per_step = per["sample_ms"] + per["gather_ms"] + per["update_ms"]
 
     value_files = ["rl_experience_collection_amd/csrc/value.hip",
                    "rl_experience_collection_amd/csrc/nets.hpp",
@@ -387,6 +436,13 @@ def main():
                 TFLOPs=DQN_FLOP * dq_exp / (dq["kernel_ms"] * 1e-3) / 1e12,
                 frac_of_fp32_peak=DQN_FLOP * dq_exp / (dq["kernel_ms"] * 1e-3) / PEAK_FP32_MFMA,
                 nonfinite_events=dq["nonfinite"]),
+            per_n8192000_b4096=dict(
+                value=per["batch"] / (per_step * 1e-3), unit="sampled transitions/s",
+                step_ms=per_step, sample_ms=per["sample_ms"], gather_ms=per["gather_ms"],
+                update_ms=per["update_ms"],
+                priority_read_GBps=4 * per["n"] / (per["sample_ms"] * 1e-3) / 1e9,
+                note="one replay step: draw 4096 of 8,192,000 (one DQN collection), gather "
+                     "their rows, update their priorities"),
             ppo_collect_n128_l500_fp32=dict(
                 value=128 * 500 * args.steps / small["wall_s"], unit="experiences/s",
                 ms_per_step=small["wall_s"] * 1000 / args.steps,

@@ -56,9 +56,11 @@ int per_gather(const int32_t *indices, int32_t batch, int64_t n, const float *st
 
 /* Priority update after a training step:
  *   priorities[indices[b]] = clamp(|td[b]|^alpha + epsilon, epsilon, max_priority)
- * with a NaN giving epsilon and +-Inf max_priority.  Of repeated indices the
- * last in batch order writes; indices outside [0, n) are skipped.
- * Errors: ROLLOUT_EINVAL (NULL, batch < 0 or > 1048576, epsilon > max_priority). */
+ * with a NaN giving epsilon and +-Inf max_priority.  An index repeated in the
+ * batch keeps the largest of its new values (independent of timing); indices
+ * outside [0, n) are skipped.  epsilon must be >= 0.
+ * Errors: ROLLOUT_EINVAL (NULL, batch < 0 or > 1048576, epsilon < 0 or
+ * epsilon > max_priority). */
 int per_update(float *priorities, int64_t n, const int32_t *indices, const float *td,
                int32_t batch, float alpha, float epsilon, float max_priority, void *hip_stream);
 

@@ -698,11 +698,16 @@ int orc_per_update(float *priorities, int64_t n, const int32_t *indices, const f
   if (!priorities || !indices || !td || batch < 0) return -1;
   for (int32_t b = 0; b < batch; ++b)
     if (indices[b] < 0 || (int64_t)indices[b] >= n) return -1;
+  unsigned char *seen = (unsigned char *)calloc((size_t)(n > 0 ? n : 1), 1);
+  if (!seen) return -1;
   for (int32_t b = 0; b < batch; ++b) {
     float v = powf(fabsf(td[b]), alpha) + epsilon;
     if (!(v >= epsilon)) v = epsilon; /* NaN */
     if (v > max_priority) v = max_priority;
-    priorities[indices[b]] = v;
+    const int32_t i = indices[b];
+    if (!seen[i] || v > priorities[i]) priorities[i] = v; /* repeats keep the largest */
+    seen[i] = 1;
   }
+  free(seen);
   return 0;
 }

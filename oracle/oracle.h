@@ -225,10 +225,11 @@ int orc_dqn_rollout(const orc_params *p, const orc_dqn_params *dq, const orc_dqn
 double orc_per_uniform(uint64_t seed, uint32_t draw);
 int orc_per_sample(const float *priorities, int64_t n, int32_t batch, uint64_t seed, float beta,
                    int32_t *indices, float *weights, double *gap);
-/* Priority update in batch order (a repeated index keeps the last value):
- * priority[i_b] = clamp(|td_b|^alpha + epsilon, epsilon, max_priority), with
- * NaN giving epsilon.  Returns -1 (nothing written) if an index is out of
- * range. */
+/* Priority update: priority[i_b] = clamp(|td_b|^alpha + epsilon, epsilon,
+ * max_priority), with NaN giving epsilon; an index repeated in the batch
+ * keeps the largest of its new values (a scatter with repeats has no order
+ * on the pages; the largest makes it independent of one).  Returns -1
+ * (nothing written) if an index is out of range. */
 int orc_per_update(float *priorities, int64_t n, const int32_t *indices, const float *td,
                    int32_t batch, float alpha, float epsilon, float max_priority);
 

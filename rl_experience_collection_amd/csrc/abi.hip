@@ -689,7 +689,8 @@ int per_update(float* priorities, int64_t n, const int32_t* indices, const float
   if (batch < 0 || batch > kPerMaxBatch) return fail(ROLLOUT_EINVAL, "per_update: bad batch %d", batch);
   if (batch == 0) return ROLLOUT_OK;
   if (!priorities || !indices || !td) return fail(ROLLOUT_EINVAL, "per_update: NULL buffer");
-  if (!(epsilon <= max_priority)) return fail(ROLLOUT_EINVAL, "per_update: epsilon > max_priority");
+  if (!(epsilon >= 0.0f && epsilon <= max_priority))
+    return fail(ROLLOUT_EINVAL, "per_update: need 0 <= epsilon <= max_priority");
   RL_HIP(rl::per_update_launch(priorities, n, indices, td, batch, alpha, epsilon, max_priority,
                                static_cast<hipStream_t>(hip_stream)),
          "per_update launch");

@@ -57,11 +57,14 @@ __device__ __forceinline__ double wave_scan(double x, int lane) {
 // (the resource starts at the block; the wave's own LDS rows are complete
 // and visible to all its lanes on return)
 __device__ __forceinline__ void stage_block(__amdgpu_buffer_rsrc_t rs, float* rows, int lane) {
-#pragma unroll 8
+  float v[kPerLane];  // all 32 loads in flight before the first LDS write
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j)
+    v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (j * kLanes + lane), 0, 0));
+#pragma unroll
   for (int j = 0; j < kPerLane; ++j) {
     const int e = j * kLanes + lane;  // element of the block
-    const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4u * e, 0, 0));
-    rows[(e / kPerLane) * kStride + (e % kPerLane)] = v;
+    rows[(e / kPerLane) * kStride + (e % kPerLane)] = v[j];
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
@@ -95,26 +98,26 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const float* __restrict
   if (lane == kLanes - 1) sums[blk] = incl;
 }
 
-// One workgroup: sums[0..nblocks) -> inclusive prefixes, fixed order.
+// One workgroup: sums[0..nblocks) -> inclusive prefixes, in a fixed order:
+// thread t owns a contiguous run of blocks, the 1024 run totals are scanned
+// by wave scans and a scan of the 16 wave totals.
 __global__ __launch_bounds__(1024) void block_scan_kernel(double* __restrict__ sums, int64_t nblocks) {
-  __shared__ double s_tot[1024];
-  const int t = threadIdx.x;
+  __shared__ double s_wave[16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t per = (nblocks + 1023) / 1024;
   const int64_t lo = t * per, hi = lo + per < nblocks ? lo + per : nblocks;
   double run = 0.0;
   for (int64_t i = lo; i < hi; ++i) run += sums[i];
-  s_tot[t] = run;
+  const double incl = wave_scan(run, lane);
+  if (lane == 63) s_wave[w] = incl;
   __syncthreads();
-  if (t == 0) {
-    double acc = 0.0;
-    for (int i = 0; i < 1024; ++i) {
-      const double v = s_tot[i];
-      s_tot[i] = acc;  // exclusive offset of thread i
-      acc += v;
-    }
+  if (w == 0) {
+    const double x = lane < 16 ? s_wave[lane] : 0.0;
+    const double wi = wave_scan(x, lane);
+    if (lane < 16) s_wave[lane] = wi - x;  // exclusive prefix of the wave totals
   }
   __syncthreads();
-  double off = s_tot[t];
+  double off = s_wave[w] + (incl - run);  // exclusive offset of this thread's run
   for (int64_t i = lo; i < hi; ++i) {
     off += sums[i];
     sums[i] = off;
@@ -242,30 +245,36 @@ __global__ __launch_bounds__(256) void gather_kernel(PerGatherArgs a) {
 }
 
 // Priority update: priority[i_b] = clamp(|td_b|^alpha + eps, eps, max), NaN
-// -> eps; of repeated indices the last in batch order writes; indices out of
-// range are skipped.
-__global__ __launch_bounds__(256) void update_kernel(float* __restrict__ pr, int64_t n,
-                                                     const int32_t* __restrict__ indices,
-                                                     const float* __restrict__ td, int32_t batch,
-                                                     float alpha, float eps, float pmax) {
-  __shared__ int32_t s_idx[2048];
-  const int32_t b = blockIdx.x * 256 + threadIdx.x;
-  const int32_t mine = b < batch ? indices[b] : -1;
-  bool last = b < batch;
-  // compare with every later entry, 2048 at a time (all threads take part)
-  for (int32_t c0 = blockIdx.x * 256; c0 < batch; c0 += 2048) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < 2048; i += 256) s_idx[i] = c0 + i < batch ? indices[c0 + i] : -1;
-    __syncthreads();
-    const int32_t cnt = batch - c0 < 2048 ? batch - c0 : 2048;
-    for (int i = 0; i < cnt; ++i)
-      if (c0 + i > b && s_idx[i] == mine) last = false;
-  }
-  if (!last || mine < 0 || (int64_t)mine >= n) return;
-  float v = powf(fabsf(td[b]), alpha) + eps;
+// -> eps; indices out of range are skipped.  Of repeated indices the
+// largest new value is kept: the entries first clear their slots, then
+// each takes the integer maximum of the (non-negative) float bits, which
+// orders them as floats, so the result does not depend on timing.
+__device__ __forceinline__ float new_priority(float td, float alpha, float eps, float pmax) {
+  float v = powf(fabsf(td), alpha) + eps;
   if (!(v >= eps)) v = eps;
-  if (v > pmax) v = pmax;
-  pr[mine] = v;
+  return v > pmax ? pmax : v;
+}
+
+__global__ __launch_bounds__(256) void update_clear_kernel(float* __restrict__ pr, int64_t n,
+                                                           const int32_t* __restrict__ indices,
+                                                           int32_t batch) {
+  const int32_t b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= batch) return;
+  const int32_t i = indices[b];
+  if (i >= 0 && (int64_t)i < n) pr[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void update_max_kernel(float* __restrict__ pr, int64_t n,
+                                                         const int32_t* __restrict__ indices,
+                                                         const float* __restrict__ td,
+                                                         int32_t batch, float alpha, float eps,
+                                                         float pmax) {
+  const int32_t b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= batch) return;
+  const int32_t i = indices[b];
+  if (i < 0 || (int64_t)i >= n) return;
+  const float v = new_priority(td[b], alpha, eps, pmax);
+  atomicMax(reinterpret_cast<int*>(pr) + i, __float_as_int(v));
 }
 
 }  // namespace
@@ -295,8 +304,10 @@ hipError_t per_gather_launch(const PerGatherArgs& a, hipStream_t st) {
 hipError_t per_update_launch(float* priorities, int64_t n, const int32_t* indices, const float* td,
                              int32_t batch, float alpha, float eps, float pmax, hipStream_t st) {
   if (batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(update_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, st,
-                     priorities, n, indices, td, batch, alpha, eps, pmax);
+  const unsigned grid = (unsigned)((batch + 255) / 256);
+  hipLaunchKernelGGL(update_clear_kernel, dim3(grid), dim3(256), 0, st, priorities, n, indices, batch);
+  hipLaunchKernelGGL(update_max_kernel, dim3(grid), dim3(256), 0, st, priorities, n, indices, td,
+                     batch, alpha, eps, pmax);
   return hipGetLastError();
 }
 

@@ -139,7 +139,7 @@ def test_update_matches_oracle(batch):
     p = priorities(n, 8, holes=False)
     idx = g.integers(0, n, batch).astype(np.int32)
     if batch > 10:
-        idx[5] = idx[2]          # a repeat: the later entry wins
+        idx[5] = idx[2]          # repeats: the largest new value is kept
         idx[batch - 1] = idx[0]
     td = (g.standard_normal(batch) * 3).astype(np.float32)
     if batch > 10:

@@ -6,7 +6,8 @@ NaN/Inf clamp of Error Handling).
 The sample is pinned by exact rational arithmetic on the same draws, by
 frequencies against p_i / sum p (chi-square), and by its special cases; the
 weights by their ratio and normalisation properties; the update by its
-closed form and its rules for NaN, Inf, repeats and range.
+closed form and its rules for NaN, Inf, repeats (the largest new value) and
+range.
 """
 from fractions import Fraction
 
@@ -114,10 +115,13 @@ def test_update_closed_form_and_clamps():
     assert np.array_equal(q[6:], p[6:])  # untouched
 
 
-def test_update_repeats_keep_the_last_value():
-    p = np.ones(4, np.float32)
-    q = oracle.per_update(p, [2, 1, 2], [3.0, 1.0, 0.25], 1.0, 0.0, 100.0)
-    assert q[2] == np.float32(0.25) and q[1] == np.float32(1.0)
+def test_update_repeats_keep_the_largest_value():
+    p = np.full(4, 50.0, np.float32)
+    q = oracle.per_update(p, [2, 1, 2, 2], [3.0, 1.0, 0.25, 2.0], 1.0, 0.0, 100.0)
+    assert q[2] == np.float32(3.0) and q[1] == np.float32(1.0)
+    assert q[0] == 50.0 and q[3] == 50.0  # untouched; at 2 the old 50 gives way to 3
+    q = oracle.per_update(p, [0, 0], [0.5, 0.25], 1.0, 0.0, 100.0)
+    assert q[0] == np.float32(0.5)
 
 
 def test_update_rejects_out_of_range():
