@@ -31,7 +31,7 @@ class Params(C.Structure):
         ("curiosity_coef", C.c_float), ("risk_coef", C.c_float),
         ("spread", C.c_float), ("barrier_scale", C.c_float),
         ("exposure", C.c_float * 5), ("cost", C.c_float * 3),
-        ("urgency_mult", C.c_float),
+        ("urgency_mult", C.c_float), ("recycle", C.c_int32),
     ]
 
 
@@ -127,6 +127,8 @@ def lib():
                                       vp, vp, C.c_int64, vp, C.c_uint64, vp, vp, i32,
                                       C.POINTER(DqnOutputs), i32]
         L.orc_dqn_rollout.restype = C.c_int
+        L.orc_recycle_bar.argtypes = [C.c_uint64, C.c_uint32, i32, i32, C.c_int64]
+        L.orc_recycle_bar.restype = C.c_int64
         L.orc_per_uniform.argtypes = [C.c_uint64, C.c_uint32]
         L.orc_per_uniform.restype = C.c_double
         L.orc_per_sample.argtypes = [vp, C.c_int64, i32, C.c_uint64, f32, vp, vp, vp]
@@ -157,6 +159,7 @@ def make_params(settings: dict, N: int = 1, L: int = 1, precision: int = FP32) -
     p.exposure = (C.c_float * 5)(*settings["exposure"])
     p.cost = (C.c_float * 3)(*settings["cost"])
     p.urgency_mult = settings["urgency_mult"]
+    p.recycle = int(settings.get("recycle", 0))
     return p
 
 
@@ -385,6 +388,10 @@ def dqn_rollout(inputs: dict, precision: int = FP32, forced_actions=None, subset
     if rc != 0:
         raise ValueError("oracle DQN rollout rejected its arguments")
     return out
+
+
+def recycle_bar(seed: int, episode: int, t: int, n_steps: int, n_bars: int) -> int:
+    return lib().orc_recycle_bar(C.c_uint64(seed), episode, t, n_steps, n_bars)
 
 
 # ---------------------------------------------------------------- prioritized replay

@@ -266,6 +266,17 @@ int orc_env_step(const orc_params *p, orc_episode *s, int a, int t, float p0, fl
   return code != 0;
 }
 
+int64_t orc_recycle_bar(uint64_t seed, uint32_t episode, int32_t t, int32_t n_steps,
+                        int64_t n_bars) {
+  const int64_t remaining = (int64_t)n_steps - t - 1;
+  const uint64_t range = (uint64_t)(n_bars - remaining);
+  const uint32_t ctr[4] = {episode, (uint32_t)t, 5u, 0u};
+  const uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return (int64_t)(((uint64_t)out[0] * range) >> 32);
+}
+
 /* ======================================================================== */
 /* GAE ([PPO] Kernel Phases, Phase B): backward over t with V(L) = last value */
 /* (0 when absent), delta_t = r_t + gamma V_{t+1} (1-d_t) - V_t,              */
@@ -317,7 +328,7 @@ void orc_gae(const float *rewards, const float *values, const uint8_t *dones,
 #define H_MAX 512
 
 static int collect_episode(const orc_params *p, const orc_nets *nets, const float *features,
-                           const float *prices, const int32_t *starts, uint64_t seed,
+                           const float *prices, int64_t n_bars, const int32_t *starts, uint64_t seed,
                            const int32_t *forced, int32_t n, const orc_outputs *out) {
   const int32_t N = p->n_episodes, L = p->n_steps;
   const int prec = p->precision;
@@ -329,8 +340,8 @@ static int collect_episode(const orc_params *p, const orc_nets *nets, const floa
   orc_episode_reset(&ep);
   const float V0 = 1.0f;
 
+  int64_t bar = starts[n];
   for (int32_t t = 0; t < L; ++t) {
-    const int64_t bar = (int64_t)starts[n] + t;
     const int64_t o = (int64_t)t * N + n;
     /* 1-2. state = 51 market features + normalised value, position, spread */
     const float *f = features + bar * ORC_N_FEATURES;
@@ -400,8 +411,12 @@ static int collect_episode(const orc_params *p, const orc_nets *nets, const floa
     out->dones[o] = (uint8_t)done;
     out->barrier[o] = (uint8_t)code;
 
-    /* 12. reset on done; the bar pointer keeps advancing */
+    /* 12. reset on done; the bar pointer keeps advancing, or with
+     * recycling the episode restarts at a fresh random bar */
     if (done) orc_episode_reset(&ep);
+    bar = (done && p->recycle && t + 1 < L)
+              ? orc_recycle_bar(seed, (uint32_t)n, t, L, n_bars)
+              : bar + 1;
   }
 
   /* Phase B: GAE over this episode's column, V(L) = 0 */
@@ -463,7 +478,7 @@ int orc_rollout(const orc_params *p, const orc_nets *nets_in, const float *featu
     for (int32_t i = 0; i < count; ++i) {
       const int32_t n = subset ? subset[i] : i;
       if (n < 0 || n >= N) { rc |= 1; continue; }
-      if (collect_episode(p, &nets, features, prices, starts, seed, forced_actions, n, out))
+      if (collect_episode(p, &nets, features, prices, n_bars, starts, seed, forced_actions, n, out))
         rc |= 1;
     }
   }
@@ -504,7 +519,8 @@ int orc_random_action(float u) {
 
 static int collect_dqn_episode(const orc_params *p, const orc_dqn_params *dq,
                                const orc_dqn_nets *nets, const float *features,
-                               const float *prices, const int32_t *starts, uint64_t seed,
+                               const float *prices, int64_t n_bars, const int32_t *starts,
+                               uint64_t seed,
                                const int32_t *forced, int32_t n, const orc_dqn_outputs *out) {
   const int32_t N = p->n_episodes, L = p->n_steps;
   const int prec = p->precision;
@@ -514,8 +530,8 @@ static int collect_dqn_episode(const orc_params *p, const orc_dqn_params *dq,
   orc_episode_reset(&ep);
   const float V0 = 1.0f;
 
+  int64_t bar = starts[n];
   for (int32_t t = 0; t < L; ++t) {
-    const int64_t bar = (int64_t)starts[n] + t;
     const int64_t o = (int64_t)t * N + n;
     /* 1-3. state = 51 market features + normalised value, position, spread */
     const float *f = features + bar * ORC_N_FEATURES;
@@ -591,8 +607,12 @@ static int collect_dqn_episode(const orc_params *p, const orc_dqn_params *dq,
     out->td[o] = td;
     out->priority[o] = powf(fabsf(td), dq->alpha);
 
-    /* 15. reset on done; the bar pointer keeps advancing */
+    /* 15. reset on done; the bar pointer keeps advancing, or with
+     * recycling the episode restarts at a fresh random bar */
     if (done) orc_episode_reset(&ep);
+    bar = (done && p->recycle && t + 1 < L)
+              ? orc_recycle_bar(seed, (uint32_t)n, t, L, n_bars)
+              : bar + 1;
   }
   return 0;
 }
@@ -621,7 +641,8 @@ int orc_dqn_rollout(const orc_params *p, const orc_dqn_params *dq, const orc_dqn
   for (int32_t i = 0; i < count; ++i) {
     const int32_t n = subset ? subset[i] : i;
     if (n < 0 || n >= N) { rc |= 1; continue; }
-    if (collect_dqn_episode(p, dq, nets, features, prices, starts, seed, forced_actions, n, out))
+    if (collect_dqn_episode(p, dq, nets, features, prices, n_bars, starts, seed, forced_actions, n,
+                            out))
       rc |= 1;
   }
   (void)n_threads;

@@ -70,6 +70,8 @@ typedef struct {
   float exposure[5];             /* exposure per exp index a/9 */
   float cost[3];                 /* cost rate per order index (a%9)/3 */
   float urgency_mult;            /* cost * (1 + mult * (a%3)) */
+  int32_t recycle;               /* 0: after a done the episode continues on the next bar;
+                                    1: it restarts at a fresh random bar (orc_recycle_bar) */
 } orc_params;
 
 /* Network weights, host pointers, [out, in] row-major (Candle convention). */
@@ -131,6 +133,14 @@ typedef struct {
 } orc_episode;
 
 void orc_episode_reset(orc_episode *s);
+/* Dynamic episode recycling ("GPU Pipeline Phase 2b", Future Phase 3
+ * Optimization): the bar at which an episode that ended at step t < L-1
+ * restarts.  With R = L - t - 1 steps left, the valid starts are
+ * 0 .. n_bars - 1 - R; the start is floor(x range / 2^32) with range =
+ * n_bars - R and x the first word of the Philox block with counter
+ * (episode, t, 5, 0) and key = the seed. */
+int64_t orc_recycle_bar(uint64_t seed, uint32_t episode, int32_t t, int32_t n_steps,
+                        int64_t n_bars);
 /* One environment step after action a at step t with prices p0 = P[bar],
  * p1 = P[bar+1].  Writes pnl, hit (+1/-1/0), barrier code, diversity term and
  * the exposure taken; returns done (0/1).  Does NOT apply the reset. */
