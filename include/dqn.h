@@ -68,6 +68,13 @@ typedef struct {
   float exposure[5];
   float cost[3];
   float urgency_mult;
+  int32_t recycle;           /* 0 (default): after a done the episode resets and
+                                runs on along its bars; 1: dynamic episode
+                                recycling ("GPU Pipeline Phase 2b", Future
+                                Phase 3 Optimization): it restarts at bar
+                                floor(x range / 2^32), x the first Philox word
+                                of counter (episode, t, 5, 0), range = n_bars -
+                                (L - t - 1) valid starts */
 } dqn_config;
 
 /* Output buffers: DEVICE pointers, caller-owned, [L][N] unless stated.

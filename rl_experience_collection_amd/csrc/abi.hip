@@ -211,6 +211,7 @@ int check_dqn_config(const dqn_config* c) {
   if (c->div_window < 1 || c->div_window > 32)
     return fail(ROLLOUT_EINVAL, "div_window must be in 1..32 (got %d)", c->div_window);
   if (c->max_hold < 1) return fail(ROLLOUT_EINVAL, "max_hold must be >= 1");
+  if (c->recycle != 0 && c->recycle != 1) return fail(ROLLOUT_EINVAL, "recycle must be 0 or 1");
   return ROLLOUT_OK;
 }
 
@@ -595,6 +596,7 @@ int dqn_collect(dqn_handle h, const int32_t* episode_starts, uint64_t seed, cons
   da.epsilon = h->cfg.epsilon;
   da.gamma = h->cfg.gamma;
   da.alpha = h->cfg.priority_alpha;
+  da.recycle = h->cfg.recycle;
   da.states = out->states;
   da.next_states = out->next_states;
   da.q_values = out->q_values;

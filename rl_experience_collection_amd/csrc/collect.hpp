@@ -59,6 +59,7 @@ struct DqnArgs {
   int32_t N, L;
   EnvParams ep;
   float epsilon, gamma, alpha;
+  int recycle;            // restart an ended episode at a fresh random bar
   float* states;          // [L][N][54]
   float* next_states;     // [L][N][54] or null
   float* q_values;        // [L][N][45] or null

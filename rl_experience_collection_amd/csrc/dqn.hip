@@ -17,7 +17,9 @@
 //     TD = r + gamma (1 - done) max Q_target - Q_online(s, a), with
 //     priority |TD|^alpha (steps 10-12, "GPU-Resident Prioritized
 //     Experience Replay", Sampling Kernels, priority update);
-//   - the stores and the reset on done (steps 14-15).
+//   - the stores and the reset on done (steps 14-15); with recycling the
+//     episode then restarts at a fresh random bar (Future Phase 3
+//     Optimization) instead of running on.
 //
 // Mapping: a workgroup of four waves owns 16 episodes for all L steps.  The
 // layers run on MFMA (v_mfma_f32_16x16x4_f32, lane l computes rows l % 16);
@@ -123,6 +125,18 @@ __device__ __forceinline__ void dueling_q(const f32x4* buf, int e, int j, float 
   for (int h = 0; h < 3; ++h) Q[h] = V + (A[h] - mean);
 }
 
+// Restart bar of an episode that ends at step t < L-1 (dynamic episode
+// recycling, "GPU Pipeline Phase 2b", Future Phase 3 Optimization): with
+// R = L - t - 1 steps left, floor(x range / 2^32) over range = n_bars - R
+// valid starts, x the first Philox word of counter (episode, t, 5, 0).
+__device__ __forceinline__ int64_t recycle_bar(uint64_t seed, uint32_t n, int32_t t, int32_t L,
+                                               int64_t n_bars) {
+  const uint4 r = philox10(make_uint4(n, (uint32_t)t, 5u, 0u), (uint32_t)seed, (uint32_t)(seed >> 32));
+  const uint64_t range = (uint64_t)(n_bars - ((int64_t)L - t - 1));
+  return (int64_t)(((uint64_t)r.x * range) >> 32);
+}
+
+template <bool RECYCLE>
 __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))) void dqn_collect_kernel(DqnArgs a) {
   __shared__ f32x4 s_opnd[kOpnd];  // state of the step
   __shared__ f32x4 s_next[kOpnd];  // next state (target network input)
@@ -180,9 +194,9 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
   if (j == 0) put_state<false>(s_opnd, e, 51, 0.0f);
   if (j == 1) put_state<false>(s_opnd, e, 52, 0.0f);
 
+  int64_t bar = st;
 #pragma unroll 1
   for (int32_t t = 0; t < a.L; ++t) {
-    const int64_t bar = st + t;
     const int64_t o = (int64_t)t * a.N + n;
 
     // the weights are the same every step: an opaque zero offset keeps the
@@ -204,6 +218,17 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     float f2[4];
     load_features(a.features, bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1, j, f2);
     const float p2 = a.prices[bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1];
+    // with recycling, the restart bar this step would take if the episode
+    // ended, and its first two bars, loaded ahead like the prefetch above
+    int64_t rbar = 0;
+    float fr0[4], fr1[4], pr0 = 0.0f, pr1 = 0.0f;
+    if constexpr (RECYCLE) {
+      rbar = t + 1 < a.L ? recycle_bar(a.seed, (uint32_t)n, t, a.L, a.n_bars) : bar;
+      load_features(a.features, rbar, j, fr0);
+      load_features(a.features, rbar + 1, j, fr1);
+      pr0 = a.prices[rbar];
+      pr1 = a.prices[rbar + 1];
+    }
 
     // ---- steps 1-3: the state (its operands were written last step) -------
     if (valid) {
@@ -396,20 +421,23 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
       pos = 0;
       ring = 0;
     }
+    // the bars of the next step: the following ones, or the restart bar
+    const bool restart = RECYCLE && done && t + 1 < a.L;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      f0[h] = restart ? fr0[h] : f1[h];
+      f1[h] = restart ? fr1[h] : f2[h];
+    }
+    p0 = restart ? pr0 : p1;
+    p1 = restart ? pr1 : p2;
+    bar = restart ? rbar : bar + 1;
     // the next step's state operands (the curiosity layer read these before
     // the last barrier)
 #pragma unroll
     for (int h = 0; h < 4; ++h)
-      if (j + 16 * h < kFeatures) put_state<false>(s_opnd, e, j + 16 * h, f1[h]);
+      if (j + 16 * h < kFeatures) put_state<false>(s_opnd, e, j + 16 * h, f0[h]);
     if (j == 0) put_state<false>(s_opnd, e, 51, V / V0 - 1.0f);
     if (j == 1) put_state<false>(s_opnd, e, 52, e_prev);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      f0[h] = f1[h];
-      f1[h] = f2[h];
-    }
-    p0 = p1;
-    p1 = p2;
   }
 }
 
@@ -418,7 +446,10 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
 hipError_t launch_dqn(const DqnArgs& a, hipStream_t st) {
   if (a.N <= 0 || a.L <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((a.N + kRowsPerWave - 1) / kRowsPerWave);
-  hipLaunchKernelGGL(dqn_collect_kernel, dim3(blocks), dim3(64 * kSplit), 0, st, a);
+  if (a.recycle)
+    hipLaunchKernelGGL(dqn_collect_kernel<true>, dim3(blocks), dim3(64 * kSplit), 0, st, a);
+  else
+    hipLaunchKernelGGL(dqn_collect_kernel<false>, dim3(blocks), dim3(64 * kSplit), 0, st, a);
   return hipGetLastError();
 }
 

@@ -101,8 +101,8 @@ def test_dqn_config_default_values(rx):
 
 
 def test_dqn_config_struct_size_matches_header(rx):
-    # 5 ints, 4 x 3 dims, 3 floats, 2 floats, 2 ints, 2 + 4 floats, 5 + 3 + 1 floats
-    assert C.sizeof(rx.DqnConfig) == 4 * (5 + 12 + 3 + 2 + 2 + 6 + 9)
+    # 5 ints, 4 x 3 dims, 3 floats, 2 floats, 2 ints, 2 + 4 floats, 5 + 3 + 1 floats, 1 int
+    assert C.sizeof(rx.DqnConfig) == 4 * (5 + 12 + 3 + 2 + 2 + 6 + 9 + 1)
     assert C.sizeof(rx.DqnOutputs) == 8 * 14
 
 

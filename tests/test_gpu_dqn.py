@@ -189,3 +189,25 @@ def test_dqn_full_size_n16384_l500_sampled_episodes():
         assert np.isfinite(gpu[k]).all(), k
     rate = gpu["explored"].mean()
     assert abs(rate - 0.1) < 5 * np.sqrt(0.09 / gpu["explored"].size)
+
+
+@pytest.mark.parametrize("N,L", [(37, 120), (300, 200)])
+def test_dqn_recycle_matches_oracle(N, L):
+    """Dynamic episode recycling: an ended episode restarts at a drawn bar."""
+    inp = small(N, L, 40 + N)
+    inp["settings"] = dict(inp["settings"], recycle=1)
+    gpu, orc = run_gpu(inp), oracle.dqn_rollout(inp)
+    assert_parity(inp, gpu, orc)
+    plain = dict(inp)
+    plain["settings"] = dict(inp["settings"], recycle=0)
+    base = run_gpu(plain)
+    assert not np.array_equal(base["states"], gpu["states"])  # restarts happened
+
+
+def test_dqn_recycle_full_size_sampled_episodes():
+    inp = synthdata.dqn_inputs("dqn_n16384_l500")
+    inp["settings"] = dict(inp["settings"], recycle=1)
+    gpu = run_gpu(inp, q_values=False)
+    sub = sorted(set(list(range(0, 16384, 2039)) + [16383, 17]))
+    orc = oracle.dqn_rollout(inp, subset=sub, with_q=False)
+    assert_parity(inp, gpu, orc, episodes=sub)
