@@ -85,6 +85,14 @@ typedef struct {
   float exposure[5];      /* exposure of a/9 = 0..4: -1, -0.5, 0, 0.5, 1 */
   float cost[3];          /* cost rate of (a%9)/3: 2e-4, 5e-4, 1e-3 */
   float urgency_mult;     /* cost * (1 + mult * (a%3)) (0.5) */
+  int32_t recycle;        /* 0 (default): after a done the episode resets and
+                             runs on along its bars; 1: dynamic episode
+                             recycling ("GPU Pipeline Phase 2b", Future Phase 3
+                             Optimization): it restarts at bar
+                             floor(x range / 2^32), x the first Philox word of
+                             counter (episode, t, 5, 0), range = n_bars -
+                             (L - t - 1) valid starts; the handle then keeps
+                             an [L][N] i32 record of the bars */
 } rollout_config;
 
 /* Output buffers of one collection: DEVICE pointers, caller-owned, [L][N].
@@ -126,7 +134,8 @@ int rollout_config_default(rollout_config *cfg, int32_t n_episodes, int32_t n_st
  * market buffers are BORROWED and must outlive the handle.  Device memory
  * for the packed weights and per-collection scratch is allocated here.
  * Errors: ROLLOUT_EINVAL (NULL, N or L < 1, dims differ from the built net,
- * n_bars < L + 1, div_window outside 1..32, unknown precision),
+ * n_bars < L + 1, div_window outside 1..32, unknown precision, recycle not
+ * 0 or 1),
  * ROLLOUT_ENOMEM, ROLLOUT_EHIP. */
 int rollout_create(const rollout_config *cfg, const float *const actor[6],
                    const float *const critic[12], const float *const curiosity[4],

@@ -171,6 +171,7 @@ int check_config(const rollout_config* c) {
   if (c->div_window < 1 || c->div_window > 32)
     return fail(ROLLOUT_EINVAL, "div_window must be in 1..32 (got %d)", c->div_window);
   if (c->max_hold < 1) return fail(ROLLOUT_EINVAL, "max_hold must be >= 1");
+  if (c->recycle != 0 && c->recycle != 1) return fail(ROLLOUT_EINVAL, "recycle must be 0 or 1");
   return ROLLOUT_OK;
 }
 
@@ -253,6 +254,7 @@ struct rollout_s {
   float* weights = nullptr;      // packed block
   int32_t* start_used = nullptr; // [N]
   unsigned long long* value_sched = nullptr;  // work counter of the value kernel
+  int32_t* bars = nullptr;       // [L][N] bar of every step (recycling only)
   GaeScratch gae;
 };
 
@@ -337,6 +339,14 @@ int rollout_create(const rollout_config* cfg, const float* const actor[6],
     return fail(ROLLOUT_ENOMEM, "cannot allocate scheduler counter");
   }
   h->value_sched = static_cast<unsigned long long*>(p);
+  if (cfg->recycle) {
+    if (hipMalloc(&p, (size_t)cfg->n_episodes * cfg->n_steps * sizeof(int32_t)) != hipSuccess) {
+      (void)hipGetLastError();
+      rollout_destroy(h);
+      return fail(ROLLOUT_ENOMEM, "cannot allocate the bar record");
+    }
+    h->bars = static_cast<int32_t*>(p);
+  }
   rc = gae_reserve(h->gae, cfg->n_steps, cfg->n_episodes, st);
   if (rc) {
     rollout_destroy(h);
@@ -404,6 +414,7 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   ra.logits = out->logits;
   ra.counters = out->counters;
   ra.bf16 = h->cfg.precision == ROLLOUT_BF16;
+  ra.bars = h->bars;
   RL_HIP(rl::launch_actor_rollout(ra, st), "actor rollout launch");
   RL_HIP(mark(1), "hipEventRecord(phase 1)");
 
@@ -413,6 +424,7 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   va.states = out->states;
   va.actions = out->actions;
   va.start_used = h->start_used;
+  va.bars = h->bars;
   va.N = N;
   va.L = L;
   va.ep = h->ep;
@@ -462,6 +474,7 @@ void rollout_destroy(rollout_handle h) {
   if (h->weights) (void)hipFree(h->weights);
   if (h->start_used) (void)hipFree(h->start_used);
   if (h->value_sched) (void)hipFree(h->value_sched);
+  if (h->bars) (void)hipFree(h->bars);
   if (h->gae.mem) (void)hipFree(h->gae.mem);
   delete h;
 }

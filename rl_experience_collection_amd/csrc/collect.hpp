@@ -29,6 +29,7 @@ struct RolloutArgs {
   float* logits;          // [L][N][45] or null
   uint32_t* counters;     // [2] or null
   int bf16;               // bf16 weights and layer inputs, fp32 accumulation
+  int32_t* bars;          // [L][N] bar of every step, or null: non-null selects recycling
 };
 
 // Batched part: critic value and curiosity bonus of every stored (t, n),
@@ -39,6 +40,7 @@ struct ValueArgs {
   const float* states;
   const int32_t* actions;
   const int32_t* start_used;
+  const int32_t* bars;    // [L][N] bar of every step (recycling), or null: start_used + t
   int32_t N, L;
   EnvParams ep;
   float* values;

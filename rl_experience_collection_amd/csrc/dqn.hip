@@ -125,17 +125,6 @@ __device__ __forceinline__ void dueling_q(const f32x4* buf, int e, int j, float 
   for (int h = 0; h < 3; ++h) Q[h] = V + (A[h] - mean);
 }
 
-// Restart bar of an episode that ends at step t < L-1 (dynamic episode
-// recycling, "GPU Pipeline Phase 2b", Future Phase 3 Optimization): with
-// R = L - t - 1 steps left, floor(x range / 2^32) over range = n_bars - R
-// valid starts, x the first Philox word of counter (episode, t, 5, 0).
-__device__ __forceinline__ int64_t recycle_bar(uint64_t seed, uint32_t n, int32_t t, int32_t L,
-                                               int64_t n_bars) {
-  const uint4 r = philox10(make_uint4(n, (uint32_t)t, 5u, 0u), (uint32_t)seed, (uint32_t)(seed >> 32));
-  const uint64_t range = (uint64_t)(n_bars - ((int64_t)L - t - 1));
-  return (int64_t)(((uint64_t)r.x * range) >> 32);
-}
-
 template <bool RECYCLE>
 __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))) void dqn_collect_kernel(DqnArgs a) {
   __shared__ f32x4 s_opnd[kOpnd];  // state of the step

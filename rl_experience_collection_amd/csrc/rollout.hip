@@ -13,7 +13,9 @@
 //     log p(a) = (l_a - max) - ln S (step 4),
 //   - steps the portfolio, the triple barrier and the diversity window,
 //     kept in registers, and forms the part of the reward that needs them
-//     (steps 6-8, 10), then resets the episode when a barrier fired (12).
+//     (steps 6-8, 10), then resets the episode when a barrier fired (12);
+//     with recycling ("GPU Pipeline Phase 2b", Future Phase 3 Optimization)
+//     the episode also restarts at a drawn bar instead of running on.
 // The critic value (step 5) and the curiosity bonus (step 9) are not read
 // by any later step, so they are evaluated afterwards by the value kernel
 // in one batched pass over every stored state.
@@ -128,8 +130,9 @@ struct PreStepper {
   }
 };
 
-template <bool BF16>
+template <bool BF16, bool RECYCLE>
 __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs a) {
+  __shared__ int s_restart[2];  // recycling: an episode of the workgroup restarted in step t (t % 2)
   __shared__ f32x4 s_bufA[kBufA];
   __shared__ f32x4 s_bufB[kBufB];
   __shared__ f32x4 s_state[4 * 64];
@@ -140,6 +143,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   const int q = threadIdx.x >> 6;
 
   if (threadIdx.x <= 32) s_ln[threadIdx.x] = threadIdx.x == 0 ? 0.0f : logf((float)threadIdx.x);
+  if (threadIdx.x < 2) s_restart[threadIdx.x] = 0;
   fill_env_table(a.ep, s_env, (int)threadIdx.x);
   // state operands start at zero: the padding slots stay zero
   s_state[threadIdx.x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -210,8 +214,8 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   pre[1] = w1.bias[1];
   reg_mfma<0, kTail>(w1, sbuf, pre, lane);
 
+  int64_t bar = st;
   for (int32_t t = 0; t < a.L; ++t) {
-    const int64_t bar = st + t;
     const int64_t o = (int64_t)t * a.N + n;
 
     // prefetch two bars ahead (independent of the outcomes), issued before
@@ -219,6 +223,18 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     float f2[4];
     load_features(a.features, bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1, j, f2);
     const float p2 = a.prices[bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1];
+    // with recycling, the restart bar this step would take if the episode
+    // ended, and its first two bars, loaded ahead the same way
+    int64_t rbar = 0;
+    float fr0[4], fr1[4], pr0 = 0.0f, pr1 = 0.0f;
+    if constexpr (RECYCLE) {
+      rbar = t + 1 < a.L ? recycle_bar(a.seed, (uint32_t)n, t, a.L, a.n_bars) : bar;
+      load_features(a.features, rbar, j, fr0);
+      load_features(a.features, rbar + 1, j, fr1);
+      pr0 = a.prices[rbar];
+      pr1 = a.prices[rbar + 1];
+      if (valid && j == 0) a.bars[o] = (int32_t)bar;  // the value kernel's next-bar index
+    }
 
     // ---- steps 1-2: state = 51 features, V/V0 - 1, exposure held, spread --
     // (the features are already in the operand buffer)
@@ -233,6 +249,17 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
       if (j < 3) srow[kFeatures + j] = j == 0 ? vn : (j == 1 ? e_prev : ep.spread);
     }
     lds_barrier();  // state operands complete; last step's logits read
+    if constexpr (RECYCLE) {
+      // an episode restarted last step: its new features replaced those the
+      // first-layer feature part was computed from, so recompute it
+      const int again = s_restart[(t + 1) & 1];
+      if (threadIdx.x == 0) s_restart[t & 1] = 0;
+      if (again) {
+        pre[0] = w1.bias[0];
+        pre[1] = w1.bias[1];
+        reg_mfma<0, kTail>(w1, sbuf, pre, lane);
+      }
+    }
 
     // the step's draw depends only on (seed, episode, step)
     const float u = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 0u);
@@ -429,13 +456,25 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
       pos = 0;
       ring = 0;
     }
+    // the bars of the next step: the following ones, or (recycling) the
+    // restart bar, whose features replace the next step's operands
+    const bool restart = RECYCLE && done && t + 1 < a.L;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      f0[h] = f1[h];
-      f1[h] = f2[h];
+      f0[h] = restart ? fr0[h] : f1[h];
+      f1[h] = restart ? fr1[h] : f2[h];
     }
-    p0 = p1;
-    p1 = p2;
+    p0 = restart ? pr0 : p1;
+    p1 = restart ? pr1 : p2;
+    bar = restart ? rbar : bar + 1;
+    if constexpr (RECYCLE) {
+      if (restart) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          if (j + 16 * h < kFeatures) put_state<BF16>(sbuf, e, j + 16 * h, f0[h]);
+        if (j == 0) s_restart[t & 1] = 1;
+      }
+    }
   }
 }
 
@@ -444,10 +483,9 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
   if (a.N <= 0 || a.L <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((a.N + kRowsPerWave - 1) / kRowsPerWave);
-  if (a.bf16)
-    hipLaunchKernelGGL(actor_rollout_kernel<true>, dim3(blocks), dim3(64 * kSplit), 0, st, a);
-  else
-    hipLaunchKernelGGL(actor_rollout_kernel<false>, dim3(blocks), dim3(64 * kSplit), 0, st, a);
+  auto kernel = a.bf16 ? (a.bars ? actor_rollout_kernel<true, true> : actor_rollout_kernel<true, false>)
+                       : (a.bars ? actor_rollout_kernel<false, true> : actor_rollout_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(64 * kSplit), 0, st, a);
   return hipGetLastError();
 }
 

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int v = a.actions[(int64_t)t * a.N + n];
     act[rt] = v < 0 ? 0 : (v >= kActions ? kActions - 1 : v);
     t_of[rt] = t;
-    start_of[rt] = a.start_used[n];
+    start_of[rt] = a.bars ? a.bars[(int64_t)t * a.N + n] - t : a.start_used[n];
   }
   const float partial = q < RT ? a.rewards[my_row] : 0.0f;
   lds_barrier();

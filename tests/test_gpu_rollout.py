@@ -184,3 +184,52 @@ def test_bf16_chip_workload_sampled_episodes():
     inp = synthdata.ppo_inputs("ppo_n8192_l500")
     sub = sorted(set(list(range(0, 8192, 397)) + [8191]))
     _bf16_compare(inp, episodes=sub)
+
+
+# ----------------------------------------------------------------- recycling
+def _recycled(spec, **kw):
+    inp = synthdata.ppo_inputs(spec, **kw)
+    inp["settings"] = dict(inp["settings"], recycle=1)
+    return inp
+
+
+@pytest.mark.parametrize("N,L,n_bars", [(16, 100, 3000), (33, 64, 3000), (1, 7, 3000),
+                                        (20, 60, 61)])
+def test_recycling_matches_oracle(N, L, n_bars):
+    """Dynamic episode recycling ("GPU Pipeline Phase 2b", Future Phase 3
+    Optimization): same protocol as the plain run; n_bars = L + 1 leaves
+    restarts only t + 2 valid bars."""
+    inp = _recycled(dict(N=N, L=L, n_bars=n_bars, seed=300 + N + L), bias_scale=0.1)
+    gpu = run_gpu(inp)
+    _assert_parity(inp, gpu, oracle.rollout(inp))
+    if N * L >= 1000:
+        assert gpu["dones"][:-1].sum() > 0
+
+
+def test_recycling_changes_the_run_after_a_done():
+    inp = _recycled(dict(N=32, L=120, n_bars=3000, seed=8), bias_scale=0.1)
+    plain = dict(inp, settings=dict(inp["settings"], recycle=0))
+    g1, g0 = run_gpu(inp), run_gpu(plain)
+    d = g0["dones"]
+    first = np.where(d.any(axis=0), d.argmax(axis=0), inp["L"])
+    moved = 0
+    for n in range(inp["N"]):
+        f = int(first[n])
+        assert np.array_equal(g1["states"][: f + 1, n], g0["states"][: f + 1, n]), n
+        if f + 1 < inp["L"]:
+            moved += int(not np.array_equal(g1["states"][f + 1, n], g0["states"][f + 1, n]))
+    assert moved > 10
+
+
+def test_recycling_chip_workload_n8192_l500_sampled_episodes():
+    inp = _recycled("ppo_n8192_l500")
+    gpu = run_gpu(inp, logits=True)
+    sub = sorted(set(list(range(0, 8192, 331)) + [8191, 8190, 15, 16]))
+    _assert_parity(inp, gpu, oracle.rollout(inp, subset=sub), episodes=sub)
+    assert np.array_equal(gpu["dones"], (gpu["barrier"] > 0).astype(np.uint8))
+    for k in ("values", "rewards", "advantages", "returns", "log_probs"):
+        assert np.isfinite(gpu[k]).all(), k
+
+
+def test_recycling_bf16_teacher_forced():
+    assert _bf16_compare(_recycled("ppo_n16_l100", bias_scale=0.1)) > 0.5
