@@ -295,12 +295,19 @@ def cpu_baseline(inp, n_episodes):
                        f"workload; episodes are independent; host CPU: {cpu}")
 
 
+def recycled(inp):
+    """The same workload with dynamic episode recycling on."""
+    return dict(inp, settings=dict(inp["settings"], recycle=1))
+
+
 def run_single(name, steps, warmup):
     """One workload, for profiler counter passes."""
     import torch
     import synthdata
     if name.startswith("collect"):
         inp = synthdata.ppo_inputs("ppo_n128_l500" if name == "collect_n128_fp32" else "ppo_n8192_l500")
+        if name.endswith("recycle"):
+            inp = recycled(inp)
         r = time_collect(inp, steps, warmup, precision=1 if name.endswith("bf16") else 0)
         return dict(workload=name, ms_per_step=r["wall_s"] * 1000 / steps,
                     phases_ms=[float(x) for x in r["phases_ms"]])
@@ -310,7 +317,8 @@ def run_single(name, steps, warmup):
         r = time_gae(spec, steps, traffic_only=name.startswith("gae_traffic"))
         return dict(workload=name, cold_ms=r["cold_ms"], warm_ms=r["warm_ms"])
     if name.startswith("dqn"):
-        r = time_dqn(synthdata.dqn_inputs("dqn_n16384_l500"), steps, warmup)
+        inp = synthdata.dqn_inputs("dqn_n16384_l500")
+        r = time_dqn(recycled(inp) if name.endswith("recycle") else inp, steps, warmup)
         return dict(workload=name, ms_per_step=r["wall_s"] * 1000 / steps, kernel_ms=r["kernel_ms"],
                     exp_per_s=r["N"] * r["L"] * steps / r["wall_s"],
                     TFLOPs=DQN_FLOP * r["N"] * r["L"] / (r["kernel_ms"] * 1e-3) / 1e12,
@@ -336,6 +344,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="all",
                     choices=("all", "collect_n8192_fp32", "collect_n8192_bf16", "collect_n128_fp32",
+                             "collect_n8192_fp32_recycle", "dqn_n16384_l500_recycle",
                              "gae_n4096_l2048", "gae_n8192_l500", "gae_traffic_n4096_l2048",
                              "gae_traffic_n8192_l500", "weight_stream_fp32", "weight_stream_bf16",
                              "dqn_n16384_l500", "per_n8192000_b4096",
@@ -345,7 +354,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the collection shards by episode and runs with no "
-              f"communication, so --gpus {args.gpus} is not supported in this build.",
+              f"communication; --gpus {args.gpus} is not supported (one GPU per process).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -369,6 +378,8 @@ def main():
     t_roll, t_val, t_gae = big["phases_ms"]
     log("timing N=8192 L=500 bf16 ...")
     bfr = time_collect(big_inp, args.steps, args.warmup, precision=1)
+    log("timing N=8192 L=500 fp32 with episode recycling ...")
+    rec = time_collect(recycled(big_inp), args.steps, args.warmup)
     log("timing N=128 L=500 fp32 ...")
     small = time_collect(synthdata.ppo_inputs("ppo_n128_l500"), args.steps, args.warmup)
     log("timing GAE N=4096 L=2048 and N=8192 L=500 ...")
@@ -382,6 +393,8 @@ def main():
     log("timing the DQN collection N=16384 L=500 ...")
     dq = time_dqn(synthdata.dqn_inputs("dqn_n16384_l500"), args.steps, args.warmup)
     dq_exp = dq["N"] * dq["L"]
+    log("timing the DQN collection N=16384 L=500 with episode recycling ...")
+    dqr = time_dqn(recycled(synthdata.dqn_inputs("dqn_n16384_l500")), args.steps, args.warmup)
     log("timing prioritized replay on 8,192,000 priorities ...")
     per = time_per(dq_exp, 4096, max(args.steps, 20))
     per_step = per["sample_ms"] + per["gather_ms"] + per["update_ms"]
@@ -436,6 +449,17 @@ def main():
                 TFLOPs=DQN_FLOP * dq_exp / (dq["kernel_ms"] * 1e-3) / 1e12,
                 frac_of_fp32_peak=DQN_FLOP * dq_exp / (dq["kernel_ms"] * 1e-3) / PEAK_FP32_MFMA,
                 nonfinite_events=dq["nonfinite"]),
+            ppo_collect_n8192_l500_fp32_recycle=dict(
+                value=N * L * args.steps / rec["wall_s"], unit="experiences/s",
+                ms_per_step=rec["wall_s"] * 1000 / args.steps,
+                phases_ms=dict(zip(("actor_rollout", "value_critic_curiosity", "gae_scan"),
+                                   map(float, rec["phases_ms"]))),
+                nonfinite_events=rec["nonfinite"]),
+            dqn_collect_n16384_l500_fp32_recycle=dict(
+                value=dq_exp * args.steps / dqr["wall_s"], unit="experiences/s",
+                ms_per_step=dqr["wall_s"] * 1000 / args.steps, kernel_ms=dqr["kernel_ms"],
+                frac_of_fp32_peak=DQN_FLOP * dq_exp / (dqr["kernel_ms"] * 1e-3) / PEAK_FP32_MFMA,
+                nonfinite_events=dqr["nonfinite"]),
             per_n8192000_b4096=dict(
                 value=per["batch"] / (per_step * 1e-3), unit="sampled transitions/s",
                 step_ms=per_step, sample_ms=per["sample_ms"], gather_ms=per["gather_ms"],

@@ -41,7 +41,7 @@ extern "C" {
 typedef struct dqn_s *dqn_handle; /* opaque, owned by the library */
 
 /* Settings of one DQN collector, copied at dqn_create.  Widths are fixed by
- * this build and must match. */
+ * this library and must match. */
 typedef struct {
   int32_t n_episodes;        /* N >= 1 */
   int32_t n_steps;           /* L >= 1 */

@@ -49,7 +49,7 @@ extern "C" {
 #define ROLLOUT_EINVAL (-1)   /* bad argument: null pointer, size, dims, alignment */
 #define ROLLOUT_ENOMEM (-2)   /* device allocation failed */
 #define ROLLOUT_EHIP (-3)     /* HIP runtime/launch error (message copied) */
-#define ROLLOUT_ENOTIMPL (-4) /* configuration not supported by this build */
+#define ROLLOUT_ENOTIMPL (-4) /* configuration not supported by this library */
 
 typedef struct rollout_s *rollout_handle; /* opaque, owned by the library */
 
@@ -59,7 +59,7 @@ typedef enum {
 } rollout_precision;
 
 /* Settings of one collector, copied at rollout_create.  The network widths
- * are fixed by this build and must match exactly; they are carried here so a
+ * are fixed by this library and must match exactly; they are carried here so a
  * mismatch is an error rather than a silent misread. */
 typedef struct {
   int32_t n_episodes;     /* N >= 1 */

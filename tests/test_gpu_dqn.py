@@ -204,6 +204,13 @@ def test_dqn_recycle_matches_oracle(N, L):
     assert not np.array_equal(base["states"], gpu["states"])  # restarts happened
 
 
+def test_dqn_recycle_minimum_market():
+    """n_bars = L + 1: a restart after step t has only t + 2 valid bars."""
+    inp = synthdata.dqn_inputs(dict(N=20, L=60, n_bars=61, seed=45), bias_scale=0.1)
+    inp["settings"] = dict(inp["settings"], recycle=1)
+    assert_parity(inp, run_gpu(inp), oracle.dqn_rollout(inp))
+
+
 def test_dqn_recycle_full_size_sampled_episodes():
     inp = synthdata.dqn_inputs("dqn_n16384_l500")
     inp["settings"] = dict(inp["settings"], recycle=1)
