@@ -4,12 +4,13 @@
 //
 //  * weight_stream_kernel: the value kernel streams the packed critic and
 //    curiosity weights from L2 into registers once per work item (16 x RT
-//    rows).  This kernel issues the same stream with no arithmetic: a
-//    persistent grid of 256-thread workgroups at the value kernel's
-//    occupancy, each reading the whole block once per work item in 16-byte
-//    lanes (1 KiB per wave instruction), 16 loads in flight per lane.  Its
-//    time for the value kernel's work-item count is the stream bound the
-//    MFMA work competes with.
+//    rows; with more than four waves the two 4-tile layers are read once per
+//    group of four).  This kernel issues the same bytes with no arithmetic:
+//    a persistent grid of 256-thread workgroups, two per CU (the value
+//    kernel's 8 waves per CU), each reading the block once per work item in
+//    16-byte lanes (1 KiB per wave instruction), 16 loads in flight per
+//    lane.  Its time for the value kernel's work-item count is the stream
+//    bound the MFMA work competes with.
 //  * gae_traffic_kernel: moves exactly the GAE scan's bytes (reads r, V, d;
 //    writes two float arrays), element-wise with no recurrence: the copy
 //    ceiling of the scan at a given size.
@@ -70,12 +71,18 @@ extern "C" {
 int bench_value_stream_shape(int bf16, long long* block_bytes, int* rows_per_item) {
   if (!block_bytes || !rows_per_item) return 1;
   long long floats = 0;
+  // the 4-tile layers (critic 128 -> 64, curiosity 128 -> 51) are read by
+  // every group of four waves
+  const int rh = rl::value_waves(bf16 != 0) / rl::kSplit;
   if (bf16) {
-    for (int l = 0; l < 5; ++l) floats += rl::packed_layer_floats_bf16(rl::kCriticB[l]);
-    for (int l = 0; l < 2; ++l) floats += rl::packed_layer_floats_bf16(rl::kCurB[l]);
+    for (int l = 0; l < 5; ++l)
+      floats += rl::packed_layer_floats_bf16(rl::kCriticB[l]) * (l == 4 ? rh : 1);
+    for (int l = 0; l < 2; ++l)
+      floats += rl::packed_layer_floats_bf16(rl::kCurB[l]) * (l == 1 ? rh : 1);
   } else {
-    for (int l = 0; l < 5; ++l) floats += rl::packed_layer_floats(rl::kCritic[l]);
-    for (int l = 0; l < 2; ++l) floats += rl::packed_layer_floats(rl::kCur[l]);
+    for (int l = 0; l < 5; ++l)
+      floats += rl::packed_layer_floats(rl::kCritic[l]) * (l == 4 ? rh : 1);
+    for (int l = 0; l < 2; ++l) floats += rl::packed_layer_floats(rl::kCur[l]) * (l == 1 ? rh : 1);
   }
   *block_bytes = floats * 4;
   *rows_per_item = 16 * rl::value_row_tiles(bf16 != 0);

@@ -35,18 +35,25 @@ struct LayerDesc {
 #define RL_VALUE_RT_F32 2
 #endif
 #ifndef RL_VALUE_RT_BF16
-#define RL_VALUE_RT_BF16 4
+#define RL_VALUE_RT_BF16 8
 #endif
 __host__ __device__ constexpr int value_row_tiles(bool bf16) {
   return bf16 ? RL_VALUE_RT_BF16 : RL_VALUE_RT_F32;
 }
+// Waves of a value-kernel workgroup.  The wide layers split their output
+// tiles over all of them; bf16 uses 8 waves (one workgroup per CU, 128 rows
+// in LDS), so each 16-byte weight operand feeds 8 row tiles: the stream of
+// operands through the CU's vector-memory data path is half that of four
+// waves with 4 row tiles each, at the same accumulator count per wave.
+__host__ __device__ constexpr int value_waves(bool bf16) { return bf16 ? 8 : kSplit; }
 
 // Weight-ring slots of a streamed layer (value kernel): layers with few
 // output tiles per wave issue little MFMA work per k-step, so they keep more
 // steps in flight (fp32: the whole layer for one tile per wave; bf16: up to
 // 8 steps of 16-byte operands).  Streamed layers need no zero padding.
 __host__ __device__ constexpr int ring_depth(bool bf16, int otw) {
-  return otw >= 4 ? (bf16 ? 3 : 4) : (bf16 ? 8 : (otw == 2 ? 16 : 32));
+  return bf16 ? (otw >= 4 ? 3 : otw == 3 ? 4 : otw == 2 ? 6 : 8)
+              : (otw >= 4 ? 4 : otw == 2 ? 16 : 32);
 }
 
 // Actor: 54 -> 128 -> 64 -> 45 (PPO CUDA Pipeline Design, Weight Layout).
@@ -405,16 +412,16 @@ __device__ __forceinline__ void relu_store_bf16(const f32x4 (&acc)[OTW], uint4* 
 // (LDS operand layout, or the raw state rows for first layers) and are read
 // one group of steps ahead.
 // ---------------------------------------------------------------------------
-template <bool BF16, int OTW, int D>
+template <bool BF16, int OTW, int D, int SPLIT = kSplit>
 struct WeightStream {
   using Op = typename std::conditional<BF16, uint4, float>::type;
-  static constexpr int kStep = kSplit * 64 * OTW;  // Op elements per k-step
+  static constexpr int kStep = SPLIT * 64 * OTW;  // Op elements per k-step (SPLIT waves)
   Op a[D][OTW];
   f32x4 bias[OTW];
 };
 
-template <bool BF16, int OTW>
-using Stream = WeightStream<BF16, OTW, ring_depth(BF16, OTW)>;
+template <bool BF16, int OTW, int SPLIT = kSplit>
+using Stream = WeightStream<BF16, OTW, ring_depth(BF16, OTW), SPLIT>;
 
 // Weight loads through a buffer resource over the packed block: a 32-bit
 // per-lane byte offset (one VGPR per layer) plus a wave-uniform byte offset
@@ -478,10 +485,10 @@ struct LdsWeights {
 };
 
 // pk_b: byte offset of the layer's packed weights in the block; pb: biases.
-template <int S, bool BF16, int OTW, int D, class WS>
-__device__ __forceinline__ void stream_begin(WeightStream<BF16, OTW, D>& st, const WS& ws,
+template <int S, bool BF16, int OTW, int D, int SPLIT, class WS>
+__device__ __forceinline__ void stream_begin(WeightStream<BF16, OTW, D, SPLIT>& st, const WS& ws,
                                              uint32_t pk_b, const float* pb, int q, int lane) {
-  constexpr uint32_t kStepB = WeightStream<BF16, OTW, D>::kStep * (BF16 ? 16u : 4u);
+  constexpr uint32_t kStepB = WeightStream<BF16, OTW, D, SPLIT>::kStep * (BF16 ? 16u : 4u);
   constexpr int kFirst = D - 1 < S ? D - 1 : S;
   const int g = lane >> 4;
 #pragma unroll
@@ -514,14 +521,14 @@ struct LdsOperands {
 
 // fp32: S k-steps of 4 inputs (S % D == 0); a row tile's f32x4 B operand
 // covers a group of 4 steps, read one group ahead.
-template <int S, int OTW, int D, int RT, class WS, class BL>
-__device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D>& st, const WS& ws,
+template <int S, int OTW, int D, int RT, int SPLIT, class WS, class BL>
+__device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D, SPLIT>& st, const WS& ws,
                                              uint32_t pk_b, const BL& bl, f32x4 (&acc)[RT][OTW],
                                              int q, int lane) {
   static_assert(D % 4 == 0 && S % D == 0, "whole groups of D steps");
   constexpr int KT = S / D;
   constexpr int G = S / 4;
-  constexpr uint32_t kStepB = WeightStream<false, OTW, D>::kStep * 4u;
+  constexpr uint32_t kStepB = WeightStream<false, OTW, D, SPLIT>::kStep * 4u;
   const uint32_t lane_b = (uint32_t)((q * 64 + lane) * OTW) * 4u;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -560,40 +567,42 @@ __device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D>& st, co
 }
 
 // bf16: S k-steps of 32 inputs; one uint4 of B per row tile and step.
-template <int S, int OTW, int D, int RT, class WS, class BL>
-__device__ __forceinline__ void stream_layer(WeightStream<true, OTW, D>& st, const WS& ws,
+template <int S, int OTW, int D, int RT, int SPLIT, class WS, class BL>
+__device__ __forceinline__ void stream_layer(WeightStream<true, OTW, D, SPLIT>& st, const WS& ws,
                                              uint32_t pk_b, const BL& bl, f32x4 (&acc)[RT][OTW],
                                              int q, int lane) {
   constexpr int KT = S / D;
   constexpr int TAIL = S % D;
-  constexpr uint32_t kStepB = WeightStream<true, OTW, D>::kStep * 16u;
+  constexpr uint32_t kStepB = WeightStream<true, OTW, D, SPLIT>::kStep * 16u;
   const uint32_t lane_b = (uint32_t)((q * 64 + lane) * OTW) * 16u;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < OTW; ++i) acc[rt][i] = st.bias[i];
-  uint4 b[RT], bn[RT];
+  uint4 b[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) b[rt] = bl.bf16(rt, 0, lane);
-  // one step: weights of step s + D - 1 (when inside the layer), B of step
-  // s + 1, then the MFMAs of step s from slot `slot`
+  // one step: weights of step s + D - 1 (when inside the layer), then per
+  // row tile the MFMAs of step s from slot `slot` followed by the reload of
+  // that tile's B operand with step s + 1 (one register set for B: the
+  // reloads spread over the step, each a step ahead of its use)
   auto step = [&](int s, int slot, uint32_t wsrc, bool load_w, bool load_b) {
     if (load_w) {
 #pragma unroll
       for (int i = 0; i < OTW; ++i) st.a[(slot + D - 1) % D][i] = ws.u4(lane_b, wsrc + 16u * i);
     }
-    if (load_b) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) bn[rt] = bl.bf16(rt, s + 1, lane);
-    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
       for (int i = 0; i < OTW; ++i) acc[rt][i] = mfma_bf16(st.a[slot][i], b[rt], acc[rt][i]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) b[rt] = bn[rt];
+      // (the scheduling barrier does not order memory reads: the empty asm
+      // keeps every operand load in program order, so the B operands of
+      // later steps cannot be read early and held)
+      asm volatile("" ::: "memory");
+      if (load_b) b[rt] = bl.bf16(rt, s + 1, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   if constexpr (KT > 0) {
 #pragma unroll 1

@@ -35,19 +35,20 @@ __global__ void pack_layer_kernel(const float* __restrict__ W, int in, int ld, i
   pk[idx] = ok ? W[(int64_t)o * ld + k] : 0.0f;
 }
 
-// bf16 form: pk[(((s*kSplit + q)*64 + lane)*OTW + i)*8 + j], 8 bf16 per
-// (k-step, lane, tile), k = kperm(s, lane / 16, j) of nets.hpp.
+// bf16 form: pk[(((s*split + q)*64 + lane)*OTW + i)*8 + j], 8 bf16 per
+// (k-step, lane, tile), k = kperm(s, lane / 16, j) of nets.hpp; `split`
+// waves share a k-step, OTW = ot / split tiles each.
 __global__ void pack_layer_bf16_kernel(const float* __restrict__ W, int in, int ld, int out,
-                                       int steps, int pad, int first, int otw,
+                                       int steps, int pad, int first, int split, int otw,
                                        uint16_t* __restrict__ pk) {
-  const int64_t total = (int64_t)(steps + pad) * kSplit * 64 * otw * 8;
+  const int64_t total = (int64_t)(steps + pad) * split * 64 * otw * 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int j = (int)(idx % 8);
   const int i = (int)((idx / 8) % otw);
   const int lane = (int)((idx / (8 * (int64_t)otw)) % 64);
-  const int q = (int)((idx / (8 * (int64_t)otw * 64)) % kSplit);
-  const int s = (int)(idx / (8 * (int64_t)otw * 64 * kSplit));
+  const int q = (int)((idx / (8 * (int64_t)otw * 64)) % split);
+  const int s = (int)(idx / (8 * (int64_t)otw * 64 * split));
   const int o = 16 * (q * otw + i) + (lane & 15);
   const int g = lane >> 4;
   const int k = first ? 32 * s + 8 * g + j : 16 * (2 * s + j / 4) + 4 * g + (j % 4);
@@ -94,10 +95,12 @@ hipError_t pack_layer(const float* W, const LayerDesc& d, int ld, float* pk, hip
   return hipGetLastError();
 }
 
-hipError_t pack_layer_bf16(const float* W, const LayerDesc& d, int ld, float* pk, hipStream_t st) {
+hipError_t pack_layer_bf16(const float* W, const LayerDesc& d, int ld, float* pk, hipStream_t st,
+                           int split = kSplit) {
+  if (split < 1 || d.ot % split != 0) return hipErrorInvalidValue;
   const int64_t total = packed_layer_floats_bf16(d) * 2;  // bf16 elements
   hipLaunchKernelGGL(pack_layer_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     W, d.in, ld, d.out, d.steps, d.pad, d.first, d.ot / kSplit,
+                     W, d.in, ld, d.out, d.steps, d.pad, d.first, split, d.ot / split,
                      reinterpret_cast<uint16_t*>(pk));
   return hipGetLastError();
 }
@@ -221,10 +224,14 @@ hipError_t pack_weights(const float* const actor[6], const float* const critic[1
     RL_TRY(pack_layer_bf16(actor[2 * l], kActorB[l], kActorB[l].in, block + P.bact_w[l], st));
     RL_TRY(pack_bias(actor[2 * l + 1], kActorB[l], block + P.bact_b[l], st));
   }
+  // the value kernel's wide layers split over its waves, the two 4-tile
+  // layers (critic 128 -> 64, curiosity 128 -> 51) over 4
   for (int l = 0; l < 5; ++l)
-    RL_TRY(pack_layer_bf16(critic[2 * l], kCriticB[l], kCriticB[l].in, block + P.bcritic_w[l], st));
-  RL_TRY(pack_layer_bf16(cur[0], kCurB[0], kState + kActions, block + P.bcur_w[0], st));
-  RL_TRY(pack_layer_bf16(cur[2], kCurB[1], kCurB[1].in, block + P.bcur_w[1], st));
+    RL_TRY(pack_layer_bf16(critic[2 * l], kCriticB[l], kCriticB[l].in, block + P.bcritic_w[l], st,
+                           l < 4 ? value_waves(true) : kSplit));
+  RL_TRY(pack_layer_bf16(cur[0], kCurB[0], kState + kActions, block + P.bcur_w[0], st,
+                         value_waves(true)));
+  RL_TRY(pack_layer_bf16(cur[2], kCurB[1], kCurB[1].in, block + P.bcur_w[1], st, kSplit));
   hipLaunchKernelGGL(round_copy_kernel, dim3(1), dim3(64), 0, st, critic[10], 64, block + P.bcritic_w6);
   RL_TRY(hipGetLastError());
   hipLaunchKernelGGL(pack_onehot_bf16_kernel, dim3((kActions * 128 + 255) / 256), dim3(256), 0, st,

@@ -29,18 +29,40 @@ namespace rl {
 namespace {
 
 constexpr PackedOffsets kP = packed_offsets();
-constexpr int kThreads = 64 * kSplit;
 
 template <bool BF16>
 struct ValueShape {
+  static constexpr int W = value_waves(BF16);  // waves per workgroup
+  static constexpr int kThreads = 64 * W;
   static constexpr int RT = value_row_tiles(BF16);
+  // The two 4-tile layers (critic 128 -> 64, curiosity 128 -> 51) split 4
+  // ways on outputs and RH ways on rows: wave q computes output tile q % 4
+  // for the RTS row tiles from (q / 4) * RTS.
+  static constexpr int RH = W / kSplit;
+  static constexpr int RTS = RT / RH;
+  // output tiles per wave of the wide layers
+  static constexpr int O1 = (BF16 ? kCriticB[0].ot : kCritic[0].ot) / W;
+  static constexpr int O2 = (BF16 ? kCriticB[1].ot : kCritic[1].ot) / W;
+  static constexpr int O3 = (BF16 ? kCriticB[2].ot : kCritic[2].ot) / W;
+  static constexpr int O4 = (BF16 ? kCriticB[3].ot : kCritic[3].ot) / W;
+  static constexpr int OC1 = (BF16 ? kCurB[0].ot : kCur[0].ot) / W;
   // 16-byte LDS operands per row tile of the widest activation (512)
   static constexpr int kTile = BF16 ? 16 * 64 : 32 * 64;
   // floats of the workgroup's state rows, and 16-byte first-layer operands
   // per row tile (bf16: 2 k-steps, fp32: 4 groups of 4 k-steps, x 64 lanes)
   static constexpr int kRaw = RT * kRowsPerWave * kState;
   static constexpr int kOpTile = BF16 ? 2 * 64 : 4 * 64;
-  static_assert(RT >= 1 && RT <= kSplit, "every row tile's result has a writing wave");
+  static_assert(RT >= 1 && RT <= W, "every row tile's result has a writing wave");
+  static_assert(W % kSplit == 0 && RT % RH == 0, "the 4-tile layers cover every row tile");
+  static_assert(O1 * W == (BF16 ? kCriticB[0].ot : kCritic[0].ot) &&
+                    O2 * W == (BF16 ? kCriticB[1].ot : kCritic[1].ot) &&
+                    O3 * W == (BF16 ? kCriticB[2].ot : kCritic[2].ot) &&
+                    O4 * W == (BF16 ? kCriticB[3].ot : kCritic[3].ot) &&
+                    OC1 * W == (BF16 ? kCurB[0].ot : kCur[0].ot),
+                "whole output tiles per wave");
+  static_assert((BF16 ? kCriticB[4].ot : kCritic[4].ot) == kSplit &&
+                    (BF16 ? kCurB[1].ot : kCur[1].ot) == kSplit,
+                "one output tile per wave in the 4-tile layers");
 };
 
 // The packed block as a buffer resource plus its base pointer (biases and
@@ -50,16 +72,16 @@ struct Weights {
   const float* W;
 };
 
-template <int S, bool BF16, int OTW, int D>
-__device__ __forceinline__ void begin(WeightStream<BF16, OTW, D>& st, const Weights& w, int64_t w32,
-                                      int64_t wb, int64_t b_off, int q, int lane) {
+template <int S, bool BF16, int OTW, int D, int SPLIT>
+__device__ __forceinline__ void begin(WeightStream<BF16, OTW, D, SPLIT>& st, const Weights& w,
+                                      int64_t w32, int64_t wb, int64_t b_off, int q, int lane) {
   stream_begin<S>(st, w.gw, (uint32_t)(4 * (BF16 ? wb : w32)), w.W + b_off, q, lane);
 }
 
-template <int S, bool BF16, int OTW, int D, int RT, class BL>
-__device__ __forceinline__ void run(WeightStream<BF16, OTW, D>& st, const Weights& w, int64_t w32,
-                                    int64_t wb, const BL& bl, f32x4 (&acc)[RT][OTW], int q,
-                                    int lane) {
+template <int S, bool BF16, int OTW, int D, int SPLIT, int RT, class BL>
+__device__ __forceinline__ void run(WeightStream<BF16, OTW, D, SPLIT>& st, const Weights& w,
+                                    int64_t w32, int64_t wb, const BL& bl,
+                                    f32x4 (&acc)[RT][OTW], int q, int lane) {
   stream_layer<S, OTW, D, RT>(st, w.gw, (uint32_t)(4 * (BF16 ? wb : w32)), bl, acc, q, lane);
 }
 
@@ -73,11 +95,15 @@ __device__ __forceinline__ void store(const f32x4 (&acc)[RT][OTW], f32x4* buf, i
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void value_kernel(ValueArgs a) {
+__global__ __launch_bounds__(ValueShape<BF16>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void value_kernel(ValueArgs a) {
   using Sh = ValueShape<BF16>;
   constexpr int RT = Sh::RT;
+  constexpr int RTS = Sh::RTS;
+  constexpr int W = Sh::W;
+  constexpr int kThreads = Sh::kThreads;
   constexpr int TS = Sh::kTile;
-  // layer k-steps (fp32 / bf16 forms differ) and per-wave output tiles
+  // layer k-steps (fp32 / bf16 forms differ)
   constexpr int S1 = BF16 ? kCriticB[0].steps : kCritic[0].steps;
   constexpr int S2 = BF16 ? kCriticB[1].steps : kCritic[1].steps;
   constexpr int S3 = BF16 ? kCriticB[2].steps : kCritic[2].steps;
@@ -88,6 +114,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ f32x4 s_buf[RT * TS];
   __shared__ f32x4 s_opnd[RT * Sh::kOpTile];
   __shared__ float s_part[2][RT][kSplit][16];
+  // action and next bar (curiosity target) of each row of the group
+  __shared__ int s_act[RT * kRowsPerWave], s_nbar[RT * kRowsPerWave];
   __shared__ float s_env[kEnvTable];
   fill_env_table(a.ep, s_env, (int)threadIdx.x);  // read after the loop's first barrier
 
@@ -169,7 +197,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   // bf16: the first layer (two k-steps, all prefetched) loads at the end of
   // the previous iteration, so its short MFMA run does not wait on L2
-  Stream<BF16, 8> w1;
+  Stream<BF16, Sh::O1, W> w1;
   if constexpr (BF16) {
     const Weights wt0{GlobalWeights{weights_rsrc(a.weights, (uint32_t)(4 * kP.total))}, a.weights};
     begin<S1>(w1, wt0, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], (int)threadIdx.x >> 6,
@@ -190,12 +218,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // from hoisting them (and the registers they would hold) out of the loop
   int32_t opaque0 = 0;  // (an offset, so W keeps the global address space)
   asm volatile("" : "+s"(opaque0));
-  const float* W = a.weights + opaque0;
-  const Weights wt{GlobalWeights{weights_rsrc(W, (uint32_t)(4 * kP.total))}, W};
+  const float* Wp = a.weights + opaque0;
+  const Weights wt{GlobalWeights{weights_rsrc(Wp, (uint32_t)(4 * kP.total))}, Wp};
   int tid = (int)threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
-  const int q = tid >> 6;
+  const int q = tid >> 6;  // wave: output tiles of the wide layers
+  const int q4 = Sh::RH > 1 ? q & (kSplit - 1) : q;  // 4-tile layers: output tile q4 ...
+  const int rs0 = Sh::RH > 1 ? (q >> 2) * RTS : 0;   // ... of row tiles rs0 .. rs0 + RTS - 1
   const int g = lane >> 4;
 
   const int64_t my_raw = (tile0 + q) * kRowsPerWave + (lane & 15);
@@ -204,6 +234,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int64_t row0 = tile0 * kRowsPerWave;
   const uint64_t t_base = (uint64_t)(row0 / a.N);
   const uint32_t n_base = (uint32_t)(row0 - (int64_t)t_base * a.N);
+  // (t, n) of row 16 rt + lane % 16 of the group (rows past the end: the last row)
+  auto row_tn = [&](int rt, int32_t& t, int32_t& n) {
+    const uint32_t x = n_base + (uint32_t)(rt * kRowsPerWave + (lane & 15));
+    const uint32_t dt = x / (uint32_t)a.N;
+    n = (int32_t)(x - dt * (uint32_t)a.N);
+    t = (int32_t)(t_base + dt);
+    if (t_base + dt >= (uint64_t)a.L) {
+      t = a.L - 1;
+      n = a.N - 1;
+    }
+  };
 
   // ticket for the next group, taken before the loads below and published
   // after the first layer (when it has long arrived)
@@ -213,35 +254,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // (this group's operands were scattered before the previous barrier)
   const LdsOperands states_in{s_opnd, Sh::kOpTile};
   const LdsOperands acts{s_buf, TS};
+  const LdsOperands acts_s{s_buf + rs0 * TS, TS};  // the 4-tile layers' row tiles
 
   // ---- critic -----------------------------------------------------------
   // the first layer reads the state operands, so s_buf is free for its output
-  Stream<BF16, 6> w2;
+  Stream<BF16, Sh::O2, W> w2;
   if constexpr (BF16 && RT % 2 == 0) {
     // all k-steps of the bf16 first layer sit in the ring: two passes of
     // RT / 2 row tiles over the same weight registers halve the accumulators
-    static_assert(S1 < ring_depth(true, 8), "first layer fully prefetched");
+    static_assert(S1 < ring_depth(true, Sh::O1), "first layer fully prefetched");
     constexpr int H = RT / 2;
-    f32x4 h1[H][8];
+    f32x4 h1[H][Sh::O1];
     run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], states_in, h1, q, lane);
-    store<BF16, 8, H>(h1, s_buf, TS, q, lane);
+    store<BF16, Sh::O1, H>(h1, s_buf, TS, q, lane);
     run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], LdsOperands{s_opnd + H * Sh::kOpTile, Sh::kOpTile},
             h1, q, lane);
     begin<S2>(w2, wt, kP.critic_w[1], kP.bcritic_w[1], kP.critic_b[1], q, lane);
-    store<BF16, 8, H>(h1, s_buf + H * TS, TS, q, lane);
+    store<BF16, Sh::O1, H>(h1, s_buf + H * TS, TS, q, lane);
   } else {
-    f32x4 h1[RT][8];
+    f32x4 h1[RT][Sh::O1];
     run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], states_in, h1, q, lane);
     begin<S2>(w2, wt, kP.critic_w[1], kP.bcritic_w[1], kP.critic_b[1], q, lane);
-    store<BF16, 8, RT>(h1, s_buf, TS, q, lane);
+    store<BF16, Sh::O1, RT>(h1, s_buf, TS, q, lane);
   }
   // every wave read the previous s_next before the barrier above
   if (tid == 0) s_next = gridDim.x + ticket;
   lds_barrier();  // the output is complete
 
-  f32x4 h2[RT][6];
+  f32x4 h2[RT][Sh::O2];
   run<S2>(w2, wt, kP.critic_w[1], kP.bcritic_w[1], acts, h2, q, lane);
-  Stream<BF16, 4> w3;
+  Stream<BF16, Sh::O3, W> w3;
   begin<S3>(w3, wt, kP.critic_w[2], kP.bcritic_w[2], kP.critic_b[2], q, lane);
   // the next group (published after the first layer): its state rows load
   // past the register peak of the wide layers (fp32 here, bf16 two layers
@@ -256,70 +298,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   if constexpr (!BF16) prefetch_next();
   lds_barrier();
-  store<BF16, 6, RT>(h2, s_buf, TS, q, lane);
+  store<BF16, Sh::O2, RT>(h2, s_buf, TS, q, lane);
   lds_barrier();
 
-  f32x4 h3[RT][4];
+  f32x4 h3[RT][Sh::O3];
   run<S3>(w3, wt, kP.critic_w[2], kP.bcritic_w[2], acts, h3, q, lane);
-  Stream<BF16, 2> w4;
+  Stream<BF16, Sh::O4, W> w4;
   begin<S4>(w4, wt, kP.critic_w[3], kP.bcritic_w[3], kP.critic_b[3], q, lane);
   // what the curiosity and reward epilogue reads, loaded past the register
-  // peak of the wide layers so it arrives during the rest: row (t, n) of
-  // every row tile, its action, its start bar and this wave's partial reward
-  int act[RT];
-  int32_t t_of[RT], start_of[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const uint32_t x = n_base + (uint32_t)(rt * kRowsPerWave + (lane & 15));
-    const uint32_t dt = x / (uint32_t)a.N;
-    int32_t n = (int32_t)(x - dt * (uint32_t)a.N);
-    int32_t t = (int32_t)(t_base + dt);
-    if (t_base + dt >= (uint64_t)a.L) {  // rows past the end: the last row
-      t = a.L - 1;
-      n = a.N - 1;
-    }
+  // peak of the wide layers so it arrives during the rest: wave q < RT
+  // loads the action and the next bar (the MSE target) of row tile q's
+  // rows; they go through LDS to every wave after the next layer
+  int my_act = 0, my_nbar = 0;
+  if (q < RT) {
+    int32_t t, n;
+    row_tn(q, t, n);
     const int v = a.actions[(int64_t)t * a.N + n];
-    act[rt] = v < 0 ? 0 : (v >= kActions ? kActions - 1 : v);
-    t_of[rt] = t;
-    start_of[rt] = a.bars ? a.bars[(int64_t)t * a.N + n] - t : a.start_used[n];
+    my_act = v < 0 ? 0 : (v >= kActions ? kActions - 1 : v);
+    my_nbar = (a.bars ? a.bars[(int64_t)t * a.N + n] : a.start_used[n] + t) + 1;
   }
   const float partial = q < RT ? a.rewards[my_row] : 0.0f;
   lds_barrier();
-  store<BF16, 4, RT>(h3, s_buf, TS, q, lane);
+  store<BF16, Sh::O3, RT>(h3, s_buf, TS, q, lane);
   lds_barrier();
 
-  f32x4 h4[RT][2];
+  f32x4 h4[RT][Sh::O4];
   run<S4>(w4, wt, kP.critic_w[3], kP.bcritic_w[3], acts, h4, q, lane);
   Stream<BF16, 1> w5;
-  begin<S5>(w5, wt, kP.critic_w[4], kP.bcritic_w[4], kP.critic_b[4], q, lane);
+  begin<S5>(w5, wt, kP.critic_w[4], kP.bcritic_w[4], kP.critic_b[4], q4, lane);
   if constexpr (BF16) prefetch_next();
-  // next-bar features of every row tile for the curiosity MSE: lane holds
-  // features 16q + 4g + r
-  f32x4 feat[RT];
+  if (q < RT && g == 0) {
+    s_act[q * kRowsPerWave + lane] = my_act;
+    s_nbar[q * kRowsPerWave + lane] = my_nbar;
+  }
+  lds_barrier();
+  // next-bar features of this wave's row tiles for the curiosity MSE: lane
+  // holds features 16 q4 + 4g + r
+  f32x4 feat[RTS];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const float* fn = a.features + ((int64_t)start_of[rt] + t_of[rt] + 1) * kFeatures;
+  for (int rt = 0; rt < RTS; ++rt) {
+    const float* fn =
+        a.features + (int64_t)s_nbar[(rs0 + rt) * kRowsPerWave + (lane & 15)] * kFeatures;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = 16 * q + 4 * g + r;  // unconditional load, masked after
+      const int j = 16 * q4 + 4 * g + r;  // unconditional load, masked after
       const float v = fn[j < kFeatures ? j : kFeatures - 1];
       feat[rt][r] = j < kFeatures ? v : 0.0f;
     }
   }
-  lds_barrier();
-  store<BF16, 2, RT>(h4, s_buf, TS, q, lane);
+  store<BF16, Sh::O4, RT>(h4, s_buf, TS, q, lane);
   lds_barrier();
 
-  f32x4 h5[RT][1];
-  run<S5>(w5, wt, kP.critic_w[4], kP.bcritic_w[4], acts, h5, q, lane);
-  Stream<BF16, 2> c1;
+  f32x4 h5[RTS][1];
+  run<S5>(w5, wt, kP.critic_w[4], kP.bcritic_w[4], acts_s, h5, q4, lane);
+  Stream<BF16, Sh::OC1, W> c1;
   begin<SC1>(c1, wt, kP.cur_w[0], kP.bcur_w[0], kP.cur_b[0], q, lane);
   {
-    // 64 -> 1 on the VALU: this wave holds hidden units 16q .. 16q+15
-    const float* w6 = W + (BF16 ? kP.bcritic_w6 : kP.critic_w6) + 16 * q + 4 * g;
+    // 64 -> 1 on the VALU: this wave holds hidden units 16 q4 .. 16 q4 + 15
+    const float* w6 = Wp + (BF16 ? kP.bcritic_w6 : kP.critic_w6) + 16 * q4 + 4 * g;
     const f32x4 w6v = *reinterpret_cast<const f32x4*>(w6);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTS; ++rt) {
       float part = 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -328,20 +367,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
       part += lane_xor16f(part, lane);
       part += lane_xor32f(part, lane);
-      if (g == 0) s_part[0][rt][q][lane] = part;
+      if (g == 0) s_part[0][rs0 + rt][q4][lane] = part;
     }
   }
 
   // ---- curiosity layer 1 (reads the state operands, not s_buf) ----------
-  f32x4 c[RT][2];
+  f32x4 c[RT][Sh::OC1];
   run<SC1>(c1, wt, kP.cur_w[0], kP.bcur_w[0], states_in, c, q, lane);
   Stream<BF16, 1> c2;
-  begin<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], kP.cur_b[1], q, lane);
+  begin<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], kP.cur_b[1], q4, lane);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const float* oh = W + (BF16 ? kP.bcur_onehot : kP.cur_onehot) + act[rt] * 128 + 4 * g;
+    const int act = s_act[rt * kRowsPerWave + (lane & 15)];
+    const float* oh = Wp + (BF16 ? kP.bcur_onehot : kP.cur_onehot) + act * 128 + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) c[rt][i] += *reinterpret_cast<const f32x4*>(oh + 16 * (2 * q + i));
+    for (int i = 0; i < Sh::OC1; ++i)
+      c[rt][i] += *reinterpret_cast<const f32x4*>(oh + 16 * (Sh::OC1 * q + i));
   }
   lds_barrier();  // critic input no longer read; value partials visible
   // the next group's state operands (the last reader of this group's was
@@ -349,21 +390,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if (grp_next < groups) scatter_states(tid, v_states);
   float value = 0.0f;
   if (q < RT)
-    value = W[kP.critic_b6] + ((s_part[0][q][0][lane & 15] + s_part[0][q][1][lane & 15]) +
-                               (s_part[0][q][2][lane & 15] + s_part[0][q][3][lane & 15]));
-  store<BF16, 2, RT>(c, s_buf, TS, q, lane);
+    value = Wp[kP.critic_b6] + ((s_part[0][q][0][lane & 15] + s_part[0][q][1][lane & 15]) +
+                                (s_part[0][q][2][lane & 15] + s_part[0][q][3][lane & 15]));
+  store<BF16, Sh::OC1, RT>(c, s_buf, TS, q, lane);
   lds_barrier();
 
   // ---- curiosity layer 2, MSE against the next bar's features -------------
-  f32x4 pr[RT][1];
-  run<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], acts, pr, q, lane);
+  f32x4 pr[RTS][1];
+  run<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], acts_s, pr, q4, lane);
   if constexpr (BF16) begin<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], q, lane);
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int rt = 0; rt < RTS; ++rt) {
     float se = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = 16 * q + 4 * g + r;
+      const int j = 16 * q4 + 4 * g + r;
       if (j < kFeatures) {
         const float d = pr[rt][0][r] - feat[rt][r];
         se += d * d;
@@ -371,7 +412,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     se += lane_xor16f(se, lane);
     se += lane_xor32f(se, lane);
-    if (g == 0) s_part[1][rt][q][lane] = se;
+    if (g == 0) s_part[1][rs0 + rt][q4][lane] = se;
   }
   lds_barrier();
 
@@ -380,9 +421,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const float sum = (s_part[1][q][0][lane] + s_part[1][q][1][lane]) +
                       (s_part[1][q][2][lane] + s_part[1][q][3][lane]);
     const float bonus = a.ep.curiosity_coef * (sum / (float)kFeatures);
-    int my_act = act[0];
-#pragma unroll
-    for (int rt = 1; rt < RT; ++rt) my_act = q == rt ? act[rt] : my_act;
     const float ex = s_env[my_act / 9];
     const float reward = (partial + bonus) - a.ep.risk_coef * fabsf(ex);
     a.values[my_row] = value;
@@ -407,7 +445,8 @@ int resident_groups() {
   if (cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, value_kernel<BF16>, kThreads, 0) !=
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, value_kernel<BF16>,
+                                                   ValueShape<BF16>::kThreads, 0) !=
           hipSuccess)
     return 0;
   cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
@@ -428,9 +467,9 @@ hipError_t launch_value(const ValueArgs& a, hipStream_t st) {
   if (!a.sched) return hipErrorInvalidValue;
   hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, st, a.sched);
   if (a.bf16)
-    hipLaunchKernelGGL(value_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(value_kernel<true>, dim3(grid), dim3(ValueShape<true>::kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(value_kernel<false>, dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(value_kernel<false>, dim3(grid), dim3(ValueShape<false>::kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -180,6 +180,13 @@ def test_bf16_tiny_teacher_forced():
     assert _bf16_compare(inp) > 0.5
 
 
+@pytest.mark.parametrize("N,L", [(1, 1), (47, 3), (33, 64), (129, 9)])
+def test_bf16_ragged_sizes(N, L):
+    """Row counts below one 128-row work item, ragged tails, several items."""
+    spec = dict(N=N, L=L, n_bars=3000, seed=200 + N + L)
+    _bf16_compare(synthdata.ppo_inputs(spec, bias_scale=0.1))
+
+
 def test_bf16_chip_workload_sampled_episodes():
     inp = synthdata.ppo_inputs("ppo_n8192_l500")
     sub = sorted(set(list(range(0, 8192, 397)) + [8191]))
