@@ -70,6 +70,29 @@ def load_traffic(name, files):
         return None
 
 
+_SLEEP_PER_MS = None
+
+
+def gpu_lead(ms):
+    """Occupy the device for about `ms` with a spin kernel that touches no
+    memory, so that the host enqueues the timed launches ahead of it: events
+    between short launches then time device work, not Python call overhead."""
+    global _SLEEP_PER_MS
+    import torch
+    import rl_experience_collection_amd as rx
+    if _SLEEP_PER_MS is None:  # spin cycles per millisecond on this device
+        ev = rx.HipEvents(2)
+        n = 1 << 20
+        torch.cuda._sleep(n)  # first launch outside the measurement
+        ev.record(0)
+        torch.cuda._sleep(n)
+        ev.record(1)
+        torch.cuda.synchronize()
+        _SLEEP_PER_MS = n / max(ev.elapsed_ms(0, 1), 1e-3)
+        ev.close()
+    torch.cuda._sleep(int(ms * _SLEEP_PER_MS))
+
+
 def time_collect(inp, steps, warmup, precision=0):
     import torch
     import numpy as np
@@ -156,19 +179,28 @@ def time_per(n, batch, reps):
                actions=torch.empty(batch, dtype=torch.int32, device="cuda"),
                rewards=torch.empty(batch, device="cuda"),
                dones=torch.empty(batch, dtype=torch.uint8, device="cuda"))
-    ev = rx.HipEvents(4)
-    t = np.zeros(3)
-    for r in range(reps + 2):
-        ev.record(0)
+    def step(r, e0=None, ev=None):
+        if ev: ev.record(e0)
         rx.per_sample(s.handle, pd, batch, 1000 + r, 0.4, idx, w)
-        ev.record(1)
+        if ev: ev.record(e0 + 1)
         rx.per_gather(idx, n, states, states, acts, rew, dn, out=out)
-        ev.record(2)
+        if ev: ev.record(e0 + 2)
         rx.per_update(pd, idx, td, 0.6, 1e-3, 100.0)
-        ev.record(3)
-        torch.cuda.synchronize()
-        if r >= 2:
-            t += [ev.elapsed_ms(0, 1), ev.elapsed_ms(1, 2), ev.elapsed_ms(2, 3)]
+        if ev: ev.record(e0 + 3)
+    for r in range(2):
+        step(r)
+    torch.cuda.synchronize()
+    # all timed steps enqueued behind a device-side lead: the events time the
+    # device, with the host ahead of it as in a training loop
+    ev = rx.HipEvents(4 * reps)
+    gpu_lead(2.0 + 0.2 * reps)
+    for r in range(reps):
+        step(2 + r, 4 * r, ev)
+    torch.cuda.synchronize()
+    t = np.zeros(3)
+    for r in range(reps):
+        t += [ev.elapsed_ms(4 * r, 4 * r + 1), ev.elapsed_ms(4 * r + 1, 4 * r + 2),
+              ev.elapsed_ms(4 * r + 2, 4 * r + 3)]
     ev.close()
     s.close()
     t = t / reps
@@ -225,6 +257,7 @@ def time_gae(spec, reps, traffic_only=False):
         if i >= 2:
             cold.append(ev.elapsed_ms(0, 1))
     launch()
+    gpu_lead(1.0 + 0.1 * reps)  # the host enqueues the warm launches ahead
     ev.record(0)
     for i in range(reps):
         launch()

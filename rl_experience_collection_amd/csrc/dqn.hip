@@ -89,7 +89,9 @@ __device__ __forceinline__ void q_network(const GlobalWeights& gw, const float* 
   f32x4 h2[1][2];
   stream_layer<32, 2, 8, 1>(s2, gw, w2, LdsOperands{bufB, 0}, h2, q, lane);
   WeightStream<false, 1, 8> s3;
-  const uint32_t w3q = q < 2 ? w3 + 16u * kHeadStepB : w3;
+  // (wave-uniform: as an SGPR it is the loads' scalar offset, not a per-lane
+  // value the compiler would loop over)
+  const uint32_t w3q = __builtin_amdgcn_readfirstlane(q < 2 ? w3 + 16u * kHeadStepB : w3);
   stream_begin<16>(s3, gw, w3q, W + kD.b[net][3], q, lane);
   relu_store_tiles<2, 1>(h2, bufA, 0, q, lane);
   lds_barrier();

@@ -5,16 +5,19 @@
 //
 // Neither output feeds a later step, so the L*N stored states are evaluated
 // as one batch.  A workgroup holds RT row tiles of 16 consecutive (t, n)
-// rows of the [L][N] layout; its kSplit = 4 waves share all RT tiles and
-// each computes a quarter of every layer's outputs for all of them:
+// rows of the [L][N] layout; its W waves (fp32: 4 waves, 2 row tiles; bf16:
+// 8 waves, 8 row tiles, one workgroup per CU) share all RT tiles and each
+// computes 1/W of the wide layers' outputs for all of them:
 //   critic 54 -> 512 -> 384 -> 256 -> 128 -> 64 (MFMA, ReLU) -> 1 (VALU),
 //   curiosity [state, one-hot(a)] -> 128 (ReLU) -> 51, MSE against the next
-//   bar's 51 features, bonus = coef * MSE.
-// Every weight operand a wave loads feeds RT MFMAs (one per row tile), and
-// the next layer's first weight steps are loaded before the barriers that
-// end the current layer.  Activations live in LDS (a layer's input is read
-// by all four waves, its output written back after a barrier).  The packed
-// weights (1.46 MB fp32, 0.73 MB bf16) stay resident in every XCD's L2.
+//   bar's 51 features, bonus = coef * MSE;
+// the two 4-tile layers (128 -> 64, 128 -> 51) give wave q tile q % 4 of
+// the row tiles of its group of four.
+// Every weight operand a wave loads feeds one MFMA per row tile, and the
+// next layer's first weight steps are loaded before the barriers that end
+// the current layer.  Activations live in LDS (a layer's input is read by
+// every wave, its output written back after a barrier).  The packed weights
+// (1.46 MB fp32, 0.73 MB bf16) stay resident in every XCD's L2.
 // The one-hot half of the curiosity input is a column gather, not a dense
 // product.
 // Precision: fp32 (v_mfma_f32_16x16x4_f32) or bf16 weights and layer inputs
