@@ -32,8 +32,8 @@ extern "C" {
 
 typedef struct per_s *per_handle; /* opaque: scratch for up to `capacity` priorities */
 
-/* Allocate the sampler's scratch (8 bytes per 2048 priorities, 8 bytes per
- * draw).  Errors: ROLLOUT_EINVAL (capacity < 1, max_batch < 1 or
+/* Allocate the sampler's scratch (520 bytes per 2048 priorities: the block
+ * prefix and 64 in-block lane prefixes in fp64; 8 bytes per draw).  Errors: ROLLOUT_EINVAL (capacity < 1, max_batch < 1 or
  * > 1048576, capacity > 2^31 - 1), ROLLOUT_ENOMEM. */
 int per_create(int64_t capacity, int32_t max_batch, per_handle *out);
 

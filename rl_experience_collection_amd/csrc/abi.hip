@@ -230,6 +230,7 @@ struct per_s {
   int64_t capacity = 0;
   int32_t max_batch = 0;
   double* prefix = nullptr;  // block prefix sums, per_blocks(capacity)
+  double* lanes = nullptr;   // in-block lane prefixes, 64 per block
   double* raw = nullptr;     // unnormalised weights, max_batch
 };
 
@@ -653,6 +654,12 @@ int per_create(int64_t capacity, int32_t max_batch, per_handle* out) {
     return fail(ROLLOUT_ENOMEM, "cannot allocate block prefixes");
   }
   h->prefix = static_cast<double*>(p);
+  if (hipMalloc(&p, (size_t)rl::per_blocks(capacity) * 64 * sizeof(double)) != hipSuccess) {
+    (void)hipGetLastError();
+    per_destroy(h);
+    return fail(ROLLOUT_ENOMEM, "cannot allocate lane prefixes");
+  }
+  h->lanes = static_cast<double*>(p);
   if (hipMalloc(&p, (size_t)max_batch * sizeof(double)) != hipSuccess) {
     (void)hipGetLastError();
     per_destroy(h);
@@ -677,8 +684,8 @@ int per_sample(per_handle h, const float* priorities, int64_t n, int32_t batch, 
   RL_HIP(hipGetDevice(&dev), "hipGetDevice");
   if (dev != h->device)
     return fail(ROLLOUT_EINVAL, "handle was created on device %d, current device is %d", h->device, dev);
-  RL_HIP(rl::per_sample_launch(priorities, n, batch, seed, beta, indices, weights, h->prefix, h->raw,
-                               static_cast<hipStream_t>(hip_stream)),
+  RL_HIP(rl::per_sample_launch(priorities, n, batch, seed, beta, indices, weights, h->prefix,
+                               h->lanes, h->raw, static_cast<hipStream_t>(hip_stream)),
          "per_sample launch");
   return ROLLOUT_OK;
 }
@@ -715,6 +722,7 @@ int per_update(float* priorities, int64_t n, const int32_t* indices, const float
 void per_destroy(per_handle h) {
   if (!h) return;
   if (h->prefix) (void)hipFree(h->prefix);
+  if (h->lanes) (void)hipFree(h->lanes);
   if (h->raw) (void)hipFree(h->raw);
   delete h;
 }

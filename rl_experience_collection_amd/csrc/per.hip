@@ -9,16 +9,18 @@
 // priorities per lane):
 //   1. block_sums_kernel: one wave per block stages the block through LDS
 //      with coalesced loads, sums each lane's 32 priorities in order (fp64)
-//      and scans the 64 lane sums; the block's total is the scan's last lane;
+//      and scans the 64 lane sums; it keeps the 64 in-block lane prefixes,
+//      and the block's total is the scan's last lane;
 //   2. block_scan_kernel: one workgroup turns the block totals into
 //      inclusive block prefixes (fp64, fixed order);
 //   3. sample_kernel: one wave per draw finds the block with a 64-way search
-//      over the block prefixes, re-stages that block and forms the same lane
-//      sums and scan as step 1, then the lane whose range holds the target
-//      walks its 32 priorities; the raw weight (n p / T)^-beta is fp64;
+//      over the block prefixes, reads that block's 64 lane prefixes, and the
+//      lane whose range holds the target loads and walks its 32 priorities;
+//      the raw weight (n p / T)^-beta is fp64;
 //   4. weights_kernel: one workgroup divides by the batch's largest weight.
-// So each call reads the priorities once (4 bytes each) plus 8 KB per draw,
-// and every sum is formed in a fixed order: results are deterministic.
+// So each call reads the priorities once (4 bytes each), writes 8 bytes per
+// 32 of them, and reads about 1.7 KB per draw; every sum is formed in a
+// fixed order: results are deterministic.
 // Negative and NaN priorities count as zero; a total that is not positive
 // and finite gives uniform draws floor(u n) with weight 1.  Draws are 53-bit
 // uniforms from Philox (counter (draw, 0, 4, 0), key = the seed).
@@ -87,7 +89,8 @@ __device__ __forceinline__ double lane_sum(const float* rows, int lane) {
 }
 
 __global__ __launch_bounds__(256) void block_sums_kernel(const float* __restrict__ p, int64_t n,
-                                                         int64_t nblocks, double* __restrict__ sums) {
+                                                         int64_t nblocks, double* __restrict__ sums,
+                                                         double* __restrict__ lanes) {
   __shared__ float s_rows[4][kLanes * kStride];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t blk = (int64_t)blockIdx.x * 4 + w;
@@ -95,7 +98,22 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const float* __restrict
   float* rows = s_rows[w];
   stage_block(block_rsrc(p, n, blk), rows, lane);
   const double incl = wave_scan(lane_sum(rows, lane), lane);
+  lanes[blk * kLanes + lane] = incl;
   if (lane == kLanes - 1) sums[blk] = incl;
+}
+
+// The 32 priorities of lane `lane` of a block (zeros past the end).
+__device__ __forceinline__ void lane_priorities(__amdgpu_buffer_rsrc_t rs, int lane,
+                                                float (&v)[kPerLane]) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < kPerLane; i += 4) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, 4u * (lane * kPerLane + i), 0, 0);
+    v[i] = __uint_as_float(x.x);
+    v[i + 1] = __uint_as_float(x.y);
+    v[i + 2] = __uint_as_float(x.z);
+    v[i + 3] = __uint_as_float(x.w);
+  }
 }
 
 // One workgroup: sums[0..nblocks) -> inclusive prefixes, in a fixed order:
@@ -126,10 +144,10 @@ __global__ __launch_bounds__(1024) void block_scan_kernel(double* __restrict__ s
 
 __global__ __launch_bounds__(256) void sample_kernel(const float* __restrict__ p, int64_t n,
                                                      const double* __restrict__ prefix,
+                                                     const double* __restrict__ lanes,
                                                      int64_t nblocks, int32_t batch, uint64_t seed,
                                                      float beta, int32_t* __restrict__ indices,
                                                      double* __restrict__ raw) {
-  __shared__ float s_rows[4][kLanes * kStride];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int32_t b = blockIdx.x * 4 + w;
   if (b >= batch) return;  // wave-uniform
@@ -164,9 +182,10 @@ __global__ __launch_bounds__(256) void sample_kernel(const float* __restrict__ p
     }
     const int64_t blk = lo < nblocks ? lo : nblocks - 1;
     const double base = blk > 0 ? prefix[blk - 1] : 0.0;
-    float* rows = s_rows[w];
-    stage_block(block_rsrc(p, n, blk), rows, lane);
-    const double incl = wave_scan(lane_sum(rows, lane), lane);
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(p, n, blk);
+    // this lane's inclusive prefix within the block (formed by
+    // block_sums_kernel, so the same values as the block totals)
+    const double incl = lanes[blk * kLanes + lane];
     const double excl = __shfl_up(incl, 1, kLanes);
     const double start = lane > 0 ? excl : 0.0;
     // the first lane whose range ends above the target walks its priorities
@@ -175,9 +194,11 @@ __global__ __launch_bounds__(256) void sample_kernel(const float* __restrict__ p
     if (m) {
       const int first = __builtin_ctzll(m);
       if (lane == first) {
+        float v[kPerLane];
+        lane_priorities(rs, lane, v);
         double run = start;
         for (int j = 0; j < kPerLane; ++j) {
-          run += per_value(rows[lane * kStride + j]);
+          run += per_value(v[j]);
           if (base + run > target) { found = lane * kPerLane + j; break; }
         }
       }
@@ -186,9 +207,11 @@ __global__ __launch_bounds__(256) void sample_kernel(const float* __restrict__ p
     if (found < 0) {
       // rounding left the target past every running sum of the block: the
       // last priority of the block that carries weight
+      float v[kPerLane];
+      lane_priorities(rs, lane, v);
       int last = -1;
       for (int j = 0; j < kPerLane; ++j)
-        if (per_value(rows[lane * kStride + j]) > 0.0) last = lane * kPerLane + j;
+        if (per_value(v[j]) > 0.0) last = lane * kPerLane + j;
       found = last;
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) {
@@ -281,14 +304,14 @@ __global__ __launch_bounds__(256) void update_max_kernel(float* __restrict__ pr,
 
 hipError_t per_sample_launch(const float* p, int64_t n, int32_t batch, uint64_t seed, float beta,
                              int32_t* indices, float* weights, double* block_prefix,
-                             double* raw_weights, hipStream_t st) {
+                             double* lane_prefix, double* raw_weights, hipStream_t st) {
   const int64_t nblocks = per_blocks(n);
   hipLaunchKernelGGL(block_sums_kernel, dim3((unsigned)((nblocks + 3) / 4)), dim3(256), 0, st, p, n,
-                     nblocks, block_prefix);
+                     nblocks, block_prefix, lane_prefix);
   hipLaunchKernelGGL(block_scan_kernel, dim3(1), dim3(1024), 0, st, block_prefix, nblocks);
   if (batch > 0) {
     hipLaunchKernelGGL(sample_kernel, dim3((unsigned)((batch + 3) / 4)), dim3(256), 0, st, p, n,
-                       block_prefix, nblocks, batch, seed, beta, indices, raw_weights);
+                       block_prefix, lane_prefix, nblocks, batch, seed, beta, indices, raw_weights);
     hipLaunchKernelGGL(weights_kernel, dim3(1), dim3(1024), 0, st, raw_weights, batch, weights);
   }
   return hipGetLastError();

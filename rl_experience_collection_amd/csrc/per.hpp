@@ -28,10 +28,11 @@ struct PerGatherArgs {
   uint8_t* out_dones;        // [batch]
 };
 
-// block_prefix: per_blocks(n) doubles; raw_weights: batch doubles (scratch).
+// Scratch: block_prefix per_blocks(n) doubles, lane_prefix 64 * per_blocks(n)
+// doubles, raw_weights batch doubles.
 hipError_t per_sample_launch(const float* priorities, int64_t n, int32_t batch, uint64_t seed,
                              float beta, int32_t* indices, float* weights, double* block_prefix,
-                             double* raw_weights, hipStream_t st);
+                             double* lane_prefix, double* raw_weights, hipStream_t st);
 hipError_t per_gather_launch(const PerGatherArgs& a, hipStream_t st);
 hipError_t per_update_launch(float* priorities, int64_t n, const int32_t* indices, const float* td,
                              int32_t batch, float alpha, float eps, float pmax, hipStream_t st);
