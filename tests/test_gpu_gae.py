@@ -100,3 +100,20 @@ def test_gae_empty_is_noop():
     import rl_experience_collection_amd as rx
     z = torch.zeros((0, 5), device="cuda")
     rx.gae_scan(z, z, torch.zeros((0, 5), dtype=torch.uint8, device="cuda"), None, 0.99, 0.95, z, z)
+
+
+@pytest.mark.parametrize("L,N", [(500, 65536), (16384, 2048)])
+def test_gae_large_sizes_sampled_episodes(L, N):
+    """Large launches (33.5 M elements, 570 MB moved): 2048 columns of the
+    single-super-chunk path, and 64 chained super-chunks per column of the
+    look-back path; the oracle recomputes a spread of episodes (episodes are
+    independent), and every return is A + V."""
+    r, v, d = synthdata.gae_inputs(N, L, seed=N + L)
+    A, R = run(r, v, d)
+    cols = np.unique(np.concatenate([np.arange(0, N, N // 37), [N - 1, N // 2 + 1]]))
+    Ao, Ro = oracle.gae(np.ascontiguousarray(r[:, cols]), np.ascontiguousarray(v[:, cols]),
+                        np.ascontiguousarray(d[:, cols]), 0.99, 0.95)
+    assert close_mask(A[:, cols], Ao).all(), np.abs(A[:, cols] - Ao).max()
+    assert close_mask(R[:, cols], Ro).all()
+    assert np.array_equal(R, (A + v).astype(np.float32))
+    assert np.isfinite(A).all()
