@@ -240,3 +240,17 @@ def test_recycling_chip_workload_n8192_l500_sampled_episodes():
 
 def test_recycling_bf16_teacher_forced():
     assert _bf16_compare(_recycled("ppo_n16_l100", bias_scale=0.1)) > 0.5
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_wide_collection_n65536_l64_sampled_episodes(precision):
+    """N = 65536: the actor launches 4096 workgroups, eight times the resident
+    ones, and the value kernel runs 4.2 M rows; a spread of episodes against
+    the oracle (fp32 by the parity protocol, bf16 teacher-forced)."""
+    inp = synthdata.ppo_inputs(dict(N=65536, L=64, n_bars=200_000, seed=31), bias_scale=0.1)
+    sub = sorted(set(list(range(0, 65536, 4093)) + [65535, 32768, 17]))
+    if precision == 0:
+        gpu = run_gpu(inp, logits=True)
+        _assert_parity(inp, gpu, oracle.rollout(inp, subset=sub), episodes=sub)
+    else:
+        _bf16_compare(inp, episodes=sub)
