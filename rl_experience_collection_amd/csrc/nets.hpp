@@ -59,7 +59,7 @@ __host__ __device__ constexpr int ring_depth(bool bf16, int otw) {
 // Actor: 54 -> 128 -> 64 -> 45 (PPO CUDA Pipeline Design, Weight Layout).
 // Its first layer takes the state in natural order (first = 2: k = 4 s + g),
 // so the portfolio inputs k >= 48 sit in k-steps 12 and 13 only.
-constexpr LayerDesc kActor[3] = {{54, 128, 16, 2, 8, 3}, {128, 64, 32, 0, 4, 3}, {64, 45, 16, 0, 4, 3}};
+constexpr LayerDesc kActor[3] = {{54, 128, 16, 2, 8, 0}, {128, 64, 32, 0, 4, 0}, {64, 45, 16, 0, 4, 0}};
 // Critic: 54 -> 512 -> 384 -> 256 -> 128 -> 64 (-> 1 handled on the VALU).
 constexpr LayerDesc kCritic[5] = {{54, 512, 16, 1, 32, 0},
                                   {512, 384, 128, 0, 24, 0},
@@ -73,7 +73,7 @@ constexpr LayerDesc kCur[2] = {{54, 128, 16, 1, 8, 0}, {128, 51, 32, 0, 4, 0}};
 // lane group.  First layers: kperm(s, g, j) = 32 s + 8 g + j (54 -> 2 steps).
 // Chained layers: kperm(s, g, j) = 16 (2 s + j / 4) + 4 g + j % 4, i.e. the
 // output tiles 2s and 2s+1 of the previous layer form k-step s.
-constexpr LayerDesc kActorB[3] = {{54, 128, 2, 1, 8, 3}, {128, 64, 4, 0, 4, 3}, {64, 45, 2, 0, 4, 3}};
+constexpr LayerDesc kActorB[3] = {{54, 128, 2, 1, 8, 0}, {128, 64, 4, 0, 4, 0}, {64, 45, 2, 0, 4, 0}};
 constexpr LayerDesc kCriticB[5] = {{54, 512, 2, 1, 32, 0},
                                    {512, 384, 16, 0, 24, 0},
                                    {384, 256, 12, 0, 16, 0},
@@ -81,10 +81,8 @@ constexpr LayerDesc kCriticB[5] = {{54, 512, 2, 1, 32, 0},
                                    {128, 64, 4, 0, 4, 0}};
 constexpr LayerDesc kCurB[2] = {{54, 128, 2, 1, 8, 0}, {128, 51, 4, 0, 4, 0}};
 
-// Packed weights of a layer, plus d.pad zero k-steps so the prefetch of the
-// layer's last steps reads inside the block.  The actor's layers (read from
-// LDS through a 4-slot ring) carry kPrefetch = 3.
-constexpr int kPrefetch = 3;
+// Packed weights of a layer, plus d.pad zero k-steps (the DQN's first layers
+// stream 16 k-steps for their 14).
 __host__ __device__ constexpr int64_t packed_layer_floats(const LayerDesc& d) {
   return (int64_t)(d.steps + d.pad) * 64 * d.ot;
 }
@@ -94,15 +92,15 @@ __host__ __device__ constexpr int64_t packed_layer_floats_bf16(const LayerDesc& 
 }
 
 struct PackedOffsets {
-  // fp32 actor block (contiguous, staged into LDS by the rollout kernel)
-  int64_t actor_w[3], actor_b[3], actor_end;
+  // fp32 actor layers and biases (loaded into registers by the rollout kernel)
+  int64_t actor_w[3], actor_b[3];
   int64_t critic_w[5], critic_b[5], critic_w6, critic_b6;
   int64_t cur_w[2], cur_b[2], cur_onehot;
-  // bf16 forms: a contiguous actor block [bact_begin, bact_end) with its own
-  // copy of the biases, the bf16 critic and curiosity layers (biases shared
-  // with the fp32 block), and bf16-rounded copies (as fp32) of the critic's
-  // 64 -> 1 row and of the curiosity one-hot columns
-  int64_t bact_begin, bact_w[3], bact_b[3], bact_end;
+  // bf16 forms: the actor layers with their own copy of the biases, the
+  // bf16 critic and curiosity layers (biases shared with the fp32 block),
+  // and bf16-rounded copies (as fp32) of the critic's 64 -> 1 row and of the
+  // curiosity one-hot columns
+  int64_t bact_w[3], bact_b[3];
   int64_t bcritic_w[5], bcur_w[2], bcritic_w6, bcur_onehot;
   int64_t total;
 };
@@ -120,7 +118,6 @@ __host__ __device__ constexpr PackedOffsets packed_offsets() {
     p.actor_b[l] = off;
     off = align64(off + 16 * kActor[l].ot);
   }
-  p.actor_end = off;
   for (int l = 0; l < 5; ++l) {
     p.critic_w[l] = off;
     off = align64(off + packed_layer_floats(kCritic[l]));
@@ -143,7 +140,6 @@ __host__ __device__ constexpr PackedOffsets packed_offsets() {
   }
   p.cur_onehot = off;
   off = align64(off + 45 * 128);
-  p.bact_begin = off;
   for (int l = 0; l < 3; ++l) {
     p.bact_w[l] = off;
     off = align64(off + packed_layer_floats_bf16(kActorB[l]));
@@ -152,8 +148,7 @@ __host__ __device__ constexpr PackedOffsets packed_offsets() {
     p.bact_b[l] = off;
     off = align64(off + 16 * kActorB[l].ot);
   }
-  p.bact_end = off;
-  for (int l = 0; l < 5; ++l) {
+    for (int l = 0; l < 5; ++l) {
     p.bcritic_w[l] = off;
     off = align64(off + packed_layer_floats_bf16(kCriticB[l]));
   }
@@ -284,45 +279,6 @@ __device__ __forceinline__ void load_operands(const float* p, float (&a)[OTW]) {
 }
 
 // ---------------------------------------------------------------------------
-// This wave's share of one layer for the 16 rows of its row group:
-// acc[i] = bias + W x for output tile q*OTW + i.  The B operands of k-steps
-// 4*kt .. 4*kt+3 of lane l sit in buf[kt*64 + l], written by lane l of the
-// producing waves (the MFMA output layout of lane l is the next layer's
-// input layout of lane l).  Software pipeline: the weights of k-step s+3 are
-// loaded before the MFMAs of step s, into a 4-slot ring indexed by s % 4;
-// scheduling barriers keep that order (the compiler would otherwise move
-// each load next to its use), so three steps of loads are always in flight.
-// Addresses are a wave-uniform base plus one 32-bit lane offset.
-// ---------------------------------------------------------------------------
-template <int S, int OTW>
-__device__ __forceinline__ void mfma_layer(const float* __restrict__ pk, const float* __restrict__ pb,
-                                           const f32x4* buf, f32x4 (&acc)[OTW], int q, int lane) {
-  static_assert(kPrefetch == 3, "the ring below holds kPrefetch + 1 = 4 steps");
-  constexpr int KT = (S + 3) / 4;
-  constexpr int kStep = kSplit * 64 * OTW;  // floats per k-step
-  const int g = lane >> 4;
-  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
-#pragma unroll
-  for (int i = 0; i < OTW; ++i)
-    acc[i] = *reinterpret_cast<const f32x4*>(pb + 16 * (q * OTW + i) + 4 * g);
-  float a[4][OTW];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) load_operands<OTW>(pk + j * kStep + lane_off, a[j]);
-#pragma unroll 1
-  for (int kt = 0; kt < KT; ++kt) {
-    const float* wk = pk + (4 * kt + 3) * kStep;  // step s + 3 of r = 0
-    const f32x4 b = buf[kt * 64 + lane];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      load_operands<OTW>(wk + r * kStep + lane_off, a[(r + 3) & 3]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < OTW; ++i) acc[i] = mfma4(a[r][i], b[r], acc[i]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
-
 // ReLU this wave's accumulators into its tiles of the shared buffer.
 template <int OTW>
 __device__ __forceinline__ void relu_store(const f32x4 (&acc)[OTW], f32x4* buf, int q, int lane) {
@@ -332,54 +288,6 @@ __device__ __forceinline__ void relu_store(const f32x4 (&acc)[OTW], f32x4* buf, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = fmaxf(v[r], 0.0f);
     buf[(q * OTW + i) * 64 + lane] = v;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 form of mfma_layer: k-step s consumes 8 bf16 B operands per lane from
-// bufb[s*64 + l] and 8 bf16 weights per output tile; accumulation is fp32.
-// The same 4-slot prefetch ring as the fp32 form.
-// ---------------------------------------------------------------------------
-template <int S, int OTW>
-__device__ __forceinline__ void mfma_layer_bf16(const uint4* __restrict__ pk,
-                                                const float* __restrict__ pb, const uint4* bufb,
-                                                f32x4 (&acc)[OTW], int q, int lane) {
-  static_assert(kPrefetch == 3, "the ring below holds kPrefetch + 1 = 4 steps");
-  constexpr int KT = S / 4;
-  constexpr int TAIL = S % 4;
-  constexpr int kStep = kSplit * 64 * OTW;  // uint4 per k-step
-  const int g = lane >> 4;
-  const uint32_t lane_off = (uint32_t)((q * 64 + lane) * OTW);
-#pragma unroll
-  for (int i = 0; i < OTW; ++i)
-    acc[i] = *reinterpret_cast<const f32x4*>(pb + 16 * (q * OTW + i) + 4 * g);
-  uint4 a[4][OTW];
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-#pragma unroll
-    for (int i = 0; i < OTW; ++i) a[j][i] = pk[j * kStep + lane_off + i];
-#pragma unroll 1
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint4* wk = pk + (4 * kt + 3) * kStep;
-    uint4 b[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) b[r] = bufb[(4 * kt + r) * 64 + lane];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int i = 0; i < OTW; ++i) a[(r + 3) & 3][i] = wk[r * kStep + lane_off + i];
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < OTW; ++i) acc[i] = mfma_bf16(a[r][i], b[r], acc[i]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // remaining steps (S % 4): their operands are already in slots 0 .. TAIL-1
-#pragma unroll
-  for (int r = 0; r < TAIL; ++r) {
-    const uint4 b = bufb[(4 * KT + r) * 64 + lane];
-#pragma unroll
-    for (int i = 0; i < OTW; ++i) acc[i] = mfma_bf16(a[r][i], b, acc[i]);
   }
 }
 
@@ -460,9 +368,9 @@ __device__ __forceinline__ void bload_operands(BufRsrc r, uint32_t vo, uint32_t 
   }
 }
 
-// Weight sources of a streamed layer: byte offsets (lane part + wave-uniform
-// step part) into the packed block, either in global memory through the
-// buffer resource or staged in LDS.
+// Weight source of a streamed layer: byte offsets (lane part + wave-uniform
+// step part) into the packed block in global memory, through the buffer
+// resource.
 struct GlobalWeights {
   BufRsrc rs;
   template <int OTW>
@@ -473,17 +381,6 @@ struct GlobalWeights {
     return bload_u4(rs, lane_b, step_b);
   }
 };
-struct LdsWeights {
-  const char* base;
-  template <int OTW>
-  __device__ __forceinline__ void f32(uint32_t lane_b, uint32_t step_b, float (&a)[OTW]) const {
-    load_operands<OTW>(reinterpret_cast<const float*>(base + step_b + lane_b), a);
-  }
-  __device__ __forceinline__ uint4 u4(uint32_t lane_b, uint32_t step_b) const {
-    return *reinterpret_cast<const uint4*>(base + step_b + lane_b);
-  }
-};
-
 // pk_b: byte offset of the layer's packed weights in the block; pb: biases.
 template <int S, bool BF16, int OTW, int D, int SPLIT, class WS>
 __device__ __forceinline__ void stream_begin(WeightStream<BF16, OTW, D, SPLIT>& st, const WS& ws,
@@ -633,32 +530,6 @@ __device__ __forceinline__ void relu_store_tiles_bf16(const f32x4 (&acc)[RT][OTW
                                                       int tile_stride, int q, int lane) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) relu_store_bf16<OTW>(acc[rt], buf + rt * tile_stride, q, lane);
-}
-
-// The 16 first-layer operands of a lane (state_k order) as LDS operands:
-// fp32: four float4 (k-steps 4 q4 .. 4 q4 + 3); bf16: two k-steps of 8.
-template <bool BF16>
-__device__ __forceinline__ void store_state_operands(const float (&B)[16], void* buf, int lane) {
-  if constexpr (BF16) {
-    uint4* b = reinterpret_cast<uint4*>(buf);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 w;
-      w.x = pack_bf16x2(B[8 * s + 0], B[8 * s + 1]);
-      w.y = pack_bf16x2(B[8 * s + 2], B[8 * s + 3]);
-      w.z = pack_bf16x2(B[8 * s + 4], B[8 * s + 5]);
-      w.w = pack_bf16x2(B[8 * s + 6], B[8 * s + 7]);
-      b[s * 64 + lane] = w;
-    }
-  } else {
-    f32x4* b = reinterpret_cast<f32x4*>(buf);
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      f32x4 v;
-      v[0] = B[4 * k4]; v[1] = B[4 * k4 + 1]; v[2] = B[4 * k4 + 2]; v[3] = B[4 * k4 + 3];
-      b[k4 * 64 + lane] = v;
-    }
-  }
 }
 
 }  // namespace rl
