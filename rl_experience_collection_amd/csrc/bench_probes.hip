@@ -12,8 +12,9 @@
 //    lane.  Its time for the value kernel's work-item count is the stream
 //    bound the MFMA work competes with.
 //  * gae_traffic_kernel: moves exactly the GAE scan's bytes (reads r, V, d;
-//    writes two float arrays), element-wise with no recurrence: the copy
-//    ceiling of the scan at a given size.
+//    writes two float arrays with streaming stores, as the scan does),
+//    element-wise with no recurrence: the copy ceiling of the scan at a
+//    given size.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,8 +59,8 @@ __global__ __launch_bounds__(kThreads) void gae_traffic_kernel(
   const uint32_t z = d[i];
   const f32x4 dz = {(float)(z & 255u), (float)((z >> 8) & 255u), (float)((z >> 16) & 255u),
                     (float)(z >> 24)};
-  a[i] = x - y * dz;
-  b[i] = x + y;
+  __builtin_nontemporal_store(x - y * dz, a + i);  // streaming stores, as the scan's
+  __builtin_nontemporal_store(x + y, b + i);
 }
 
 }  // namespace

@@ -239,8 +239,9 @@ __global__ __launch_bounds__(64 * kGaeWaves) void gae_scan_kernel(
     if (i < cnt) {
       A = r[i] + (gl * (1.0f - d[i])) * A;
       const int64_t o = (int64_t)(t0 + i) * N + n;
-      adv[o] = A;
-      ret[o] = A + v[i];
+      // streaming stores: written once here, not read again by the scan
+      __builtin_nontemporal_store(A, adv + o);
+      __builtin_nontemporal_store(A + v[i], ret + o);
     }
   }
 }
