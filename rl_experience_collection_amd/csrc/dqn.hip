@@ -49,13 +49,13 @@ constexpr int kBufC = 4 * 64;   // curiosity prediction: 64 = 4 tiles
 // included, B operands from the LDS operand layout.  With four workgroups
 // per CU the weight ring needs fewer steps in flight than the value
 // kernel's: 4 steps for 4 tiles per wave, 8 otherwise.
-template <int S, int OTW>
+template <int S, int OTW, int SK = S>
 __device__ __forceinline__ void dense(const GlobalWeights& gw, uint32_t pk_b, const float* pb,
                                       const f32x4* in, f32x4 (&acc)[1][OTW], int q, int lane) {
   constexpr int D = OTW >= 4 ? 4 : 8;
   WeightStream<false, OTW, D> st;
   stream_begin<S>(st, gw, pk_b, pb, q, lane);
-  stream_layer<S, OTW, D, 1>(st, gw, pk_b, LdsOperands{in, 0}, acc, q, lane);
+  stream_layer<S, OTW, D, 1, SK>(st, gw, pk_b, LdsOperands{in, 0}, acc, q, lane);
 }
 
 // Dueling Q-network `net` (0 online, 1 target) on the state operands `in`:
@@ -75,7 +75,7 @@ __device__ __forceinline__ void q_network(const GlobalWeights& gw, const float* 
   WeightStream<false, 4, 4> s0;
   stream_begin<16>(s0, gw, w0, W + kD.b[net][0], q, lane);
   f32x4 h0[1][4];
-  stream_layer<16, 4, 4, 1>(s0, gw, w0, LdsOperands{in, 0}, h0, q, lane);
+  stream_layer<16, 4, 4, 1, 14>(s0, gw, w0, LdsOperands{in, 0}, h0, q, lane);  // 2 padding steps
   WeightStream<false, 2, 8> s1;
   stream_begin<64>(s1, gw, w1, W + kD.b[net][1], q, lane);
   relu_store_tiles<4, 1>(h0, bufA, 0, q, lane);
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     // ---- step 9: curiosity on [state, one-hot(action)] ----------------------
     {
       f32x4 h[1][2];
-      dense<16, 2>(gw, 4u * (uint32_t)kD.cw[0], W + kD.cb[0], s_opnd, h, q, lane);
+      dense<16, 2, 14>(gw, 4u * (uint32_t)kD.cw[0], W + kD.cb[0], s_opnd, h, q, lane);
       // the one-hot half of the input is a column gather: + W[:, 54 + a]
       const int ra = s_act[lane & 15];
       const float* oh = W + kD.c_onehot + ra * 128 + 4 * (lane >> 4);

@@ -417,12 +417,15 @@ struct LdsOperands {
 };
 
 // fp32: S k-steps of 4 inputs (S % D == 0); a row tile's f32x4 B operand
-// covers a group of 4 steps, read one group ahead.
-template <int S, int OTW, int D, int RT, int SPLIT, class WS, class BL>
+// covers a group of 4 steps, read one group ahead.  Steps from SK on carry
+// only zero padding (first layers: 54 inputs in 14 of 16 steps): their
+// weights stream with the rest but issue no MFMA.
+template <int S, int OTW, int D, int RT, int SK = S, int SPLIT, class WS, class BL>
 __device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D, SPLIT>& st, const WS& ws,
                                              uint32_t pk_b, const BL& bl, f32x4 (&acc)[RT][OTW],
                                              int q, int lane) {
   static_assert(D % 4 == 0 && S % D == 0, "whole groups of D steps");
+  static_assert(SK > S - D && SK <= S, "padding only in the last group");
   constexpr int KT = S / D;
   constexpr int G = S / 4;
   constexpr uint32_t kStepB = WeightStream<false, OTW, D, SPLIT>::kStep * 4u;
@@ -446,11 +449,13 @@ __device__ __forceinline__ void stream_layer(WeightStream<false, OTW, D, SPLIT>&
         for (int rt = 0; rt < RT; ++rt) bn[rt] = bl.f32(rt, gn < G ? gn : G - 1, lane);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (!LAST || D * (S / D - 1) + r < SK) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < OTW; ++i)
-          acc[rt][i] = mfma4(st.a[r][i], b[rt][r % 4], acc[rt][i]);
+          for (int i = 0; i < OTW; ++i)
+            acc[rt][i] = mfma4(st.a[r][i], b[rt][r % 4], acc[rt][i]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (r % 4 == 3) {
 #pragma unroll

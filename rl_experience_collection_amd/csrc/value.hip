@@ -81,11 +81,16 @@ __device__ __forceinline__ void begin(WeightStream<BF16, OTW, D, SPLIT>& st, con
   stream_begin<S>(st, w.gw, (uint32_t)(4 * (BF16 ? wb : w32)), w.W + b_off, q, lane);
 }
 
-template <int S, bool BF16, int OTW, int D, int SPLIT, int RT, class BL>
+// SK: the fp32 k-steps that hold inputs (the first layers' 54 inputs fill 14
+// of their 16 steps; the rest is zero padding and issues no MFMA)
+template <int S, int SK = S, bool BF16, int OTW, int D, int SPLIT, int RT, class BL>
 __device__ __forceinline__ void run(WeightStream<BF16, OTW, D, SPLIT>& st, const Weights& w,
                                     int64_t w32, int64_t wb, const BL& bl,
                                     f32x4 (&acc)[RT][OTW], int q, int lane) {
-  stream_layer<S, OTW, D, RT>(st, w.gw, (uint32_t)(4 * (BF16 ? wb : w32)), bl, acc, q, lane);
+  if constexpr (BF16)
+    stream_layer<S, OTW, D, RT>(st, w.gw, (uint32_t)(4 * wb), bl, acc, q, lane);
+  else
+    stream_layer<S, OTW, D, RT, SK>(st, w.gw, (uint32_t)(4 * w32), bl, acc, q, lane);
 }
 
 template <bool BF16, int OTW, int RT>
@@ -276,7 +281,7 @@ void value_kernel(ValueArgs a) {
     store<BF16, Sh::O1, H>(h1, s_buf + H * TS, TS, q, lane);
   } else {
     f32x4 h1[RT][Sh::O1];
-    run<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], states_in, h1, q, lane);
+    run<S1, kFirstSteps>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], states_in, h1, q, lane);
     begin<S2>(w2, wt, kP.critic_w[1], kP.bcritic_w[1], kP.critic_b[1], q, lane);
     store<BF16, Sh::O1, RT>(h1, s_buf, TS, q, lane);
   }
@@ -376,7 +381,7 @@ void value_kernel(ValueArgs a) {
 
   // ---- curiosity layer 1 (reads the state operands, not s_buf) ----------
   f32x4 c[RT][Sh::OC1];
-  run<SC1>(c1, wt, kP.cur_w[0], kP.bcur_w[0], states_in, c, q, lane);
+  run<SC1, BF16 ? SC1 : kFirstSteps>(c1, wt, kP.cur_w[0], kP.bcur_w[0], states_in, c, q, lane);
   Stream<BF16, 1> c2;
   begin<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], kP.cur_b[1], q4, lane);
 #pragma unroll
