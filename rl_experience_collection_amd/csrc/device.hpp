@@ -9,6 +9,9 @@
 namespace rl {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// four floats at a 4-byte aligned address (rows of 51 features): one
+// 16-byte load where all four are wanted
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kFeatures = 51;

@@ -341,17 +341,21 @@ void value_kernel(ValueArgs a) {
   }
   lds_barrier();
   // next-bar features of this wave's row tiles for the curiosity MSE: lane
-  // holds features 16 q4 + 4g + r
+  // holds features j0 .. j0 + 3, j0 = 16 q4 + 4g.  Where all four lie in the
+  // row they are one 16-byte load (rows are 204 bytes, so 4-byte aligned):
+  // per-lane rows make each load touch 16 lines, and one wide load instead
+  // of four keeps the address work per row at one pass.
   f32x4 feat[RTS];
+  const int j0 = 16 * q4 + 4 * g;
 #pragma unroll
   for (int rt = 0; rt < RTS; ++rt) {
     const float* fn =
         a.features + (int64_t)s_nbar[(rs0 + rt) * kRowsPerWave + (lane & 15)] * kFeatures;
+    if (j0 + 3 < kFeatures) {
+      feat[rt] = *reinterpret_cast<const f32x4_a4*>(fn + j0);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 16 * q4 + 4 * g + r;  // unconditional load, masked after
-      const float v = fn[j < kFeatures ? j : kFeatures - 1];
-      feat[rt][r] = j < kFeatures ? v : 0.0f;
+      for (int r = 0; r < 4; ++r) feat[rt][r] = j0 + r < kFeatures ? fn[j0 + r] : 0.0f;
     }
   }
   store<BF16, Sh::O4, RT>(h4, s_buf, TS, q, lane);
