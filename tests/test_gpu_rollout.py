@@ -187,6 +187,14 @@ def test_bf16_ragged_sizes(N, L):
     _bf16_compare(synthdata.ppo_inputs(spec, bias_scale=0.1))
 
 
+def test_bf16_episodes_reaching_the_last_bar():
+    """Every episode starts at the last valid start, so the curiosity target
+    of the final step is the market's last feature row (the row-end loads)."""
+    inp = synthdata.ppo_inputs(dict(N=40, L=30, n_bars=400, seed=17), bias_scale=0.1)
+    inp["starts"] = np.full(40, 400 - 30 - 1, dtype=np.int32)
+    _bf16_compare(inp)
+
+
 def test_bf16_chip_workload_sampled_episodes():
     inp = synthdata.ppo_inputs("ppo_n8192_l500")
     sub = sorted(set(list(range(0, 8192, 397)) + [8191]))
