@@ -27,6 +27,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 namespace rl {
 
 namespace {
@@ -448,21 +450,24 @@ void value_kernel(ValueArgs a) {
 __global__ void zero_u64_kernel(unsigned long long* p) { p[threadIdx.x] = 0ull; }
 
 // Resident workgroups of a value kernel on the current device (all CUs at
-// the kernel's occupancy), cached per device.
+// the kernel's occupancy), cached per device (callers on several host
+// threads may fill an entry concurrently; they store the same value).
 template <bool BF16>
 int resident_groups() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] > 0) return cache[dev];
+  const int known = cache[dev].load(std::memory_order_relaxed);
+  if (known > 0) return known;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, value_kernel<BF16>,
                                                    ValueShape<BF16>::kThreads, 0) !=
           hipSuccess)
     return 0;
-  cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
-  return cache[dev];
+  const int groups = cus * (per_cu > 0 ? per_cu : 1);
+  cache[dev].store(groups, std::memory_order_relaxed);
+  return groups;
 }
 
 }  // namespace
