@@ -93,6 +93,15 @@ typedef struct {
                              counter (episode, t, 5, 0), range = n_bars -
                              (L - t - 1) valid starts; the handle then keeps
                              an [L][N] i32 record of the bars */
+  int32_t overlap;        /* -1 (default): in fp32, when the rollout's
+                             workgroups (16 episodes each) fill at most a
+                             quarter of the CUs (N <= 1024 on 256 CUs),
+                             split the rollout into 2..8 launches of
+                             consecutive steps (L / 64 of them) and run the
+                             value pass over each finished part on a second
+                             stream of the handle, on the CUs the rollout
+                             leaves free, while the next part runs; 0: never;
+                             1: always.  The results do not depend on it. */
 } rollout_config;
 
 /* Output buffers of one collection: DEVICE pointers, caller-owned, [L][N].
@@ -114,8 +123,9 @@ typedef struct {
                          to be clamped */
   void *const *phase_events; /* NULL or [4] caller-created hipEvent_t (as
                          void*), recorded on hip_stream before the rollout
-                         kernel, after it, after the value kernel and after
-                         the GAE scan, for per-phase timing */
+                         kernel, after it (its last part when split), after
+                         the value pass and after the GAE scan, for
+                         per-phase timing */
 } rollout_outputs;
 
 /* Fill `cfg` with the default settings (the values in the comments above)

@@ -44,7 +44,7 @@ class RolloutConfig(C.Structure):
         ("curiosity_coef", C.c_float), ("risk_coef", C.c_float), ("spread", C.c_float),
         ("barrier_scale", C.c_float),
         ("exposure", C.c_float * 5), ("cost", C.c_float * 3), ("urgency_mult", C.c_float),
-        ("recycle", C.c_int32),
+        ("recycle", C.c_int32), ("overlap", C.c_int32),
     ]
 
 

@@ -11,6 +11,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "../../include/dqn.h"
 #include "../../include/per.h"
@@ -172,7 +173,22 @@ int check_config(const rollout_config* c) {
     return fail(ROLLOUT_EINVAL, "div_window must be in 1..32 (got %d)", c->div_window);
   if (c->max_hold < 1) return fail(ROLLOUT_EINVAL, "max_hold must be >= 1");
   if (c->recycle != 0 && c->recycle != 1) return fail(ROLLOUT_EINVAL, "recycle must be 0 or 1");
+  if (c->overlap < -1 || c->overlap > 1) return fail(ROLLOUT_EINVAL, "overlap must be -1, 0 or 1");
   return ROLLOUT_OK;
+}
+
+// Launches the rollout of one collection is split into, so that the value
+// pass over each finished part runs on another stream while the rollout
+// continues.  By default only where it pays: fp32 (the bf16 value pass is
+// too short to repay the extra launches) with the rollout's workgroups (16
+// episodes each) leaving at least three quarters of the CUs idle; `overlap`
+// 1 forces it, 0 turns it off.
+int overlap_parts(const rollout_config& c, int cus) {
+  if (c.overlap == 0 || c.n_steps < 2) return 1;
+  const int64_t blocks = ((int64_t)c.n_episodes + 15) / 16;
+  if (c.overlap < 0 && (c.precision != ROLLOUT_FP32 || blocks * 4 > (int64_t)cus)) return 1;
+  const int k = c.n_steps / 64;
+  return k < 2 ? 2 : (k > 8 ? 8 : k);
 }
 
 int check_weights(const float* const actor[6], const float* const critic[12],
@@ -257,6 +273,15 @@ struct rollout_s {
   unsigned long long* value_sched = nullptr;  // work counter of the value kernel
   int32_t* bars = nullptr;       // [L][N] bar of every step (recycling only)
   GaeScratch gae;
+  // the rollout split into `parts` launches, the value pass of each part on
+  // `side` (only when parts > 1)
+  int parts = 1;
+  int32_t* carry = nullptr;      // [N][kCarryWords] episode state between parts
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> part_done;  // [parts] rollout part finished
+  hipEvent_t values_done = nullptr;   // last value pass finished
+  int32_t ov_grid = 0;  // value workgroups while a rollout part runs
+  int32_t ov_pad = 0;   // their LDS reservation
 };
 
 extern "C" {
@@ -290,6 +315,7 @@ int rollout_config_default(rollout_config* cfg, int32_t n_episodes, int32_t n_st
   std::memcpy(cfg->exposure, ex, sizeof(ex));
   std::memcpy(cfg->cost, co, sizeof(co));
   cfg->urgency_mult = 0.5f;
+  cfg->overlap = -1;
   return ROLLOUT_OK;
 }
 
@@ -347,6 +373,57 @@ int rollout_create(const rollout_config* cfg, const float* const actor[6],
       return fail(ROLLOUT_ENOMEM, "cannot allocate the bar record");
     }
     h->bars = static_cast<int32_t*>(p);
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
+  if (e != hipSuccess) {
+    rollout_destroy(h);
+    return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  h->parts = overlap_parts(*cfg, cus);
+  if (h->parts > 1) {
+    if (hipMalloc(&p, (size_t)cfg->n_episodes * rl::kCarryWords * sizeof(int32_t)) != hipSuccess) {
+      (void)hipGetLastError();
+      rollout_destroy(h);
+      return fail(ROLLOUT_ENOMEM, "cannot allocate the episode carry");
+    }
+    h->carry = static_cast<int32_t*>(p);
+    // non-blocking: the caller's stream may be the null stream, which a
+    // blocking stream would serialise against
+    e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+    for (int i = 0; e == hipSuccess && i <= h->parts; ++i) {
+      hipEvent_t ev = nullptr;
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) break;
+      if (i < h->parts)
+        h->part_done.push_back(ev);
+      else
+        h->values_done = ev;
+    }
+    if (e != hipSuccess) {
+      rollout_destroy(h);
+      return hip_fail(e, "side stream and events");
+    }
+    // While a rollout part runs, its workgroups must keep their CUs to
+    // themselves (a value workgroup beside one slows the sequential chain):
+    // the value passes reserve enough LDS that none fits beside a rollout
+    // workgroup, and leave as many CUs free as the rollout has workgroups.
+    const bool bf16 = cfg->precision == ROLLOUT_BF16;
+    int lds_cu = 0;
+    e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              h->device);
+    const int a_lds = rl::actor_lds_bytes(bf16, cfg->recycle != 0);
+    const int v_lds = rl::value_lds_bytes(bf16);
+    if (e != hipSuccess || a_lds < 0 || v_lds < 0) {
+      rollout_destroy(h);
+      return fail(ROLLOUT_EHIP, "kernel LDS sizes");
+    }
+    const int need = lds_cu - a_lds - v_lds + 256;  // value + pad + rollout > lds_cu
+    const int64_t blocks = ((int64_t)cfg->n_episodes + 15) / 16;
+    if (blocks < cus) {  // (otherwise the rollout holds every CU: no limit)
+      h->ov_pad = need > 0 ? need : 0;
+      h->ov_grid = (int32_t)(cus - blocks);
+    }
   }
   rc = gae_reserve(h->gae, cfg->n_steps, cfg->n_episodes, st);
   if (rc) {
@@ -416,8 +493,9 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   ra.counters = out->counters;
   ra.bf16 = h->cfg.precision == ROLLOUT_BF16;
   ra.bars = h->bars;
-  RL_HIP(rl::launch_actor_rollout(ra, st), "actor rollout launch");
-  RL_HIP(mark(1), "hipEventRecord(phase 1)");
+  ra.t_begin = 0;
+  ra.t_end = L;
+  ra.carry = h->carry;
 
   rl::ValueArgs va;
   va.weights = h->weights;
@@ -434,7 +512,45 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   va.counters = out->counters;
   va.sched = h->value_sched;
   va.bf16 = h->cfg.precision == ROLLOUT_BF16;
-  RL_HIP(rl::launch_value(va, st), "value launch");
+  va.t_off = 0;
+  va.max_grid = 0;
+  va.lds_pad = 0;
+
+  if (h->parts == 1) {
+    RL_HIP(rl::launch_actor_rollout(ra, st), "actor rollout launch");
+    RL_HIP(mark(1), "hipEventRecord(phase 1)");
+    RL_HIP(rl::launch_value(va, st), "value launch");
+  } else {
+    // part k of the rollout, then (on the side stream, once it is done) the
+    // value pass over its rows, while part k + 1 runs; the rows of a part
+    // are a contiguous block of the [L][N] outputs
+    for (int k = 0; k < h->parts; ++k) {
+      const int32_t t0 = (int32_t)((int64_t)L * k / h->parts);
+      const int32_t t1 = (int32_t)((int64_t)L * (k + 1) / h->parts);
+      ra.t_begin = t0;
+      ra.t_end = t1;
+      RL_HIP(rl::launch_actor_rollout(ra, st), "actor rollout launch");
+      RL_HIP(hipEventRecord(h->part_done[k], st), "hipEventRecord(part)");
+      RL_HIP(hipStreamWaitEvent(h->side, h->part_done[k], 0), "hipStreamWaitEvent(side)");
+      const int64_t r0 = (int64_t)t0 * N;
+      rl::ValueArgs vk = va;
+      vk.states = out->states + r0 * 54;
+      vk.actions = out->actions + r0;
+      vk.bars = h->bars ? h->bars + r0 : nullptr;
+      vk.values = out->values + r0;
+      vk.rewards = out->rewards + r0;
+      vk.L = t1 - t0;
+      vk.t_off = t0;
+      if (k + 1 < h->parts) {  // the last pass runs after the rollout, on the whole device
+        vk.max_grid = h->ov_grid;
+        vk.lds_pad = h->ov_pad;
+      }
+      RL_HIP(rl::launch_value(vk, h->side), "value launch");
+    }
+    RL_HIP(mark(1), "hipEventRecord(phase 1)");
+    RL_HIP(hipEventRecord(h->values_done, h->side), "hipEventRecord(values)");
+    RL_HIP(hipStreamWaitEvent(st, h->values_done, 0), "hipStreamWaitEvent(values)");
+  }
   RL_HIP(mark(2), "hipEventRecord(phase 2)");
 
   rl::GaeArgs ga;
@@ -477,6 +593,11 @@ void rollout_destroy(rollout_handle h) {
   if (h->value_sched) (void)hipFree(h->value_sched);
   if (h->bars) (void)hipFree(h->bars);
   if (h->gae.mem) (void)hipFree(h->gae.mem);
+  if (h->side) (void)hipStreamSynchronize(h->side);
+  for (hipEvent_t ev : h->part_done) (void)hipEventDestroy(ev);
+  if (h->values_done) (void)hipEventDestroy(h->values_done);
+  if (h->side) (void)hipStreamDestroy(h->side);
+  if (h->carry) (void)hipFree(h->carry);
   delete h;
 }
 

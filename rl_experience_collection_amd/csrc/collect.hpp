@@ -30,7 +30,14 @@ struct RolloutArgs {
   uint32_t* counters;     // [2] or null
   int bf16;               // bf16 weights and layer inputs, fp32 accumulation
   int32_t* bars;          // [L][N] bar of every step, or null: non-null selects recycling
+  int32_t t_begin, t_end; // the steps of this launch: [0, L) for the whole rollout
+  int32_t* carry;         // [N][kCarryWords] episode state between launches, or null
 };
+
+// Episode state a launch that ends before step L leaves for the next one:
+// bar (2 words), V, exposure held, entry price, armed, side, open step,
+// the three window counts, pushes, slot, window ring (2 words).
+constexpr int kCarryWords = 16;
 
 // Batched part: critic value and curiosity bonus of every stored (t, n),
 // which no later step reads, then the final reward.
@@ -48,6 +55,9 @@ struct ValueArgs {
   uint32_t* counters;
   unsigned long long* sched;  // [1] work counter of the persistent grid (zeroed per launch)
   int bf16;
+  int32_t t_off;  // global step of row 0 (a launch over the steps from t_off on)
+  int32_t max_grid;  // > 0: at most this many workgroups
+  int32_t lds_pad;   // extra LDS bytes reserved per workgroup (placement only)
 };
 
 // DQN collection: every step of every episode in one sequential kernel.
@@ -80,5 +90,8 @@ struct DqnArgs {
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st);
 hipError_t launch_dqn(const DqnArgs& a, hipStream_t st);
 hipError_t launch_value(const ValueArgs& a, hipStream_t st);
+// Static LDS bytes of a workgroup of the rollout / value kernel (-1 on error).
+int actor_lds_bytes(bool bf16, bool recycle);
+int value_lds_bytes(bool bf16);
 
 }  // namespace rl

@@ -176,32 +176,46 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   const int32_t n = valid ? n_raw : a.N - 1;
   const EnvParams& ep = a.ep;
 
-  // clamp the start so every read stays inside the market buffers
-  const int64_t hi = a.n_bars - (int64_t)a.L - 1;
-  int64_t st = a.starts[n];
-  const bool clamped = st < 0 || st > hi;
-  st = st < 0 ? 0 : (st > hi ? hi : st);
-  if (valid && j == 0) {
-    a.start_used[n] = (int32_t)st;
-    if (clamped && a.counters) atomicAdd(a.counters + 1, 1u);
-  }
-
-  f32x4* bufA = s_bufA;
-  f32x4* bufB = s_bufB;
-  f32x4* sbuf = s_state;
-
-  // features of steps t and t+1 (bars st + t, st + t + 1)
-  float f0[4], f1[4];
-  load_features(a.features, st, j, f0);
-  load_features(a.features, st + 1, j, f1);
-  float p0 = a.prices[st], p1 = a.prices[st + 1];
-
   // episode state (PPO CUDA Pipeline Design, Phase A steps 6-8, 12)
   float V = 1.0f, e_prev = 0.0f, entry = 0.0f;
   int armed = 0, side = 0, t_open = 0;
   int cnt0 = 0, cnt1 = 0, cnt2 = 0, pushed = 0, pos = 0;
   uint64_t ring = 0;  // 2 bits per window slot
   const float V0 = 1.0f;
+  int64_t bar;  // the bar of step t
+  if (a.t_begin == 0) {
+    // clamp the start so every read stays inside the market buffers
+    const int64_t hi = a.n_bars - (int64_t)a.L - 1;
+    int64_t st = a.starts[n];
+    const bool clamped = st < 0 || st > hi;
+    st = st < 0 ? 0 : (st > hi ? hi : st);
+    if (valid && j == 0) {
+      a.start_used[n] = (int32_t)st;
+      if (clamped && a.counters) atomicAdd(a.counters + 1, 1u);
+    }
+    bar = st;
+  } else {
+    // a later launch of a rollout split over several: the episode's state
+    // as the previous launch left it (every lane of the row reads it)
+    const int32_t* c = a.carry + (int64_t)n * kCarryWords;
+    bar = (int64_t)(uint32_t)c[0] | ((int64_t)c[1] << 32);
+    V = __int_as_float(c[2]);
+    e_prev = __int_as_float(c[3]);
+    entry = __int_as_float(c[4]);
+    armed = c[5]; side = c[6]; t_open = c[7];
+    cnt0 = c[8]; cnt1 = c[9]; cnt2 = c[10]; pushed = c[11]; pos = c[12];
+    ring = (uint64_t)(uint32_t)c[13] | ((uint64_t)(uint32_t)c[14] << 32);
+  }
+
+  f32x4* bufA = s_bufA;
+  f32x4* bufB = s_bufB;
+  f32x4* sbuf = s_state;
+
+  // features and prices of the first step's bar and the one after
+  float f0[4], f1[4];
+  load_features(a.features, bar, j, f0);
+  load_features(a.features, bar + 1, j, f1);
+  float p0 = a.prices[bar], p1 = a.prices[bar + 1];
   lds_barrier();  // operand buffer cleared
   if (j == 2) put_state<BF16>(sbuf, e, 53, ep.spread);  // constant element
 #pragma unroll
@@ -214,8 +228,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   pre[1] = w1.bias[1];
   reg_mfma<0, kTail>(w1, sbuf, pre, lane);
 
-  int64_t bar = st;
-  for (int32_t t = 0; t < a.L; ++t) {
+  for (int32_t t = a.t_begin; t < a.t_end; ++t) {
     const int64_t o = (int64_t)t * a.N + n;
 
     // prefetch two bars ahead (independent of the outcomes), issued before
@@ -476,12 +489,33 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
       }
     }
   }
+  if (a.t_end < a.L && valid && j == 0) {
+    int32_t* c = a.carry + (int64_t)n * kCarryWords;
+    c[0] = (int32_t)(uint32_t)bar; c[1] = (int32_t)(bar >> 32);
+    c[2] = __float_as_int(V); c[3] = __float_as_int(e_prev); c[4] = __float_as_int(entry);
+    c[5] = armed; c[6] = side; c[7] = t_open;
+    c[8] = cnt0; c[9] = cnt1; c[10] = cnt2; c[11] = pushed; c[12] = pos;
+    c[13] = (int32_t)(uint32_t)ring; c[14] = (int32_t)(uint32_t)(ring >> 32);
+  }
 }
 
 }  // namespace
 
+int actor_lds_bytes(bool bf16, bool recycle) {
+  auto kernel = bf16 ? (recycle ? actor_rollout_kernel<true, true> : actor_rollout_kernel<true, false>)
+                     : (recycle ? actor_rollout_kernel<false, true> : actor_rollout_kernel<false, false>);
+  hipFuncAttributes at;
+  if (hipFuncGetAttributes(&at, reinterpret_cast<const void*>(kernel)) != hipSuccess) return -1;
+  return (int)at.sharedSizeBytes;
+}
+
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
   if (a.N <= 0 || a.L <= 0) return hipSuccess;
+  // a launch covers steps [t_begin, t_end); one that starts after step 0
+  // or ends before L reads or leaves the episode state in `carry`
+  if (a.t_begin < 0 || a.t_end > a.L || a.t_begin >= a.t_end ||
+      ((a.t_begin > 0 || a.t_end < a.L) && !a.carry))
+    return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((a.N + kRowsPerWave - 1) / kRowsPerWave);
   auto kernel = a.bf16 ? (a.bars ? actor_rollout_kernel<true, true> : actor_rollout_kernel<true, false>)
                        : (a.bars ? actor_rollout_kernel<false, true> : actor_rollout_kernel<false, false>);

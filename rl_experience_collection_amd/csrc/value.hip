@@ -325,7 +325,7 @@ void value_kernel(ValueArgs a) {
     row_tn(q, t, n);
     const int v = a.actions[(int64_t)t * a.N + n];
     my_act = v < 0 ? 0 : (v >= kActions ? kActions - 1 : v);
-    my_nbar = (a.bars ? a.bars[(int64_t)t * a.N + n] : a.start_used[n] + t) + 1;
+    my_nbar = (a.bars ? a.bars[(int64_t)t * a.N + n] : a.start_used[n] + a.t_off + t) + 1;
   }
   const float partial = q < RT ? a.rewards[my_row] : 0.0f;
   lds_barrier();
@@ -472,6 +472,14 @@ int resident_groups() {
 
 }  // namespace
 
+int value_lds_bytes(bool bf16) {
+  hipFuncAttributes at;
+  const void* k = bf16 ? reinterpret_cast<const void*>(value_kernel<true>)
+                       : reinterpret_cast<const void*>(value_kernel<false>);
+  if (hipFuncGetAttributes(&at, k) != hipSuccess) return -1;
+  return (int)at.sharedSizeBytes;
+}
+
 hipError_t launch_value(const ValueArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.L * a.N;
   if (rows <= 0) return hipSuccess;
@@ -480,13 +488,18 @@ hipError_t launch_value(const ValueArgs& a, hipStream_t st) {
   const int64_t groups = (tiles + RT - 1) / RT;
   const int resident = a.bf16 ? resident_groups<true>() : resident_groups<false>();
   if (resident <= 0) return hipErrorInvalidDevice;
-  const unsigned grid = (unsigned)(groups < resident ? groups : resident);
-  if (!a.sched) return hipErrorInvalidValue;
+  int64_t cap = resident;
+  if (a.max_grid > 0 && a.max_grid < cap) cap = a.max_grid;
+  const unsigned grid = (unsigned)(groups < cap ? groups : cap);
+  if (!a.sched || a.lds_pad < 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, st, a.sched);
+  // (lds_pad reserves LDS the kernel does not use, which only limits where
+  // and how many of its workgroups the dispatcher can place)
+  const unsigned pad = (unsigned)a.lds_pad;
   if (a.bf16)
-    hipLaunchKernelGGL(value_kernel<true>, dim3(grid), dim3(ValueShape<true>::kThreads), 0, st, a);
+    hipLaunchKernelGGL(value_kernel<true>, dim3(grid), dim3(ValueShape<true>::kThreads), pad, st, a);
   else
-    hipLaunchKernelGGL(value_kernel<false>, dim3(grid), dim3(ValueShape<false>::kThreads), 0, st, a);
+    hipLaunchKernelGGL(value_kernel<false>, dim3(grid), dim3(ValueShape<false>::kThreads), pad, st, a);
   return hipGetLastError();
 }
 

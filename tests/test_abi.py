@@ -55,7 +55,7 @@ def test_config_default_values(rx):
 
 def test_config_struct_size_matches_header(rx):
     # 5 + 4 + 7 + 3 + 1 ints, 2 + 2 floats, 1 int, 1 int + 2 floats, 4 floats, 5 + 3 + 1 floats
-    assert C.sizeof(rx.RolloutConfig) == 4 * (5 + 4 + 7 + 3 + 1 + 2 + 2 + 1 + 1 + 2 + 4 + 9 + 1)
+    assert C.sizeof(rx.RolloutConfig) == 4 * (5 + 4 + 7 + 3 + 1 + 2 + 2 + 1 + 1 + 2 + 4 + 9 + 1 + 1)
 
 
 def test_host_side_errors_without_gpu(rx):

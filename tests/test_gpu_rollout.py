@@ -262,3 +262,29 @@ def test_wide_collection_n65536_l64_sampled_episodes(precision):
         _assert_parity(inp, gpu, oracle.rollout(inp, subset=sub), episodes=sub)
     else:
         _bf16_compare(inp, episodes=sub)
+
+
+# ------------------------------------- split rollout, overlapped value pass
+@pytest.mark.parametrize("N,L,precision,recycle",
+                         [(16, 100, 0, 0), (40, 37, 0, 1), (128, 300, 1, 0), (33, 130, 0, 0),
+                          (8192, 64, 0, 0), (128, 500, 1, 1)])
+def test_split_rollout_equals_one_launch(N, L, precision, recycle):
+    """The rollout split into launches of consecutive steps (the episode
+    state carried between them), each part's value pass on the handle's
+    second stream, gives the single launch's outputs bit for bit."""
+    inp = synthdata.ppo_inputs(dict(N=N, L=L, n_bars=3000, seed=300 + N + L), bias_scale=0.1)
+    base = dict(inp["settings"], recycle=recycle)
+    one = run_gpu(inp, settings=dict(base, overlap=0), precision=precision)
+    split = run_gpu(inp, settings=dict(base, overlap=1), precision=precision)
+    for k, v in one.items():
+        if v is not None:
+            assert v.tobytes() == split[k].tobytes(), k
+
+
+def test_split_rollout_matches_oracle():
+    """Parity of the split rollout (3 parts of 45, 45 and 46 steps) with
+    the oracle, clamped starts included."""
+    inp = synthdata.ppo_inputs(dict(N=24, L=136, n_bars=400, seed=41))
+    inp["starts"][5] = 400 - 136 - 1
+    gpu = run_gpu(inp, settings=dict(inp["settings"], overlap=1))
+    _assert_parity(inp, gpu, oracle.rollout(inp))
