@@ -282,6 +282,7 @@ struct rollout_s {
   hipEvent_t values_done = nullptr;   // last value pass finished
   int32_t ov_grid = 0;  // value workgroups while a rollout part runs
   int32_t ov_pad = 0;   // their LDS reservation
+  int32_t last_steps = 0;  // steps of the final part (its pass is not overlapped)
 };
 
 extern "C" {
@@ -424,6 +425,13 @@ int rollout_create(const rollout_config* cfg, const float* const actor[6],
       h->ov_pad = need > 0 ? need : 0;
       h->ov_grid = (int32_t)(cus - blocks);
     }
+    // The final part's value pass runs after the rollout: keep it to at most
+    // one work item (32 fp32 / 128 bf16 rows) per CU, which takes one item's
+    // time, by making that part shorter than the others.
+    const int64_t item_rows = bf16 ? 128 : 32;
+    const int64_t fit = (int64_t)cus * item_rows / cfg->n_episodes;
+    const int64_t even = ((int64_t)cfg->n_steps + h->parts - 1) / h->parts;
+    h->last_steps = (int32_t)(fit < 1 ? 1 : (fit < even ? fit : even));
   }
   rc = gae_reserve(h->gae, cfg->n_steps, cfg->n_episodes, st);
   if (rc) {
@@ -524,9 +532,11 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
     // part k of the rollout, then (on the side stream, once it is done) the
     // value pass over its rows, while part k + 1 runs; the rows of a part
     // are a contiguous block of the [L][N] outputs
+    const int64_t head = L - h->last_steps;  // steps of the parts before the last
     for (int k = 0; k < h->parts; ++k) {
-      const int32_t t0 = (int32_t)((int64_t)L * k / h->parts);
-      const int32_t t1 = (int32_t)((int64_t)L * (k + 1) / h->parts);
+      const bool last = k + 1 == h->parts;
+      const int32_t t0 = (int32_t)(head * k / (h->parts - 1));
+      const int32_t t1 = last ? L : (int32_t)(head * (k + 1) / (h->parts - 1));
       ra.t_begin = t0;
       ra.t_end = t1;
       RL_HIP(rl::launch_actor_rollout(ra, st), "actor rollout launch");
