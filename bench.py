@@ -504,7 +504,10 @@ def main():
                 value=128 * 500 * args.steps / small["wall_s"], unit="experiences/s",
                 ms_per_step=small["wall_s"] * 1000 / args.steps,
                 phases_ms=dict(zip(("actor_rollout", "value_critic_curiosity", "gae_scan"),
-                                   map(float, small["phases_ms"])))),
+                                   map(float, small["phases_ms"]))),
+                note="the rollout runs as 7 launches of consecutive steps; the value pass of "
+                     "each finished part overlaps the next part on the CUs the rollout leaves "
+                     "free, so value_critic_curiosity is only the pass after the rollout"),
             gae_scan_n4096_l2048=dict(
                 value=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / 1e9, unit="GB/s",
                 frac_of_hbm_peak=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / PEAK_HBM,
