@@ -80,6 +80,12 @@ def test_host_side_errors_without_gpu(rx):
     assert lib.rollout_create(C.byref(cfg), arr, arr, arr, C.c_void_p(1), C.c_void_p(1), 100,
                               None, C.byref(h)) == rx.ROLLOUT_EINVAL
     assert "n_bars" in rx.rollout_last_error()
+    cfg = rx.rollout_config_default(16, 100)
+    assert cfg.overlap == -1
+    cfg.overlap = 2
+    assert lib.rollout_create(C.byref(cfg), arr, arr, arr, C.c_void_p(1), C.c_void_p(1), 20000,
+                              None, C.byref(h)) == rx.ROLLOUT_EINVAL
+    assert "overlap" in rx.rollout_last_error()
     assert lib.rollout_collect(None, None, 0, None, None) == rx.ROLLOUT_EINVAL
     assert lib.gae_scan(None, None, None, None, 0, 5, 0.99, 0.95, None, None, None) == rx.ROLLOUT_OK
     assert lib.gae_scan(None, None, None, None, 3, 5, 0.99, 0.95, None, None, None) == rx.ROLLOUT_EINVAL
