@@ -142,7 +142,9 @@ int rollout_config_default(rollout_config *cfg, int32_t n_episodes, int32_t n_st
  * The weights are copied and repacked into the library's own MFMA layout
  * (stream-ordered on hip_stream); the caller may free them afterwards.  The
  * market buffers are BORROWED and must outlive the handle.  Device memory
- * for the packed weights and per-collection scratch is allocated here.
+ * for the packed weights and per-collection scratch is allocated here, and,
+ * when the rollout is split (see `overlap`), a non-blocking stream of the
+ * handle and its events; rollout_destroy releases them.
  * Errors: ROLLOUT_EINVAL (NULL, N or L < 1, dims differ from the built net,
  * n_bars < L + 1, div_window outside 1..32, unknown precision, recycle not
  * 0 or 1),
