@@ -209,17 +209,6 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     float f2[4];
     load_features(a.features, bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1, j, f2);
     const float p2 = a.prices[bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1];
-    // with recycling, the restart bar this step would take if the episode
-    // ended, and its first two bars, loaded ahead like the prefetch above
-    int64_t rbar = 0;
-    float fr0[4], fr1[4], pr0 = 0.0f, pr1 = 0.0f;
-    if constexpr (RECYCLE) {
-      rbar = t + 1 < a.L ? recycle_bar(a.seed, (uint32_t)n, t, a.L, a.n_bars) : bar;
-      load_features(a.features, rbar, j, fr0);
-      load_features(a.features, rbar + 1, j, fr1);
-      pr0 = a.prices[rbar];
-      pr1 = a.prices[rbar + 1];
-    }
 
     // ---- steps 1-3: the state (its operands were written last step) -------
     if (valid) {
@@ -234,6 +223,20 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     // ---- step 4: online Q --------------------------------------------------
     q_network(gw, W, 0, s_opnd, s_bufA, s_bufB, q, lane);
     lds_barrier();
+
+    // with recycling, the restart bar this step would take if the episode
+    // ended, and its first two bars: random rows, so loaded here, where the
+    // row work below (no weight loads) covers their latency before the
+    // target network's first weight wait (the memory counter is in order)
+    int64_t rbar = 0;
+    float fr0[4], fr1[4], pr0 = 0.0f, pr1 = 0.0f;
+    if constexpr (RECYCLE) {
+      rbar = t + 1 < a.L ? recycle_bar(a.seed, (uint32_t)n, t, a.L, a.n_bars) : bar;
+      load_features(a.features, rbar, j, fr0);
+      load_features(a.features, rbar + 1, j, fr1);
+      pr0 = a.prices[rbar];
+      pr1 = a.prices[rbar + 1];
+    }
 
     // ---- step 5: epsilon-greedy on the episode rows -------------------------
     float Q[3];
