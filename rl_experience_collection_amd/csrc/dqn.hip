@@ -205,10 +205,6 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     const int e = 4 * q + (lane >> 4);
     const int j = lane & 15;
 
-    // prefetch two bars ahead (independent of the outcomes)
-    float f2[4];
-    load_features(a.features, bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1, j, f2);
-    const float p2 = a.prices[bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1];
 
     // ---- steps 1-3: the state (its operands were written last step) -------
     if (valid) {
@@ -224,10 +220,15 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     q_network(gw, W, 0, s_opnd, s_bufA, s_bufB, q, lane);
     lds_barrier();
 
-    // with recycling, the restart bar this step would take if the episode
-    // ended, and its first two bars: random rows, so loaded here, where the
-    // row work below (no weight loads) covers their latency before the
-    // target network's first weight wait (the memory counter is in order)
+    // Market rows loaded here, where the row work below (no weight loads)
+    // covers their latency before the target network's first weight wait
+    // (the memory counter is in order; at the top of the step the online
+    // network's weight waits waited for them): the bar two ahead
+    // (independent of the outcomes) and, with recycling, the restart bar
+    // this step would take if the episode ended, and its first two bars.
+    float f2[4];
+    load_features(a.features, bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1, j, f2);
+    const float p2 = a.prices[bar + 2 < a.n_bars ? bar + 2 : a.n_bars - 1];
     int64_t rbar = 0;
     float fr0[4], fr1[4], pr0 = 0.0f, pr1 = 0.0f;
     if constexpr (RECYCLE) {
