@@ -276,6 +276,10 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
 
     // the step's draw depends only on (seed, episode, step)
     const float u = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 0u);
+    // the layer chain runs at a raised wave priority, so where the two
+    // workgroups of a CU meet, the one in its chain issues first (the draw
+    // and environment below return to the base priority)
+    __builtin_amdgcn_s_setprio(2);
 
     // ---- step 3: actor, a quarter of each layer per wave ------------------
     // (MFMA layout: lane l computes rows l % 16 of the workgroup)
@@ -312,6 +316,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     }
     lds_barrier();
 
+    __builtin_amdgcn_s_setprio(0);
     // first-layer feature part of the next step: its k-steps are spread
     // over the draw and environment below (one k-step per point, pinned by
     // scheduling fences), so the MFMAs run while the VALU works
