@@ -276,9 +276,9 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
 
     // the step's draw depends only on (seed, episode, step)
     const float u = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 0u);
-    // the layer chain runs at a raised wave priority, so where the two
-    // workgroups of a CU meet, the one in its chain issues first (the draw
-    // and environment below return to the base priority)
+    // the layer chain and the draw run at a raised wave priority, so where
+    // the two workgroups of a CU meet, the one in them issues first (the
+    // environment step below returns to the base priority)
     __builtin_amdgcn_s_setprio(2);
 
     // ---- step 3: actor, a quarter of each layer per wave ------------------
@@ -316,7 +316,6 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     }
     lds_barrier();
 
-    __builtin_amdgcn_s_setprio(0);
     // first-layer feature part of the next step: its k-steps are spread
     // over the draw and environment below (one k-step per point, pinned by
     // scheduling fences), so the MFMAs run while the VALU works
@@ -385,6 +384,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     ps.template step<5>(pre);
     bad = row_max_i(bad);
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- step 6: portfolio (exposure fraction of equity, turnover cost) ---
     const int xi = act_a / 9;
     const int oi = (act_a % 9) / 3;
