@@ -239,6 +239,11 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
       pr1 = a.prices[rbar + 1];
     }
 
+    // The row work (epsilon-greedy and the environment here, the TD and the
+    // stores below) runs at a raised wave priority and the networks at the
+    // base one: where the four workgroups of a CU meet, the one doing its
+    // short row work issues first and returns to its weight stream sooner.
+    __builtin_amdgcn_s_setprio(2);
     // ---- step 5: epsilon-greedy on the episode rows -------------------------
     float Q[3];
     bool ok[3];
@@ -347,6 +352,7 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     if (j == 0) s_act[e] = act;
     lds_barrier();
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- step 11: target Q of the next state --------------------------------
     q_network(gw, W, 1, s_next, s_bufA, s_bufB, q, lane);
     lds_barrier();  // every wave is done reading bufA
@@ -371,6 +377,7 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     }
     lds_barrier();
 
+    __builtin_amdgcn_s_setprio(2);
     // ---- steps 12-14: target max, curiosity bonus, reward, TD, stores ------
     float Qt[3];
     bool okt[3];
@@ -406,6 +413,7 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
       if (bad && a.counters) atomicAdd(a.counters, 1u);
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- step 15: reset on done; the bar pointer keeps advancing ------------
     if (done) {
       V = 1.0f;
