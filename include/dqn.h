@@ -52,7 +52,8 @@ typedef struct {
   int32_t value_dims[3];     /* 128, 64, 1 */
   int32_t advantage_dims[3]; /* 128, 64, 45 */
   int32_t cur_dims[3];       /* 99 (= 54 + 45 one-hot), 128, 51 */
-  float epsilon;             /* exploration probability, in [0, 1] (0.1) */
+  float epsilon;             /* exploration probability, in [0, 1] (0.1);
+                                dqn_set_epsilon changes it between launches */
   float gamma;               /* TD discount (0.99) */
   float priority_alpha;      /* priority = |td|^alpha (0.6) */
   float profit_take;         /* the environment settings, as in rollout_config */
@@ -124,6 +125,16 @@ int dqn_create(const dqn_config *cfg, const float *const online[12],
  * network (a target sync passes only `target`).  Stream-ordered. */
 int dqn_set_weights(dqn_handle h, const float *const online[12], const float *const target[12],
                     const float *const curiosity[4], void *hip_stream);
+
+/* Set the exploration probability of later collections ("GPU Pipeline Phase
+ * 2b", Concerns and Mitigations, Epsilon Decay: epsilon is a scalar handed to
+ * each launch, decayed on the host between rounds).  The value is copied into
+ * the kernel arguments when dqn_collect enqueues, so it applies to every
+ * collection enqueued after this call returns, on any stream, and to none
+ * enqueued before; no device work, no synchronisation.  Not safe against a
+ * concurrent dqn_collect on the same handle from another host thread.
+ * Errors: ROLLOUT_EINVAL (NULL handle, epsilon outside [0, 1] or NaN). */
+int dqn_set_epsilon(dqn_handle h, float epsilon);
 
 /* Collect one batch of N x L transitions.  episode_starts = [N] i32 device
  * array; a start outside [0, n_bars - L - 1] is clamped on the device and

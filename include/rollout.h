@@ -117,10 +117,12 @@ typedef struct {
   float *advantages;  /* [L][N] f32, GAE with V(L) = 0 */
   float *returns;     /* [L][N] f32, advantages + values */
   float *logits;      /* [L][N][45] f32 or NULL (debug / parity only) */
-  uint32_t *counters; /* [2] or NULL: reset then accumulated by this call:
+  uint32_t *counters; /* [3] or NULL: reset then accumulated by this call:
                          [0] non-finite events (a step's logit vector, its
                          value or its reward), [1] episodes whose start had
-                         to be clamped */
+                         to be clamped, [2] GAE look-backs that gave up
+                         waiting (never expected: see gae_scan; the
+                         advantages and returns they reach are NaN) */
   void *const *phase_events; /* NULL or [4] caller-created hipEvent_t (as
                          void*), recorded on hip_stream before the rollout
                          kernel, after it (its last part when split), after
@@ -154,9 +156,13 @@ int rollout_create(const rollout_config *cfg, const float *const actor[6],
                    const float *features, const float *prices, int64_t n_bars,
                    void *hip_stream, rollout_handle *out);
 
-/* Replace the weights (same layout as rollout_create).  Stream-ordered: a
- * collection enqueued later on the same stream sees the new weights; one
- * enqueued earlier on another stream must be complete first. */
+/* Replace the weights after a policy update (PPO CUDA Pipeline Design,
+ * Trainer Integration: the actor, critic and curiosity weights are synced to
+ * the collector after every update).  Same layout as rollout_create; the
+ * weights are repacked on the device.  Stream-ordered: a collection enqueued
+ * later on the same stream sees the new weights; one enqueued earlier on
+ * another stream must be complete first.
+ * Errors: ROLLOUT_EINVAL (NULL handle, array or tensor), ROLLOUT_EHIP. */
 int rollout_set_weights(rollout_handle h, const float *const actor[6],
                         const float *const critic[12], const float *const curiosity[4],
                         void *hip_stream);
@@ -182,6 +188,14 @@ int rollout_collect(rollout_handle h, const int32_t *episode_starts, uint64_t se
  * per-(device, stream) scratch for the inter-chunk carries, allocated on the
  * first call for that stream; concurrent calls on the same stream are
  * serialised by the stream itself.
+ * Rollouts longer than 512 steps are cut into chunks whose carries pass
+ * between workgroups through a bounded wait.  A wait that reaches its bound
+ * (never expected: every wait is on a workgroup that is already running)
+ * ends, and its chunk's carry is NaN, so the advantages and returns of that
+ * episode from the chunk back to step 0 are NaN rather than silently wrong;
+ * rollout_collect also counts such events in counters[2].  The environment
+ * variable ROLLOUT_GAE_SPIN_LIMIT, read at each call, lowers the bound (to
+ * exercise this path); it cannot raise it.
  * Errors: ROLLOUT_EINVAL (NULL pointer, negative size), ROLLOUT_ENOMEM,
  * ROLLOUT_EHIP. */
 int gae_scan(const float *rewards, const float *values, const uint8_t *dones,

@@ -9,7 +9,8 @@ The functions carry the C names:
     rollout_config_default, rollout_create, rollout_set_weights,
     rollout_collect, gae_scan, rollout_destroy, rollout_last_error
     (include/rollout.h), dqn_config_default, dqn_create,
-    dqn_set_weights, dqn_collect, dqn_destroy (include/dqn.h), and
+    dqn_set_weights, dqn_set_epsilon, dqn_collect, dqn_destroy
+    (include/dqn.h), and
     per_create, per_sample, per_gather, per_update, per_destroy
     (include/per.h),
 plus helpers: `alloc_outputs`, `alloc_dqn_outputs` and the `Collector` and
@@ -28,7 +29,8 @@ ROLLOUT_FP32, ROLLOUT_BF16 = 0, 1
 STATE_DIM, N_ACTIONS, N_FEATURES = 54, 45, 51
 EXPORTED = ("rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
             "gae_scan", "rollout_destroy", "rollout_last_error",
-            "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_collect", "dqn_destroy",
+            "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_set_epsilon",
+            "dqn_collect", "dqn_destroy",
             "per_create", "per_sample", "per_gather", "per_update", "per_destroy")
 
 
@@ -116,6 +118,7 @@ def load_library(path: str = LIB_PATH):
     L.dqn_create.argtypes = [C.POINTER(DqnConfig), C.POINTER(vp), C.POINTER(vp), C.POINTER(vp),
                              vp, vp, i64, vp, C.POINTER(vp)]
     L.dqn_set_weights.argtypes = [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp]
+    L.dqn_set_epsilon.argtypes = [vp, C.c_float]
     L.dqn_collect.argtypes = [vp, vp, C.c_uint64, C.POINTER(DqnOutputs), vp]
     L.dqn_destroy.argtypes = [vp]
     L.dqn_destroy.restype = None
@@ -128,7 +131,7 @@ def load_library(path: str = LIB_PATH):
     L.per_destroy.restype = None
     for name in ("rollout_config_default", "rollout_create", "rollout_set_weights",
                  "rollout_collect", "gae_scan", "dqn_config_default", "dqn_create",
-                 "dqn_set_weights", "dqn_collect", "per_create", "per_sample", "per_gather",
+                 "dqn_set_weights", "dqn_set_epsilon", "dqn_collect", "per_create", "per_sample", "per_gather",
                  "per_update"):
         getattr(L, name).restype = C.c_int
     _lib = L
@@ -236,7 +239,7 @@ def alloc_outputs(N: int, L: int, device="cuda", logits: bool = False, counters:
         advantages=torch.empty((L, N), **f32),
         returns=torch.empty((L, N), **f32),
         logits=torch.empty((L, N, N_ACTIONS), **f32) if logits else None,
-        counters=torch.zeros(2, dtype=torch.int32, device=device) if counters else None,
+        counters=torch.zeros(3, dtype=torch.int32, device=device) if counters else None,
     )
     return out
 
@@ -257,7 +260,7 @@ def rollout_collect(handle: int, episode_starts, seed: int, outputs: dict, strea
     o.advantages = _dev_ptr(outputs["advantages"], torch.float32, (L, N), "advantages")
     o.returns = _dev_ptr(outputs["returns"], torch.float32, (L, N), "returns")
     o.logits = _dev_ptr(outputs.get("logits"), torch.float32, (L, N, N_ACTIONS), "logits")
-    o.counters = _dev_ptr(outputs.get("counters"), torch.int32, (2,), "counters")
+    o.counters = _dev_ptr(outputs.get("counters"), torch.int32, (3,), "counters")
     ev = None
     if phase_events is not None:
         if len(phase_events) != 4:
@@ -407,6 +410,11 @@ def dqn_set_weights(handle: int, online=None, target=None, curiosity=None, strea
         _nullable_array(curiosity, CURIOSITY_SHAPES, "curiosity"), _stream(stream)))
 
 
+def dqn_set_epsilon(handle: int, epsilon: float):
+    """Exploration probability of the collections enqueued after this call."""
+    _check(load_library().dqn_set_epsilon(C.c_void_p(handle), float(epsilon)))
+
+
 def alloc_dqn_outputs(N: int, L: int, device="cuda", next_states: bool = True,
                       q_values: bool = False, explored: bool = True, counters: bool = True):
     import torch
@@ -475,6 +483,9 @@ class DqnCollector:
 
     def set_weights(self, online=None, target=None, curiosity=None, stream=None):
         dqn_set_weights(self.handle, online, target, curiosity, stream)
+
+    def set_epsilon(self, epsilon: float):
+        dqn_set_epsilon(self.handle, epsilon)
 
     def collect(self, episode_starts, seed: int, outputs: dict | None = None, q_values=False,
                 stream=None, phase_events=None) -> dict:

@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -72,7 +73,7 @@ int gae_prepare(GaeScratch& s, const rl::GaeShape& shape, int32_t N, hipStream_t
     }
     s.mem = static_cast<char*>(p);
     s.bytes = need;
-    RL_HIP(hipMemsetAsync(s.mem, 0, 256, st), "hipMemsetAsync(gae ticket)");
+    RL_HIP(rl::zero_words(reinterpret_cast<uint32_t*>(s.mem), 64, st), "clear gae ticket");
     s.ticket_base = 0;
     relayout = true;
   }
@@ -80,8 +81,9 @@ int gae_prepare(GaeScratch& s, const rl::GaeShape& shape, int32_t N, hipStream_t
   // changes (or the epoch wraps), so that stale words never carry the
   // current epoch.
   if (relayout || s.epoch >= (1u << 28)) {
-    RL_HIP(hipMemsetAsync(s.mem + 256, 0, rl::gae_words_bytes(shape.nk, N), st),
-           "hipMemsetAsync(gae words)");
+    RL_HIP(rl::zero_words(reinterpret_cast<uint32_t*>(s.mem + 256),
+                          rl::gae_words_bytes(shape.nk, N) / 4, st),
+           "clear gae words");
     s.epoch = 0;
     s.nk = shape.nk;
     s.nc = shape.nc;
@@ -89,15 +91,27 @@ int gae_prepare(GaeScratch& s, const rl::GaeShape& shape, int32_t N, hipStream_t
   }
   s.epoch += 1;
   view->ticket = reinterpret_cast<uint32_t*>(s.mem);
-  view->error = reinterpret_cast<uint32_t*>(s.mem + 4);
   view->words = reinterpret_cast<uint64_t*>(s.mem + 256);
   view->ticket_base = s.ticket_base;
   view->epoch = s.epoch;
   return ROLLOUT_OK;
 }
 
-int gae_run(GaeScratch& s, const rl::GaeArgs& a, hipStream_t st) {
+// Polls of a GAE look-back before it gives up: the built-in limit, unless
+// the environment variable ROLLOUT_GAE_SPIN_LIMIT sets another (a test of the
+// give-up path lowers it; it never needs raising).
+uint32_t gae_spin_limit() {
+  const char* v = std::getenv("ROLLOUT_GAE_SPIN_LIMIT");
+  if (!v || !*v) return rl::kGaeSpinLimit;
+  char* end = nullptr;
+  const unsigned long x = std::strtoul(v, &end, 10);
+  if (end == v || *end) return rl::kGaeSpinLimit;
+  return x > rl::kGaeSpinLimit ? rl::kGaeSpinLimit : (uint32_t)x;
+}
+
+int gae_run(GaeScratch& s, rl::GaeArgs a, hipStream_t st) {
   if (a.L == 0 || a.N == 0) return ROLLOUT_OK;
+  a.spin_limit = gae_spin_limit();
   const rl::GaeShape shape = rl::gae_shape(a.L, a.N);
   if (shape.tiles() >= (int64_t)1 << 31) return fail(ROLLOUT_EINVAL, "gae_scan: too many tiles");
   rl::GaeScratchView view;
@@ -473,7 +487,7 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const int32_t N = h->cfg.n_episodes, L = h->cfg.n_steps;
   int rc = ROLLOUT_OK;
-  if (out->counters) RL_HIP(hipMemsetAsync(out->counters, 0, 2 * sizeof(uint32_t), st), "counters");
+  if (out->counters) RL_HIP(rl::zero_words(out->counters, 3, st), "clear counters");
   auto mark = [&](int i) -> hipError_t {
     if (!out->phase_events || !out->phase_events[i]) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(out->phase_events[i]), st);
@@ -574,6 +588,8 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   ga.lambda = h->cfg.lambda;
   ga.advantages = out->advantages;
   ga.returns = out->returns;
+  ga.status = out->counters ? out->counters + 2 : nullptr;
+  ga.spin_limit = rl::kGaeSpinLimit;
   rc = gae_run(h->gae, ga, st);
   if (rc) return rc;
   RL_HIP(mark(3), "hipEventRecord(phase 3)");
@@ -591,19 +607,23 @@ int gae_scan(const float* rewards, const float* values, const uint8_t* dones,
   int dev = -1;
   RL_HIP(hipGetDevice(&dev), "hipGetDevice");
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  rl::GaeArgs ga{rewards, values, dones, last_values, L, N, gamma, lambda, advantages, returns};
+  rl::GaeArgs ga{rewards, values,     dones,   last_values, L,
+                 N,       gamma,      lambda,  advantages,  returns,
+                 nullptr, rl::kGaeSpinLimit};
   std::lock_guard<std::mutex> lock(g_gae_mu);
   return gae_run(gae_cache()[std::make_pair(dev, st)], ga, st);
 }
 
 void rollout_destroy(rollout_handle h) {
   if (!h) return;
+  // value passes of a split rollout may still run on the handle's own
+  // stream, reading the packed weights and the scratch freed below
+  if (h->side) (void)hipStreamSynchronize(h->side);
   if (h->weights) (void)hipFree(h->weights);
   if (h->start_used) (void)hipFree(h->start_used);
   if (h->value_sched) (void)hipFree(h->value_sched);
   if (h->bars) (void)hipFree(h->bars);
   if (h->gae.mem) (void)hipFree(h->gae.mem);
-  if (h->side) (void)hipStreamSynchronize(h->side);
   for (hipEvent_t ev : h->part_done) (void)hipEventDestroy(ev);
   if (h->values_done) (void)hipEventDestroy(h->values_done);
   if (h->side) (void)hipStreamDestroy(h->side);
@@ -709,6 +729,14 @@ int dqn_set_weights(dqn_handle h, const float* const online[12], const float* co
   return ROLLOUT_OK;
 }
 
+int dqn_set_epsilon(dqn_handle h, float epsilon) {
+  if (!(epsilon >= 0.0f && epsilon <= 1.0f))
+    return fail(ROLLOUT_EINVAL, "epsilon must be in [0, 1]");
+  if (!h) return fail(ROLLOUT_EINVAL, "handle is NULL");
+  h->cfg.epsilon = epsilon;
+  return ROLLOUT_OK;
+}
+
 int dqn_collect(dqn_handle h, const int32_t* episode_starts, uint64_t seed, const dqn_outputs* out,
                 void* hip_stream) {
   if (!h) return fail(ROLLOUT_EINVAL, "handle is NULL");
@@ -722,7 +750,7 @@ int dqn_collect(dqn_handle h, const int32_t* episode_starts, uint64_t seed, cons
   if (dev != h->device)
     return fail(ROLLOUT_EINVAL, "handle was created on device %d, current device is %d", h->device, dev);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  if (out->counters) RL_HIP(hipMemsetAsync(out->counters, 0, 2 * sizeof(uint32_t), st), "counters");
+  if (out->counters) RL_HIP(rl::zero_words(out->counters, 2, st), "clear counters");
   auto mark = [&](int i) -> hipError_t {
     if (!out->phase_events || !out->phase_events[i]) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(out->phase_events[i]), st);

@@ -45,7 +45,6 @@ namespace rl {
 namespace {
 
 constexpr uint32_t kAgg = 1u, kIncl = 2u;
-constexpr uint32_t kSpinLimit = 1u << 24;
 constexpr int kWalk = 8;   // aggregates held before waiting on an inclusive
 constexpr int kBatch = 4;  // later super-chunks read per look-back round
 
@@ -70,7 +69,8 @@ template <int COLS>
 __global__ __launch_bounds__(64 * kGaeWaves) void gae_scan_kernel(
     const float* __restrict__ rew, const float* __restrict__ val, const uint8_t* __restrict__ don,
     const float* __restrict__ last_values, int32_t L, int32_t N, float gamma, float gl,
-    float* __restrict__ adv, float* __restrict__ ret, GaeScratchView sc, int32_t NC, int32_t NK) {
+    float* __restrict__ adv, float* __restrict__ ret, GaeScratchView sc, int32_t NC, int32_t NK,
+    uint32_t* __restrict__ status, uint32_t spin_limit) {
   constexpr int kSlots = gae_slots(COLS);
   constexpr int kSuper = gae_super(COLS);
   __shared__ uint32_t s_tile;
@@ -211,8 +211,14 @@ __global__ __launch_bounds__(64 * kGaeWaves) void gae_scan_kernel(
             m += got;
             if (found) break;
             if (got == 0) {
-              if (++spins > kSpinLimit) {  // never expected: keeps the grid draining
-                __hip_atomic_fetch_add(sc.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (++spins > spin_limit) {
+                // never expected: the wait ends so the grid drains, and the
+                // carry is NaN, so this column's results from here back to
+                // step 0 are NaN instead of silently wrong
+                if (status)
+                  __hip_atomic_fetch_add(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                x = __builtin_nanf("");
+                m = 0;
                 break;
               }
               __builtin_amdgcn_s_sleep(1);
@@ -261,7 +267,24 @@ hipError_t gae_launch(const GaeArgs& a, const GaeShape& shape, const GaeScratchV
   auto kernel = shape.cols == 32 ? gae_scan_kernel<32> : gae_scan_kernel<64>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)shape.tiles()), dim3(64 * kGaeWaves), 0, stream,
                      a.rewards, a.values, a.dones, a.last_values, a.L, a.N, a.gamma,
-                     a.gamma * a.lambda, a.advantages, a.returns, sc, shape.nc, shape.nk);
+                     a.gamma * a.lambda, a.advantages, a.returns, sc, shape.nc, shape.nk,
+                     a.status, a.spin_limit);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ void zero_words_kernel(uint32_t* p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+}  // namespace
+
+hipError_t zero_words(uint32_t* p, size_t words, hipStream_t stream) {
+  if (words == 0) return hipSuccess;
+  const size_t blocks = (words + 255) / 256;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256),
+                     0, stream, p, words);
   return hipGetLastError();
 }
 

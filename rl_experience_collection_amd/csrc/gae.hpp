@@ -30,7 +30,16 @@ struct GaeArgs {
   float gamma, lambda;
   float* advantages;
   float* returns;
+  // nullable: incremented once per look-back that gave up waiting (never
+  // expected; the carry of that super-chunk is NaN, so the advantages and
+  // returns of its column from there back to step 0 are NaN)
+  uint32_t* status;
+  // polls of a look-back before it gives up (kGaeSpinLimit unless the host
+  // sets another, e.g. to exercise the give-up path)
+  uint32_t spin_limit;
 };
+
+constexpr uint32_t kGaeSpinLimit = 1u << 24;
 
 struct GaeShape {
   int32_t cols;    // episodes per column (32 or 64)
@@ -42,7 +51,6 @@ struct GaeShape {
 struct GaeScratchView {
   uint64_t* words;     // [nk * N]: value | (epoch << 3 | has_done << 2 | status) << 32
   uint32_t* ticket;    // monotonically increasing ticket counter
-  uint32_t* error;     // spin-limit events (never expected)
   uint32_t ticket_base;
   uint32_t epoch;      // < 2^29
 };
@@ -53,6 +61,9 @@ inline size_t gae_words_bytes(int32_t nk, int32_t N) {
 inline size_t gae_scratch_bytes(int32_t nk, int32_t N) { return 256 + gae_words_bytes(nk, N); }
 
 GaeShape gae_shape(int32_t L, int32_t N);
+// Zero `words` 32-bit words at p, stream-ordered, with a kernel (a memset node
+// is avoided so that the launch sequence can be captured into a graph).
+hipError_t zero_words(uint32_t* p, size_t words, hipStream_t stream);
 hipError_t gae_launch(const GaeArgs& a, const GaeShape& shape, const GaeScratchView& sc,
                       hipStream_t stream);
 

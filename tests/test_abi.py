@@ -31,8 +31,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
          "gae_scan", "rollout_destroy", "rollout_last_error",
-         "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_collect", "dqn_destroy",
-         "per_create", "per_sample", "per_gather", "per_update", "per_destroy"])
+         "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_set_epsilon",
+         "dqn_collect", "dqn_destroy", "per_create", "per_sample", "per_gather", "per_update", "per_destroy"])
 
 
 def test_library_exports_every_declared_symbol(rx):
@@ -129,6 +129,18 @@ def test_dqn_host_side_errors_without_gpu(rx):
     assert "trunk" in rx.rollout_last_error()
     assert lib.dqn_collect(None, None, 0, None, None) == rx.ROLLOUT_EINVAL
     lib.dqn_destroy(None)
+
+
+def test_dqn_set_epsilon_rejects_values_outside_unit_interval(rx):
+    """Epsilon Decay ("GPU Pipeline Phase 2b", Concerns and Mitigations): a
+    per-launch probability; the value is checked before the handle."""
+    lib = rx.load_library()
+    for bad in (-0.01, 1.0001, float("nan"), float("inf"), -float("inf")):
+        assert lib.dqn_set_epsilon(None, bad) == rx.ROLLOUT_EINVAL
+        assert "epsilon" in rx.rollout_last_error()
+    for ok in (0.0, 0.05, 1.0):
+        assert lib.dqn_set_epsilon(None, ok) == rx.ROLLOUT_EINVAL
+        assert "handle" in rx.rollout_last_error()
 
 
 def test_per_host_side_errors_without_gpu(rx):

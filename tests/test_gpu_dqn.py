@@ -18,17 +18,15 @@ import pytest
 
 import oracle
 import synthdata
-from parity import close_mask, gpu_available
+from parity import compare_dqn, gpu_available, record
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
 
-INT_KEYS = ("actions", "explored", "dones", "barrier")
-FLOAT_KEYS = ("states", "next_states", "q_values", "q_taken", "q_next_max", "rewards")
-TIE = 1e-5
-
-
-def run_gpu(inputs: dict, q_values: bool = True, seed: int | None = None, target=None):
+def run_gpu(inputs: dict, q_values: bool = True, seed: int | None = None, target=None,
+            epsilons=None):
+    """One DQN collection (or, with epsilons, one per value on the same
+    handle, epsilon set by dqn_set_epsilon before each; a list of results)."""
     import torch
     import rl_experience_collection_amd as rx
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -39,69 +37,24 @@ def run_gpu(inputs: dict, q_values: bool = True, seed: int | None = None, target
                           dqn=inputs["dqn"])
     if target is not None:
         col.set_weights(target=[dev(x) for x in target])
-    out = col.collect(dev(inputs["starts"].astype(np.int32)),
-                      inputs["sampler_seed"] if seed is None else seed, q_values=q_values)
-    torch.cuda.synchronize()
-    res = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+    starts = dev(inputs["starts"].astype(np.int32))
+    seed = inputs["sampler_seed"] if seed is None else seed
+    res = []
+    for eps in (epsilons or [None]):
+        if eps is not None:
+            col.set_epsilon(eps)
+        out = col.collect(starts, seed, q_values=q_values)
+        torch.cuda.synchronize()
+        res.append({k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()})
     col.close()
-    return res
+    return res if epsilons else res[0]
 
 
-def compare(inputs: dict, gpu: dict, orc: dict, episodes=None, report=None):
-    L, N = gpu["actions"].shape
-    gamma, alpha = inputs["dqn"]["gamma"], inputs["dqn"]["alpha"]
-    fails, flagged = [], []
-    for n in (range(N) if episodes is None else episodes):
-        o = orc
-        mism = np.nonzero(gpu["actions"][:, n] != orc["actions"][:, n])[0]
-        if mism.size:
-            t = int(mism[0])
-            q = orc["q_values"][t, n] if orc.get("q_values") is not None else None
-            scale = 1.0 + (float(np.abs(q).max()) if q is not None
-                           else abs(float(orc["q_taken"][t, n])))
-            tie = (orc["explored"][t, n] == 0 and gpu["explored"][t, n] == 0
-                   and orc["q_gap"][t, n] < TIE * scale)
-            if not tie:
-                fails.append(f"episode {n} step {t}: action {gpu['actions'][t, n]} vs "
-                             f"{orc['actions'][t, n]} (gap {orc['q_gap'][t, n]:.3g})")
-                continue
-            flagged.append((n, t, float(orc["q_gap"][t, n])))
-            forced = np.zeros((L, N), np.int32)
-            forced[:, n] = gpu["actions"][:, n]
-            o = oracle.dqn_rollout(inputs, forced_actions=forced, subset=[n])
-        for k in INT_KEYS:
-            if gpu.get(k) is None:
-                continue
-            if not np.array_equal(gpu[k][:, n], o[k][:, n]):
-                t = int(np.nonzero(gpu[k][:, n] != o[k][:, n])[0][0])
-                fails.append(f"episode {n}: {k} differs first at step {t}")
-        for k in FLOAT_KEYS:
-            if gpu.get(k) is None or o.get(k) is None:
-                continue
-            ok = close_mask(gpu[k][:, n], o[k][:, n])
-            if not ok.all():
-                idx = tuple(np.argwhere(~ok)[0])
-                fails.append(f"episode {n}: {k} at {idx}: gpu {gpu[k][:, n][idx]!r} "
-                             f"oracle {o[k][:, n][idx]!r}")
-        scale = (np.abs(o["rewards"][:, n]) + gamma * np.abs(o["q_next_max"][:, n])
-                 + np.abs(o["q_taken"][:, n])).astype(np.float64)
-        err = np.abs(gpu["td"][:, n].astype(np.float64) - o["td"][:, n])
-        if not (err <= 1e-5 + 1e-4 * scale).all():
-            t = int(np.argmax(err - 1e-4 * scale))
-            fails.append(f"episode {n}: td at {t}: gpu {gpu['td'][t, n]!r} oracle {o['td'][t, n]!r}")
-    # the priority is |td|^alpha of the GPU's own td, everywhere
-    want = np.abs(gpu["td"].astype(np.float64)) ** alpha
-    if not np.allclose(gpu["priorities"], want, rtol=5e-6, atol=1e-30):
-        fails.append("priorities differ from |td|^alpha")
-    if report is not None:
-        report["flagged"] = flagged
-    return fails
-
-
-def assert_parity(inputs, gpu, orc, episodes=None, max_flags=None):
+def assert_parity(inputs, gpu, orc, episodes=None, max_flags=None, name="dqn"):
     rep = {}
-    fails = compare(inputs, gpu, orc, episodes, rep)
-    print(f"near-tie flags: {len(rep['flagged'])} {rep['flagged'][:5]}")
+    fails = compare_dqn(inputs, gpu, orc, episodes, rep)
+    record(name, N=inputs["N"], L=inputs["L"], epsilon=inputs["dqn"]["epsilon"],
+           flagged=len(rep["flagged"]), first_flags=rep["flagged"][:5], failures=len(fails))
     assert not fails, "\n".join(fails[:20])
     if max_flags is not None:
         assert len(rep["flagged"]) <= max_flags
@@ -132,6 +85,27 @@ def test_dqn_all_random_actions_bit_exact():
     assert gpu["explored"].all()
     assert np.array_equal(gpu["actions"], orc["actions"])
     assert_parity(inp, gpu, orc, max_flags=0)
+
+
+def test_dqn_epsilon_per_launch():
+    """Epsilon Decay ("GPU Pipeline Phase 2b", Concerns and Mitigations):
+    epsilon is a per-launch scalar decayed by the host between rounds.  Three
+    launches on one handle at 0.1, 0.05 and 0.3 each match the oracle at that
+    epsilon; the explored steps of each launch are those whose stream-1 draw
+    lies below its epsilon, so they nest."""
+    inp = small(40, 70, 11)
+    epss = [0.1, 0.05, 0.3]
+    runs = run_gpu(inp, epsilons=epss)
+    for eps, gpu in zip(epss, runs):
+        e = dict(inp, dqn=dict(inp["dqn"], epsilon=eps))
+        assert_parity(e, gpu, oracle.dqn_rollout(e), name=f"dqn_epsilon_{eps}")
+    u1 = oracle.uniform(inp["sampler_seed"], np.tile(np.arange(40), 70),
+                        np.repeat(np.arange(70), 40), 1).reshape(70, 40)
+    for eps, gpu in zip(epss, runs):
+        # exploration decided by the draw alone where the trajectories agree
+        # up to the step; at t = 0 they always do
+        assert np.array_equal(gpu["explored"][0], (u1[0] < np.float32(eps)).astype(np.uint8))
+    assert runs[1]["explored"].sum() < runs[0]["explored"].sum() < runs[2]["explored"].sum()
 
 
 def test_dqn_all_greedy():
@@ -183,7 +157,7 @@ def test_dqn_full_size_n16384_l500_sampled_episodes():
     gpu = run_gpu(inp, q_values=False)
     sub = sorted(set(list(range(0, 16384, 1021)) + [16383, 16382, 15, 16, 8191, 8192]))
     orc = oracle.dqn_rollout(inp, subset=sub, with_q=False)
-    assert_parity(inp, gpu, orc, episodes=sub)
+    assert_parity(inp, gpu, orc, episodes=sub, name="dqn_n16384_l500_sampled")
     assert np.array_equal(gpu["dones"], (gpu["barrier"] > 0).astype(np.uint8))
     for k in ("rewards", "td", "priorities", "q_taken", "q_next_max"):
         assert np.isfinite(gpu[k]).all(), k

@@ -49,10 +49,15 @@ def check_sample(p, batch, seed, beta=0.4):
     gi, gw = gpu_sample(p, batch, seed, beta)
     oi, ow, gap = oracle.per_sample(p, batch, seed, beta)
     mism = np.nonzero(gi != oi)[0]
+    nz = np.nonzero(p > 0)[0]  # the indices that carry weight
     for b in mism:
         assert gap[b] < TIE, f"draw {b}: gpu {gi[b]} oracle {oi[b]} gap {gap[b]:.3g}"
-        assert abs(int(gi[b]) - int(oi[b])) <= 2048, b
-        assert p[gi[b]] > 0, b
+        # a near tie lies on the boundary between the oracle's index and the
+        # previous or next index that carries weight: the GPU may take that one
+        k = int(np.searchsorted(nz, oi[b]))
+        assert k < nz.size and nz[k] == oi[b], b
+        near = [int(nz[j]) for j in (k - 1, k + 1) if 0 <= j < nz.size]
+        assert int(gi[b]) in near, f"draw {b}: gpu {gi[b]} not a weighted neighbour of {oi[b]}"
     ok = np.setdiff1d(np.arange(batch), mism)
     assert np.allclose(gw[ok], ow[ok], rtol=1e-6, atol=0), np.abs(gw - ow).max()
     if batch:

@@ -5,17 +5,26 @@ import pytest
 
 import oracle
 import synthdata
-from parity import compare_rollout, gpu_available, run_gpu, close_mask
+from parity import (bf16_floors, close_mask, compare_bf16, compare_rollout, gpu_available,
+                    record, run_gpu)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
 
 
-def _assert_parity(inp, gpu, orc, episodes=None, **kw):
+def _assert_parity(inp, gpu, orc, episodes=None, name=None, **kw):
+    """The fp32 protocol; the near-tie flags and the oracle's near-boundary
+    draws go to the parity record.  A flagged episode's first mismatch lies
+    within 1e-6 of a CDF boundary by construction, so flags never exceed the
+    near-boundary draws."""
     rep = {}
     fails = compare_rollout(inp, gpu, orc, episodes=episodes, report=rep, **kw)
-    print(f"near-tie flags: {len(rep['flagged'])} {rep['flagged'][:5]}")
+    record(name or "rollout", N=inp["N"], L=inp["L"], episodes=rep["draws"] // inp["L"],
+           flagged=len(rep["flagged"]), near_boundary_draws=rep.get("near_boundary_draws"),
+           draws=rep["draws"], first_flags=rep["flagged"][:5], failures=len(fails))
     assert not fails, "\n".join(fails[:20])
+    if rep.get("near_boundary_draws") is not None:
+        assert len(rep["flagged"]) <= rep["near_boundary_draws"]
     return rep
 
 
@@ -38,22 +47,25 @@ def test_ragged_sizes(N, L):
 
 def test_default_workload_n128_l500():
     inp = synthdata.ppo_inputs("ppo_n128_l500")
-    rep = _assert_parity(inp, run_gpu(inp), oracle.rollout(inp))
+    rep = _assert_parity(inp, run_gpu(inp), oracle.rollout(inp), name="ppo_n128_l500_fp32")
     assert len(rep["flagged"]) <= 64
 
 
-def test_chip_workload_n8192_l500_sampled_episodes():
-    """Full-size launch; the oracle recomputes a spread of episodes."""
+def test_chip_workload_n8192_l500_all_episodes():
+    """Full-size launch, every one of the 8192 episodes against the oracle
+    (the oracle on all host cores: about 35 s on 16).  Near-boundary draws
+    expected: 4,096,000 draws x 44 boundaries x 2e-6 = about 360."""
     inp = synthdata.ppo_inputs("ppo_n8192_l500")
     gpu = run_gpu(inp, logits=True)
-    sub = sorted(set(list(range(0, 8192, 331)) + [8191, 8190, 15, 16]))
-    orc = oracle.rollout(inp, subset=sub)
-    _assert_parity(inp, gpu, orc, episodes=sub)
+    orc = oracle.rollout(inp)
+    rep = _assert_parity(inp, gpu, orc, name="ppo_n8192_l500_fp32_all")
+    assert 100 < rep["near_boundary_draws"] < 1000
     # every (t, n): integer codes consistent, finite floats
     assert np.array_equal(gpu["dones"], (gpu["barrier"] > 0).astype(np.uint8))
     for k in ("values", "rewards", "advantages", "returns", "log_probs"):
         assert np.isfinite(gpu[k]).all(), k
     assert np.array_equal(gpu["returns"], (gpu["advantages"] + gpu["values"]).astype(np.float32))
+    assert int(gpu["counters"][0]) == 0 and int(gpu["counters"][2]) == 0
 
 
 def test_gae_inside_collect_matches_oracle_gae_on_gpu_streams():
@@ -135,56 +147,36 @@ def test_sampler_chi_square_on_gpu():
 
 
 # --------------------------------------------------------------------------- bf16
-BF16_RTOL, BF16_ATOL = 2e-2, 1e-5
-
-
-def _bf16_compare(inp, episodes=None):
+def _bf16_compare(inp, episodes=None, name="bf16"):
     """GPU bf16 collection vs the oracle's bf16 mode with the GPU's actions
-    teacher-forced: integers bit-exact; floats within 1e-5 + 2e-2 * scale,
-    where the scale is max(|o|, rms of that output over the compared set) (for
-    logits the row's largest |logit|): a bf16 result is a sum whose terms are
-    rounded to 8 bits, so a one-ulp flip of an activation near a rounding
-    boundary (different fp32 summation order) moves it by an amount that
-    follows the terms' size, not a cancelled sum.  Element-wise-relative
-    outliers are counted and reported."""
+    teacher-forced, by the bf16 gate of tests/parity.py: integers bit-exact,
+    states at the fp32 tolerance, every other float element-wise within
+    floor + 2e-2 |o| up to a fixed outlier budget, the floor being the
+    measured effect of one bf16 rounding decision taken the other way.  The
+    free-running action agreement is recorded, not gated."""
     gpu = run_gpu(inp, precision=1)
     free = oracle.rollout(inp, precision=oracle.BF16, subset=episodes)
     cols = list(range(inp["N"])) if episodes is None else list(episodes)
     agree = float((free["actions"][:, cols] == gpu["actions"][:, cols]).mean())
     forced = oracle.rollout(inp, precision=oracle.BF16, forced_actions=gpu["actions"], subset=episodes)
-    for k in ("dones", "barrier"):
-        assert np.array_equal(gpu[k][:, cols], forced[k][:, cols]), k
-    worst = {}
-    for k, ko in (("states", "states"), ("logits", "logits"), ("log_probs", "log_probs"),
-                  ("values", "values"), ("rewards", "rewards"), ("advantages", "adv"),
-                  ("returns", "ret")):
-        g, o = gpu[k][:, cols].astype(np.float64), forced[ko][:, cols].astype(np.float64)
-        rms = float(np.sqrt((o * o).mean()))
-        if k == "logits":
-            # a logit vector is one dot product per action: relative to the row's scale
-            scale = np.broadcast_to(np.abs(o).max(axis=-1, keepdims=True), o.shape)
-        else:
-            scale = np.maximum(np.abs(o), rms)
-        err = np.abs(g - o) - (BF16_ATOL + BF16_RTOL * scale)
-        outl = np.abs(g - o) > BF16_ATOL + BF16_RTOL * np.abs(o)
-        worst[k] = (float(err.max()), int((err > 0).sum()), int(outl.sum()), g.size)
-    print(f"bf16: free-running action agreement {agree:.4f}; per output (worst excess, "
-          f"beyond tolerance, element-wise-relative outliers, count): {worst}")
-    for k, (mx, nbad, _, n) in worst.items():
-        assert nbad == 0, f"{k}: {nbad} of {n} beyond tolerance (worst excess {mx:.3g})"
+    floors = bf16_floors(inp, forced, cols)
+    fails, stats = compare_bf16(inp, gpu, forced, cols, floors)
+    record(name, N=inp["N"], L=inp["L"], episodes=len(cols), action_agreement=agree,
+           outputs=stats, failures=fails)
+    assert not fails, "\n".join(fails)
     return agree
 
 
 def test_bf16_tiny_teacher_forced():
     inp = synthdata.ppo_inputs("ppo_n16_l100", bias_scale=0.1)
-    assert _bf16_compare(inp) > 0.5
+    assert _bf16_compare(inp, name="bf16_n16_l100") > 0.5
 
 
 @pytest.mark.parametrize("N,L", [(1, 1), (47, 3), (33, 64), (129, 9)])
 def test_bf16_ragged_sizes(N, L):
     """Row counts below one 128-row work item, ragged tails, several items."""
     spec = dict(N=N, L=L, n_bars=3000, seed=200 + N + L)
-    _bf16_compare(synthdata.ppo_inputs(spec, bias_scale=0.1))
+    _bf16_compare(synthdata.ppo_inputs(spec, bias_scale=0.1), name=f"bf16_n{N}_l{L}")
 
 
 def test_bf16_episodes_reaching_the_last_bar():
@@ -197,8 +189,8 @@ def test_bf16_episodes_reaching_the_last_bar():
 
 def test_bf16_chip_workload_sampled_episodes():
     inp = synthdata.ppo_inputs("ppo_n8192_l500")
-    sub = sorted(set(list(range(0, 8192, 397)) + [8191]))
-    _bf16_compare(inp, episodes=sub)
+    sub = sorted(set(list(range(0, 8192, 97)) + [8191]))
+    assert _bf16_compare(inp, episodes=sub, name="bf16_n8192_l500_sampled") > 0.9
 
 
 # ----------------------------------------------------------------- recycling
@@ -247,7 +239,7 @@ def test_recycling_chip_workload_n8192_l500_sampled_episodes():
 
 
 def test_recycling_bf16_teacher_forced():
-    assert _bf16_compare(_recycled("ppo_n16_l100", bias_scale=0.1)) > 0.5
+    assert _bf16_compare(_recycled("ppo_n16_l100", bias_scale=0.1), name="bf16_recycle_n16_l100") > 0.5
 
 
 @pytest.mark.parametrize("precision", [0, 1])
@@ -261,7 +253,7 @@ def test_wide_collection_n65536_l64_sampled_episodes(precision):
         gpu = run_gpu(inp, logits=True)
         _assert_parity(inp, gpu, oracle.rollout(inp, subset=sub), episodes=sub)
     else:
-        _bf16_compare(inp, episodes=sub)
+        _bf16_compare(inp, episodes=sub, name="bf16_n65536_l64_sampled")
 
 
 # ------------------------------------- split rollout, overlapped value pass
@@ -288,3 +280,65 @@ def test_split_rollout_matches_oracle():
     inp["starts"][5] = 400 - 136 - 1
     gpu = run_gpu(inp, settings=dict(inp["settings"], overlap=1))
     _assert_parity(inp, gpu, oracle.rollout(inp))
+
+
+# -------------------------------------------------------- failure reporting
+def _nan_planted(which):
+    inp = synthdata.ppo_inputs(dict(N=40, L=50, n_bars=3000, seed=51), bias_scale=0.1)
+    w = inp["weights"]
+    if which == "critic":
+        w["critic"][11] = np.array([np.nan], np.float32)  # the output bias
+    else:
+        w["actor"][4] = w["actor"][4].copy()
+        w["actor"][4][7, 3] = np.nan  # one weight of the logit layer
+    return inp
+
+
+@pytest.mark.parametrize("which", ["critic", "actor"])
+@pytest.mark.parametrize("precision", [0, 1])
+def test_nonfinite_weights_are_counted_and_the_collection_completes(which, precision):
+    """A NaN in the critic's output bias makes every value non-finite; a NaN
+    in one weight of the actor's logit layer makes logit 7 of every step
+    non-finite.  The collection completes with valid actions and codes, and
+    counters[0] reports the steps (every one of the L x N)."""
+    inp = _nan_planted(which)
+    gpu = run_gpu(inp, precision=precision)
+    L, N = inp["L"], inp["N"]
+    assert int(gpu["counters"][0]) == L * N
+    assert ((gpu["actions"] >= 0) & (gpu["actions"] < 45)).all()
+    assert np.isin(gpu["barrier"], [0, 1, 2, 3]).all()
+    if which == "critic":
+        assert np.isnan(gpu["values"]).all() and np.isnan(gpu["advantages"]).all()
+        assert np.isfinite(gpu["log_probs"]).all()
+    else:
+        assert np.isnan(gpu["logits"][:, :, 7]).all()
+        assert np.isfinite(gpu["values"]).all()
+        # a NaN logit weighs nothing in the draw: action 7 is never taken
+        assert not (gpu["actions"] == 7).any()
+    record(f"nonfinite_{which}_{'bf16' if precision else 'fp32'}", counters=gpu["counters"].tolist())
+
+
+def test_gae_lookback_give_up_is_reported_not_silent(monkeypatch):
+    """Rollouts longer than 512 steps chain their GAE chunks through bounded
+    waits.  With the bound lowered to one poll (from the host, so every wait
+    still ends) some chunks may give up; a chunk that does counts itself in
+    counters[2] and poisons its column with NaN.  Every advantage is either
+    the oracle's (within the fp32 tolerance) or NaN, never silently wrong,
+    and the NaN columns are exactly as many as counters[2] allows."""
+    monkeypatch.setenv("ROLLOUT_GAE_SPIN_LIMIT", "1")
+    inp = synthdata.ppo_inputs(dict(N=300, L=1300, n_bars=5000, seed=52), bias_scale=0.1)
+    gpu = run_gpu(inp, logits=False)
+    A, R = oracle.gae(gpu["rewards"], gpu["values"], gpu["dones"], 0.99, 0.95)
+    nan = np.isnan(gpu["advantages"])
+    ok = close_mask(gpu["advantages"], A) | nan
+    assert ok.all()
+    assert np.array_equal(nan, np.isnan(gpu["returns"]))
+    gave_up = int(gpu["counters"][2])
+    cols = int(nan.any(axis=0).sum())
+    assert (gave_up == 0) == (cols == 0)
+    assert cols <= gave_up
+    record("gae_give_up_spin1", gave_up=gave_up, nan_columns=cols)
+    monkeypatch.delenv("ROLLOUT_GAE_SPIN_LIMIT")
+    gpu2 = run_gpu(inp, logits=False)
+    assert int(gpu2["counters"][2]) == 0
+    assert close_mask(gpu2["advantages"], A).all()

@@ -39,67 +39,8 @@ import pytest
 import oracle
 import synthdata
 
-U = 2.0 ** -24
-LAMBDA = 8.0
-
-
-def bf16(x):
-    """Round to the nearest bfloat16 (ties to even), returned as float64."""
-    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
-    return b.astype(np.uint32).view(np.float32).astype(np.float64)
-
-
-def dense(W, b, x, var, relu, bf=False):
-    """One [out, in] layer on a batch of rows x [R, in] whose entries carry
-    error variance proxies var.  Returns (y, var) in fp64."""
-    W64 = np.asarray(W, np.float64)
-    if bf:
-        W64 = bf16(W)
-        # an input known exactly (var == 0, the stored state) rounds the same
-        # on both sides; one with an error may land on the neighbouring value
-        var = np.where(var > 0, var + (2.0 ** -7 * np.abs(x)) ** 2, 0.0)
-        x = bf16(x)
-    b64 = np.asarray(b, np.float64)
-    y = x @ W64.T + b64
-    k = W64.shape[1]
-    absum = np.abs(x) @ np.abs(W64).T + np.abs(b64)
-    var = var @ (W64 * W64).T + (2 * k + 2) * U * U * absum * absum
-    if relu:
-        y = np.maximum(y, 0.0)
-    return y, var
-
-
-def mlp(ws, x, relu_mask, bf=False):
-    """Chain of layers: ws = [W1, b1, W2, b2, ...]; relu_mask[l] says whether
-    layer l is followed by ReLU."""
-    return _chain(ws, x, np.zeros_like(x), relu_mask, bf)
-
-
-def _chain(ws, x, var, relu_mask, bf=False):
-    for l in range(len(ws) // 2):
-        x, var = dense(ws[2 * l], ws[2 * l + 1], x, var, relu_mask[l], bf)
-    return x, var
-
-
-ACTOR_RELU = (True, True, False)
-CRITIC_RELU = (True, True, True, True, True, False)
-CURIOSITY_RELU = (True, False)
-
-
-def dueling(ws, s, trunk_relu=(True, True), head_relu=(True, True)):
-    """Q of a dueling net on rows s and its variance proxy; ws = [trunk 1,
-    trunk 2, value 1, value 2, advantage 1, advantage 2] as (W, b) pairs."""
-    h, vh = mlp(ws[0:4], s, trunk_relu)
-    v, vv = _chain(ws[4:8], h, vh, (head_relu[0], False))
-    a, va = _chain(ws[8:12], h, vh, (head_relu[1], False))
-    mean = a.sum(axis=1, keepdims=True) / 45.0
-    vmean = (va.sum(axis=1, keepdims=True)
-             + 92 * U * U * np.abs(a).sum(axis=1, keepdims=True) ** 2) / 45.0 ** 2
-    q = v + (a - mean)
-    # (x + y + z)^2 <= 3 (x^2 + y^2 + z^2): the three parts are correlated
-    vq = 3 * (vv + va + vmean) + 3 * U * U * (np.abs(v) + np.abs(a) + np.abs(mean)) ** 2
-    return q, vq
+from nets_ref import (ACTOR_RELU, CRITIC_RELU, CURIOSITY_RELU, LAMBDA, U, bf16, dense,  # noqa: F401
+                      dueling, mlp, _chain)
 
 
 def without(mask, l):
