@@ -194,8 +194,9 @@ int rollout_collect(rollout_handle h, const int32_t *episode_starts, uint64_t se
  * ends, and its chunk's carry is NaN, so the advantages and returns of that
  * episode from the chunk back to step 0 are NaN rather than silently wrong;
  * rollout_collect also counts such events in counters[2].  The environment
- * variable ROLLOUT_GAE_SPIN_LIMIT, read at each call, lowers the bound (to
- * exercise this path); it cannot raise it.
+ * variable ROLLOUT_GAE_SPIN_LIMIT, read at each call, lowers the bound (a
+ * number of polls; it cannot raise it); 0 makes every chunk but the latest
+ * give up without waiting, which exercises this path deterministically.
  * Errors: ROLLOUT_EINVAL (NULL pointer, negative size), ROLLOUT_ENOMEM,
  * ROLLOUT_EHIP. */
 int gae_scan(const float *rewards, const float *values, const uint8_t *dones,

@@ -183,7 +183,10 @@ __global__ __launch_bounds__(64 * kGaeWaves) void gae_scan_kernel(
           int m = 0;
           uint32_t spins = 0;
           float x = 0.0f;
-          for (;;) {
+          // a limit of 0 polls gives up without waiting (set by the host
+          // only to exercise the reporting below)
+          bool gave_up = spin_limit == 0;
+          while (!gave_up) {
             uint64_t wd[kBatch];
 #pragma unroll
             for (int q = 0; q < kBatch; ++q) {
@@ -212,17 +215,20 @@ __global__ __launch_bounds__(64 * kGaeWaves) void gae_scan_kernel(
             if (found) break;
             if (got == 0) {
               if (++spins > spin_limit) {
-                // never expected: the wait ends so the grid drains, and the
-                // carry is NaN, so this column's results from here back to
-                // step 0 are NaN instead of silently wrong
-                if (status)
-                  __hip_atomic_fetch_add(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                x = __builtin_nanf("");
-                m = 0;
+                gave_up = true;
                 break;
               }
               __builtin_amdgcn_s_sleep(1);
             }
+          }
+          if (gave_up) {
+            // never expected: the wait ended so the grid drains, and the
+            // carry is NaN, so this column's results from here back to
+            // step 0 are NaN instead of silently wrong
+            if (status)
+              __hip_atomic_fetch_add(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            x = __builtin_nanf("");
+            m = 0;
           }
 #pragma unroll
           for (int z = kWalk - 1; z >= 0; --z)

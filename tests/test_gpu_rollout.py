@@ -319,26 +319,34 @@ def test_nonfinite_weights_are_counted_and_the_collection_completes(which, preci
 
 
 def test_gae_lookback_give_up_is_reported_not_silent(monkeypatch):
-    """Rollouts longer than 512 steps chain their GAE chunks through bounded
-    waits.  With the bound lowered to one poll (from the host, so every wait
-    still ends) some chunks may give up; a chunk that does counts itself in
-    counters[2] and poisons its column with NaN.  Every advantage is either
-    the oracle's (within the fp32 tolerance) or NaN, never silently wrong,
-    and the NaN columns are exactly as many as counters[2] allows."""
-    monkeypatch.setenv("ROLLOUT_GAE_SPIN_LIMIT", "1")
-    inp = synthdata.ppo_inputs(dict(N=300, L=1300, n_bars=5000, seed=52), bias_scale=0.1)
+    """Rollouts longer than 512 steps chain 256-step GAE chunks through
+    bounded waits.  With the bound set to zero polls from the host (so every
+    kernel still ends normally), every chunk but the latest gives up: each
+    episode counts one event per such chunk in counters[2], and its
+    advantages and returns before the latest chunk are NaN, never silently
+    wrong; the latest chunk needs no carry and matches the oracle.  Then the
+    standalone scan on the same streams, and the default bound again."""
+    import torch
+    import rl_experience_collection_amd as rx
+    N, L = 300, 1300
+    nk, last = -(-L // 256), (L - 1) // 256 * 256
+    monkeypatch.setenv("ROLLOUT_GAE_SPIN_LIMIT", "0")
+    inp = synthdata.ppo_inputs(dict(N=N, L=L, n_bars=5000, seed=52), bias_scale=0.1)
     gpu = run_gpu(inp, logits=False)
     A, R = oracle.gae(gpu["rewards"], gpu["values"], gpu["dones"], 0.99, 0.95)
-    nan = np.isnan(gpu["advantages"])
-    ok = close_mask(gpu["advantages"], A) | nan
-    assert ok.all()
-    assert np.array_equal(nan, np.isnan(gpu["returns"]))
-    gave_up = int(gpu["counters"][2])
-    cols = int(nan.any(axis=0).sum())
-    assert (gave_up == 0) == (cols == 0)
-    assert cols <= gave_up
-    record("gae_give_up_spin1", gave_up=gave_up, nan_columns=cols)
+    assert int(gpu["counters"][2]) == N * (nk - 1)
+    assert np.isnan(gpu["advantages"][:last]).all() and np.isnan(gpu["returns"][:last]).all()
+    assert close_mask(gpu["advantages"][last:], A[last:]).all()
+    assert close_mask(gpu["returns"][last:], R[last:]).all()
+    dev = {k: torch.from_numpy(gpu[k]).cuda() for k in ("rewards", "values", "dones")}
+    Ag, Rg = torch.empty_like(dev["rewards"]), torch.empty_like(dev["rewards"])
+    rx.gae_scan(dev["rewards"], dev["values"], dev["dones"], None, 0.99, 0.95, Ag, Rg)
+    torch.cuda.synchronize()
+    Ag = Ag.cpu().numpy()
+    assert np.isnan(Ag[:last]).all() and close_mask(Ag[last:], A[last:]).all()
+    record("gae_give_up_zero_polls", N=N, L=L, gave_up=int(gpu["counters"][2]),
+           nan_rows=int(last))
     monkeypatch.delenv("ROLLOUT_GAE_SPIN_LIMIT")
     gpu2 = run_gpu(inp, logits=False)
     assert int(gpu2["counters"][2]) == 0
-    assert close_mask(gpu2["advantages"], A).all()
+    assert close_mask(gpu2["advantages"], A).all() and close_mask(gpu2["returns"], R).all()
