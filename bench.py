@@ -303,29 +303,58 @@ def time_weight_stream(rows, bf16, reps):
                 bytes_per_launch=total, TBps=total / (ms * 1e-3) / 1e12)
 
 
-def cpu_baseline(inp, n_episodes):
-    """The oracle as it stands on a bounded episode subset of the same workload."""
-    import numpy as np
-    import oracle
-
-    sub = np.linspace(0, inp["N"] - 1, n_episodes).astype(np.int32)
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
-    t0 = time.perf_counter()
-    oracle.rollout(inp, subset=sub, n_threads=threads, with_logits=False)
-    dt = time.perf_counter() - t0
-    exp = n_episodes * inp["L"]
-    cpu = "unknown"
+def _host_cpu():
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return dict(value=exp / dt, unit="experiences/s", cores=threads, kind="oracle",
-                sample=f"{n_episodes} of {inp['N']} episodes x {inp['L']} steps "
-                       f"({exp} experiences, {dt:.1f} s) of the N={inp['N']} L={inp['L']} "
-                       f"workload; episodes are independent; host CPU: {cpu}")
+    return "unknown"
+
+
+def _threads():
+    return int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+
+
+def cpu_baseline(inp, n_episodes, precision=0, dqn=False):
+    """The oracle as it stands on a bounded episode subset of the same
+    workload (all of it when n_episodes >= N)."""
+    import numpy as np
+    import oracle
+
+    n_episodes = min(n_episodes, inp["N"])
+    sub = None if n_episodes == inp["N"] else np.linspace(0, inp["N"] - 1, n_episodes).astype(np.int32)
+    threads = _threads()
+    t0 = time.perf_counter()
+    if dqn:
+        oracle.dqn_rollout(inp, subset=sub, n_threads=threads, with_q=False, with_next=False)
+    else:
+        oracle.rollout(inp, precision=precision, subset=sub, n_threads=threads, with_logits=False)
+    dt = time.perf_counter() - t0
+    exp = n_episodes * inp["L"]
+    part = ("all" if sub is None else f"{n_episodes} of") + f" {inp['N']} episodes"
+    return dict(value=exp / dt, unit="transitions/s" if dqn else "experiences/s", cores=threads,
+                kind="oracle",
+                sample=f"{part} x {inp['L']} steps ({exp} {'transitions' if dqn else 'experiences'}, "
+                       f"{dt:.1f} s) of the N={inp['N']} L={inp['L']} "
+                       f"{'DQN ' if dqn else ''}workload{' in the bf16 mode' if precision else ''}"
+                       f"; episodes are independent; host CPU: {_host_cpu()}")
+
+
+def cpu_baseline_gae(spec):
+    """The oracle's GAE scan (one host thread: it is a plain loop) on the
+    whole standalone workload."""
+    import oracle
+    import synthdata
+    r, v, d = synthdata.gae_inputs(spec["N"], spec["L"], spec["seed"])
+    t0 = time.perf_counter()
+    oracle.gae(r, v, d, 0.99, 0.95)
+    dt = time.perf_counter() - t0
+    n = spec["N"] * spec["L"]
+    return dict(value=GAE_BYTES * n / dt / 1e9, unit="GB/s", elements_per_s=n / dt, cores=1,
+                kind="oracle", sample=f"all {n} elements (N={spec['N']} L={spec['L']}, {dt:.3f} s); "
+                                      f"host CPU: {_host_cpu()}")
 
 
 def recycled(inp):
@@ -424,10 +453,11 @@ def main():
     ws_f = time_weight_stream(N * L, False, 5)
     ws_b = time_weight_stream(N * L, True, 5)
     log("timing the DQN collection N=16384 L=500 ...")
-    dq = time_dqn(synthdata.dqn_inputs("dqn_n16384_l500"), args.steps, args.warmup)
+    dq_inp = synthdata.dqn_inputs("dqn_n16384_l500")
+    dq = time_dqn(dq_inp, args.steps, args.warmup)
     dq_exp = dq["N"] * dq["L"]
     log("timing the DQN collection N=16384 L=500 with episode recycling ...")
-    dqr = time_dqn(recycled(synthdata.dqn_inputs("dqn_n16384_l500")), args.steps, args.warmup)
+    dqr = time_dqn(recycled(dq_inp), args.steps, args.warmup)
     log("timing prioritized replay on 8,192,000 priorities ...")
     per = time_per(dq_exp, 4096, max(args.steps, 20))
     per_step = per["sample_ms"] + per["gather_ms"] + per["update_ms"]
@@ -447,6 +477,18 @@ def main():
                     weight_stream_bound=dict(ms=ws_f["ms"], TBps=ws_f["TBps"],
                                              bytes_per_launch=ws_f["bytes_per_launch"]))
     mlp_util = MLP_FLOP * N * L / ((t_roll + t_val) * 1e-3) / PEAK_FP32_MFMA
+    # N=128: 8 workgroups of 16 episodes hold 8 CUs through the sequential
+    # chain; the actor's work against the fp32 MFMA peak of those CUs
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    active = -(-128 // 16)
+    t_small_actor = float(small["phases_ms"][0])
+    small_achieved = ACTOR_FLOP * 128 * 500 / (t_small_actor * 1e-3)
+    small_roof = dict(bound="mfma", kernel="actor_rollout_kernel (sequential chain, 8 workgroups)",
+                      achieved=small_achieved / 1e12, unit="TFLOP/s",
+                      peak=PEAK_FP32_MFMA * active / cus / 1e12, active_cus=active,
+                      frac=small_achieved / (PEAK_FP32_MFMA * active / cus),
+                      actor_ms=t_small_actor, flop_per_launch=ACTOR_FLOP * 128 * 500,
+                      note="peak = the fp32 MFMA peak scaled to the CUs the rollout occupies")
     gae_in = 17 * N * L / (t_gae * 1e-3)
 
     line = dict(
@@ -505,6 +547,7 @@ def main():
                 ms_per_step=small["wall_s"] * 1000 / args.steps,
                 phases_ms=dict(zip(("actor_rollout", "value_critic_curiosity", "gae_scan"),
                                    map(float, small["phases_ms"]))),
+                roofline=small_roof,
                 note="the rollout runs as 7 launches of consecutive steps; the value pass of "
                      "each finished part overlaps the next part on the CUs the rollout leaves "
                      "free, so value_critic_curiosity is only the pass after the rollout"),
@@ -528,6 +571,17 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         line["cpu_baseline"] = cpu_baseline(big_inp, args.cpu_episodes)
+        also = line["also"]
+        also["ppo_collect_n128_l500_fp32"]["cpu_baseline"] = cpu_baseline(
+            synthdata.ppo_inputs("ppo_n128_l500"), 128)
+        also["ppo_collect_n8192_l500_bf16"]["cpu_baseline"] = cpu_baseline(
+            big_inp, max(args.cpu_episodes // 4, 16), precision=1)
+        also["gae_scan_n4096_l2048"]["cpu_baseline"] = cpu_baseline_gae(
+            synthdata.WORKLOADS["gae_n4096_l2048"])
+        also["gae_scan_n8192_l500"]["cpu_baseline"] = cpu_baseline_gae(
+            dict(N=N, L=L, seed=spec["seed"]))
+        also["dqn_collect_n16384_l500_fp32"]["cpu_baseline"] = cpu_baseline(
+            dq_inp, max(args.cpu_episodes // 2, 16), dqn=True)
     print(json.dumps(line), flush=True)
 
 
