@@ -203,6 +203,26 @@ int gae_scan(const float *rewards, const float *values, const uint8_t *dones,
              const float *last_values, int32_t L, int32_t N, float gamma, float lambda,
              float *advantages, float *returns, void *hip_stream);
 
+/* gae_scan without any device allocation, for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, layout, results (bit for bit) and errors as
+ * gae_scan.  Rollouts longer than 512 steps pass carries between 256-step
+ * chunks through a scratch that here is a fixed array in the library's
+ * device memory (4 MiB + 256 bytes, held by each device the library runs on
+ * until the process ends) instead of memory allocated on first use: such a
+ * scan needs ceil(L / 256) * N <= 524288 (e.g. L = 2048 with N <= 65536);
+ * larger ones are rejected with ROLLOUT_EINVAL before anything is enqueued.
+ * Rollouts of at most 512 steps need no scratch and have no such limit.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (its ticket counter and tagged carries; what must start at
+ * zero is cleared by a kernel on the caller's stream, never by a memset):
+ * calls that overlap on one device race, so callers serialise them, e.g. on
+ * one stream.  Errors: as gae_scan, plus ROLLOUT_EINVAL for a scan beyond the
+ * scratch and ROLLOUT_EHIP if the array's address cannot be resolved. */
+int gae_scan_noalloc(const float *rewards, const float *values, const uint8_t *dones,
+                     const float *last_values, int32_t L, int32_t N, float gamma, float lambda,
+                     float *advantages, float *returns, void *hip_stream);
+
 /* Release a collector and its device memory (NULL-safe).  Work already
  * enqueued that uses the handle must be complete. */
 void rollout_destroy(rollout_handle h);

@@ -7,7 +7,8 @@ fails to load, importing the functions raises.
 
 The functions carry the C names:
     rollout_config_default, rollout_create, rollout_set_weights,
-    rollout_collect, gae_scan, rollout_destroy, rollout_last_error
+    rollout_collect, gae_scan, gae_scan_noalloc, rollout_destroy,
+    rollout_last_error
     (include/rollout.h), dqn_config_default, dqn_create,
     dqn_set_weights, dqn_set_epsilon, dqn_collect, dqn_destroy
     (include/dqn.h), and
@@ -28,7 +29,7 @@ ROLLOUT_OK, ROLLOUT_EINVAL, ROLLOUT_ENOMEM, ROLLOUT_EHIP, ROLLOUT_ENOTIMPL = 0, 
 ROLLOUT_FP32, ROLLOUT_BF16 = 0, 1
 STATE_DIM, N_ACTIONS, N_FEATURES = 54, 45, 51
 EXPORTED = ("rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
-            "gae_scan", "rollout_destroy", "rollout_last_error",
+            "gae_scan", "gae_scan_noalloc", "rollout_destroy", "rollout_last_error",
             "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_set_epsilon",
             "dqn_collect", "dqn_destroy",
             "per_create", "per_sample", "per_gather", "per_update", "per_destroy")
@@ -110,6 +111,7 @@ def load_library(path: str = LIB_PATH):
     L.rollout_set_weights.argtypes = [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp]
     L.rollout_collect.argtypes = [vp, vp, C.c_uint64, C.POINTER(RolloutOutputs), vp]
     L.gae_scan.argtypes = [vp, vp, vp, vp, i32, i32, C.c_float, C.c_float, vp, vp, vp]
+    L.gae_scan_noalloc.argtypes = L.gae_scan.argtypes
     L.rollout_destroy.argtypes = [vp]
     L.rollout_destroy.restype = None
     L.rollout_last_error.argtypes = []
@@ -130,7 +132,8 @@ def load_library(path: str = LIB_PATH):
     L.per_destroy.argtypes = [vp]
     L.per_destroy.restype = None
     for name in ("rollout_config_default", "rollout_create", "rollout_set_weights",
-                 "rollout_collect", "gae_scan", "dqn_config_default", "dqn_create",
+                 "rollout_collect", "gae_scan", "gae_scan_noalloc", "dqn_config_default",
+                 "dqn_create",
                  "dqn_set_weights", "dqn_set_epsilon", "dqn_collect", "per_create", "per_sample", "per_gather",
                  "per_update"):
         getattr(L, name).restype = C.c_int
@@ -273,10 +276,14 @@ def rollout_collect(handle: int, episode_starts, seed: int, outputs: dict, strea
 
 
 def gae_scan(rewards, values, dones, last_values, gamma: float, lam: float, advantages, returns,
-             stream=None):
+             stream=None, noalloc: bool = False):
+    """noalloc=True calls gae_scan_noalloc (no device allocation; its scratch
+    is a fixed array of the library)."""
     import torch
     L, N = rewards.shape
-    _check(load_library().gae_scan(
+    lib = load_library()
+    fn = lib.gae_scan_noalloc if noalloc else lib.gae_scan
+    _check(fn(
         _dev_ptr(rewards, torch.float32, (L, N), "rewards"),
         _dev_ptr(values, torch.float32, (L, N), "values"),
         _dev_ptr(dones, torch.uint8, (L, N), "dones"),

@@ -22,6 +22,10 @@
 #include "gae.hpp"
 #include "pack.hpp"
 
+// The fixed scratch of gae_scan_noalloc (see NoAllocDevice below): 4 MiB +
+// 256 bytes per device.
+static __device__ __align__(256) unsigned char scratch[256 + ((size_t)1 << 19) * 8];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -50,6 +54,7 @@ int hip_fail(hipError_t e, const char* what) {
 struct GaeScratch {
   char* mem = nullptr;
   size_t bytes = 0;
+  bool fixed = false;  // memory not owned by the scratch: never reallocated
   int32_t nk = 0, nc = 0, n = 0;
   uint32_t ticket_base = 0;
   uint32_t epoch = 0;
@@ -59,6 +64,8 @@ int gae_prepare(GaeScratch& s, const rl::GaeShape& shape, int32_t N, hipStream_t
                 rl::GaeScratchView* view) {
   const size_t need = rl::gae_scratch_bytes(shape.nk, N);
   bool relayout = (shape.nk != s.nk || N != s.n);
+  if (s.bytes < need && s.fixed)
+    return fail(ROLLOUT_EINVAL, "gae scratch: %zu bytes needed, %zu available", need, s.bytes);
   if (s.bytes < need) {
     if (s.mem) {
       hipError_t e = hipFree(s.mem);
@@ -114,9 +121,12 @@ int gae_run(GaeScratch& s, rl::GaeArgs a, hipStream_t st) {
   a.spin_limit = gae_spin_limit();
   const rl::GaeShape shape = rl::gae_shape(a.L, a.N);
   if (shape.tiles() >= (int64_t)1 << 31) return fail(ROLLOUT_EINVAL, "gae_scan: too many tiles");
-  rl::GaeScratchView view;
-  int rc = gae_prepare(s, shape, a.N, st, &view);
-  if (rc) return rc;
+  // a single chunk per episode passes no carry: no scratch
+  rl::GaeScratchView view{};
+  if (shape.nk > 1) {
+    const int rc = gae_prepare(s, shape, a.N, st, &view);
+    if (rc) return rc;
+  }
   hipError_t e = rl::gae_launch(a, shape, view, st);
   if (e != hipSuccess) return hip_fail(e, "gae_scan launch");
   if (shape.nk > 1) s.ticket_base += (uint32_t)shape.tiles();  // tickets are taken only then
@@ -126,11 +136,29 @@ int gae_run(GaeScratch& s, rl::GaeArgs a, hipStream_t st) {
 // Reserve the scratch for the largest tile grid an (L, N) scan can use.
 int gae_reserve(GaeScratch& s, int32_t L, int32_t N, hipStream_t st) {
   const rl::GaeShape shape = rl::gae_shape(L, N);
+  if (shape.nk == 1) return ROLLOUT_OK;  // no carries to keep
   rl::GaeScratchView view;
   const int rc = gae_prepare(s, shape, N, st, &view);
   s.epoch -= 1;  // nothing was launched with this epoch
   return rc;
 }
+
+// Scratch of gae_scan_noalloc, for callers that cannot allocate: the
+// inter-chunk carries of one scan (a 256-byte header holding the ticket
+// counter, then 8 bytes per episode and 256-step chunk), at most
+// kNoAllocCarries of them.  Each device holds its own copy until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device.
+constexpr size_t kNoAllocCarries = (size_t)1 << 19;
+constexpr size_t kNoAllocBytes = 256 + kNoAllocCarries * 8;
+constexpr int kMaxDevices = 64;
+
+struct NoAllocDevice {
+  bool ready = false;
+  GaeScratch s;  // s.mem: this device's address of `scratch`
+};
+std::mutex g_noalloc_mu;
+NoAllocDevice g_noalloc[kMaxDevices];
 
 std::mutex g_gae_mu;
 std::map<std::pair<int, hipStream_t>, GaeScratch>& gae_cache() {
@@ -612,6 +640,48 @@ int gae_scan(const float* rewards, const float* values, const uint8_t* dones,
                  nullptr, rl::kGaeSpinLimit};
   std::lock_guard<std::mutex> lock(g_gae_mu);
   return gae_run(gae_cache()[std::make_pair(dev, st)], ga, st);
+}
+
+int gae_scan_noalloc(const float* rewards, const float* values, const uint8_t* dones,
+                     const float* last_values, int32_t L, int32_t N, float gamma, float lambda,
+                     float* advantages, float* returns, void* hip_stream) {
+  static_assert(sizeof(scratch) == kNoAllocBytes, "scratch size");
+  if (L < 0 || N < 0)
+    return fail(ROLLOUT_EINVAL, "gae_scan_noalloc: negative size (L=%d, N=%d)", L, N);
+  if (L == 0 || N == 0) return ROLLOUT_OK;
+  if (!rewards || !values || !dones || !advantages || !returns)
+    return fail(ROLLOUT_EINVAL, "gae_scan_noalloc: NULL buffer");
+  if ((int64_t)L * N >= (int64_t)1 << 40) return fail(ROLLOUT_EINVAL, "gae_scan_noalloc: too large");
+  const rl::GaeShape shape = rl::gae_shape(L, N);
+  if (shape.nk > 1 && (size_t)shape.nk * (size_t)N > kNoAllocCarries)
+    return fail(ROLLOUT_EINVAL,
+                "gae_scan_noalloc: %d chunks of 256 steps x %d episodes need %zu carries, more "
+                "than the %zu of its fixed scratch (rollouts of at most 512 steps need none)",
+                shape.nk, N, (size_t)shape.nk * (size_t)N, kNoAllocCarries);
+  int dev = -1;
+  RL_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ROLLOUT_EINVAL, "gae_scan_noalloc: device %d beyond %d", dev, kMaxDevices);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  NoAllocDevice& d = g_noalloc[dev];
+  if (!d.ready) {
+    // once per device, with it current: this device's copy of the array
+    void* ptr = nullptr;
+    RL_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(ROLLOUT_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    // the ticket counter starts at zero (the carries are cleared on first
+    // use of each layout, in gae_prepare)
+    RL_HIP(rl::zero_words(static_cast<uint32_t*>(ptr), 64, st), "clear noalloc ticket");
+    d.s.mem = static_cast<char*>(ptr);
+    d.s.bytes = kNoAllocBytes;
+    d.s.fixed = true;
+    d.ready = true;
+  }
+  rl::GaeArgs ga{rewards, values,     dones,   last_values, L,
+                 N,       gamma,      lambda,  advantages,  returns,
+                 nullptr, rl::kGaeSpinLimit};
+  return gae_run(d.s, ga, st);
 }
 
 void rollout_destroy(rollout_handle h) {

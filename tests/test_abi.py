@@ -30,7 +30,7 @@ def rx():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
-         "gae_scan", "rollout_destroy", "rollout_last_error",
+         "gae_scan", "gae_scan_noalloc", "rollout_destroy", "rollout_last_error",
          "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_set_epsilon",
          "dqn_collect", "dqn_destroy", "per_create", "per_sample", "per_gather", "per_update", "per_destroy"])
 
@@ -91,6 +91,24 @@ def test_host_side_errors_without_gpu(rx):
     assert lib.gae_scan(None, None, None, None, 3, 5, 0.99, 0.95, None, None, None) == rx.ROLLOUT_EINVAL
     assert lib.gae_scan(None, None, None, None, -1, 5, 0.99, 0.95, None, None, None) == rx.ROLLOUT_EINVAL
     lib.rollout_destroy(None)
+
+
+def test_gae_scan_noalloc_rejects_scans_beyond_its_scratch(rx):
+    """The allocation-free scan holds 524,288 chunk carries: a scan longer
+    than 512 steps needing more is refused on the host, before any device
+    call; short scans need none."""
+    lib = rx.load_library()
+    d = C.c_void_p(1)
+    assert lib.gae_scan_noalloc(d, d, d, None, 2048, 65537, 0.99, 0.95, d, d, None) == \
+        rx.ROLLOUT_EINVAL
+    msg = rx.rollout_last_error()
+    assert "524288" in msg and "8 chunks" in msg and "65537" in msg
+    assert lib.gae_scan_noalloc(None, None, None, None, 0, 5, 0.99, 0.95, None, None, None) == \
+        rx.ROLLOUT_OK
+    assert lib.gae_scan_noalloc(None, None, None, None, 3, 5, 0.99, 0.95, None, None, None) == \
+        rx.ROLLOUT_EINVAL
+    assert lib.gae_scan_noalloc(None, None, None, None, 3, -5, 0.99, 0.95, None, None, None) == \
+        rx.ROLLOUT_EINVAL
 
 
 def test_dqn_config_default_values(rx):
