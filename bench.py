@@ -218,6 +218,7 @@ def probe_lib():
     lib.bench_value_stream_shape.argtypes = [C.c_int, C.POINTER(C.c_longlong), C.POINTER(C.c_int)]
     lib.bench_weight_stream.argtypes = [P, C.c_longlong, C.c_longlong, P, P]
     lib.bench_gae_traffic.argtypes = [P, P, P, P, P, C.c_longlong, P]
+    lib.bench_lds_activation.argtypes = [C.c_longlong, P, C.POINTER(C.c_longlong), P]
     return lib
 
 
@@ -317,6 +318,37 @@ def _threads():
     return int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
 
 
+def time_lds_activation(rows, reps):
+    """The bf16 value kernel's LDS activation traffic alone (reads of every
+    layer's B operands, the ReLU/pack stores, the barriers) for `rows`
+    stored states: the LDS bound of that kernel."""
+    import ctypes as C
+    import torch
+    import rl_experience_collection_amd as rx
+    lib = probe_lib()
+    groups = -(-rows // 128)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    per = C.c_longlong()
+    st = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = lib.bench_lds_activation(groups, sink.data_ptr(), C.byref(per), st)
+        if rc:
+            raise RuntimeError(f"bench_lds_activation: {rc}")
+    for _ in range(2):
+        launch()
+    ev = rx.HipEvents(2)
+    ev.record(0)
+    for _ in range(reps):
+        launch()
+    ev.record(1)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / reps
+    ev.close()
+    return dict(ms=ms, items=groups, bytes_per_item=per.value,
+                TBps=per.value * groups / (ms * 1e-3) / 1e12)
+
+
 def cpu_baseline(inp, n_episodes, precision=0, dqn=False):
     """The oracle as it stands on a bounded episode subset of the same
     workload (all of it when n_episodes >= N)."""
@@ -387,6 +419,8 @@ def run_single(name, steps, warmup):
                     nonfinite=r["nonfinite"])
     if name.startswith("per"):
         return dict(workload=name, **time_per(16384 * 500, 4096, steps))
+    if name == "lds_activation_bf16":
+        return dict(workload=name, **time_lds_activation(8192 * 500, steps))
     if name.startswith("weight_stream"):
         return dict(workload=name, **time_weight_stream(8192 * 500, name.endswith("bf16"), steps))
     a = torch.ones(1 << 28, device="cuda")  # copy_1gib: 1 GiB read + 1 GiB written per copy
@@ -409,6 +443,7 @@ def main():
                              "collect_n8192_fp32_recycle", "dqn_n16384_l500_recycle",
                              "gae_n4096_l2048", "gae_n8192_l500", "gae_traffic_n4096_l2048",
                              "gae_traffic_n8192_l500", "weight_stream_fp32", "weight_stream_bf16",
+                             "lds_activation_bf16",
                              "dqn_n16384_l500", "per_n8192000_b4096",
                              "copy_1gib"),
                     help="one workload only (for profiler counter passes); prints its own "
@@ -452,6 +487,7 @@ def main():
     gae_cx = time_gae(dict(N=N, L=L, seed=spec["seed"]), max(args.steps, 20), traffic_only=True)
     ws_f = time_weight_stream(N * L, False, 5)
     ws_b = time_weight_stream(N * L, True, 5)
+    lds_b = time_lds_activation(N * L, 5)
     log("timing the DQN collection N=16384 L=500 ...")
     dq_inp = synthdata.dqn_inputs("dqn_n16384_l500")
     dq = time_dqn(dq_inp, args.steps, args.warmup)
@@ -515,7 +551,11 @@ def main():
                 # the bound is the slower of the MFMA peak and that stream alone
                 weight_stream_bound_ms=ws_b["ms"], weight_stream_TBps=ws_b["TBps"],
                 weight_stream_bytes_per_launch=ws_b["bytes_per_launch"],
-                value_kernel_frac_of_bound=max(ws_b["ms"], VALUE_KERNEL_FLOP * N * L /
+                # its activation operands cross the CU's LDS once per wave and layer:
+                # that traffic alone, with the kernel's barriers
+                lds_stream_bound_ms=lds_b["ms"], lds_stream_TBps=lds_b["TBps"],
+                lds_bytes_per_item=lds_b["bytes_per_item"],
+                value_kernel_frac_of_bound=max(ws_b["ms"], lds_b["ms"], VALUE_KERNEL_FLOP * N * L /
                                                PEAK_BF16_MFMA * 1e3) / float(bfr["phases_ms"][1])),
             dqn_collect_n16384_l500_fp32=dict(
                 value=dq_exp * args.steps / dq["wall_s"], unit="experiences/s",

@@ -13,9 +13,15 @@ SOURCES = ["abi.hip", "pack.hip", "rollout.hip", "value.hip", "gae.hip", "dqn.hi
 PROBE_LIB = os.path.join(PKG, "libbenchprobes.so")
 PROBE_SOURCES = ["bench_probes.hip"]
 ARCH = os.environ.get("ROLLOUT_OFFLOAD_ARCH", "gfx950")
+# The device compiler's atomic optimizer turns an atomic that one lane
+# issues into a wave-aggregated one whose returned value is broadcast at once,
+# which waits for every load the wave has in flight (the value kernel's work
+# ticket, taken while its next layer's weights stream in); none of the
+# library's atomics gains from aggregation, so it is off.
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xarch_device", "-mllvm=-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

@@ -11,6 +11,14 @@
 //    16-byte lanes (1 KiB per wave instruction), 16 loads in flight per
 //    lane.  Its time for the value kernel's work-item count is the stream
 //    bound the MFMA work competes with.
+//  * lds_activation_kernel: the bf16 value kernel's activation traffic
+//    through LDS alone: per 128-row work item, every B-operand read of every
+//    layer (each of the 8 waves reads all row tiles of a layer's input,
+//    16 bytes per lane per k-step and row tile), every ReLU/pack store of a
+//    layer's output, the scatter of the next item's state operands, and the
+//    same barriers, with the value kernel's block shape and LDS footprint
+//    (one workgroup per CU) and no MFMA or weight loads: the bound the LDS
+//    data path sets on that kernel.
 //  * gae_traffic_kernel: moves exactly the GAE scan's bytes (reads r, V, d;
 //    writes two float arrays with streaming stores, as the scan does),
 //    element-wise with no recurrence: the copy ceiling of the scan at a
@@ -46,6 +54,82 @@ weight_stream_kernel(const uint4* __restrict__ blob, uint32_t rows, int64_t grou
     }
   }
   if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;  // keeps the loads live
+}
+
+// ---- LDS activation traffic of the bf16 value kernel ----------------------
+constexpr int kLW = 8;                    // waves
+constexpr int kLThreads = 64 * kLW;
+constexpr int kLRT = 8;                   // row tiles of 16 rows per work item
+constexpr int kLTile = 16 * 64;           // 16-byte operands per row tile (512 inputs)
+constexpr int kLOp = 2 * 64;              // first-layer operands per row tile
+
+// S k-steps of a layer's input over `rts` row tiles (from rt0), folded into x
+template <int S>
+__device__ __forceinline__ void lds_read_layer(const uint4* buf, int tile_stride, int rt0, int rts,
+                                               int lane, uint4& x) {
+#pragma unroll 1
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int rt = 0; rt < kLRT; ++rt) {
+      if (rt >= rts) break;
+      const uint4 b = buf[(rt0 + rt) * tile_stride + s * 64 + lane];
+      asm volatile("" ::: "memory");  // every read issued, in order
+      x.x ^= b.x; x.y += b.y; x.z ^= b.z; x.w += b.w;
+    }
+}
+
+// OTW output tiles x 8 row tiles of one wave, as packed bf16 pairs
+template <int OTW>
+__device__ __forceinline__ void lds_store_layer(uint4* buf, int q, int lane, const uint4& x) {
+  uint2* half = reinterpret_cast<uint2*>(buf);
+#pragma unroll
+  for (int rt = 0; rt < kLRT; ++rt)
+#pragma unroll
+    for (int i = 0; i < OTW; ++i) {
+      const int t = q * OTW + i;
+      half[rt * kLTile * 2 + ((t >> 1) * 64 + lane) * 2 + (t & 1)] = make_uint2(x.x + rt, x.y ^ i);
+    }
+}
+
+__global__ __launch_bounds__(kLThreads) void lds_activation_kernel(int64_t groups,
+                                                                   uint32_t* __restrict__ sink) {
+  __shared__ uint4 s_buf[kLRT * kLTile];
+  __shared__ uint4 s_opnd[kLRT * kLOp];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  uint4 x = make_uint4(threadIdx.x, 1, 2, 3);
+  for (int i = threadIdx.x; i < kLRT * kLOp; i += kLThreads) s_opnd[i] = x;
+  __syncthreads();
+  for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
+    // critic 54 -> 512 (2 k-steps from the state operands, 4 tiles per wave)
+    lds_read_layer<2>(s_opnd, kLOp, 0, kLRT, lane, x);
+    lds_store_layer<4>(s_buf, q, lane, x);
+    __syncthreads();
+    lds_read_layer<16>(s_buf, kLTile, 0, kLRT, lane, x);  // 512 -> 384
+    __syncthreads();
+    lds_store_layer<3>(s_buf, q, lane, x);
+    __syncthreads();
+    lds_read_layer<12>(s_buf, kLTile, 0, kLRT, lane, x);  // 384 -> 256
+    __syncthreads();
+    lds_store_layer<2>(s_buf, q, lane, x);
+    __syncthreads();
+    lds_read_layer<8>(s_buf, kLTile, 0, kLRT, lane, x);   // 256 -> 128
+    __syncthreads();
+    lds_store_layer<1>(s_buf, q, lane, x);
+    __syncthreads();
+    // 128 -> 64: a wave reads half the row tiles (4 output tiles x 2 halves)
+    lds_read_layer<4>(s_buf, kLTile, (q >> 2) * 4, 4, lane, x);
+    // curiosity 54 -> 128 (state operands, 1 tile per wave)
+    lds_read_layer<2>(s_opnd, kLOp, 0, kLRT, lane, x);
+    __syncthreads();
+    // the next item's state operands: 2 chunks of 16 bytes per thread
+    s_opnd[threadIdx.x] = x;
+    s_opnd[threadIdx.x + kLThreads] = x;
+    lds_store_layer<1>(s_buf, q, lane, x);
+    __syncthreads();
+    lds_read_layer<4>(s_buf, kLTile, (q >> 2) * 4, 4, lane, x);  // 128 -> 51
+    __syncthreads();
+  }
+  if ((x.x ^ x.y ^ x.z ^ x.w) == 0x9E3779B9u) sink[threadIdx.x & 255] = x.x;  // keeps it live
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -110,6 +194,30 @@ int bench_weight_stream(const void* blob, long long bytes, long long groups, uin
   const unsigned grid = (unsigned)(groups < resident ? groups : resident);
   hipLaunchKernelGGL(weight_stream_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                      (const uint4*)blob, (uint32_t)(bytes / (kThreads * 16)), (int64_t)groups, sink);
+  return (int)hipGetLastError();
+}
+
+// The bf16 value kernel's LDS activation traffic alone for `groups` work
+// items of 128 rows, one workgroup per CU; `sink` (256 uint32) is written
+// only if the checksum hits a fixed value.  Returns the LDS bytes read and
+// written per work item in *bytes_per_item.
+int bench_lds_activation(long long groups, uint32_t* sink, long long* bytes_per_item,
+                         void* stream) {
+  if (!sink || groups <= 0 || !bytes_per_item) return (int)hipErrorInvalidValue;
+  // reads: 8 waves x (2 + 16 + 12 + 8 + 2) k-steps x 8 row tiles + 8 x 2 x 4 x 4
+  //        (the two 4-tile layers, half the row tiles each), 1 KiB each;
+  // writes: 8 waves x 8 row tiles x (4 + 3 + 2 + 1 + 1) tiles x 512 bytes,
+  //         plus the state operands (16 KiB)
+  const long long reads = (8LL * 40 * 8 + 8LL * 2 * 4 * 4) * 1024;
+  const long long writes = 8LL * 8 * 11 * 512 + kLRT * kLOp * 16;
+  *bytes_per_item = reads + writes;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return (int)e;
+  const unsigned grid = (unsigned)(groups < cus ? groups : cus);
+  hipLaunchKernelGGL(lds_activation_kernel, dim3(grid), dim3(kLThreads), 0, (hipStream_t)stream,
+                     (int64_t)groups, sink);
   return (int)hipGetLastError();
 }
 

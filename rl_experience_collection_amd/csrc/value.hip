@@ -57,7 +57,14 @@ struct ValueShape {
   // per row tile (bf16: 2 k-steps, fp32: 4 groups of 4 k-steps, x 64 lanes)
   static constexpr int kRaw = RT * kRowsPerWave * kState;
   static constexpr int kOpTile = BF16 ? 2 * 64 : 4 * 64;
-  static_assert(RT >= 1 && RT <= W, "every row tile's result has a writing wave");
+  // row tiles whose epilogue (action, next bar, partial reward, value and
+  // reward) one wave handles: wave q takes row tiles q + W e, e < ER
+  static constexpr int ER = (RT + W - 1) / W;
+  // waves per SIMD: fp32 runs two 4-wave workgroups per CU; bf16 one
+  // workgroup per CU (its 128 rows of activations fill the LDS) of one or
+  // two waves per SIMD
+  static constexpr int kWavesPerEU = BF16 && W == kSplit ? 1 : 2;
+  static_assert(RT >= 1 && ER <= 2, "at most two row tiles per wave in the epilogue");
   static_assert(W % kSplit == 0 && RT % RH == 0, "the 4-tile layers cover every row tile");
   static_assert(O1 * W == (BF16 ? kCriticB[0].ot : kCritic[0].ot) &&
                     O2 * W == (BF16 ? kCriticB[1].ot : kCritic[1].ot) &&
@@ -105,7 +112,8 @@ __device__ __forceinline__ void store(const f32x4 (&acc)[RT][OTW], f32x4* buf, i
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(ValueShape<BF16>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(ValueShape<BF16>::kThreads)
+__attribute__((amdgpu_waves_per_eu(ValueShape<BF16>::kWavesPerEU)))
 void value_kernel(ValueArgs a) {
   using Sh = ValueShape<BF16>;
   constexpr int RT = Sh::RT;
@@ -238,8 +246,15 @@ void value_kernel(ValueArgs a) {
   const int rs0 = Sh::RH > 1 ? (q >> 2) * RTS : 0;   // ... of row tiles rs0 .. rs0 + RTS - 1
   const int g = lane >> 4;
 
-  const int64_t my_raw = (tile0 + q) * kRowsPerWave + (lane & 15);
-  const int64_t my_row = my_raw < rows ? my_raw : rows - 1;  // tail rows recompute the last row
+  constexpr int ER = Sh::ER;
+  // the epilogue's rows: row tile q + W e, lane % 16 (tail rows recompute
+  // the last row)
+  int64_t my_raw[ER], my_row[ER];
+#pragma unroll
+  for (int e = 0; e < ER; ++e) {
+    my_raw[e] = (tile0 + q + W * e) * kRowsPerWave + (lane & 15);
+    my_row[e] = my_raw[e] < rows ? my_raw[e] : rows - 1;
+  }
   // (t, n) of the workgroup's first row; a row tile's rows are row0 + off
   const int64_t row0 = tile0 * kRowsPerWave;
   const uint64_t t_base = (uint64_t)(row0 / a.N);
@@ -319,15 +334,23 @@ void value_kernel(ValueArgs a) {
   // peak of the wide layers so it arrives during the rest: wave q < RT
   // loads the action and the next bar (the MSE target) of row tile q's
   // rows; they go through LDS to every wave after the next layer
-  int my_act = 0, my_nbar = 0;
-  if (q < RT) {
+  // (one load per value, with no branch around it: a load behind a branch
+  // writes the registers another path loads into, and the compiler then
+  // waits for every load in flight)
+  int my_act[ER], my_nbar[ER];
+  float partial[ER];
+#pragma unroll
+  for (int e = 0; e < ER; ++e) {
+    const int rt = q + W * e < RT ? q + W * e : RT - 1;
     int32_t t, n;
-    row_tn(q, t, n);
-    const int v = a.actions[(int64_t)t * a.N + n];
-    my_act = v < 0 ? 0 : (v >= kActions ? kActions - 1 : v);
-    my_nbar = (a.bars ? a.bars[(int64_t)t * a.N + n] : a.start_used[n] + a.t_off + t) + 1;
+    row_tn(rt, t, n);
+    const int64_t o = (int64_t)t * a.N + n;
+    my_act[e] = a.actions[o];
+    // the bar of the step (recorded, or start + step), + 1 added at its use
+    my_nbar[e] = a.bars ? a.bars[o] : a.start_used[n];
+    if (!a.bars) my_nbar[e] += a.t_off + t;
+    partial[e] = a.rewards[my_row[e]];
   }
-  const float partial = q < RT ? a.rewards[my_row] : 0.0f;
   lds_barrier();
   store<BF16, Sh::O3, RT>(h3, s_buf, TS, q, lane);
   lds_barrier();
@@ -337,27 +360,32 @@ void value_kernel(ValueArgs a) {
   Stream<BF16, 1> w5;
   begin<S5>(w5, wt, kP.critic_w[4], kP.bcritic_w[4], kP.critic_b[4], q4, lane);
   if constexpr (BF16) prefetch_next();
-  if (q < RT && g == 0) {
-    s_act[q * kRowsPerWave + lane] = my_act;
-    s_nbar[q * kRowsPerWave + lane] = my_nbar;
-  }
+#pragma unroll
+  for (int e = 0; e < ER; ++e)
+    if (q + W * e < RT && g == 0) {
+      const int v = my_act[e];
+      s_act[(q + W * e) * kRowsPerWave + lane] = v < 0 ? 0 : (v >= kActions ? kActions - 1 : v);
+      s_nbar[(q + W * e) * kRowsPerWave + lane] = my_nbar[e] + 1;
+    }
   lds_barrier();
   // next-bar features of this wave's row tiles for the curiosity MSE: lane
-  // holds features j0 .. j0 + 3, j0 = 16 q4 + 4g.  Where all four lie in the
-  // row they are one 16-byte load (rows are 204 bytes, so 4-byte aligned):
-  // per-lane rows make each load touch 16 lines, and one wide load instead
-  // of four keeps the address work per row at one pass.
+  // holds features j0 .. j0 + 3, j0 = 16 q4 + 4g, one 16-byte load per row
+  // (rows are 204 bytes, so 4-byte aligned) with no branch around it: the
+  // row's last four where j0 + 3 lies past it (48 .. 50 are then moved down
+  // one; lanes past the row keep zeros).
   f32x4 feat[RTS];
   const int j0 = 16 * q4 + 4 * g;
+  const int jl = j0 + 3 < kFeatures ? j0 : kFeatures - 4;
 #pragma unroll
   for (int rt = 0; rt < RTS; ++rt) {
     const float* fn =
         a.features + (int64_t)s_nbar[(rs0 + rt) * kRowsPerWave + (lane & 15)] * kFeatures;
-    if (j0 + 3 < kFeatures) {
-      feat[rt] = *reinterpret_cast<const f32x4_a4*>(fn + j0);
-    } else {
+    const f32x4 v = *reinterpret_cast<const f32x4_a4*>(fn + jl);
+    const bool shift = jl != j0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) feat[rt][r] = j0 + r < kFeatures ? fn[j0 + r] : 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      const float s1 = r < 3 ? v[r + 1] : 0.0f;
+      feat[rt][r] = j0 + r < kFeatures ? (shift ? s1 : v[r]) : 0.0f;
     }
   }
   store<BF16, Sh::O4, RT>(h4, s_buf, TS, q, lane);
@@ -402,10 +430,13 @@ void value_kernel(ValueArgs a) {
   // the next group's state operands (the last reader of this group's was
   // the curiosity layer above); the final barrier makes them visible
   if (grp_next < groups) scatter_states(tid, v_states);
-  float value = 0.0f;
-  if (q < RT)
-    value = Wp[kP.critic_b6] + ((s_part[0][q][0][lane & 15] + s_part[0][q][1][lane & 15]) +
-                                (s_part[0][q][2][lane & 15] + s_part[0][q][3][lane & 15]));
+  float value[ER];
+#pragma unroll
+  for (int e = 0; e < ER; ++e) {
+    const int rt = q + W * e < RT ? q + W * e : 0;
+    value[e] = Wp[kP.critic_b6] + ((s_part[0][rt][0][lane & 15] + s_part[0][rt][1][lane & 15]) +
+                                   (s_part[0][rt][2][lane & 15] + s_part[0][rt][3][lane & 15]));
+  }
   store<BF16, Sh::OC1, RT>(c, s_buf, TS, q, lane);
   lds_barrier();
 
@@ -430,16 +461,21 @@ void value_kernel(ValueArgs a) {
   }
   lds_barrier();
 
-  // ---- step 10: reward = partial + curiosity - risk (wave q: row tile q) ---
-  if (q < RT && g == 0 && my_raw < rows) {
-    const float sum = (s_part[1][q][0][lane] + s_part[1][q][1][lane]) +
-                      (s_part[1][q][2][lane] + s_part[1][q][3][lane]);
-    const float bonus = a.ep.curiosity_coef * (sum / (float)kFeatures);
-    const float ex = s_env[my_act / 9];
-    const float reward = (partial + bonus) - a.ep.risk_coef * fabsf(ex);
-    a.values[my_row] = value;
-    a.rewards[my_row] = reward;
-    if (a.counters && (!isfinite(value) || !isfinite(reward))) atomicAdd(a.counters, 1u);
+  // ---- step 10: reward = partial + curiosity - risk (wave q: row tiles
+  // q + W e) ---------------------------------------------------------------
+#pragma unroll
+  for (int e = 0; e < ER; ++e) {
+    const int rt = q + W * e;
+    if (rt < RT && g == 0 && my_raw[e] < rows) {
+      const float sum = (s_part[1][rt][0][lane] + s_part[1][rt][1][lane]) +
+                        (s_part[1][rt][2][lane] + s_part[1][rt][3][lane]);
+      const float bonus = a.ep.curiosity_coef * (sum / (float)kFeatures);
+      const float ex = s_env[s_act[rt * kRowsPerWave + lane] / 9];
+      const float reward = (partial[e] + bonus) - a.ep.risk_coef * fabsf(ex);
+      a.values[my_row[e]] = value[e];
+      a.rewards[my_row[e]] = reward;
+      if (a.counters && (!isfinite(value[e]) || !isfinite(reward))) atomicAdd(a.counters, 1u);
+    }
   }
   // the same value in every lane: keep the loop control scalar
   grp = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)grp_next) |
