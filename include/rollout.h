@@ -188,8 +188,8 @@ int rollout_collect(rollout_handle h, const int32_t *episode_starts, uint64_t se
  * per-(device, stream) scratch for the inter-chunk carries, allocated on the
  * first call for that stream; concurrent calls on the same stream are
  * serialised by the stream itself.
- * Rollouts longer than 512 steps are cut into chunks whose carries pass
- * between workgroups through a bounded wait.  A wait that reaches its bound
+ * Rollouts longer than 512 steps are cut into 512-step chunks whose carries
+ * pass between workgroups through a bounded wait.  A wait that reaches its bound
  * (never expected: every wait is on a workgroup that is already running)
  * ends, and its chunk's carry is NaN, so the advantages and returns of that
  * episode from the chunk back to step 0 are NaN rather than silently wrong;
@@ -206,11 +206,11 @@ int gae_scan(const float *rewards, const float *values, const uint8_t *dones,
 /* gae_scan without any device allocation, for callers that cannot allocate:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, layout, results (bit for bit) and errors as
- * gae_scan.  Rollouts longer than 512 steps pass carries between 256-step
+ * gae_scan.  Rollouts longer than 512 steps pass carries between 512-step
  * chunks through a scratch that here is a fixed array in the library's
  * device memory (4 MiB + 256 bytes, held by each device the library runs on
  * until the process ends) instead of memory allocated on first use: such a
- * scan needs ceil(L / 256) * N <= 524288 (e.g. L = 2048 with N <= 65536);
+ * scan needs ceil(L / 512) * N <= 524288 (e.g. L = 4096 with N <= 65536);
  * larger ones are rejected with ROLLOUT_EINVAL before anything is enqueued.
  * Rollouts of at most 512 steps need no scratch and have no such limit.
  * Every call on one device shares that device's array, which keeps the last

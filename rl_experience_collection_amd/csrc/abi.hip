@@ -145,7 +145,7 @@ int gae_reserve(GaeScratch& s, int32_t L, int32_t N, hipStream_t st) {
 
 // Scratch of gae_scan_noalloc, for callers that cannot allocate: the
 // inter-chunk carries of one scan (a 256-byte header holding the ticket
-// counter, then 8 bytes per episode and 256-step chunk), at most
+// counter, then 8 bytes per episode and 512-step chunk), at most
 // kNoAllocCarries of them.  Each device holds its own copy until the process
 // ends; host code reaches it only through the address hipGetSymbolAddress
 // returns for the current device.
@@ -655,7 +655,7 @@ int gae_scan_noalloc(const float* rewards, const float* values, const uint8_t* d
   const rl::GaeShape shape = rl::gae_shape(L, N);
   if (shape.nk > 1 && (size_t)shape.nk * (size_t)N > kNoAllocCarries)
     return fail(ROLLOUT_EINVAL,
-                "gae_scan_noalloc: %d chunks of 256 steps x %d episodes need %zu carries, more "
+                "gae_scan_noalloc: %d chunks of 512 steps x %d episodes need %zu carries, more "
                 "than the %zu of its fixed scratch (rollouts of at most 512 steps need none)",
                 shape.nk, N, (size_t)shape.nk * (size_t)N, kNoAllocCarries);
   int dev = -1;

@@ -5,37 +5,43 @@
 // is affine in A_{t+1}: a run of steps [t0, t1) maps A_{t1} to
 // A_{t0} = alpha + beta A_{t1}, with beta = 0 as soon as the run holds a done.
 //
-// Layout: a workgroup owns a column of COLS episodes x a super-chunk of
-// kGaeWaves * 64 / COLS time slots of kGaeChunk steps.  With COLS = 32 (one
-// 128-byte row of floats per step, 512-step super-chunks) each wave holds
-// two slots (lanes 0-31 and 32-63); with COLS = 64 (256-step super-chunks)
-// one.  Each thread keeps kGaeChunk consecutive steps of one episode in
-// registers, so every load instruction reads whole rows.  Every thread folds its chunk into (alpha, beta);
-// one lane per episode then forms, in one backward pass over the slots, the
-// map of all later slots for each slot, and every thread applies its own to
-// the incoming carry and writes A and R.
+// Layout: a workgroup of 16 waves owns a column of COLS episodes x a
+// super-chunk of 512 steps, cut into time slots of consecutive steps, one
+// slot per thread and episode.  Each thread keeps its slot's steps in
+// registers, so every load instruction reads whole rows of the column.
+// Every thread folds its slot into (alpha, beta); one lane per episode then
+// forms, in one backward pass over the slots, the map of all later slots for
+// each slot, and every thread applies its own to the incoming carry and
+// writes A and R.
 //
-// A rollout of at most 512 steps runs with COLS = 32 as one super-chunk: no
-// carry crosses workgroups, and workgroups map to columns by index, with the column order
-// permuted so that the columns that share a 128-byte line of dones sit on
-// one XCD (workgroups are dispatched round-robin over the 8 XCDs).
+// A rollout of at most 512 steps is one super-chunk: COLS = 32 (one
+// 128-byte row of floats per step, two 16-step slots per wave), no carry
+// crosses workgroups, and workgroups map to columns by index, with the
+// column order permuted so that the columns that share a 128-byte line of
+// dones sit on one XCD (workgroups are dispatched round-robin over the 8
+// XCDs).
 //
-// Longer rollouts run with COLS = 64, whose shorter super-chunks keep more
-// of them in flight, and chain the super-chunks of a column by a
-// decoupled look-back: workgroups take super-chunks in reverse-time order
-// from an atomic ticket, publish their aggregate alpha_S (or at once their
-// inclusive value when the super-chunk holds a done or is the latest), look
-// back to the nearest published inclusive value, fold the aggregates in
-// between innermost-first and publish their own inclusive value
-// alpha_S + beta_S * carry.  Every published value is one 64-bit word
-// (value | epoch and status tag) stored and polled with device-coherent
-// relaxed atomics, so no fences are needed.  A reader rebuilds the beta_S of
-// an aggregate (no done inside) as the same product of gl^kGaeChunk factors
-// the owner formed, so every carry is the same floating-point expression
-// whatever the timing: results are bit-deterministic.  Every wait is on a
-// workgroup holding an earlier ticket (already running) and the latest
-// super-chunk never waits, so all waits end.  HBM traffic is the algorithmic
-// 17 B per element plus 8 B per episode per super-chunk.
+// Longer rollouts run with COLS = 64 and 32-step slots (one per wave), so a
+// super-chunk is still 512 steps and a launch holds as few of them as
+// possible: each costs a look-back, and a launch that fits the chip in one
+// round of workgroups never waits for a second round's loads.  The values
+// wait in LDS between the two passes, which keeps the registers held across
+// the look-back within a 1024-thread workgroup's budget.  The super-chunks
+// of a column are chained by a decoupled look-back: workgroups take
+// super-chunks in reverse-time order from an atomic ticket, publish their
+// aggregate alpha_S (or at once their inclusive value when the super-chunk
+// holds a done or is the latest), look back to the nearest published
+// inclusive value, fold the aggregates in between innermost-first and
+// publish their own inclusive value alpha_S + beta_S * carry.  Every
+// published value is one 64-bit word (value | epoch and status tag) stored
+// and polled with device-coherent relaxed atomics, so no fences are needed.  A reader
+// rebuilds the beta_S of an aggregate (no done inside) as the same product
+// of gl^32 factors the owner formed, so every carry is the same
+// floating-point expression whatever the timing: results are
+// bit-deterministic.  Every wait is on a workgroup holding an earlier
+// ticket (already running) and the latest super-chunk never waits, so all
+// waits end.  HBM traffic is the algorithmic 17 B per element
+// plus 8 B per episode per super-chunk.
 #include "gae.hpp"
 
 #include <hip/hip_runtime.h>
@@ -46,7 +52,7 @@ namespace {
 
 constexpr uint32_t kAgg = 1u, kIncl = 2u;
 constexpr int kWalk = 8;   // aggregates held before waiting on an inclusive
-constexpr int kBatch = 4;  // later super-chunks read per look-back round
+constexpr int kBatch = 2;  // later super-chunks read per look-back round
 
 __device__ __forceinline__ void put_u64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -65,7 +71,9 @@ __device__ __forceinline__ int32_t column_of(uint32_t p, int32_t NC) {
   return (int32_t)(p & 7u) * (NC >> 3) + (int32_t)(p >> 3);
 }
 
-template <int COLS>
+// COLS = 32: one super-chunk per column; COLS = 64: chained super-chunks.
+// OFF32: the host has checked that a super-chunk's bytes stay below 4 GiB.
+template <int COLS, bool OFF32>
 __global__ __launch_bounds__(64 * kGaeWaves) void gae_scan_kernel(
     const float* __restrict__ rew, const float* __restrict__ val, const uint8_t* __restrict__ don,
     const float* __restrict__ last_values, int32_t L, int32_t N, float gamma, float gl,
@@ -73,97 +81,130 @@ __global__ __launch_bounds__(64 * kGaeWaves) void gae_scan_kernel(
     uint32_t* __restrict__ status, uint32_t spin_limit) {
   constexpr int kSlots = gae_slots(COLS);
   constexpr int kSuper = gae_super(COLS);
+  constexpr int kChunk = gae_chunk(COLS);
+  constexpr bool kChain = COLS == 64;
+  constexpr int kG = 8;  // slots' maps held in registers at a time
+  static_assert(kChunk <= 32, "dones of a slot are kept as one 32-bit mask");
+  static_assert(kSlots % kG == 0, "suffix maps are formed kG slots at a time");
   __shared__ uint32_t s_tile;
   __shared__ float s_a[kSlots][COLS];
   __shared__ float s_b[kSlots][COLS];
+  // chained shape: each thread's values, between the two passes
+  __shared__ float s_v[kChain ? kChunk : 1][kChain ? 64 * kGaeWaves : 1];
 
-  const int lane = threadIdx.x & 63;
-  const int e = lane & (COLS - 1);
+  const int e = (int)threadIdx.x & (COLS - 1);
   const int slot = (int)(threadIdx.x / COLS);
+  int32_t S = 0, c;
   uint32_t tile = blockIdx.x;
-  if (NK > 1) {
+  if constexpr (kChain) {
+    // tiles in ticket order: the latest super-chunks of every column first
     if (threadIdx.x == 0)
       s_tile = __hip_atomic_fetch_add(sc.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
                sc.ticket_base;
     __syncthreads();
-    tile = s_tile;
-    if (tile >= (uint32_t)NC * (uint32_t)NK) return;  // stale ticket base: never expected (uniform)
+    tile = __builtin_amdgcn_readfirstlane(s_tile);
+    if (tile >= (uint32_t)NC * (uint32_t)NK) return;  // stale ticket base: never expected
+    S = NK - 1 - (int32_t)(tile / (uint32_t)NC);
   }
-  const int32_t S = NK - 1 - (int32_t)(tile / (uint32_t)NC);
-  const int32_t c = column_of(tile % (uint32_t)NC, NC);
+  c = column_of(tile % (uint32_t)NC, NC);
   const int32_t n = c * COLS + e;
   const bool active = n < N;
-  const int32_t t0 = S * kSuper + slot * kGaeChunk;
-  const int32_t cnt = active ? max(0, min(kGaeChunk, L - t0)) : 0;
+  const int32_t t0 = S * kSuper + slot * kChunk;
+  const int32_t cnt = active ? max(0, min(kChunk, L - t0)) : 0;
 
-  // ---- load this thread's chunk ------------------------------------------
+  // ---- load this thread's slot --------------------------------------------
   // Every load is issued before any is waited on: indices are clamped into
-  // the buffers (steps past the chunk and idle lanes read a valid element
+  // the buffers (steps past the slot and idle lanes read a valid element
   // that is never used), so no load sits behind a branch.
-  float r[kGaeChunk], v[kGaeChunk], d[kGaeChunk];
-  uint32_t db[kGaeChunk];
+  float r[kChunk], v[kChunk];
+  uint32_t db[kChunk];
   const int32_t nl = active ? n : N - 1;
+  if constexpr (OFF32) {
+    // addresses are a workgroup-uniform base plus one running 32-bit offset
+    // instead of a 64-bit address per load
+    const int64_t base = (int64_t)S * kSuper * N + (int64_t)c * COLS;
+    const char* rb = reinterpret_cast<const char*>(rew + base);
+    const char* vb = reinterpret_cast<const char*>(val + base);
+    const char* db0 = reinterpret_cast<const char*>(don + base);
+    uint32_t off = (uint32_t)(min(t0, L - 1) - S * kSuper) * (uint32_t)N + (uint32_t)(nl - c * COLS);
 #pragma unroll
-  for (int i = 0; i < kGaeChunk; ++i) {
-    const int32_t t = min(t0 + i, L - 1);
-    const int64_t o = (int64_t)t * N + nl;
-    r[i] = rew[o];
-    v[i] = val[o];
-    db[i] = don[o];
+    for (int i = 0; i < kChunk; ++i) {
+      r[i] = *reinterpret_cast<const float*>(rb + (off << 2));
+      v[i] = *reinterpret_cast<const float*>(vb + (off << 2));
+      db[i] = *reinterpret_cast<const uint8_t*>(db0 + off);
+      off += (t0 + i + 1 < L) ? (uint32_t)N : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int32_t t = min(t0 + i, L - 1);
+      const int64_t o = (int64_t)t * N + nl;
+      r[i] = rew[o];
+      v[i] = val[o];
+      db[i] = don[o];
+    }
   }
   const int32_t tn = min(t0 + cnt, L - 1);
   const float v_after = val[(int64_t)tn * N + nl];
-  const float v_last = last_values ? last_values[nl] : 0.0f;
-#pragma unroll
-  for (int i = 0; i < kGaeChunk; ++i) d[i] = (float)db[i];
+  // no load behind a branch: without last values, read a value and drop it
+  const float v_lrd = (last_values ? last_values : val)[nl];
+  const float v_last = last_values ? v_lrd : 0.0f;
   float vnext = 0.0f;
   if (cnt > 0) vnext = (t0 + cnt < L) ? v_after : v_last;
 
-  // ---- chunk map: delta_t in place of r_t, A_t0 = alpha + beta A_t1 --------
+  // ---- slot map: delta_t in place of r_t, A_t0 = alpha + beta A_t1 ---------
+  // The dones leave the registers here as a bit mask for the second pass.
   float alpha = 0.0f, beta = 1.0f;
+  uint32_t dmask = 0u;
   {
     float vn = vnext;
 #pragma unroll
-    for (int i = kGaeChunk - 1; i >= 0; --i) {
-      if (i < cnt) {
-        const float nd = 1.0f - d[i];
-        const float delta = r[i] + gamma * vn * nd - v[i];
-        const float ci = gl * nd;
-        alpha = delta + ci * alpha;
-        beta = ci * beta;
-        r[i] = delta;
-        vn = v[i];
-      }
+    for (int i = kChunk - 1; i >= 0; --i) {
+      // steps past the slot's end leave the map unchanged (selects, not
+      // branches)
+      const bool in = i < cnt;
+      dmask |= (db[i] != 0u ? 1u : 0u) << i;
+      const float nd = 1.0f - (float)db[i];
+      const float delta = r[i] + gamma * vn * nd - v[i];
+      const float ci = gl * nd;
+      alpha = in ? delta + ci * alpha : alpha;
+      beta = in ? ci * beta : beta;
+      r[i] = delta;
+      vn = in ? v[i] : vn;
     }
+  }
+  if constexpr (kChain) {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) s_v[i][threadIdx.x] = v[i];
   }
   s_a[slot][e] = alpha;
   s_b[slot][e] = beta;
   __syncthreads();
 
-  // ---- suffix maps and super-chunk carry (lanes 0-31 of wave 0) ----------
+  // ---- suffix maps and super-chunk carry (one lane per episode) -----------
   // The carry into slot j is the map of slots j+1..kSlots-1 applied to the
   // super-chunk's carry.  One lane per episode forms every suffix map in one
   // backward pass (in place of the slot maps), publishes and looks back with
   // the whole-super-chunk map, and leaves each slot's carry in s_a.
   if (threadIdx.x < COLS) {
     float aS = 0.0f, bS = 1.0f;
+#pragma unroll 1
+    for (int g0 = kSlots - kG; g0 >= 0; g0 -= kG) {
+      float ca[kG], cb[kG];
 #pragma unroll
-    for (int g0 = kSlots - 8; g0 >= 0; g0 -= 8) {
-      float ca[8], cb[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kG; ++q) {
         ca[q] = s_a[g0 + q][e];
         cb[q] = s_b[g0 + q][e];
       }
 #pragma unroll
-      for (int q = 7; q >= 0; --q) {
+      for (int q = kG - 1; q >= 0; --q) {
         s_a[g0 + q][e] = aS;
         s_b[g0 + q][e] = bS;
         aS = ca[q] + cb[q] * aS;
         bS = cb[q] * bS;
       }
     }
-    if (NK > 1) {
+    if constexpr (kChain) {
       const bool doneS = bS == 0.0f;
       const uint32_t tag = sc.epoch << 3;
       uint64_t* my = sc.words + (int64_t)S * N + n;
@@ -175,7 +216,7 @@ __global__ __launch_bounds__(64 * kGaeWaves) void gae_scan_kernel(
           // beta of a full super-chunk without dones, built like the owner's bS
           float gl_c = 1.0f;
 #pragma unroll
-          for (int i = 0; i < kGaeChunk; ++i) gl_c = gl * gl_c;
+          for (int i = 0; i < kChunk; ++i) gl_c = gl * gl_c;
           float gl_s = 1.0f;
 #pragma unroll
           for (int w = 0; w < kSlots; ++w) gl_s = gl_c * gl_s;
@@ -243,17 +284,19 @@ __global__ __launch_bounds__(64 * kGaeWaves) void gae_scan_kernel(
   }
   __syncthreads();
 
-  // ---- carry into this thread's chunk, then A and R -----------------------
+  // ---- carry into this thread's slot, then A and R ------------------------
   if (cnt <= 0) return;
   float A = s_a[slot][e];
 #pragma unroll
-  for (int i = kGaeChunk - 1; i >= 0; --i) {
+  for (int i = kChunk - 1; i >= 0; --i) {
     if (i < cnt) {
-      A = r[i] + (gl * (1.0f - d[i])) * A;
+      // gl * (1 - d) for a done d of 0 or 1
+      A = r[i] + (((dmask >> i) & 1u) ? 0.0f : gl) * A;
       const int64_t o = (int64_t)(t0 + i) * N + n;
+      const float vi = kChain ? s_v[i][threadIdx.x] : v[i];
       // streaming stores: written once here, not read again by the scan
       __builtin_nontemporal_store(A, adv + o);
-      __builtin_nontemporal_store(A + v[i], ret + o);
+      __builtin_nontemporal_store(A + vi, ret + o);
     }
   }
 }
@@ -270,7 +313,10 @@ GaeShape gae_shape(int32_t L, int32_t N) {
 
 hipError_t gae_launch(const GaeArgs& a, const GaeShape& shape, const GaeScratchView& sc,
                       hipStream_t stream) {
-  auto kernel = shape.cols == 32 ? gae_scan_kernel<32> : gae_scan_kernel<64>;
+  const bool off32 = (int64_t)gae_super(shape.cols) * a.N * 4 < ((int64_t)1 << 32);
+  auto kernel = shape.cols == 32 ? gae_scan_kernel<32, false>
+                : off32          ? gae_scan_kernel<64, true>
+                                 : gae_scan_kernel<64, false>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)shape.tiles()), dim3(64 * kGaeWaves), 0, stream,
                      a.rewards, a.values, a.dones, a.last_values, a.L, a.N, a.gamma,
                      a.gamma * a.lambda, a.advantages, a.returns, sc, shape.nc, shape.nk,

@@ -6,19 +6,15 @@
 
 namespace rl {
 
-#ifndef RL_GAE_CHUNK
-#define RL_GAE_CHUNK 16
-#endif
-#ifndef RL_GAE_WAVES
-#define RL_GAE_WAVES 16
-#endif
-constexpr int kGaeChunk = RL_GAE_CHUNK;  // steps per thread, held in registers (3 words each)
-constexpr int kGaeWaves = RL_GAE_WAVES;  // waves per workgroup
-// A column is 32 or 64 episodes: 2 or 1 time slots per wave, super-chunks of
-// 512 or 256 steps.
+// Two shapes: rollouts of at most 512 steps use columns of 32 episodes and
+// 16-step slots (two per wave), longer ones columns of 64 episodes and
+// 32-step slots (one per wave) with super-chunks chained by a look-back.
+// Both have 16-wave workgroups and 512-step super-chunks; each thread holds
+// one slot in registers (3 words per step).
+constexpr int kGaeWaves = 16;
+constexpr int gae_chunk(int cols) { return cols == 32 ? 16 : 32; }
 constexpr int gae_slots(int cols) { return kGaeWaves * 64 / cols; }
-constexpr int gae_super(int cols) { return gae_slots(cols) * kGaeChunk; }
-
+constexpr int gae_super(int cols) { return gae_slots(cols) * gae_chunk(cols); }
 inline int32_t cdiv_i(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 struct GaeArgs {
@@ -44,7 +40,7 @@ constexpr uint32_t kGaeSpinLimit = 1u << 24;
 struct GaeShape {
   int32_t cols;    // episodes per column (32 or 64)
   int32_t nc, nk;  // columns and super-chunks
-  int64_t tiles() const { return (int64_t)nc * nk; }
+  int64_t tiles() const { return (int64_t)nc * nk; }  // workgroups of a launch
 };
 
 // Device view of the carry scratch of one stream/collector.

@@ -89,6 +89,19 @@ int main() {
   expect(gae_scan(dummy, dummy, reinterpret_cast<const uint8_t*>(dummy), nullptr, 1 << 21,
                   1 << 20, 0.99f, 0.95f, dummy, dummy, nullptr),
          ROLLOUT_EINVAL, "gae_scan(too large)", "too large");
+  expect(gae_scan_noalloc(nullptr, nullptr, nullptr, nullptr, 0, 5, 0.99f, 0.95f, nullptr,
+                          nullptr, nullptr),
+         ROLLOUT_OK, "gae_scan_noalloc(L = 0)");
+  expect(gae_scan_noalloc(nullptr, nullptr, nullptr, nullptr, 3, 5, 0.99f, 0.95f, nullptr,
+                          nullptr, nullptr),
+         ROLLOUT_EINVAL, "gae_scan_noalloc(NULL)", "NULL");
+  expect(gae_scan_noalloc(nullptr, nullptr, nullptr, nullptr, 3, -5, 0.99f, 0.95f, nullptr,
+                          nullptr, nullptr),
+         ROLLOUT_EINVAL, "gae_scan_noalloc(N < 0)", "negative");
+  // 5 chunks of 512 steps x 104858 episodes: more carries than the fixed scratch holds
+  expect(gae_scan_noalloc(dummy, dummy, reinterpret_cast<const uint8_t*>(dummy), nullptr, 2304,
+                          104858, 0.99f, 0.95f, dummy, dummy, nullptr),
+         ROLLOUT_EINVAL, "gae_scan_noalloc(beyond scratch)", "524288");
   rollout_destroy(nullptr);
 
   dqn_config dc;

@@ -99,10 +99,10 @@ def test_gae_scan_noalloc_rejects_scans_beyond_its_scratch(rx):
     call; short scans need none."""
     lib = rx.load_library()
     d = C.c_void_p(1)
-    assert lib.gae_scan_noalloc(d, d, d, None, 2048, 65537, 0.99, 0.95, d, d, None) == \
+    assert lib.gae_scan_noalloc(d, d, d, None, 2304, 104858, 0.99, 0.95, d, d, None) == \
         rx.ROLLOUT_EINVAL
     msg = rx.rollout_last_error()
-    assert "524288" in msg and "8 chunks" in msg and "65537" in msg
+    assert "524288" in msg and "5 chunks" in msg and "104858" in msg
     assert lib.gae_scan_noalloc(None, None, None, None, 0, 5, 0.99, 0.95, None, None, None) == \
         rx.ROLLOUT_OK
     assert lib.gae_scan_noalloc(None, None, None, None, 3, 5, 0.99, 0.95, None, None, None) == \

@@ -44,7 +44,8 @@ def check(r, v, d, gamma=0.99, lam=0.95, last=None, offset=0):
 
 @pytest.mark.parametrize("L,N", [(1, 1), (2, 3), (17, 5), (16, 1024), (100, 16), (37, 1000),
                                  (33, 2049), (500, 8192), (129, 4100), (512, 96), (513, 31),
-                                 (700, 33), (1025, 100), (1537, 40)])
+                                 (700, 33), (1025, 100), (1537, 40), (2048, 17),
+                                 (2049, 20), (2600, 70)])
 def test_gae_matches_oracle(L, N):
     r, v, d = synthdata.gae_inputs(N, L, seed=L * 7 + N)
     check(r, v, d)
@@ -79,7 +80,7 @@ def test_gae_dense_dones_and_extreme_params():
     assert np.array_equal(A, r - v)
 
 
-@pytest.mark.parametrize("L,N", [(512, 4096), (2048, 1024)])
+@pytest.mark.parametrize("L,N", [(512, 4096), (2048, 1024), (2600, 1024)])
 def test_gae_deterministic_across_calls(L, N):
     r, v, d = synthdata.gae_inputs(N, L, seed=3)
     A1, R1 = run(r, v, d)
@@ -102,12 +103,12 @@ def test_gae_empty_is_noop():
     rx.gae_scan(z, z, torch.zeros((0, 5), dtype=torch.uint8, device="cuda"), None, 0.99, 0.95, z, z)
 
 
-@pytest.mark.parametrize("L,N", [(500, 65536), (16384, 2048)])
+@pytest.mark.parametrize("L,N", [(500, 65536), (2048, 16384), (16384, 2048)])
 def test_gae_large_sizes_sampled_episodes(L, N):
     """Large launches (33.5 M elements, 570 MB moved): 2048 columns of the
-    single-super-chunk path, and 64 chained super-chunks per column of the
-    look-back path; the oracle recomputes a spread of episodes (episodes are
-    independent), and every return is A + V."""
+    single-super-chunk path, 256 columns of 4 chained super-chunks, and 32
+    chained super-chunks per column; the oracle recomputes a spread of
+    episodes (episodes are independent), and every return is A + V."""
     r, v, d = synthdata.gae_inputs(N, L, seed=N + L)
     A, R = run(r, v, d)
     cols = np.unique(np.concatenate([np.arange(0, N, N // 37), [N - 1, N // 2 + 1]]))
@@ -117,3 +118,32 @@ def test_gae_large_sizes_sampled_episodes(L, N):
     assert close_mask(R[:, cols], Ro).all()
     assert np.array_equal(R, (A + v).astype(np.float32))
     assert np.isfinite(A).all()
+
+
+@pytest.mark.parametrize("L,N", [(513, 524288), (513, 2097157)])
+def test_gae_many_episodes_both_address_widths(L, N):
+    """Chained scans of very many episodes: 524,288 episodes address a
+    super-chunk with 32-bit offsets, 2,097,157 (over 2^21, so a super-chunk
+    spans more than 4 GiB of floats) with 64-bit addresses.  The inputs
+    repeat a block of 8191 episodes on the device (8191 is prime, so every
+    repeat lands at another place in the 64-episode columns), which keeps
+    the host's work small; the oracle recomputes a spread of episodes from
+    the block, and every return is A + V."""
+    import torch
+    import rl_experience_collection_amd as rx
+    B = 8191
+    blk = synthdata.gae_inputs(B, L, seed=N + L)
+    reps = -(-N // B)
+    R, V, D = (torch.from_numpy(x).cuda().repeat(1, reps)[:, :N].contiguous() for x in blk)
+    A, Rt = torch.empty_like(R), torch.empty_like(R)
+    rx.gae_scan(R, V, D, None, 0.99, 0.95, A, Rt)
+    torch.cuda.synchronize()
+    assert torch.equal(Rt, A + V)
+    assert bool(torch.isfinite(A).all())
+    cols = np.unique(np.concatenate([np.arange(0, N, N // 41), [N - 1, N // 2 + 1, 2 ** 21]]))
+    cols = cols[cols < N]
+    Ao, Ro = oracle.gae(*(np.ascontiguousarray(x[:, cols % B]) for x in blk), 0.99, 0.95)
+    Ag = A[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    Rg = Rt[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    assert close_mask(Ag, Ao).all(), np.abs(Ag - Ao).max()
+    assert close_mask(Rg, Ro).all()

@@ -319,7 +319,7 @@ def test_nonfinite_weights_are_counted_and_the_collection_completes(which, preci
 
 
 def test_gae_lookback_give_up_is_reported_not_silent(monkeypatch):
-    """Rollouts longer than 512 steps chain 256-step GAE chunks through
+    """Rollouts longer than 512 steps chain 512-step GAE chunks through
     bounded waits.  With the bound set to zero polls from the host (so every
     kernel still ends normally), every chunk but the latest gives up: each
     episode counts one event per such chunk in counters[2], and its
@@ -329,7 +329,7 @@ def test_gae_lookback_give_up_is_reported_not_silent(monkeypatch):
     import torch
     import rl_experience_collection_amd as rx
     N, L = 300, 1300
-    nk, last = -(-L // 256), (L - 1) // 256 * 256
+    nk, last = -(-L // 512), (L - 1) // 512 * 512
     monkeypatch.setenv("ROLLOUT_GAE_SPIN_LIMIT", "0")
     inp = synthdata.ppo_inputs(dict(N=N, L=L, n_bars=5000, seed=52), bias_scale=0.1)
     gpu = run_gpu(inp, logits=False)
