@@ -125,6 +125,57 @@ def time_collect(inp, steps, warmup, precision=0):
                 nonfinite=bad)
 
 
+def actor_phase_stamps(inp, reps, precision=0):
+    """Per-phase shader-clock cycles of one sequential step (the instrumented
+    step kernel, rollout_phase_cycles), averaged over every wave and step of
+    `reps` collections, beside the plain kernel's step time from the same
+    handle (phase events of as many plain collections)."""
+    import torch
+    import numpy as np
+    import rl_experience_collection_amd as rx
+
+    N, L = inp["N"], inp["L"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    w = inp["weights"]
+    weights = dict(actor=[dev(x) for x in w["actor"]], critic=[dev(x) for x in w["critic"]],
+                   curiosity=[dev(x) for x in w["curiosity"]])
+    feats, prices, starts = dev(inp["features"]), dev(inp["prices"]), dev(inp["starts"])
+    col = rx.Collector(N, L, weights, feats, prices, settings=inp["settings"], precision=precision)
+    outs = rx.alloc_outputs(N, L, "cuda")
+    seed = inp["sampler_seed"]
+    ev = rx.HipEvents(4 * reps)
+
+    def run(tag):
+        for i in range(reps):
+            col.collect(starts, seed + i, outputs=outs, phase_events=ev.handles[4 * i:4 * i + 4])
+        torch.cuda.synchronize()
+        return float(np.mean([ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(reps)]))
+
+    col.collect(starts, seed, outputs=outs)
+    plain_ms = run("plain")
+    col.phase_cycles(True)
+    col.collect(starts, seed, outputs=outs)  # warm the instrumented kernel
+    col.phase_cycles(True)                   # drop its counts
+    stamped_ms = run("stamped")
+    st = col.phase_cycles(False).astype(np.float64)
+    ev.close()
+    col.close()
+    real = st[:, 11] > 0  # waves that counted steps
+    steps = st[real, 11]
+    per = st[real, :11].sum(axis=0) / steps.sum()
+    loop = st[real, 12].sum() / steps.sum()
+    names = [f"{k:02d} {n}" for k, n in enumerate(rx.STAMP_PHASES)]
+    return dict(N=N, L=L, precision="bf16" if precision else "fp32", collections=reps,
+                waves=int(real.sum()), cycles_per_step=dict(zip(names, [round(x, 1) for x in per])),
+                phase_sum_cycles_per_step=round(float(per.sum()), 1),
+                loop_cycles_per_step=round(float(loop), 1),
+                # the stamped kernel's rollout phase (events) against its own loop cycles
+                clock_GHz=round(float(loop * L / (stamped_ms * 1e-3) / 1e9), 3),
+                plain_rollout_ms=round(plain_ms, 4), stamped_rollout_ms=round(stamped_ms, 4),
+                plain_us_per_step=round(plain_ms * 1e3 / L, 3),
+                stamped_us_per_step=round(stamped_ms * 1e3 / L, 3))
+
+
 def time_dqn(inp, steps, warmup):
     """DQN collections at the input's size; events around each launch."""
     import torch
@@ -448,6 +499,10 @@ def main():
                              "copy_1gib"),
                     help="one workload only (for profiler counter passes); prints its own "
                          "JSON line instead of the benchmark line")
+    ap.add_argument("--actor-stamps", action="store_true",
+                    help="per-phase cycles of the sequential step (instrumented kernel) at "
+                         "N=128 L=500 fp32 and bf16 and N=8192 L=500 fp32, one JSON line each, "
+                         "instead of the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the collection shards by episode and runs with no "
@@ -462,6 +517,11 @@ def main():
 
     if args.workload != "all":
         print(json.dumps(run_single(args.workload, args.steps, args.warmup)), flush=True)
+        return
+    if args.actor_stamps:
+        for name, prec in (("ppo_n128_l500", 0), ("ppo_n128_l500", 1), ("ppo_n8192_l500", 0)):
+            r = actor_phase_stamps(synthdata.ppo_inputs(name), max(3, min(args.steps, 10)), prec)
+            print(json.dumps(dict(workload=name, **r)), flush=True)
         return
 
     spec = dict(synthdata.WORKLOADS["ppo_n8192_l500"])

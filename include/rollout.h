@@ -176,6 +176,30 @@ int rollout_set_weights(rollout_handle h, const float *const actor[6],
 int rollout_collect(rollout_handle h, const int32_t *episode_starts, uint64_t seed,
                     const rollout_outputs *out, void *hip_stream);
 
+/* Profiling aid for the sequential step (PPO CUDA Pipeline Design, Kernel
+ * Phases, Phase A), whose chain of dependent work sets the time of a small
+ * batch.  A nonzero `enable` makes later rollout_collect calls on the handle
+ * run an instrumented build of the step kernel: every wave reads the clock
+ * (s_memtime, shader-clock cycles) at each phase boundary of each step and
+ * adds the cycles of every phase into a device buffer of the handle
+ * (allocated and cleared on the first enable); 0 switches back to the plain
+ * kernel.  With `out` (host, u64) not NULL the device is synchronized, the
+ * totals gathered since the previous such call are copied to `out` and
+ * cleared, and *n_written (if not NULL) gets the number of words:
+ * ROLLOUT_STAMP_WORDS per wave, 4 waves per workgroup of 16 episodes,
+ * ceil(N / 16) workgroups, so out_len must be at least
+ * 64 * ceil(N / 16).  Per wave: [0] state assembly and stores, [1] state
+ * barrier, [2] first layer, [3] barrier, [4] second layer, [5] barrier,
+ * [6] third layer, [7] barrier, [8] draw, [9] environment step, [10] stores
+ * and reset, [11] steps counted, [12] cycles of the whole step loop.  The
+ * clock is read through the scalar memory path, whose waits also cover the
+ * LDS reads in flight, so the instrumented step is slower than the plain
+ * one.  Errors: ROLLOUT_EINVAL (NULL handle, other device, out_len too
+ * small), ROLLOUT_ENOMEM, ROLLOUT_EHIP. */
+#define ROLLOUT_STAMP_WORDS 16
+int rollout_phase_cycles(rollout_handle h, int32_t enable, uint64_t *out, int64_t out_len,
+                         int64_t *n_written);
+
 /* Standalone GAE backward scan (PPO CUDA Pipeline Design, Kernel Phases,
  * Phase B) over [L][N] time-major inputs:
  *   delta_t = r_t + gamma * V_{t+1} * (1 - d_t) - V_t,  V_L = last_values[n]

@@ -28,7 +28,12 @@ LIB_PATH = os.path.join(PKG_DIR, "librollout.so")
 ROLLOUT_OK, ROLLOUT_EINVAL, ROLLOUT_ENOMEM, ROLLOUT_EHIP, ROLLOUT_ENOTIMPL = 0, -1, -2, -3, -4
 ROLLOUT_FP32, ROLLOUT_BF16 = 0, 1
 STATE_DIM, N_ACTIONS, N_FEATURES = 54, 45, 51
+STAMP_WORDS = 16  # per wave, rollout_phase_cycles
+STAMP_PHASES = ("state assembly and stores", "state barrier", "first layer", "barrier",
+                "second layer", "barrier", "third layer", "barrier", "draw",
+                "environment step", "stores and reset")
 EXPORTED = ("rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
+            "rollout_phase_cycles",
             "gae_scan", "gae_scan_noalloc", "rollout_destroy", "rollout_last_error",
             "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_set_epsilon",
             "dqn_collect", "dqn_destroy",
@@ -110,6 +115,7 @@ def load_library(path: str = LIB_PATH):
                                  C.POINTER(vp), vp, vp, i64, vp, C.POINTER(vp)]
     L.rollout_set_weights.argtypes = [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp), vp]
     L.rollout_collect.argtypes = [vp, vp, C.c_uint64, C.POINTER(RolloutOutputs), vp]
+    L.rollout_phase_cycles.argtypes = [vp, i32, vp, i64, C.POINTER(i64)]
     L.gae_scan.argtypes = [vp, vp, vp, vp, i32, i32, C.c_float, C.c_float, vp, vp, vp]
     L.gae_scan_noalloc.argtypes = L.gae_scan.argtypes
     L.rollout_destroy.argtypes = [vp]
@@ -132,7 +138,7 @@ def load_library(path: str = LIB_PATH):
     L.per_destroy.argtypes = [vp]
     L.per_destroy.restype = None
     for name in ("rollout_config_default", "rollout_create", "rollout_set_weights",
-                 "rollout_collect", "gae_scan", "gae_scan_noalloc", "dqn_config_default",
+                 "rollout_collect", "rollout_phase_cycles", "gae_scan", "gae_scan_noalloc", "dqn_config_default",
                  "dqn_create",
                  "dqn_set_weights", "dqn_set_epsilon", "dqn_collect", "per_create", "per_sample", "per_gather",
                  "per_update"):
@@ -353,6 +359,19 @@ class Collector:
             outputs = alloc_outputs(self.N, self.L, episode_starts.device, logits=logits)
         rollout_collect(self.handle, episode_starts, seed, outputs, stream, phase_events)
         return outputs
+
+    def phase_cycles(self, enable: bool):
+        """rollout_phase_cycles: switch the instrumented step kernel on or
+        off for later collections and return the per-wave cycle totals
+        gathered since the last call, shape [waves, STAMP_WORDS] (uint64)."""
+        import numpy as np
+        waves = 4 * -(-self.N // 16)
+        out = np.zeros((waves, STAMP_WORDS), np.uint64)
+        n = C.c_int64()
+        _check(load_library().rollout_phase_cycles(
+            C.c_void_p(self.handle), int(bool(enable)), out.ctypes.data_as(C.c_void_p),
+            out.size, C.byref(n)))
+        return out
 
     def close(self):
         if self.handle:

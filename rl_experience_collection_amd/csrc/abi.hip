@@ -116,6 +116,20 @@ uint32_t gae_spin_limit() {
   return x > rl::kGaeSpinLimit ? rl::kGaeSpinLimit : (uint32_t)x;
 }
 
+// Largest market (in bars) for which a collector keeps the actor's
+// first-layer feature table (512 bytes a bar): 2^21 bars, unless the
+// environment variable ROLLOUT_FEATURE_TABLE_MAX_BARS, read at
+// rollout_create, sets another bound (0: never; the step then computes that
+// part itself).
+int64_t feature_table_max_bars() {
+  const char* v = std::getenv("ROLLOUT_FEATURE_TABLE_MAX_BARS");
+  if (!v || !*v) return (int64_t)1 << 21;
+  char* end = nullptr;
+  const long long x = std::strtoll(v, &end, 10);
+  if (end == v || *end || x < 0) return (int64_t)1 << 21;
+  return (int64_t)x;
+}
+
 int gae_run(GaeScratch& s, rl::GaeArgs a, hipStream_t st) {
   if (a.L == 0 || a.N == 0) return ROLLOUT_OK;
   a.spin_limit = gae_spin_limit();
@@ -314,6 +328,7 @@ struct rollout_s {
   int32_t* start_used = nullptr; // [N]
   unsigned long long* value_sched = nullptr;  // work counter of the value kernel
   int32_t* bars = nullptr;       // [L][N] bar of every step (recycling only)
+  float* ftable = nullptr;       // [n_bars][128] actor first-layer feature part, or null
   GaeScratch gae;
   // the rollout split into `parts` launches, the value pass of each part on
   // `side` (only when parts > 1)
@@ -325,6 +340,10 @@ struct rollout_s {
   int32_t ov_grid = 0;  // value workgroups while a rollout part runs
   int32_t ov_pad = 0;   // their LDS reservation
   int32_t last_steps = 0;  // steps of the final part (its pass is not overlapped)
+  // per-wave phase cycle totals of the instrumented step kernel
+  uint64_t* stamps = nullptr;
+  size_t stamp_words = 0;
+  bool stamping = false;
 };
 
 extern "C" {
@@ -409,6 +428,15 @@ int rollout_create(const rollout_config* cfg, const float* const actor[6],
     return fail(ROLLOUT_ENOMEM, "cannot allocate scheduler counter");
   }
   h->value_sched = static_cast<unsigned long long*>(p);
+  if (n_bars <= feature_table_max_bars()) {
+    if (hipMalloc(&p, (size_t)n_bars * rl::kActorOut1 * sizeof(float)) != hipSuccess) {
+      (void)hipGetLastError();
+      rollout_destroy(h);
+      return fail(ROLLOUT_ENOMEM, "cannot allocate the feature table (%lld bars)",
+                  (long long)n_bars);
+    }
+    h->ftable = static_cast<float*>(p);
+  }
   if (cfg->recycle) {
     if (hipMalloc(&p, (size_t)cfg->n_episodes * cfg->n_steps * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
@@ -546,6 +574,12 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   ra.t_begin = 0;
   ra.t_end = L;
   ra.carry = h->carry;
+  ra.stamps = h->stamping ? h->stamps : nullptr;
+  ra.ftable = h->ftable;
+  // the feature part of every bar for the current weights and features
+  if (h->ftable)
+    RL_HIP(rl::launch_feature_table(h->weights, h->features, h->n_bars, ra.bf16 != 0, h->ftable, st),
+           "feature table launch");
 
   rl::ValueArgs va;
   va.weights = h->weights;
@@ -684,6 +718,49 @@ int gae_scan_noalloc(const float* rewards, const float* values, const uint8_t* d
   return gae_run(d.s, ga, st);
 }
 
+int rollout_phase_cycles(rollout_handle h, int32_t enable, uint64_t* out, int64_t out_len,
+                         int64_t* n_written) {
+  static_assert(ROLLOUT_STAMP_WORDS == rl::kStampWords, "stamp layout");
+  static_assert(rl::kSplit == 4 && rl::kRowsPerWave == 16, "stamp layout");
+  if (!h) return fail(ROLLOUT_EINVAL, "handle is NULL");
+  int dev = -1;
+  RL_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev != h->device)
+    return fail(ROLLOUT_EINVAL, "handle was created on device %d, current device is %d", h->device, dev);
+  const size_t words = (size_t)rl::kStampWords * rl::kSplit *
+                       (size_t)((h->cfg.n_episodes + rl::kRowsPerWave - 1) / rl::kRowsPerWave);
+  if (out && out_len < (int64_t)words)
+    return fail(ROLLOUT_EINVAL, "rollout_phase_cycles: out_len %lld < %zu words",
+                (long long)out_len, words);
+  if (n_written) *n_written = 0;
+  if (out) {
+    RL_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    if (h->stamps) {
+      RL_HIP(hipMemcpy(out, h->stamps, words * 8, hipMemcpyDeviceToHost), "copy stamps");
+      RL_HIP(rl::zero_words(reinterpret_cast<uint32_t*>(h->stamps), words * 2, nullptr),
+             "clear stamps");
+      RL_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    } else {
+      std::memset(out, 0, words * 8);
+    }
+    if (n_written) *n_written = (int64_t)words;
+  }
+  if (enable && !h->stamps) {
+    void* p = nullptr;
+    if (hipMalloc(&p, words * 8) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ROLLOUT_ENOMEM, "stamps: cannot allocate %zu bytes", words * 8);
+    }
+    h->stamps = static_cast<uint64_t*>(p);
+    h->stamp_words = words;
+    RL_HIP(rl::zero_words(reinterpret_cast<uint32_t*>(h->stamps), words * 2, nullptr),
+           "clear stamps");
+    RL_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  }
+  h->stamping = enable != 0;
+  return ROLLOUT_OK;
+}
+
 void rollout_destroy(rollout_handle h) {
   if (!h) return;
   // value passes of a split rollout may still run on the handle's own
@@ -698,6 +775,8 @@ void rollout_destroy(rollout_handle h) {
   if (h->values_done) (void)hipEventDestroy(h->values_done);
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->carry) (void)hipFree(h->carry);
+  if (h->stamps) (void)hipFree(h->stamps);
+  if (h->ftable) (void)hipFree(h->ftable);
   delete h;
 }
 

@@ -32,7 +32,18 @@ struct RolloutArgs {
   int32_t* bars;          // [L][N] bar of every step, or null: non-null selects recycling
   int32_t t_begin, t_end; // the steps of this launch: [0, L) for the whole rollout
   int32_t* carry;         // [N][kCarryWords] episode state between launches, or null
+  // [blocks * kSplit][kStampWords] per-wave cycle totals (instrumented
+  // kernel), or null: the plain kernel
+  uint64_t* stamps;
+  // [n_bars][kActorOut1] first-layer feature part of every bar (written by
+  // launch_feature_table), or null: computed in the step
+  const float* ftable;
 };
+
+// Cycle totals of one wave of the instrumented step kernel: kStampPhases
+// phases of every step, then the steps counted and the whole loop's cycles.
+constexpr int kStampWords = 16;
+constexpr int kStampPhases = 11;
 
 // Episode state a launch that ends before step L leaves for the next one:
 // bar (2 words), V, exposure held, entry price, armed, side, open step,
@@ -88,6 +99,9 @@ struct DqnArgs {
 };
 
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st);
+// The feature table of RolloutArgs::ftable for the packed weights' actor.
+hipError_t launch_feature_table(const float* weights, const float* features, int64_t n_bars,
+                                bool bf16, float* table, hipStream_t st);
 hipError_t launch_dqn(const DqnArgs& a, hipStream_t st);
 hipError_t launch_value(const ValueArgs& a, hipStream_t st);
 // Static LDS bytes of a workgroup of the rollout / value kernel (-1 on error).

@@ -60,6 +60,7 @@ __host__ __device__ constexpr int ring_depth(bool bf16, int otw) {
 // Its first layer takes the state in natural order (first = 2: k = 4 s + g),
 // so the portfolio inputs k >= 48 sit in k-steps 12 and 13 only.
 constexpr LayerDesc kActor[3] = {{54, 128, 16, 2, 8, 0}, {128, 64, 32, 0, 4, 0}, {64, 45, 16, 0, 4, 0}};
+constexpr int kActorOut1 = 128;  // first-layer outputs of the actor
 // Critic: 54 -> 512 -> 384 -> 256 -> 128 -> 64 (-> 1 handled on the VALU).
 constexpr LayerDesc kCritic[5] = {{54, 512, 16, 1, 32, 0},
                                   {512, 384, 128, 0, 24, 0},

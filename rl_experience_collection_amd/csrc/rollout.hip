@@ -100,7 +100,9 @@ __device__ __forceinline__ void reg_mfma(const RegLayer<BF16, S, OTW>& L, const 
 // MFMAs of k-step p (the whole part for bf16, where it is one k-step) with
 // scheduling fences on both sides, so callers can place them between
 // independent VALU work.  The B operands are read once, at construction.
-template <bool BF16, int S, int TAIL>
+// With ACTIVE false (the part comes from the feature table instead) it
+// reads and issues nothing.
+template <bool BF16, int S, int TAIL, bool ACTIVE>
 struct PreStepper {
   const RegLayer<BF16, S, 2>& L;
   typename std::conditional<BF16, uint4, f32x4>::type b[BF16 ? TAIL : (TAIL + 3) / 4];
@@ -108,7 +110,9 @@ struct PreStepper {
       : L(layer) {
 #pragma unroll
     for (int i = 0; i < (BF16 ? TAIL : (TAIL + 3) / 4); ++i) {
-      if constexpr (BF16)
+      if constexpr (!ACTIVE)
+        ;
+      else if constexpr (BF16)
         b[i] = reinterpret_cast<const uint4*>(buf)[i * 64 + lane];
       else
         b[i] = buf[i * 64 + lane];
@@ -116,7 +120,7 @@ struct PreStepper {
   }
   template <int P>
   __device__ __forceinline__ void step(f32x4 (&acc)[2]) const {
-    if constexpr (P < TAIL) {
+    if constexpr (ACTIVE && P < TAIL) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -130,7 +134,60 @@ struct PreStepper {
   }
 };
 
-template <bool BF16, bool RECYCLE>
+// The actor's first-layer feature part: the first kTail k-steps of the first
+// layer (k < 48 in fp32, k < 32 in bf16) read only the bar's market features
+// (the portfolio inputs come after them), so bias + that part is a function
+// of the bar alone.  The feature table holds it for every bar, [n_bars][128]
+// fp32 at output o = 16 * tile + 4 * g + c (the accumulator layout: lane
+// e + 16 g of the wave that owns `tile` holds outputs 4g .. 4g+3 of row e).
+template <bool BF16>
+constexpr int feature_tail() { return BF16 ? 1 : 12; }
+
+__device__ __forceinline__ void load_table_part(const float* __restrict__ table, int64_t bar, int q,
+                                                int lane, f32x4 (&pre)[2]) {
+  const float* row = table + bar * kActorOut1 + 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pre[i] = *reinterpret_cast<const f32x4*>(row + 16 * (2 * q + i));
+}
+
+// One workgroup per 16 bars: the same operands, MFMA instructions and order
+// as the step kernel's in-place computation, so the table holds the same
+// bits.
+template <bool BF16>
+__global__ __launch_bounds__(64 * kSplit) void feature_table_kernel(const float* __restrict__ weights,
+                                                                    const float* __restrict__ features,
+                                                                    int64_t n_bars,
+                                                                    float* __restrict__ table) {
+  constexpr int kTail = feature_tail<BF16>();
+  __shared__ f32x4 s_state[4 * 64];
+  const int lane = threadIdx.x & 63;
+  const int q = threadIdx.x >> 6;
+  RegLayer<BF16, kTail, 2> w1;
+  load_reg_layer(w1, weights + (BF16 ? kP.bact_w[0] : kP.actor_w[0]),
+                 weights + (BF16 ? kP.bact_b[0] : kP.actor_b[0]), q, lane);
+  s_state[threadIdx.x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  __syncthreads();
+  const int64_t bar0 = (int64_t)blockIdx.x * kRowsPerWave;
+  constexpr int kIn = BF16 ? 32 * kTail : 4 * kTail;  // inputs of the part
+  for (int x = threadIdx.x; x < kRowsPerWave * kIn; x += 64 * kSplit) {
+    const int e = x / kIn, k = x % kIn;
+    const int64_t bar = bar0 + e < n_bars ? bar0 + e : n_bars - 1;
+    put_state<BF16>(s_state, e, k, features[bar * kFeatures + k]);
+  }
+  __syncthreads();
+  f32x4 pre[2] = {w1.bias[0], w1.bias[1]};
+  reg_mfma<0, kTail>(w1, s_state, pre, lane);
+  const int64_t bar = bar0 + (lane & 15);
+  if (bar < n_bars) {
+    float* row = table + bar * kActorOut1 + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<f32x4*>(row + 16 * (2 * q + i)) = pre[i];
+  }
+}
+
+// TABLE: the first-layer feature part comes from the feature table
+// (a.ftable), loaded a step ahead, instead of being computed in the step.
+template <bool BF16, bool RECYCLE, bool STAMPS, bool TABLE>
 __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs a) {
   __shared__ int s_restart[2];  // recycling: an episode of the workgroup restarted in step t (t % 2)
   __shared__ f32x4 s_bufA[kBufA];
@@ -138,6 +195,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   __shared__ f32x4 s_state[4 * 64];
   __shared__ float s_ln[33];  // ln k for window counts k = 0..32 (ln 0 unused: times 0)
   __shared__ float s_env[kEnvTable];
+  __shared__ int64_t s_bar[kRowsPerWave];  // feature table: each row's bar of the step
 
   const int lane = threadIdx.x & 63;
   const int q = threadIdx.x >> 6;
@@ -155,7 +213,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   constexpr int kS3 = BF16 ? kActorB[2].steps : kActor[2].steps;
   // first k-step holding a portfolio input (k = 48 .. 53): the steps before
   // it depend only on market features, known a step ahead
-  constexpr int kTail = BF16 ? 1 : 12;
+  constexpr int kTail = feature_tail<BF16>();
   RegLayer<BF16, kS1, 2> w1;
   RegLayer<BF16, kS2, 1> w2;
   RegLayer<BF16, kS3, 1> w3;
@@ -210,25 +268,53 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   f32x4* bufA = s_bufA;
   f32x4* bufB = s_bufB;
   f32x4* sbuf = s_state;
+  uint32_t n_bad = 0;  // this row's steps with a non-finite logit (lane j = 0)
 
   // features and prices of the first step's bar and the one after
   float f0[4], f1[4];
   load_features(a.features, bar, j, f0);
   load_features(a.features, bar + 1, j, f1);
   float p0 = a.prices[bar], p1 = a.prices[bar + 1];
+  if (TABLE && j == 0) s_bar[e] = bar;
   lds_barrier();  // operand buffer cleared
   if (j == 2) put_state<BF16>(sbuf, e, 53, ep.spread);  // constant element
 #pragma unroll
   for (int h = 0; h < 4; ++h)
     if (j + 16 * h < kFeatures) put_state<BF16>(sbuf, e, j + 16 * h, f0[h]);
   lds_barrier();
-  // first-layer feature part of step 0
+  // first-layer feature part of step 0; with the table, the bar of this
+  // lane's MFMA row (episode lane % 16), which then advances by one a step
+  // (recycling: read again each step)
   f32x4 pre[2];
-  pre[0] = w1.bias[0];
-  pre[1] = w1.bias[1];
-  reg_mfma<0, kTail>(w1, sbuf, pre, lane);
+  int64_t bar_m = 0;
+  if constexpr (TABLE) {
+    bar_m = s_bar[lane & 15];
+    load_table_part(a.ftable, bar_m, q, lane, pre);
+  } else {
+    pre[0] = w1.bias[0];
+    pre[1] = w1.bias[1];
+    reg_mfma<0, kTail>(w1, sbuf, pre, lane);
+  }
+
+  // instrumented build: the clock at each phase boundary of a step, added
+  // up per phase (the same value in every lane of the wave)
+  uint64_t ph[kStampPhases];
+  uint64_t t_prev = 0, t_loop = 0;
+  if constexpr (STAMPS) {
+#pragma unroll
+    for (int k = 0; k < kStampPhases; ++k) ph[k] = 0;
+    t_loop = __builtin_amdgcn_s_memtime();
+  }
+  auto stamp = [&](int k) {
+    if constexpr (STAMPS) {
+      const uint64_t now = __builtin_amdgcn_s_memtime();
+      ph[k] += now - t_prev;
+      t_prev = now;
+    }
+  };
 
   for (int32_t t = a.t_begin; t < a.t_end; ++t) {
+    if constexpr (STAMPS) t_prev = __builtin_amdgcn_s_memtime();
     const int64_t o = (int64_t)t * a.N + n;
 
     // prefetch two bars ahead (independent of the outcomes), issued before
@@ -246,7 +332,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
       load_features(a.features, rbar + 1, j, fr1);
       pr0 = a.prices[rbar];
       pr1 = a.prices[rbar + 1];
-      if (valid && j == 0) a.bars[o] = (int32_t)bar;  // the value kernel's next-bar index
+      a.bars[o] = (int32_t)bar;  // the value kernel's next-bar index
     }
 
     // ---- steps 1-2: state = 51 features, V/V0 - 1, exposure held, spread --
@@ -254,13 +340,23 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     const float vn = V / V0 - 1.0f;
     if (j == 0) put_state<BF16>(sbuf, e, 51, vn);
     if (j == 1) put_state<BF16>(sbuf, e, 52, e_prev);
-    if (valid) {
+    {
+      // The step's memory stores carry no branches, so every path leaves
+      // the same number of memory operations in flight and the wait for the
+      // bars loaded ahead does not cover this step's stores: every lane
+      // stores (lanes past the row's 54 elements repeat the last one), and
+      // rows past N repeat episode N-1, whose very trajectory they run, so
+      // repeated stores write the same bytes.
       float* srow = a.states + o * kState;
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        if (j + 16 * h < kFeatures) srow[j + 16 * h] = f0[h];
-      if (j < 3) srow[kFeatures + j] = j == 0 ? vn : (j == 1 ? e_prev : ep.spread);
+      for (int h = 0; h < 4; ++h) {
+        const int k = j + 16 * h;
+        float x = f0[h];
+        if (h == 3 && k >= kFeatures) x = k == kFeatures ? vn : (k == kFeatures + 1 ? e_prev : ep.spread);
+        srow[k < kState ? k : kState - 1] = x;
+      }
     }
+    stamp(0);       // state assembly and stores
     lds_barrier();  // state operands complete; last step's logits read
     if constexpr (RECYCLE) {
       // an episode restarted last step: its new features replaced those the
@@ -273,7 +369,16 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
         reg_mfma<0, kTail>(w1, sbuf, pre, lane);
       }
     }
+    // the table part of the next step's bar (recycling: the bar after this
+    // one; a restart in this step is caught by the recompute above)
+    f32x4 pre_next[2];
+    if constexpr (TABLE) {
+      if constexpr (RECYCLE) bar_m = s_bar[lane & 15];
+      load_table_part(a.ftable, bar_m + 1 < a.n_bars ? bar_m + 1 : a.n_bars - 1, q, lane, pre_next);
+      bar_m += 1;
+    }
 
+    stamp(1);  // state barrier
     // the step's draw depends only on (seed, episode, step)
     const float u = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 0u);
     // the layer chain and the draw run at a raised wave priority, so where
@@ -291,7 +396,9 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
       else
         relu_store<2>(h, bufA, q, lane);
     }
+    stamp(2);  // first layer
     lds_barrier();
+    stamp(3);
     // next step's features into the operand buffer (this step's state has
     // been read); the next feature part reads them after the next barrier
 #pragma unroll
@@ -305,7 +412,9 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
       else
         relu_store<1>(h, bufB, q, lane);
     }
+    stamp(4);  // second layer (and the next step's features into LDS)
     lds_barrier();
+    stamp(5);
     {
       f32x4 h[1] = {w3.bias[0]};
       reg_mfma<0, kS3>(w3, bufB, h, lane);
@@ -314,14 +423,21 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
       // logit k of row e at bufA[(k / 16) * 64 + e + 16 * (k % 16 / 4)][k % 4]
       bufA[q * 64 + lane] = h[0];
     }
+    stamp(6);  // third layer
     lds_barrier();
+    stamp(7);
 
     // first-layer feature part of the next step: its k-steps are spread
     // over the draw and environment below (one k-step per point, pinned by
     // scheduling fences), so the MFMAs run while the VALU works
-    pre[0] = w1.bias[0];
-    pre[1] = w1.bias[1];
-    PreStepper<BF16, kS1, kTail> ps(w1, sbuf, lane);
+    if constexpr (TABLE) {
+      pre[0] = pre_next[0];
+      pre[1] = pre_next[1];
+    } else {
+      pre[0] = w1.bias[0];
+      pre[1] = w1.bias[1];
+    }
+    PreStepper<BF16, kS1, kTail, !TABLE> ps(w1, sbuf, lane);
 
     // ---- step 4: softmax, CDF, inverse-CDF draw, log-prob -----------------
     // lane j of the episode's row holds logits k = j + 16 h, h = 0..2
@@ -383,6 +499,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     const float logp = (la - m) - logf(S);
     ps.template step<5>(pre);
     bad = row_max_i(bad);
+    stamp(8);  // draw
 
     __builtin_amdgcn_s_setprio(0);
     // ---- step 6: portfolio (exposure fraction of equity, turnover cost) ---
@@ -441,25 +558,25 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
                      (((float)cnt0 * s_ln[cnt0] + (float)cnt1 * s_ln[cnt1]) + (float)cnt2 * s_ln[cnt2]);
     const float div = hn < ep.div_threshold * (float)nn ? ep.div_penalty : 0.0f;
 
+    stamp(9);  // environment
     // ---- steps 10-11: partial reward and stores (lane 0 of the row) -------
     const float partial = pnl * (1.0f + ep.barrier_scale * (float)hit) + div;
     ps.template step<10>(pre);
     const int done = code != 0;
-    if (valid) {
-      if (j == 0) {
-        a.actions[o] = act_a;
-        a.log_probs[o] = logp;
-        a.rewards[o] = partial;
-        a.dones[o] = (uint8_t)done;
-        a.barrier[o] = (uint8_t)code;
-        if (bad && a.counters) atomicAdd(a.counters, 1u);
-      }
-      if (a.logits) {
-        float* lrow = a.logits + o * kActions;
-#pragma unroll
-        for (int h = 0; h < 3; ++h)
-          if (ok[h]) lrow[j + 16 * h] = l[h];
-      }
+    // every lane of the row holds the same results: all store (see the
+    // state stores above)
+    a.actions[o] = act_a;
+    a.log_probs[o] = logp;
+    a.rewards[o] = partial;
+    a.dones[o] = (uint8_t)done;
+    a.barrier[o] = (uint8_t)code;
+    n_bad += (bad && valid && j == 0) ? 1u : 0u;
+    if (a.logits) {
+      float* lrow = a.logits + o * kActions;
+      lrow[j] = l[0];
+      lrow[j + 16] = l[1];
+      // lanes past logit 44 repeat their logit j + 16
+      lrow[ok[2] ? j + 32 : j + 16] = ok[2] ? l[2] : l[1];
     }
 
     // ---- step 12: reset on done; the bar pointer keeps advancing ------------
@@ -492,8 +609,24 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
           if (j + 16 * h < kFeatures) put_state<BF16>(sbuf, e, j + 16 * h, f0[h]);
         if (j == 0) s_restart[t & 1] = 1;
       }
+      // the bar of the next step, for the feature table (read after the
+      // next step's first barrier)
+      if (TABLE && j == 0) s_bar[e] = bar;
+    }
+    stamp(10);  // stores and reset
+  }
+  if constexpr (STAMPS) {
+    const uint64_t loop = __builtin_amdgcn_s_memtime() - t_loop;
+    if (lane == 0) {
+      // one wave per slot; the launches of a collection are stream-ordered
+      uint64_t* s = a.stamps + ((int64_t)blockIdx.x * kSplit + q) * kStampWords;
+#pragma unroll
+      for (int k = 0; k < kStampPhases; ++k) s[k] += ph[k];
+      s[kStampPhases] += (uint64_t)(a.t_end - a.t_begin);
+      s[kStampPhases + 1] += loop;
     }
   }
+  if (n_bad && a.counters) atomicAdd(a.counters, n_bad);
   if (a.t_end < a.L && valid && j == 0) {
     int32_t* c = a.carry + (int64_t)n * kCarryWords;
     c[0] = (int32_t)(uint32_t)bar; c[1] = (int32_t)(bar >> 32);
@@ -507,8 +640,10 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
 }  // namespace
 
 int actor_lds_bytes(bool bf16, bool recycle) {
-  auto kernel = bf16 ? (recycle ? actor_rollout_kernel<true, true> : actor_rollout_kernel<true, false>)
-                     : (recycle ? actor_rollout_kernel<false, true> : actor_rollout_kernel<false, false>);
+  auto kernel = bf16 ? (recycle ? actor_rollout_kernel<true, true, false, true>
+                                : actor_rollout_kernel<true, false, false, true>)
+                     : (recycle ? actor_rollout_kernel<false, true, false, true>
+                                : actor_rollout_kernel<false, false, false, true>);
   hipFuncAttributes at;
   if (hipFuncGetAttributes(&at, reinterpret_cast<const void*>(kernel)) != hipSuccess) return -1;
   return (int)at.sharedSizeBytes;
@@ -522,9 +657,25 @@ hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
       ((a.t_begin > 0 || a.t_end < a.L) && !a.carry))
     return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((a.N + kRowsPerWave - 1) / kRowsPerWave);
-  auto kernel = a.bf16 ? (a.bars ? actor_rollout_kernel<true, true> : actor_rollout_kernel<true, false>)
-                       : (a.bars ? actor_rollout_kernel<false, true> : actor_rollout_kernel<false, false>);
+  auto pick = [&](auto stamps, auto table) {
+    constexpr bool S = decltype(stamps)::value, T = decltype(table)::value;
+    return a.bf16 ? (a.bars ? actor_rollout_kernel<true, true, S, T> : actor_rollout_kernel<true, false, S, T>)
+                  : (a.bars ? actor_rollout_kernel<false, true, S, T> : actor_rollout_kernel<false, false, S, T>);
+  };
+  auto kernel = a.ftable ? (a.stamps ? pick(std::true_type{}, std::true_type{})
+                                     : pick(std::false_type{}, std::true_type{}))
+                         : (a.stamps ? pick(std::true_type{}, std::false_type{})
+                                     : pick(std::false_type{}, std::false_type{}));
   hipLaunchKernelGGL(kernel, dim3(blocks), dim3(64 * kSplit), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_feature_table(const float* weights, const float* features, int64_t n_bars,
+                                bool bf16, float* table, hipStream_t st) {
+  if (n_bars <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n_bars + kRowsPerWave - 1) / kRowsPerWave);
+  hipLaunchKernelGGL(bf16 ? feature_table_kernel<true> : feature_table_kernel<false>, dim3(blocks),
+                     dim3(64 * kSplit), 0, st, weights, features, n_bars, table);
   return hipGetLastError();
 }
 

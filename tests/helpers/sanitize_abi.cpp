@@ -77,6 +77,8 @@ int main() {
          "handle");
   expect(rollout_collect(nullptr, nullptr, 0, nullptr, nullptr), ROLLOUT_EINVAL, "collect(NULL)",
          "handle");
+  expect(rollout_phase_cycles(nullptr, 1, nullptr, 0, nullptr), ROLLOUT_EINVAL,
+         "phase_cycles(NULL)", "handle");
   expect(gae_scan(nullptr, nullptr, nullptr, nullptr, 0, 5, 0.99f, 0.95f, nullptr, nullptr,
                   nullptr),
          ROLLOUT_OK, "gae_scan(L = 0)");

@@ -30,6 +30,7 @@ def rx():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["rollout_config_default", "rollout_create", "rollout_set_weights", "rollout_collect",
+         "rollout_phase_cycles",
          "gae_scan", "gae_scan_noalloc", "rollout_destroy", "rollout_last_error",
          "dqn_config_default", "dqn_create", "dqn_set_weights", "dqn_set_epsilon",
          "dqn_collect", "dqn_destroy", "per_create", "per_sample", "per_gather", "per_update", "per_destroy"])
@@ -109,6 +110,13 @@ def test_gae_scan_noalloc_rejects_scans_beyond_its_scratch(rx):
         rx.ROLLOUT_EINVAL
     assert lib.gae_scan_noalloc(None, None, None, None, 3, -5, 0.99, 0.95, None, None, None) == \
         rx.ROLLOUT_EINVAL
+
+
+def test_rollout_phase_cycles_rejects_a_null_handle(rx):
+    lib = rx.load_library()
+    n = C.c_int64(7)
+    assert lib.rollout_phase_cycles(None, 1, None, 0, C.byref(n)) == rx.ROLLOUT_EINVAL
+    assert "handle" in rx.rollout_last_error()
 
 
 def test_dqn_config_default_values(rx):

@@ -350,3 +350,67 @@ def test_gae_lookback_give_up_is_reported_not_silent(monkeypatch):
     gpu2 = run_gpu(inp, logits=False)
     assert int(gpu2["counters"][2]) == 0
     assert close_mask(gpu2["advantages"], A).all() and close_mask(gpu2["returns"], R).all()
+
+
+@pytest.mark.parametrize("precision,recycle", [(0, 0), (1, 1)])
+def test_instrumented_step_kernel_gives_the_same_collection(precision, recycle):
+    """rollout_phase_cycles switches in a build of the step kernel that reads
+    the clock at every phase boundary: the collection it produces is bit for
+    bit the plain kernel's (N=128 is split into several launches with value
+    passes beside them), every wave counts all L steps, and the phases add
+    up to no more than the loop's cycles."""
+    import torch
+    import rl_experience_collection_amd as rx
+    from parity import to_device
+    inp = synthdata.ppo_inputs(dict(N=128, L=500, n_bars=3000, seed=61), bias_scale=0.1)
+    d = to_device(inp)
+    settings = dict(inp["settings"], recycle=recycle)
+    col = rx.Collector(inp["N"], inp["L"], d["weights"], d["features"], d["prices"],
+                       settings=settings, precision=precision)
+    plain = {k: v.clone() for k, v in col.collect(d["starts"], inp["sampler_seed"]).items()
+             if v is not None}
+    col.phase_cycles(True)
+    stamped = col.collect(d["starts"], inp["sampler_seed"])
+    st = col.phase_cycles(False)
+    torch.cuda.synchronize()
+    for k, v in plain.items():
+        assert torch.equal(v, stamped[k]), k
+    assert st.shape == (4 * 128 // 16, rx.STAMP_WORDS)
+    assert (st[:, 11] == inp["L"]).all()
+    assert (st[:, :11].sum(axis=1) <= st[:, 12]).all() and (st[:, 12] > 0).all()
+    # switched off again: the plain kernel counts nothing
+    col.collect(d["starts"], inp["sampler_seed"])
+    assert (col.phase_cycles(False) == 0).all()
+    col.close()
+
+
+@pytest.mark.parametrize("precision,recycle", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_feature_table_gives_the_same_collection(monkeypatch, precision, recycle):
+    """By default the actor's first-layer feature part (bias plus the
+    k-steps that read only market features) comes from a per-bar table
+    computed at each collection; with ROLLOUT_FEATURE_TABLE_MAX_BARS=0 at
+    create the step computes it itself.  Both use the same MFMA instructions
+    on the same operands, so the collections match bit for bit, restarts of
+    recycled episodes included (N=40 leaves a ragged workgroup; N=128 is
+    split into launches)."""
+    import torch
+    import rl_experience_collection_amd as rx
+    from parity import to_device
+    for N, L in ((40, 130), (128, 300)):
+        inp = synthdata.ppo_inputs(dict(N=N, L=L, n_bars=2000, seed=71 + N), bias_scale=0.1)
+        d = to_device(inp)
+        settings = dict(inp["settings"], recycle=recycle)
+        outs = []
+        for table in (True, False):
+            if not table:
+                monkeypatch.setenv("ROLLOUT_FEATURE_TABLE_MAX_BARS", "0")
+            col = rx.Collector(N, L, d["weights"], d["features"], d["prices"], settings=settings,
+                               precision=precision)
+            outs.append(col.collect(d["starts"], inp["sampler_seed"], logits=True))
+            torch.cuda.synchronize()
+            col.close()
+            monkeypatch.delenv("ROLLOUT_FEATURE_TABLE_MAX_BARS", raising=False)
+        for k, v in outs[0].items():
+            if v is not None:
+                assert torch.equal(v, outs[1][k]), (N, k)
+        assert int(outs[0]["dones"].sum()) > 0
