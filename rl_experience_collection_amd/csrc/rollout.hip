@@ -194,7 +194,6 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   __shared__ f32x4 s_bufB[kBufB];
   __shared__ f32x4 s_state[4 * 64];
   __shared__ float s_ln[33];  // ln k for window counts k = 0..32 (ln 0 unused: times 0)
-  __shared__ float s_env[kEnvTable];
   __shared__ int64_t s_bar[kRowsPerWave];  // feature table: each row's bar of the step
 
   const int lane = threadIdx.x & 63;
@@ -202,7 +201,6 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
 
   if (threadIdx.x <= 32) s_ln[threadIdx.x] = threadIdx.x == 0 ? 0.0f : logf((float)threadIdx.x);
   if (threadIdx.x < 2) s_restart[threadIdx.x] = 0;
-  fill_env_table(a.ep, s_env, (int)threadIdx.x);
   // state operands start at zero: the padding slots stay zero
   s_state[threadIdx.x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -313,9 +311,18 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     }
   };
 
+  // the step's draw (and, recycling, its restart bar), 16 steps at a time
+  RowDraws u_pool, rb_pool;
   for (int32_t t = a.t_begin; t < a.t_end; ++t) {
     if constexpr (STAMPS) t_prev = __builtin_amdgcn_s_memtime();
     const int64_t o = (int64_t)t * a.N + n;
+    const int slot16 = (t - a.t_begin) & 15;
+    if (slot16 == 0) {
+      const int32_t tj = t + j;
+      u_pool.pool = __float_as_uint(draw_uniform(a.seed, (uint32_t)n, (uint32_t)tj, 0u));
+      if constexpr (RECYCLE)
+        rb_pool.pool = tj + 1 < a.L ? (uint32_t)recycle_bar(a.seed, (uint32_t)n, tj, a.L, a.n_bars) : 0u;
+    }
 
     // prefetch two bars ahead (independent of the outcomes), issued before
     // this step's stores so that no wait in the step covers them
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     int64_t rbar = 0;
     float fr0[4], fr1[4], pr0 = 0.0f, pr1 = 0.0f;
     if constexpr (RECYCLE) {
-      rbar = t + 1 < a.L ? recycle_bar(a.seed, (uint32_t)n, t, a.L, a.n_bars) : bar;
+      rbar = t + 1 < a.L ? (int64_t)rb_pool.take(slot16, lane) : bar;
       load_features(a.features, rbar, j, fr0);
       load_features(a.features, rbar + 1, j, fr1);
       pr0 = a.prices[rbar];
@@ -380,7 +387,7 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
 
     stamp(1);  // state barrier
     // the step's draw depends only on (seed, episode, step)
-    const float u = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 0u);
+    const float u = __uint_as_float(u_pool.take(slot16, lane));
     // the layer chain and the draw run at a raised wave priority, so where
     // the two workgroups of a CU meet, the one in them issues first (the
     // environment step below returns to the base priority)
@@ -506,50 +513,57 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     const int xi = act_a / 9;
     const int oi = (act_a % 9) / 3;
     const int ui = act_a % 3;
-    const float exq = s_env[xi];
-    const float cost = s_env[5 + oi] * (1.0f + ep.urgency_mult * (float)ui);
+    // the exposure and cost-rate tables by selects on the kernel arguments
+    // (no table lookup in the step's dependent chain)
+    float exq = ep.ex0, rate = ep.cost0;
+    exq = xi == 1 ? ep.ex1 : exq;
+    exq = xi == 2 ? ep.ex2 : exq;
+    exq = xi == 3 ? ep.ex3 : exq;
+    exq = xi == 4 ? ep.ex4 : exq;
+    rate = oi == 1 ? ep.cost1 : rate;
+    rate = oi == 2 ? ep.cost2 : rate;
+    const float cost = rate * (1.0f + ep.urgency_mult * (float)ui);
     const float ret = p1 / p0 - 1.0f;
     const float pnl = exq * ret - cost * fabsf(exq - e_prev);
     V = V * (1.0f + pnl);
     ps.template step<6>(pre);
 
     // ---- step 7: triple barrier on raw prices ------------------------------
-    if (exq != 0.0f) {
+    // (selects: the four episodes of a wave take different branches)
+    {
       const int sd = exq > 0.0f ? 1 : -1;
       const int prev = e_prev > 0.0f ? 1 : (e_prev < 0.0f ? -1 : 0);
-      if (prev == 0 || prev != sd) {
-        armed = 1;
-        side = sd;
-        entry = p0;
-        t_open = t;
-      }
-    } else {
-      armed = 0;
+      // a position opens, or flips side: the barriers are set at this bar
+      const bool open = exq != 0.0f && (prev == 0 || prev != sd);
+      armed = exq != 0.0f ? (open ? 1 : armed) : 0;
+      side = open ? sd : side;
+      entry = open ? p0 : entry;
+      t_open = open ? t : t_open;
     }
-    int hit = 0, code = 0;
     ps.template step<7>(pre);
-    if (armed) {
-      if (side > 0) {
-        if (p1 >= entry * ep.up_pt) { hit = 1; code = 1; }
-        else if (p1 <= entry * ep.dn_sl) { hit = -1; code = 2; }
-      } else {
-        if (p1 <= entry * ep.dn_pt) { hit = 1; code = 1; }
-        else if (p1 >= entry * ep.up_sl) { hit = -1; code = 2; }
-      }
-      if (code == 0 && t + 1 - t_open >= ep.max_hold) code = 3;
-    }
+    const bool lng = side > 0;
+    const float take_px = entry * (lng ? ep.up_pt : ep.dn_pt);
+    const float stop_px = entry * (lng ? ep.dn_sl : ep.up_sl);
+    const bool take = lng ? p1 >= take_px : p1 <= take_px;
+    const bool stop = lng ? p1 <= stop_px : p1 >= stop_px;
+    const bool expire = t + 1 - t_open >= ep.max_hold;
+    const int hit = armed ? (take ? 1 : (stop ? -1 : 0)) : 0;
+    const int code = armed ? (take ? 1 : (stop ? 2 : (expire ? 3 : 0))) : 0;
 
     // ---- step 8: diversity window, 3-class entropy in nats -----------------
     // H = ln n - (sum_c n_c ln n_c) / n, compared as n ln n - sum n_c ln n_c
     // < threshold * n; ln of the counts 0..32 comes from an LDS table
     const int cat = xi <= 1 ? 0 : (xi == 2 ? 1 : 2);
     ps.template step<8>(pre);
-    if (pushed >= ep.div_window) {
+    {
+      // a full window drops its oldest entry, the one this slot holds
+      const bool full = pushed >= ep.div_window;
       const int old = (int)((ring >> (2 * pos)) & 3u);
-      cnt0 -= old == 0; cnt1 -= old == 1; cnt2 -= old == 2;
+      cnt0 += (cat == 0) - (full && old == 0);
+      cnt1 += (cat == 1) - (full && old == 1);
+      cnt2 += (cat == 2) - (full && old == 2);
     }
     ring = (ring & ~(3ull << (2 * pos))) | ((uint64_t)cat << (2 * pos));
-    cnt0 += cat == 0; cnt1 += cat == 1; cnt2 += cat == 2;
     ++pushed;
     pos = pos + 1 == ep.div_window ? 0 : pos + 1;
     const int nn = cnt0 + cnt1 + cnt2;

@@ -43,6 +43,28 @@ __device__ __forceinline__ int row_max_i(int x) {
   x = max(x, dpp_i<kHalfMirror>(x));
   return max(x, dpp_i<kMirror>(x));
 }
+// The value lane `src` (uniform, 0..15) of this lane's row holds.
+__device__ __forceinline__ uint32_t row_pick_u32(uint32_t x, int src, int lane) {
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, src);
+  const uint32_t r1 = __builtin_amdgcn_readlane(x, 16 + src);
+  const uint32_t r2 = __builtin_amdgcn_readlane(x, 32 + src);
+  const uint32_t r3 = __builtin_amdgcn_readlane(x, 48 + src);
+  const int row = lane >> 4;
+  return row == 0 ? r0 : (row == 1 ? r1 : (row == 2 ? r2 : r3));
+}
+
+// Counter-based draws of one episode row, 16 steps at a time: at every 16th
+// step of a launch (t - t_begin = 0 mod 16) lane j evaluates the generator
+// for step t + j, and each step takes its draw from lane (t - t_begin) % 16.
+// One evaluation per lane per 16 steps instead of one per step: Philox's 40
+// 32-bit multiplies per evaluation are quarter-rate instructions.
+struct RowDraws {
+  uint32_t pool = 0;
+  __device__ __forceinline__ uint32_t take(int src, int lane) const {
+    return row_pick_u32(pool, src, lane);
+  }
+};
+
 // inclusive prefix sum over the row (lanes below the shift read 0)
 __device__ __forceinline__ float row_scan(float x) {
   x = x + dpp_f<0x111>(x);  // row_shr:1
