@@ -135,14 +135,12 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
   __shared__ f32x4 s_bufB[kBufB];
   __shared__ f32x4 s_bufC[kBufC];
   __shared__ float s_ln[33];  // ln k for window counts k = 0..32
-  __shared__ float s_env[kEnvTable];
   __shared__ int s_act[kRowsPerWave];
 
   const int lane = threadIdx.x & 63;
   const int q = threadIdx.x >> 6;
 
   if (threadIdx.x <= 32) s_ln[threadIdx.x] = threadIdx.x == 0 ? 0.0f : logf((float)threadIdx.x);
-  fill_env_table(a.ep, s_env, (int)threadIdx.x);
   // operands start at zero: the padding slots (k >= 54) stay zero
   s_opnd[threadIdx.x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   s_next[threadIdx.x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -186,9 +184,20 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
   if (j == 1) put_state<false>(s_opnd, e, 52, 0.0f);
 
   int64_t bar = st;
+  // the step's two draws (and, recycling, its restart bar), 16 steps at a
+  // time per episode row
+  RowDraws ue_pool, ua_pool, rb_pool;
 #pragma unroll 1
   for (int32_t t = 0; t < a.L; ++t) {
     const int64_t o = (int64_t)t * a.N + n;
+    const int slot16 = t & 15;
+    if (slot16 == 0) {
+      const int32_t tj = t + (int)(threadIdx.x & 15);
+      ue_pool.pool = __float_as_uint(draw_uniform(a.seed, (uint32_t)n, (uint32_t)tj, 1u));
+      ua_pool.pool = __float_as_uint(draw_uniform(a.seed, (uint32_t)n, (uint32_t)tj, 2u));
+      if constexpr (RECYCLE)
+        rb_pool.pool = tj + 1 < a.L ? (uint32_t)recycle_bar(a.seed, (uint32_t)n, tj, a.L, a.n_bars) : 0u;
+    }
 
     // the weights are the same every step: an opaque zero offset keeps the
     // compiler from hoisting their loads (and registers) out of the loop
@@ -232,7 +241,7 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     int64_t rbar = 0;
     float fr0[4], fr1[4], pr0 = 0.0f, pr1 = 0.0f;
     if constexpr (RECYCLE) {
-      rbar = t + 1 < a.L ? recycle_bar(a.seed, (uint32_t)n, t, a.L, a.n_bars) : bar;
+      rbar = t + 1 < a.L ? (int64_t)rb_pool.take(slot16, lane) : bar;
       load_features(a.features, rbar, j, fr0);
       load_features(a.features, rbar + 1, j, fr1);
       pr0 = a.prices[rbar];
@@ -263,8 +272,8 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
       if (ok[h] && Q[h] == mx) greedy = j + 16 * h;
     greedy = row_min_i(greedy);
     if (greedy >= kActions) greedy = 0;  // every Q non-finite (counted below)
-    const float u_explore = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 1u);
-    const float u_action = draw_uniform(a.seed, (uint32_t)n, (uint32_t)t, 2u);
+    const float u_explore = __uint_as_float(ue_pool.take(slot16, lane));
+    const float u_action = __uint_as_float(ua_pool.take(slot16, lane));
     const bool explore = u_explore < a.epsilon;
     // u = m 2^-24 with m < 2^24: floor(45 u) = (45 m) >> 24, exactly
     const int random_a = (int)(((uint32_t)(u_action * 16777216.0f) * (uint32_t)kActions) >> 24);
@@ -285,48 +294,53 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(4))
     const int xi = act / 9;
     const int oi = (act % 9) / 3;
     const int ui = act % 3;
-    const float exq = s_env[xi];
-    const float cost = s_env[5 + oi] * (1.0f + ep.urgency_mult * (float)ui);
+    // the exposure and cost-rate tables by selects on the kernel arguments
+    float exq = ep.ex0, rate = ep.cost0;
+    exq = xi == 1 ? ep.ex1 : exq;
+    exq = xi == 2 ? ep.ex2 : exq;
+    exq = xi == 3 ? ep.ex3 : exq;
+    exq = xi == 4 ? ep.ex4 : exq;
+    rate = oi == 1 ? ep.cost1 : rate;
+    rate = oi == 2 ? ep.cost2 : rate;
+    const float cost = rate * (1.0f + ep.urgency_mult * (float)ui);
     const float ret = p1 / p0 - 1.0f;
     const float pnl = exq * ret - cost * fabsf(exq - e_prev);
     V = V * (1.0f + pnl);
 
-    // ---- step 7: triple barrier on raw prices ------------------------------
-    if (exq != 0.0f) {
+    // ---- step 7: triple barrier on raw prices (selects, no branches) -------
+    {
       const int sd = exq > 0.0f ? 1 : -1;
       const int prev = e_prev > 0.0f ? 1 : (e_prev < 0.0f ? -1 : 0);
-      if (prev == 0 || prev != sd) {
-        armed = 1;
-        side = sd;
-        entry = p0;
-        t_open = t;
-      }
-    } else {
-      armed = 0;
+      // a position opens, or flips side: the barriers are set at this bar
+      const bool open = exq != 0.0f && (prev == 0 || prev != sd);
+      armed = exq != 0.0f ? (open ? 1 : armed) : 0;
+      side = open ? sd : side;
+      entry = open ? p0 : entry;
+      t_open = open ? t : t_open;
     }
-    int hit = 0, code = 0;
-    if (armed) {
-      if (side > 0) {
-        if (p1 >= entry * ep.up_pt) { hit = 1; code = 1; }
-        else if (p1 <= entry * ep.dn_sl) { hit = -1; code = 2; }
-      } else {
-        if (p1 <= entry * ep.dn_pt) { hit = 1; code = 1; }
-        else if (p1 >= entry * ep.up_sl) { hit = -1; code = 2; }
-      }
-      if (code == 0 && t + 1 - t_open >= ep.max_hold) code = 3;
-    }
+    const bool lng = side > 0;
+    const float take_px = entry * (lng ? ep.up_pt : ep.dn_pt);
+    const float stop_px = entry * (lng ? ep.dn_sl : ep.up_sl);
+    const bool take = lng ? p1 >= take_px : p1 <= take_px;
+    const bool stop = lng ? p1 <= stop_px : p1 >= stop_px;
+    const bool expire = t + 1 - t_open >= ep.max_hold;
+    const int hit = armed ? (take ? 1 : (stop ? -1 : 0)) : 0;
+    const int code = armed ? (take ? 1 : (stop ? 2 : (expire ? 3 : 0))) : 0;
     const int done = code != 0;
 
     // ---- step 8: diversity window, 3-class entropy in nats -----------------
     // H = ln n - (sum_c n_c ln n_c) / n, compared as n ln n - sum n_c ln n_c
     // < threshold * n
     const int cat = xi <= 1 ? 0 : (xi == 2 ? 1 : 2);
-    if (pushed >= ep.div_window) {
+    {
+      // a full window drops its oldest entry, the one this slot holds
+      const bool full = pushed >= ep.div_window;
       const int old = (int)((ring >> (2 * pos)) & 3u);
-      cnt0 -= old == 0; cnt1 -= old == 1; cnt2 -= old == 2;
+      cnt0 += (cat == 0) - (full && old == 0);
+      cnt1 += (cat == 1) - (full && old == 1);
+      cnt2 += (cat == 2) - (full && old == 2);
     }
     ring = (ring & ~(3ull << (2 * pos))) | ((uint64_t)cat << (2 * pos));
-    cnt0 += cat == 0; cnt1 += cat == 1; cnt2 += cat == 2;
     ++pushed;
     pos = pos + 1 == ep.div_window ? 0 : pos + 1;
     const int nn = cnt0 + cnt1 + cnt2;
