@@ -143,10 +143,16 @@ int rollout_config_default(rollout_config *cfg, int32_t n_episodes, int32_t n_st
  *  features      = [n_bars][51] f32, prices = [n_bars] f32 (positive).
  * The weights are copied and repacked into the library's own MFMA layout
  * (stream-ordered on hip_stream); the caller may free them afterwards.  The
- * market buffers are BORROWED and must outlive the handle.  Device memory
- * for the packed weights and per-collection scratch is allocated here, and,
- * when the rollout is split (see `overlap`), a non-blocking stream of the
- * handle and its events; rollout_destroy releases them.
+ * market buffers are BORROWED and must outlive the handle; they are read at
+ * every collection.  Device memory for the packed weights and per-collection
+ * scratch is allocated here, and, when the rollout is split (see `overlap`),
+ * a non-blocking stream of the handle and its events; rollout_destroy
+ * releases them.  A collection without recycling whose episodes fill fewer
+ * 16-episode workgroups than the device has compute units also keeps a
+ * table of the actor's first-layer market-feature part for every step
+ * (512 bytes per step and episode, when that is at most 256 MiB), filled at
+ * each collection (the same bits as computing it in the step; the
+ * environment variable ROLLOUT_FEATURE_TABLE=0, read here, turns it off).
  * Errors: ROLLOUT_EINVAL (NULL, N or L < 1, dims differ from the built net,
  * n_bars < L + 1, div_window outside 1..32, unknown precision, recycle not
  * 0 or 1),

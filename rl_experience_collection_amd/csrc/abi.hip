@@ -116,18 +116,12 @@ uint32_t gae_spin_limit() {
   return x > rl::kGaeSpinLimit ? rl::kGaeSpinLimit : (uint32_t)x;
 }
 
-// Largest market (in bars) for which a collector keeps the actor's
-// first-layer feature table (512 bytes a bar): 2^21 bars, unless the
-// environment variable ROLLOUT_FEATURE_TABLE_MAX_BARS, read at
-// rollout_create, sets another bound (0: never; the step then computes that
-// part itself).
-int64_t feature_table_max_bars() {
-  const char* v = std::getenv("ROLLOUT_FEATURE_TABLE_MAX_BARS");
-  if (!v || !*v) return (int64_t)1 << 21;
-  char* end = nullptr;
-  const long long x = std::strtoll(v, &end, 10);
-  if (end == v || *end || x < 0) return (int64_t)1 << 21;
-  return (int64_t)x;
+// Whether a collector may keep the actor's first-layer feature table: yes,
+// unless the environment variable ROLLOUT_FEATURE_TABLE, read at
+// rollout_create, is "0" (the step then always computes that part itself).
+bool feature_table_enabled() {
+  const char* v = std::getenv("ROLLOUT_FEATURE_TABLE");
+  return !(v && v[0] == '0' && v[1] == 0);
 }
 
 int gae_run(GaeScratch& s, rl::GaeArgs a, hipStream_t st) {
@@ -328,7 +322,8 @@ struct rollout_s {
   int32_t* start_used = nullptr; // [N]
   unsigned long long* value_sched = nullptr;  // work counter of the value kernel
   int32_t* bars = nullptr;       // [L][N] bar of every step (recycling only)
-  float* ftable = nullptr;       // [n_bars][128] actor first-layer feature part, or null
+  float* ftable = nullptr;       // [L][N][128] actor first-layer feature part, or null
+  int32_t cus = 0;               // compute units of the device
   GaeScratch gae;
   // the rollout split into `parts` launches, the value pass of each part on
   // `side` (only when parts > 1)
@@ -428,15 +423,6 @@ int rollout_create(const rollout_config* cfg, const float* const actor[6],
     return fail(ROLLOUT_ENOMEM, "cannot allocate scheduler counter");
   }
   h->value_sched = static_cast<unsigned long long*>(p);
-  if (n_bars <= feature_table_max_bars()) {
-    if (hipMalloc(&p, (size_t)n_bars * rl::kActorOut1 * sizeof(float)) != hipSuccess) {
-      (void)hipGetLastError();
-      rollout_destroy(h);
-      return fail(ROLLOUT_ENOMEM, "cannot allocate the feature table (%lld bars)",
-                  (long long)n_bars);
-    }
-    h->ftable = static_cast<float*>(p);
-  }
   if (cfg->recycle) {
     if (hipMalloc(&p, (size_t)cfg->n_episodes * cfg->n_steps * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
@@ -452,6 +438,22 @@ int rollout_create(const rollout_config* cfg, const float* const actor[6],
     return hip_fail(e, "hipDeviceGetAttribute");
   }
   h->parts = overlap_parts(*cfg, cus);
+  h->cus = cus;
+  // The feature table pays where the rollout's chain is latency-bound: fewer
+  // workgroups (16 episodes each) than compute units.  Recycled episodes
+  // leave their start + t bar sequence, so they compute the part in the step.
+  const size_t table_bytes =
+      (size_t)cfg->n_episodes * (size_t)cfg->n_steps * rl::kActorOut1 * sizeof(float);
+  if (feature_table_enabled() && !cfg->recycle &&
+      (cfg->n_episodes + rl::kRowsPerWave - 1) / rl::kRowsPerWave < cus &&
+      table_bytes <= ((size_t)1 << 28)) {
+    if (hipMalloc(&p, table_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      rollout_destroy(h);
+      return fail(ROLLOUT_ENOMEM, "cannot allocate the feature table (%zu bytes)", table_bytes);
+    }
+    h->ftable = static_cast<float*>(p);
+  }
   if (h->parts > 1) {
     if (hipMalloc(&p, (size_t)cfg->n_episodes * rl::kCarryWords * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
@@ -576,9 +578,10 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   ra.carry = h->carry;
   ra.stamps = h->stamping ? h->stamps : nullptr;
   ra.ftable = h->ftable;
-  // the feature part of every bar for the current weights and features
+  // the feature part of every step for the current weights and features
   if (h->ftable)
-    RL_HIP(rl::launch_feature_table(h->weights, h->features, h->n_bars, ra.bf16 != 0, h->ftable, st),
+    RL_HIP(rl::launch_feature_table(h->weights, h->features, episode_starts, h->n_bars, N, L,
+                                    ra.bf16 != 0, h->ftable, 4 * h->cus, st),
            "feature table launch");
 
   rl::ValueArgs va;

@@ -35,8 +35,9 @@ struct RolloutArgs {
   // [blocks * kSplit][kStampWords] per-wave cycle totals (instrumented
   // kernel), or null: the plain kernel
   uint64_t* stamps;
-  // [n_bars][kActorOut1] first-layer feature part of every bar (written by
-  // launch_feature_table), or null: computed in the step
+  // [L][N][kActorOut1] first-layer feature part of every step (written by
+  // launch_feature_table; never with recycling), or null: computed in the
+  // step
   const float* ftable;
 };
 
@@ -99,9 +100,11 @@ struct DqnArgs {
 };
 
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st);
-// The feature table of RolloutArgs::ftable for the packed weights' actor.
-hipError_t launch_feature_table(const float* weights, const float* features, int64_t n_bars,
-                                bool bf16, float* table, hipStream_t st);
+// The feature table of RolloutArgs::ftable for the packed weights' actor,
+// episodes starting at the clamped `starts` (at most `grid` workgroups).
+hipError_t launch_feature_table(const float* weights, const float* features, const int32_t* starts,
+                                int64_t n_bars, int32_t N, int32_t L, bool bf16, float* table,
+                                int grid, hipStream_t st);
 hipError_t launch_dqn(const DqnArgs& a, hipStream_t st);
 hipError_t launch_value(const ValueArgs& a, hipStream_t st);
 // Static LDS bytes of a workgroup of the rollout / value kernel (-1 on error).

@@ -314,9 +314,8 @@ GaeShape gae_shape(int32_t L, int32_t N) {
 hipError_t gae_launch(const GaeArgs& a, const GaeShape& shape, const GaeScratchView& sc,
                       hipStream_t stream) {
   const bool off32 = (int64_t)gae_super(shape.cols) * a.N * 4 < ((int64_t)1 << 32);
-  auto kernel = shape.cols == 32 ? gae_scan_kernel<32, false>
-                : off32          ? gae_scan_kernel<64, true>
-                                 : gae_scan_kernel<64, false>;
+  auto kernel = shape.cols == 32 ? (off32 ? gae_scan_kernel<32, true> : gae_scan_kernel<32, false>)
+                                 : (off32 ? gae_scan_kernel<64, true> : gae_scan_kernel<64, false>);
   hipLaunchKernelGGL(kernel, dim3((unsigned)shape.tiles()), dim3(64 * kGaeWaves), 0, stream,
                      a.rewards, a.values, a.dones, a.last_values, a.L, a.N, a.gamma,
                      a.gamma * a.lambda, a.advantages, a.returns, sc, shape.nc, shape.nk,

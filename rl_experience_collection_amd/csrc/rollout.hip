@@ -136,29 +136,33 @@ struct PreStepper {
 
 // The actor's first-layer feature part: the first kTail k-steps of the first
 // layer (k < 48 in fp32, k < 32 in bf16) read only the bar's market features
-// (the portfolio inputs come after them), so bias + that part is a function
-// of the bar alone.  The feature table holds it for every bar, [n_bars][128]
-// fp32 at output o = 16 * tile + 4 * g + c (the accumulator layout: lane
-// e + 16 g of the wave that owns `tile` holds outputs 4g .. 4g+3 of row e).
+// (the portfolio inputs come after them), so bias + that part is known for
+// every step of an episode that is not recycled (its bar is start + t)
+// before the rollout runs.  The feature table holds it for every (t, n),
+// [L][N][128] fp32 at output o = 16 * tile + 4 * g + c (the accumulator
+// layout: lane e + 16 g of the wave that owns `tile` holds outputs
+// 4g .. 4g+3 of row e).
 template <bool BF16>
 constexpr int feature_tail() { return BF16 ? 1 : 12; }
 
-__device__ __forceinline__ void load_table_part(const float* __restrict__ table, int64_t bar, int q,
+__device__ __forceinline__ void load_table_part(const float* __restrict__ table, int64_t row, int q,
                                                 int lane, f32x4 (&pre)[2]) {
-  const float* row = table + bar * kActorOut1 + 4 * (lane >> 4);
+  const float* p = table + row * kActorOut1 + 4 * (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) pre[i] = *reinterpret_cast<const f32x4*>(row + 16 * (2 * q + i));
+  for (int i = 0; i < 2; ++i) pre[i] = *reinterpret_cast<const f32x4*>(p + 16 * (2 * q + i));
 }
 
-// One workgroup per 16 bars: the same operands, MFMA instructions and order
-// as the step kernel's in-place computation, so the table holds the same
-// bits.
+// Persistent workgroups over groups of 16 consecutive (t, n) rows, the
+// first layer's feature k-steps held in registers throughout: the same
+// operands, MFMA instructions and order as the step kernel's in-place
+// computation, so the table holds the same bits.
 template <bool BF16>
-__global__ __launch_bounds__(64 * kSplit) void feature_table_kernel(const float* __restrict__ weights,
-                                                                    const float* __restrict__ features,
-                                                                    int64_t n_bars,
-                                                                    float* __restrict__ table) {
+__global__ __launch_bounds__(64 * kSplit) void feature_table_kernel(
+    const float* __restrict__ weights, const float* __restrict__ features,
+    const int32_t* __restrict__ starts, int64_t n_bars, int32_t N, int32_t L,
+    float* __restrict__ table) {
   constexpr int kTail = feature_tail<BF16>();
+  constexpr int kIn = BF16 ? 32 * kTail : 4 * kTail;  // inputs of the part
   __shared__ f32x4 s_state[4 * 64];
   const int lane = threadIdx.x & 63;
   const int q = threadIdx.x >> 6;
@@ -166,27 +170,35 @@ __global__ __launch_bounds__(64 * kSplit) void feature_table_kernel(const float*
   load_reg_layer(w1, weights + (BF16 ? kP.bact_w[0] : kP.actor_w[0]),
                  weights + (BF16 ? kP.bact_b[0] : kP.actor_b[0]), q, lane);
   s_state[threadIdx.x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  __syncthreads();
-  const int64_t bar0 = (int64_t)blockIdx.x * kRowsPerWave;
-  constexpr int kIn = BF16 ? 32 * kTail : 4 * kTail;  // inputs of the part
-  for (int x = threadIdx.x; x < kRowsPerWave * kIn; x += 64 * kSplit) {
-    const int e = x / kIn, k = x % kIn;
-    const int64_t bar = bar0 + e < n_bars ? bar0 + e : n_bars - 1;
-    put_state<BF16>(s_state, e, k, features[bar * kFeatures + k]);
-  }
-  __syncthreads();
-  f32x4 pre[2] = {w1.bias[0], w1.bias[1]};
-  reg_mfma<0, kTail>(w1, s_state, pre, lane);
-  const int64_t bar = bar0 + (lane & 15);
-  if (bar < n_bars) {
-    float* row = table + bar * kActorOut1 + 4 * (lane >> 4);
+  const int64_t rows = (int64_t)L * N;
+  const int64_t groups = (rows + kRowsPerWave - 1) / kRowsPerWave;
+  const int64_t hi = n_bars - (int64_t)L - 1;  // the step kernel's start clamp
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    __syncthreads();  // the previous group's operands are read
+    for (int x = threadIdx.x; x < kRowsPerWave * kIn; x += 64 * kSplit) {
+      const int e = x / kIn, k = x % kIn;
+      int64_t r = grp * kRowsPerWave + e;
+      r = r < rows ? r : rows - 1;
+      const int32_t t = (int32_t)(r / N), n = (int32_t)(r % N);
+      int64_t st = starts[n];
+      st = st < 0 ? 0 : (st > hi ? hi : st);
+      put_state<BF16>(s_state, e, k, features[(st + t) * kFeatures + k]);
+    }
+    __syncthreads();
+    f32x4 pre[2] = {w1.bias[0], w1.bias[1]};
+    reg_mfma<0, kTail>(w1, s_state, pre, lane);
+    const int64_t r = grp * kRowsPerWave + (lane & 15);
+    if (r < rows) {
+      float* p = table + r * kActorOut1 + 4 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<f32x4*>(row + 16 * (2 * q + i)) = pre[i];
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<f32x4*>(p + 16 * (2 * q + i)) = pre[i];
+    }
   }
 }
 
-// TABLE: the first-layer feature part comes from the feature table
-// (a.ftable), loaded a step ahead, instead of being computed in the step.
+// TABLE (never with RECYCLE): the first-layer feature part comes from the
+// feature table (a.ftable), loaded a step ahead, instead of being computed
+// in the step.
 template <bool BF16, bool RECYCLE, bool STAMPS, bool TABLE>
 __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs a) {
   __shared__ int s_restart[2];  // recycling: an episode of the workgroup restarted in step t (t % 2)
@@ -194,7 +206,6 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   __shared__ f32x4 s_bufB[kBufB];
   __shared__ f32x4 s_state[4 * 64];
   __shared__ float s_ln[33];  // ln k for window counts k = 0..32 (ln 0 unused: times 0)
-  __shared__ int64_t s_bar[kRowsPerWave];  // feature table: each row's bar of the step
 
   const int lane = threadIdx.x & 63;
   const int q = threadIdx.x >> 6;
@@ -273,21 +284,20 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
   load_features(a.features, bar, j, f0);
   load_features(a.features, bar + 1, j, f1);
   float p0 = a.prices[bar], p1 = a.prices[bar + 1];
-  if (TABLE && j == 0) s_bar[e] = bar;
   lds_barrier();  // operand buffer cleared
   if (j == 2) put_state<BF16>(sbuf, e, 53, ep.spread);  // constant element
 #pragma unroll
   for (int h = 0; h < 4; ++h)
     if (j + 16 * h < kFeatures) put_state<BF16>(sbuf, e, j + 16 * h, f0[h]);
   lds_barrier();
-  // first-layer feature part of step 0; with the table, the bar of this
-  // lane's MFMA row (episode lane % 16), which then advances by one a step
-  // (recycling: read again each step)
+  // first-layer feature part of the first step; with the table, that of
+  // this lane's MFMA row (episode lane % 16)
+  static_assert(!(TABLE && RECYCLE), "the table assumes the bar of step t is start + t");
   f32x4 pre[2];
-  int64_t bar_m = 0;
+  int32_t n_m = blockIdx.x * kRowsPerWave + (lane & 15);
+  n_m = n_m < a.N ? n_m : a.N - 1;
   if constexpr (TABLE) {
-    bar_m = s_bar[lane & 15];
-    load_table_part(a.ftable, bar_m, q, lane, pre);
+    load_table_part(a.ftable, (int64_t)a.t_begin * a.N + n_m, q, lane, pre);
   } else {
     pre[0] = w1.bias[0];
     pre[1] = w1.bias[1];
@@ -376,14 +386,10 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
         reg_mfma<0, kTail>(w1, sbuf, pre, lane);
       }
     }
-    // the table part of the next step's bar (recycling: the bar after this
-    // one; a restart in this step is caught by the recompute above)
+    // the table part of the next step
     f32x4 pre_next[2];
-    if constexpr (TABLE) {
-      if constexpr (RECYCLE) bar_m = s_bar[lane & 15];
-      load_table_part(a.ftable, bar_m + 1 < a.n_bars ? bar_m + 1 : a.n_bars - 1, q, lane, pre_next);
-      bar_m += 1;
-    }
+    if constexpr (TABLE)
+      load_table_part(a.ftable, (int64_t)(t + 1 < a.L ? t + 1 : t) * a.N + n_m, q, lane, pre_next);
 
     stamp(1);  // state barrier
     // the step's draw depends only on (seed, episode, step)
@@ -623,9 +629,6 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
           if (j + 16 * h < kFeatures) put_state<BF16>(sbuf, e, j + 16 * h, f0[h]);
         if (j == 0) s_restart[t & 1] = 1;
       }
-      // the bar of the next step, for the feature table (read after the
-      // next step's first barrier)
-      if (TABLE && j == 0) s_bar[e] = bar;
     }
     stamp(10);  // stores and reset
   }
@@ -654,10 +657,10 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
 }  // namespace
 
 int actor_lds_bytes(bool bf16, bool recycle) {
-  auto kernel = bf16 ? (recycle ? actor_rollout_kernel<true, true, false, true>
-                                : actor_rollout_kernel<true, false, false, true>)
-                     : (recycle ? actor_rollout_kernel<false, true, false, true>
-                                : actor_rollout_kernel<false, false, false, true>);
+  auto kernel = bf16 ? (recycle ? actor_rollout_kernel<true, true, false, false>
+                                : actor_rollout_kernel<true, false, false, false>)
+                     : (recycle ? actor_rollout_kernel<false, true, false, false>
+                                : actor_rollout_kernel<false, false, false, false>);
   hipFuncAttributes at;
   if (hipFuncGetAttributes(&at, reinterpret_cast<const void*>(kernel)) != hipSuccess) return -1;
   return (int)at.sharedSizeBytes;
@@ -671,10 +674,11 @@ hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
       ((a.t_begin > 0 || a.t_end < a.L) && !a.carry))
     return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((a.N + kRowsPerWave - 1) / kRowsPerWave);
+  if (a.ftable && a.bars) return hipErrorInvalidValue;  // no table with recycling
   auto pick = [&](auto stamps, auto table) {
     constexpr bool S = decltype(stamps)::value, T = decltype(table)::value;
-    return a.bf16 ? (a.bars ? actor_rollout_kernel<true, true, S, T> : actor_rollout_kernel<true, false, S, T>)
-                  : (a.bars ? actor_rollout_kernel<false, true, S, T> : actor_rollout_kernel<false, false, S, T>);
+    return a.bf16 ? (a.bars ? actor_rollout_kernel<true, true, S, false> : actor_rollout_kernel<true, false, S, T>)
+                  : (a.bars ? actor_rollout_kernel<false, true, S, false> : actor_rollout_kernel<false, false, S, T>);
   };
   auto kernel = a.ftable ? (a.stamps ? pick(std::true_type{}, std::true_type{})
                                      : pick(std::false_type{}, std::true_type{}))
@@ -684,12 +688,14 @@ hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_feature_table(const float* weights, const float* features, int64_t n_bars,
-                                bool bf16, float* table, hipStream_t st) {
-  if (n_bars <= 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n_bars + kRowsPerWave - 1) / kRowsPerWave);
+hipError_t launch_feature_table(const float* weights, const float* features, const int32_t* starts,
+                                int64_t n_bars, int32_t N, int32_t L, bool bf16, float* table,
+                                int grid, hipStream_t st) {
+  if (N <= 0 || L <= 0) return hipSuccess;
+  const int64_t groups = ((int64_t)L * N + kRowsPerWave - 1) / kRowsPerWave;
+  const unsigned blocks = (unsigned)(groups < grid ? groups : grid);
   hipLaunchKernelGGL(bf16 ? feature_table_kernel<true> : feature_table_kernel<false>, dim3(blocks),
-                     dim3(64 * kSplit), 0, st, weights, features, n_bars, table);
+                     dim3(64 * kSplit), 0, st, weights, features, starts, n_bars, N, L, table);
   return hipGetLastError();
 }
 

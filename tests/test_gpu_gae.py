@@ -120,11 +120,12 @@ def test_gae_large_sizes_sampled_episodes(L, N):
     assert np.isfinite(A).all()
 
 
-@pytest.mark.parametrize("L,N", [(513, 524288), (513, 2097157)])
+@pytest.mark.parametrize("L,N", [(513, 524288), (513, 2097157), (300, 2097157)])
 def test_gae_many_episodes_both_address_widths(L, N):
-    """Chained scans of very many episodes: 524,288 episodes address a
+    """Scans of very many episodes: 524,288 episodes address a 512-step
     super-chunk with 32-bit offsets, 2,097,157 (over 2^21, so a super-chunk
-    spans more than 4 GiB of floats) with 64-bit addresses.  The inputs
+    spans more than 4 GiB of floats) with 64-bit addresses, chained (513
+    steps) or in one super-chunk (300 steps).  The inputs
     repeat a block of 8191 episodes on the device (8191 is prime, so every
     repeat lands at another place in the 64-episode columns), which keeps
     the host's work small; the oracle recomputes a spread of episodes from

@@ -386,13 +386,14 @@ def test_instrumented_step_kernel_gives_the_same_collection(precision, recycle):
 
 @pytest.mark.parametrize("precision,recycle", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_feature_table_gives_the_same_collection(monkeypatch, precision, recycle):
-    """By default the actor's first-layer feature part (bias plus the
-    k-steps that read only market features) comes from a per-bar table
-    computed at each collection; with ROLLOUT_FEATURE_TABLE_MAX_BARS=0 at
-    create the step computes it itself.  Both use the same MFMA instructions
-    on the same operands, so the collections match bit for bit, restarts of
-    recycled episodes included (N=40 leaves a ragged workgroup; N=128 is
-    split into launches)."""
+    """Without recycling and with few workgroups, the actor's first-layer
+    feature part (bias plus the k-steps that read only market features)
+    comes by default from a per-step table computed at each collection;
+    with ROLLOUT_FEATURE_TABLE=0 at create the step computes it itself.
+    Both use the same MFMA instructions on the same operands, so the
+    collections match bit for bit (N=40 leaves a ragged workgroup; N=128 is
+    split into launches; recycled collections always compute in the
+    step)."""
     import torch
     import rl_experience_collection_amd as rx
     from parity import to_device
@@ -403,13 +404,13 @@ def test_feature_table_gives_the_same_collection(monkeypatch, precision, recycle
         outs = []
         for table in (True, False):
             if not table:
-                monkeypatch.setenv("ROLLOUT_FEATURE_TABLE_MAX_BARS", "0")
+                monkeypatch.setenv("ROLLOUT_FEATURE_TABLE", "0")
             col = rx.Collector(N, L, d["weights"], d["features"], d["prices"], settings=settings,
                                precision=precision)
             outs.append(col.collect(d["starts"], inp["sampler_seed"], logits=True))
             torch.cuda.synchronize()
             col.close()
-            monkeypatch.delenv("ROLLOUT_FEATURE_TABLE_MAX_BARS", raising=False)
+            monkeypatch.delenv("ROLLOUT_FEATURE_TABLE", raising=False)
         for k, v in outs[0].items():
             if v is not None:
                 assert torch.equal(v, outs[1][k]), (N, k)
