@@ -233,12 +233,30 @@ int check_config(const rollout_config* c) {
 // too short to repay the extra launches) with the rollout's workgroups (16
 // episodes each) leaving at least three quarters of the CUs idle; `overlap`
 // 1 forces it, 0 turns it off.
+// How many: the last part is kept to at most one value work item per CU (its
+// pass runs after the rollout, see rollout_create); each earlier part's pass,
+// on the CUs the rollout leaves free, should end within the part after it,
+// so a part holds at most the rows those CUs finish in the rounds of work
+// items that fit in the last part's duration.  A work item takes about as
+// long as kItemSteps rollout steps (measured at N=128: ~55 us against
+// ~2.7 us).  Fewer parts mean fewer launch and event gaps (~7 us each):
+// N=128 L=500 fp32 runs as 4 parts, 1.43 -> 1.41 ms against 7.
+constexpr int64_t kItemSteps = 20;
 int overlap_parts(const rollout_config& c, int cus) {
   if (c.overlap == 0 || c.n_steps < 2) return 1;
+  const bool bf16 = c.precision != ROLLOUT_FP32;
   const int64_t blocks = ((int64_t)c.n_episodes + 15) / 16;
-  if (c.overlap < 0 && (c.precision != ROLLOUT_FP32 || blocks * 4 > (int64_t)cus)) return 1;
-  const int k = c.n_steps / 64;
-  return k < 2 ? 2 : (k > 8 ? 8 : k);
+  if (c.overlap < 0 && (bf16 || blocks * 4 > (int64_t)cus)) return 1;
+  const int64_t item_rows = bf16 ? 128 : 32;
+  const int64_t fit = (int64_t)cus * item_rows / c.n_episodes;
+  const int64_t half = (c.n_steps + 1) / 2;
+  const int64_t last = fit < 1 ? 1 : (fit < half ? fit : half);
+  const int64_t free_cus = (int64_t)cus - blocks > 0 ? (int64_t)cus - blocks : 1;
+  const int64_t rounds = last / kItemSteps > 1 ? last / kItemSteps : 1;
+  int64_t per_part = rounds * free_cus * item_rows / c.n_episodes;
+  per_part = per_part < 1 ? 1 : per_part;
+  const int64_t k = 1 + (c.n_steps - last + per_part - 1) / per_part;
+  return (int)(k < 2 ? 2 : (k > 8 ? 8 : k));
 }
 
 int check_weights(const float* const actor[6], const float* const critic[12],
@@ -332,8 +350,11 @@ struct rollout_s {
   hipStream_t side = nullptr;
   std::vector<hipEvent_t> part_done;  // [parts] rollout part finished
   hipEvent_t values_done = nullptr;   // last value pass finished
+  hipEvent_t table_go = nullptr;      // the caller's stream reached the feature table
+  hipEvent_t table_done = nullptr;    // the table rows of the later parts are written
   int32_t ov_grid = 0;  // value workgroups while a rollout part runs
   int32_t ov_pad = 0;   // their LDS reservation
+  int32_t tab_pad = 0;  // the same for the feature table's later rows
   int32_t last_steps = 0;  // steps of the final part (its pass is not overlapped)
   // per-wave phase cycle totals of the instrumented step kernel
   uint64_t* stamps = nullptr;
@@ -464,14 +485,18 @@ int rollout_create(const rollout_config* cfg, const float* const actor[6],
     // non-blocking: the caller's stream may be the null stream, which a
     // blocking stream would serialise against
     e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
-    for (int i = 0; e == hipSuccess && i <= h->parts; ++i) {
+    for (int i = 0; e == hipSuccess && i <= h->parts + 2; ++i) {
       hipEvent_t ev = nullptr;
       e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
       if (e != hipSuccess) break;
       if (i < h->parts)
         h->part_done.push_back(ev);
-      else
+      else if (i == h->parts)
         h->values_done = ev;
+      else if (i == h->parts + 1)
+        h->table_go = ev;
+      else
+        h->table_done = ev;
     }
     if (e != hipSuccess) {
       rollout_destroy(h);
@@ -487,14 +512,17 @@ int rollout_create(const rollout_config* cfg, const float* const actor[6],
                               h->device);
     const int a_lds = rl::actor_lds_bytes(bf16, cfg->recycle != 0);
     const int v_lds = rl::value_lds_bytes(bf16);
-    if (e != hipSuccess || a_lds < 0 || v_lds < 0) {
+    const int t_lds = rl::feature_table_lds_bytes(bf16);
+    if (e != hipSuccess || a_lds < 0 || v_lds < 0 || t_lds < 0) {
       rollout_destroy(h);
       return fail(ROLLOUT_EHIP, "kernel LDS sizes");
     }
     const int need = lds_cu - a_lds - v_lds + 256;  // value + pad + rollout > lds_cu
+    const int need_t = lds_cu - a_lds - t_lds + 256;
     const int64_t blocks = ((int64_t)cfg->n_episodes + 15) / 16;
     if (blocks < cus) {  // (otherwise the rollout holds every CU: no limit)
       h->ov_pad = need > 0 ? need : 0;
+      h->tab_pad = need_t > 0 ? need_t : 0;
       h->ov_grid = (int32_t)(cus - blocks);
     }
     // The final part's value pass runs after the rollout: keep it to at most
@@ -578,11 +606,33 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
   ra.carry = h->carry;
   ra.stamps = h->stamping ? h->stamps : nullptr;
   ra.ftable = h->ftable;
-  // the feature part of every step for the current weights and features
-  if (h->ftable)
+  // The feature part of every step for the current weights and features.
+  // A split rollout needs only its first part's rows (and the next step's)
+  // before it starts: the rest are written on the handle's second stream
+  // while that part runs, and the second part waits for them.
+  const int64_t rows_all = (int64_t)L * N;
+  const int64_t head = L - h->last_steps;  // steps of the parts before the last
+  if (h->ftable) {
+    int64_t rows_first = rows_all;
+    if (h->parts > 1) {
+      const int64_t t1 = head / (h->parts - 1);  // first step of the second part
+      rows_first = (t1 + 1) * N < rows_all ? (t1 + 1) * N : rows_all;
+    }
     RL_HIP(rl::launch_feature_table(h->weights, h->features, episode_starts, h->n_bars, N, L,
-                                    ra.bf16 != 0, h->ftable, 4 * h->cus, st),
+                                    ra.bf16 != 0, h->ftable, 0, rows_first, 4 * h->cus, 0, st),
            "feature table launch");
+    if (rows_first < rows_all) {
+      RL_HIP(hipEventRecord(h->table_go, st), "hipEventRecord(table)");
+      RL_HIP(hipStreamWaitEvent(h->side, h->table_go, 0), "hipStreamWaitEvent(table)");
+      // (one workgroup per CU the rollout leaves free, none beside a rollout
+      // workgroup: see the value passes below)
+      RL_HIP(rl::launch_feature_table(h->weights, h->features, episode_starts, h->n_bars, N, L,
+                                      ra.bf16 != 0, h->ftable, rows_first, rows_all,
+                                      h->ov_grid > 0 ? h->ov_grid : h->cus, h->tab_pad, h->side),
+             "feature table launch");
+      RL_HIP(hipEventRecord(h->table_done, h->side), "hipEventRecord(table)");
+    }
+  }
 
   rl::ValueArgs va;
   va.weights = h->weights;
@@ -611,13 +661,14 @@ int rollout_collect(rollout_handle h, const int32_t* episode_starts, uint64_t se
     // part k of the rollout, then (on the side stream, once it is done) the
     // value pass over its rows, while part k + 1 runs; the rows of a part
     // are a contiguous block of the [L][N] outputs
-    const int64_t head = L - h->last_steps;  // steps of the parts before the last
     for (int k = 0; k < h->parts; ++k) {
       const bool last = k + 1 == h->parts;
       const int32_t t0 = (int32_t)(head * k / (h->parts - 1));
       const int32_t t1 = last ? L : (int32_t)(head * (k + 1) / (h->parts - 1));
       ra.t_begin = t0;
       ra.t_end = t1;
+      if (k == 1 && h->ftable)
+        RL_HIP(hipStreamWaitEvent(st, h->table_done, 0), "hipStreamWaitEvent(table)");
       RL_HIP(rl::launch_actor_rollout(ra, st), "actor rollout launch");
       RL_HIP(hipEventRecord(h->part_done[k], st), "hipEventRecord(part)");
       RL_HIP(hipStreamWaitEvent(h->side, h->part_done[k], 0), "hipStreamWaitEvent(side)");
@@ -776,6 +827,8 @@ void rollout_destroy(rollout_handle h) {
   if (h->gae.mem) (void)hipFree(h->gae.mem);
   for (hipEvent_t ev : h->part_done) (void)hipEventDestroy(ev);
   if (h->values_done) (void)hipEventDestroy(h->values_done);
+  if (h->table_go) (void)hipEventDestroy(h->table_go);
+  if (h->table_done) (void)hipEventDestroy(h->table_done);
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->carry) (void)hipFree(h->carry);
   if (h->stamps) (void)hipFree(h->stamps);

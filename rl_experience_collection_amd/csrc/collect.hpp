@@ -100,11 +100,14 @@ struct DqnArgs {
 };
 
 hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st);
-// The feature table of RolloutArgs::ftable for the packed weights' actor,
-// episodes starting at the clamped `starts` (at most `grid` workgroups).
+// Rows [row0, row1) of the feature table of RolloutArgs::ftable for the
+// packed weights' actor, episodes starting at the clamped `starts` (at most
+// `grid` workgroups, each reserving lds_pad bytes of LDS it does not use).
 hipError_t launch_feature_table(const float* weights, const float* features, const int32_t* starts,
                                 int64_t n_bars, int32_t N, int32_t L, bool bf16, float* table,
-                                int grid, hipStream_t st);
+                                int64_t row0, int64_t row1, int grid, int lds_pad,
+                                hipStream_t st);
+int feature_table_lds_bytes(bool bf16);
 hipError_t launch_dqn(const DqnArgs& a, hipStream_t st);
 hipError_t launch_value(const ValueArgs& a, hipStream_t st);
 // Static LDS bytes of a workgroup of the rollout / value kernel (-1 on error).

@@ -159,8 +159,8 @@ __device__ __forceinline__ void load_table_part(const float* __restrict__ table,
 template <bool BF16>
 __global__ __launch_bounds__(64 * kSplit) void feature_table_kernel(
     const float* __restrict__ weights, const float* __restrict__ features,
-    const int32_t* __restrict__ starts, int64_t n_bars, int32_t N, int32_t L,
-    float* __restrict__ table) {
+    const int32_t* __restrict__ starts, int64_t n_bars, int32_t N, int32_t L, int64_t row0,
+    int64_t row1, float* __restrict__ table) {
   constexpr int kTail = feature_tail<BF16>();
   constexpr int kIn = BF16 ? 32 * kTail : 4 * kTail;  // inputs of the part
   __shared__ f32x4 s_state[4 * 64];
@@ -170,15 +170,15 @@ __global__ __launch_bounds__(64 * kSplit) void feature_table_kernel(
   load_reg_layer(w1, weights + (BF16 ? kP.bact_w[0] : kP.actor_w[0]),
                  weights + (BF16 ? kP.bact_b[0] : kP.actor_b[0]), q, lane);
   s_state[threadIdx.x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int64_t rows = (int64_t)L * N;
-  const int64_t groups = (rows + kRowsPerWave - 1) / kRowsPerWave;
+  // rows [row0, row1) of the [L][N] table, in groups of 16
+  const int64_t groups = (row1 - row0 + kRowsPerWave - 1) / kRowsPerWave;
   const int64_t hi = n_bars - (int64_t)L - 1;  // the step kernel's start clamp
   for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
     __syncthreads();  // the previous group's operands are read
     for (int x = threadIdx.x; x < kRowsPerWave * kIn; x += 64 * kSplit) {
       const int e = x / kIn, k = x % kIn;
-      int64_t r = grp * kRowsPerWave + e;
-      r = r < rows ? r : rows - 1;
+      int64_t r = row0 + grp * kRowsPerWave + e;
+      r = r < row1 ? r : row1 - 1;
       const int32_t t = (int32_t)(r / N), n = (int32_t)(r % N);
       int64_t st = starts[n];
       st = st < 0 ? 0 : (st > hi ? hi : st);
@@ -187,8 +187,8 @@ __global__ __launch_bounds__(64 * kSplit) void feature_table_kernel(
     __syncthreads();
     f32x4 pre[2] = {w1.bias[0], w1.bias[1]};
     reg_mfma<0, kTail>(w1, s_state, pre, lane);
-    const int64_t r = grp * kRowsPerWave + (lane & 15);
-    if (r < rows) {
+    const int64_t r = row0 + grp * kRowsPerWave + (lane & 15);
+    if (r < row1) {
       float* p = table + r * kActorOut1 + 4 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < 2; ++i) *reinterpret_cast<f32x4*>(p + 16 * (2 * q + i)) = pre[i];
@@ -688,14 +688,29 @@ hipError_t launch_actor_rollout(const RolloutArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+int feature_table_lds_bytes(bool bf16) {
+  hipFuncAttributes at;
+  const void* k = bf16 ? reinterpret_cast<const void*>(feature_table_kernel<true>)
+                       : reinterpret_cast<const void*>(feature_table_kernel<false>);
+  if (hipFuncGetAttributes(&at, k) != hipSuccess) return -1;
+  return (int)at.sharedSizeBytes;
+}
+
 hipError_t launch_feature_table(const float* weights, const float* features, const int32_t* starts,
                                 int64_t n_bars, int32_t N, int32_t L, bool bf16, float* table,
-                                int grid, hipStream_t st) {
-  if (N <= 0 || L <= 0) return hipSuccess;
-  const int64_t groups = ((int64_t)L * N + kRowsPerWave - 1) / kRowsPerWave;
+                                int64_t row0, int64_t row1, int grid, int lds_pad,
+                                hipStream_t st) {
+  const int64_t rows = (int64_t)L * N;
+  if (N <= 0 || L <= 0 || row0 < 0 || row1 > rows || row0 > row1 || grid < 1 || lds_pad < 0)
+    return hipErrorInvalidValue;
+  if (row0 == row1) return hipSuccess;
+  const int64_t groups = (row1 - row0 + kRowsPerWave - 1) / kRowsPerWave;
   const unsigned blocks = (unsigned)(groups < grid ? groups : grid);
+  // (lds_pad reserves LDS the kernel does not use, which only limits where
+  // its workgroups can be placed)
   hipLaunchKernelGGL(bf16 ? feature_table_kernel<true> : feature_table_kernel<false>, dim3(blocks),
-                     dim3(64 * kSplit), 0, st, weights, features, starts, n_bars, N, L, table);
+                     dim3(64 * kSplit), (unsigned)lds_pad, st, weights, features, starts, n_bars, N,
+                     L, row0, row1, table);
   return hipGetLastError();
 }
 
