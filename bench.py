@@ -125,6 +125,40 @@ def time_collect(inp, steps, warmup, precision=0):
                 nonfinite=bad)
 
 
+def time_gemm_reference(dtype_name, n=8192, reps=10):
+    """A square n x n x n matrix product in torch (the vendor GEMM library)
+    on random operands, timed with events around `reps` products: what the
+    matrix cores sustain on this device, at the clock they then run at, for
+    a large dense product with no data movement of its own (bf16: the faster
+    of 8192 and 16384 is reported)."""
+    import torch
+    dt = dict(bf16=torch.bfloat16, fp32=torch.float32)[dtype_name]
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(n, n, device="cuda", dtype=dt, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=dt, generator=g)
+    for _ in range(3):
+        c = a @ b
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        c = a @ b
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b, c
+    return dict(op=f"torch.matmul {dtype_name} {n}x{n}x{n}, random operands", ms=ms,
+                TFLOPs=2.0 * n ** 3 / (ms * 1e-3) / 1e12)
+
+
+def zero_value_weights(inp):
+    """The same inputs with the critic and curiosity weights zeroed: the value
+    kernel then does identical work on zero operands."""
+    w = dict(inp["weights"])
+    w["critic"] = [x * 0 for x in w["critic"]]
+    w["curiosity"] = [x * 0 for x in w["curiosity"]]
+    return dict(inp, weights=w)
+
+
 def actor_phase_stamps(inp, reps, precision=0):
     """Per-phase shader-clock cycles of one sequential step (the instrumented
     step kernel, rollout_phase_cycles), averaged over every wave and step of
@@ -535,6 +569,8 @@ def main():
     t_roll, t_val, t_gae = big["phases_ms"]
     log("timing N=8192 L=500 bf16 ...")
     bfr = time_collect(big_inp, args.steps, args.warmup, precision=1)
+    log("timing N=8192 L=500 bf16 with zeroed critic and curiosity weights ...")
+    bfz = time_collect(zero_value_weights(big_inp), args.steps, args.warmup, precision=1)
     log("timing N=8192 L=500 fp32 with episode recycling ...")
     rec = time_collect(recycled(big_inp), args.steps, args.warmup)
     log("timing N=128 L=500 fp32 ...")
@@ -548,6 +584,10 @@ def main():
     ws_f = time_weight_stream(N * L, False, 5)
     ws_b = time_weight_stream(N * L, True, 5)
     lds_b = time_lds_activation(N * L, 5)
+    log("timing the vendor GEMM references (bf16, fp32) ...")
+    gemm_b = max((time_gemm_reference("bf16"), time_gemm_reference("bf16", 16384, reps=3)),
+                 key=lambda r: r["TFLOPs"])
+    gemm_f = time_gemm_reference("fp32", reps=3)
     log("timing the DQN collection N=16384 L=500 ...")
     dq_inp = synthdata.dqn_inputs("dqn_n16384_l500")
     dq = time_dqn(dq_inp, args.steps, args.warmup)
@@ -571,7 +611,9 @@ def main():
                     kernel="value_kernel (critic + curiosity, fp32 MFMA 16x16x4)",
                     flop_per_launch=VALUE_KERNEL_FLOP * N * L, avg_launch_ms=t_val,
                     weight_stream_bound=dict(ms=ws_f["ms"], TBps=ws_f["TBps"],
-                                             bytes_per_launch=ws_f["bytes_per_launch"]))
+                                             bytes_per_launch=ws_f["bytes_per_launch"]),
+                    gemm_reference=dict(gemm_f, frac_of_fp32_peak=gemm_f["TFLOPs"] * 1e12 / PEAK_FP32_MFMA,
+                                        value_kernel_frac_of_gemm=achieved / 1e12 / gemm_f["TFLOPs"]))
     mlp_util = MLP_FLOP * N * L / ((t_roll + t_val) * 1e-3) / PEAK_FP32_MFMA
     # N=128: 8 workgroups of 16 episodes hold 8 CUs through the sequential
     # chain; the actor's work against the fp32 MFMA peak of those CUs
@@ -616,7 +658,15 @@ def main():
                 lds_stream_bound_ms=lds_b["ms"], lds_stream_TBps=lds_b["TBps"],
                 lds_bytes_per_item=lds_b["bytes_per_item"],
                 value_kernel_frac_of_bound=max(ws_b["ms"], lds_b["ms"], VALUE_KERNEL_FLOP * N * L /
-                                               PEAK_BF16_MFMA * 1e3) / float(bfr["phases_ms"][1])),
+                                               PEAK_BF16_MFMA * 1e3) / float(bfr["phases_ms"][1]),
+                # what the matrix cores sustain here on random bf16 operands (a
+                # large square product in the vendor library), and the value
+                # kernel on zero operands: the bf16 rate is bounded by power,
+                # and so the clock, not by the published peak
+                gemm_reference=dict(gemm_b, frac_of_bf16_peak=gemm_b["TFLOPs"] * 1e12 / PEAK_BF16_MFMA,
+                                    value_kernel_frac_of_gemm=VALUE_KERNEL_FLOP * N * L /
+                                    (bfr["phases_ms"][1] * 1e-3) / 1e12 / gemm_b["TFLOPs"]),
+                value_kernel_ms_zero_weights=float(bfz["phases_ms"][1])),
             dqn_collect_n16384_l500_fp32=dict(
                 value=dq_exp * args.steps / dq["wall_s"], unit="experiences/s",
                 ms_per_step=dq["wall_s"] * 1000 / args.steps, kernel_ms=dq["kernel_ms"],
@@ -648,9 +698,10 @@ def main():
                 phases_ms=dict(zip(("actor_rollout", "value_critic_curiosity", "gae_scan"),
                                    map(float, small["phases_ms"]))),
                 roofline=small_roof,
-                note="the rollout runs as 7 launches of consecutive steps; the value pass of "
-                     "each finished part overlaps the next part on the CUs the rollout leaves "
-                     "free, so value_critic_curiosity is only the pass after the rollout"),
+                note="the rollout runs as a few launches of consecutive steps (4 on 256 CUs: "
+                     "3 of 145-146 steps, then 64); the value pass of each finished part "
+                     "overlaps the next part on the CUs the rollout leaves free, so "
+                     "value_critic_curiosity is only the pass after the rollout"),
             gae_scan_n4096_l2048=dict(
                 value=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / 1e9, unit="GB/s",
                 frac_of_hbm_peak=GAE_BYTES * gae["elements"] / (gae["cold_ms"] * 1e-3) / PEAK_HBM,

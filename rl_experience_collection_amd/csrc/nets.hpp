@@ -498,7 +498,13 @@ __device__ __forceinline__ void stream_layer(WeightStream<true, OTW, D, SPLIT>& 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-      for (int i = 0; i < OTW; ++i) acc[rt][i] = mfma_bf16(st.a[slot][i], b[rt], acc[rt][i]);
+      for (int i = 0; i < OTW; ++i) {
+        acc[rt][i] = mfma_bf16(st.a[slot][i], b[rt], acc[rt][i]);
+        // (the MFMA is issued here: without this the compiler may defer the
+        // MFMAs of a fully prefetched layer past all its B reads, which then
+        // all stay live)
+        asm volatile("" : "+v"(acc[rt][i]));
+      }
       // (the scheduling barrier does not order memory reads: the empty asm
       // keeps every operand load in program order, so the B operands of
       // later steps cannot be read early and held)

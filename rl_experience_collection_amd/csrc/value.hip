@@ -77,6 +77,18 @@ struct ValueShape {
                 "one output tile per wave in the 4-tile layers");
 };
 
+// An empty asm that takes and returns every accumulator of a layer: the
+// layer's MFMAs are then all issued before it, so the compiler cannot sink
+// them past the barrier and loads that follow in program order (an inline
+// asm orders memory operations only).
+template <int RT, int OTW>
+__device__ __forceinline__ void pin_tiles(f32x4 (&acc)[RT][OTW]) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < OTW; ++i) asm volatile("" : "+v"(acc[rt][i]));
+}
+
 // The packed block as a buffer resource plus its base pointer (biases and
 // small tables are read through the pointer).
 struct Weights {
@@ -136,6 +148,24 @@ void value_kernel(ValueArgs a) {
   __shared__ int s_act[RT * kRowsPerWave], s_nbar[RT * kRowsPerWave];
   __shared__ float s_env[kEnvTable];
   fill_env_table(a.ep, s_env, (int)threadIdx.x);  // read after the loop's first barrier
+  // bf16 keeps the third and fourth layers' outputs at their own k-step
+  // counts per row tile (8 and 4), so the tail's staged weights and biases
+  // (uint4 units from kTailAt: kTailW of weights, then 80 of biases and the
+  // 64 -> 1 row) fit beside the third layer's output
+  constexpr int TS3 = BF16 ? 8 * 64 : TS;
+  constexpr int TS4 = BF16 ? 4 * 64 : TS;
+  constexpr int kTailW = 3 * 1024;
+  constexpr int kTailN = kTailW + 80;
+  constexpr int kTailAt = RT * TS3;
+  constexpr int kStageN = BF16 ? (kTailN + kThreads - 1) / kThreads : 1;
+  static_assert(!BF16 || (kTailAt + kTailN <= RT * TS && S5 == 4 && SC1 == 2 && SC2 == 4 &&
+                          RT * TS4 <= kTailAt),
+                "bf16 tail layout");
+  static_assert(!BF16 || (kP.bcur_w[0] == kP.bcritic_w[4] + 4 * kTailW / 3 &&
+                          kP.bcur_w[1] == kP.bcur_w[0] + 4 * kTailW / 3 &&
+                          packed_layer_floats_bf16(kCurB[1]) == 4 * kTailW / 3),
+                "the three tail layers are one run of the packed block");
+  uint32_t n_bad = 0;  // rows with a non-finite value or reward (bf16 tail)
 
   const int64_t rows = (int64_t)a.L * a.N;
   const int64_t groups = ((rows + kRowsPerWave - 1) / kRowsPerWave + RT - 1) / RT;
@@ -153,11 +183,17 @@ void value_kernel(ValueArgs a) {
   // chunk c of the operand buffer is (row tile, k-group, lane) = (c / (64 G),
   // c / 64 % G, c % 64), i.e. the inputs k0 .. k0 + kCF - 1 of row
   // 16 rt + lane % 16 for lane group lane / 16; they are consecutive floats
-  // of the state row, and the chunk store is one 16-byte LDS write.
+  // of the state row, and the chunk store is one 16-byte LDS write.  In
+  // bf16 wave q handles the chunks of row tile q (its own rows in the tail,
+  // which then needs no barrier before the store).
   constexpr int kG = BF16 ? 2 : 4;          // k-groups per row tile
   constexpr int kCF = BF16 ? 8 : 4;         // floats per chunk
   constexpr int kCPT = RT * Sh::kOpTile / kThreads;
   static_assert(RT * Sh::kOpTile % kThreads == 0, "whole chunks per thread");
+  static_assert(!BF16 || (RT == W && kCPT * 64 == Sh::kOpTile), "bf16: one row tile per wave");
+  auto chunk_of = [](int i, int tid_) {
+    return BF16 ? (tid_ >> 6) * Sh::kOpTile + i * 64 + (tid_ & 63) : i * kThreads + tid_;
+  };
   // floats of a group's state rows present in [L][N][54]
   auto avail_of = [&](int64_t g_) -> int {
     const int64_t av = (rows - g_ * RT * kRowsPerWave) * kState;
@@ -175,7 +211,7 @@ void value_kernel(ValueArgs a) {
         0x00020000);
 #pragma unroll
     for (int i = 0; i < kCPT; ++i) {
-      const int c = i * kThreads + tid_;
+      const int c = chunk_of(i, tid_);
       const int row = (c >> 6) / kG * kRowsPerWave + (c & 15);
       const uint32_t off = 4u * (uint32_t)(row * kState + chunk_k0(c));
 #pragma unroll
@@ -192,7 +228,7 @@ void value_kernel(ValueArgs a) {
   auto scatter_states = [&](int tid_, const float (&v)[kCPT][kCF]) {
 #pragma unroll
     for (int i = 0; i < kCPT; ++i) {
-      const int c = i * kThreads + tid_;
+      const int c = chunk_of(i, tid_);
       const int k0 = chunk_k0(c);
       float x[kCF];
 #pragma unroll
@@ -333,10 +369,11 @@ void value_kernel(ValueArgs a) {
   // what the curiosity and reward epilogue reads, loaded past the register
   // peak of the wide layers so it arrives during the rest: wave q < RT
   // loads the action and the next bar (the MSE target) of row tile q's
-  // rows; they go through LDS to every wave after the next layer
+  // rows (fp32: they go through LDS to every wave after the next layer)
   // (one load per value, with no branch around it: a load behind a branch
   // writes the registers another path loads into, and the compiler then
   // waits for every load in flight)
+  if constexpr (BF16) pin_tiles(h3);  // the layer's MFMAs stay ahead of the staging below
   int my_act[ER], my_nbar[ER];
   float partial[ER];
 #pragma unroll
@@ -352,14 +389,169 @@ void value_kernel(ValueArgs a) {
     partial[e] = a.rewards[my_row[e]];
   }
   lds_barrier();
-  store<BF16, Sh::O3, RT>(h3, s_buf, TS, q, lane);
+  // bf16: the tail layers' weights (critic 128 -> 64, curiosity 1 and 2:
+  // one 48 KB run of the packed block), their biases and the 64 -> 1 row,
+  // loaded now (past the register peak) and written into LDS next to the
+  // third layer's output once the fourth layer has run; every wave then runs
+  // the tail on its own row tile with no barrier between layers
+  uint4 stage[kStageN];
+  if constexpr (BF16) {
+    static_assert(kTailW % kThreads == 0 && kTailN - kTailW <= kThreads, "one bias round");
+#pragma unroll
+    for (int i = 0; i < kStageN - 1; ++i)  // weights: 16-byte chunk i * kThreads + tid
+      stage[i] = wt.gw.u4(4u * (uint32_t)(kP.bcritic_w[4] + 4 * (i * kThreads + tid)), 0u);
+    // then chunk b of the biases (critic 128 -> 64: 16, curiosity 1: 32,
+    // curiosity 2: 16) and the 64 -> 1 row (16), b clamped (duplicates
+    // store equal bytes); the offset as sums of selects, not branches
+    const int b = tid < kTailN - kTailW ? tid : kTailN - kTailW - 1;
+    const uint32_t fo = (uint32_t)(kP.critic_b[4] + 4 * b) +
+                        (b >= 16 ? (uint32_t)(kP.cur_b[0] - kP.critic_b[4] - 64) : 0u) +
+                        (b >= 48 ? (uint32_t)(kP.cur_b[1] - kP.cur_b[0] - 128) : 0u) +
+                        (b >= 64 ? (uint32_t)(kP.bcritic_w6 - kP.cur_b[1] - 64) : 0u);
+    stage[kStageN - 1] = wt.gw.u4(4u * fo, 0u);
+  }
+  store<BF16, Sh::O3, RT>(h3, s_buf, TS3, q, lane);
   lds_barrier();
 
   f32x4 h4[RT][Sh::O4];
-  run<S4>(w4, wt, kP.critic_w[3], kP.bcritic_w[3], acts, h4, q, lane);
+  run<S4>(w4, wt, kP.critic_w[3], kP.bcritic_w[3], LdsOperands{s_buf, TS3}, h4, q, lane);
+  if constexpr (BF16) {
+    uint4* st4 = reinterpret_cast<uint4*>(s_buf) + kTailAt;
+#pragma unroll
+    for (int i = 0; i < kStageN - 1; ++i) st4[i * kThreads + tid] = stage[i];
+    st4[kTailW + (tid < kTailN - kTailW ? tid : kTailN - kTailW - 1)] = stage[kStageN - 1];
+    // ---- tail: wave q evaluates the rest for row tile q alone -------------
+    prefetch_next();
+    // the row's action (clamped for the gather) and the MSE targets: the
+    // next bar's features at this lane's outputs 16 i + 4 g + r of the
+    // curiosity head, one 16-byte load each (rows are 204 bytes, so 4-byte
+    // aligned; the row's last four where the four run past it, 48 .. 50
+    // then moved down one; outputs past the row are zero)
+    const int act = my_act[0] < 0 ? 0 : (my_act[0] >= kActions ? kActions - 1 : my_act[0]);
+    const float* fn = a.features + (int64_t)(my_nbar[0] + 1) * kFeatures;
+    f32x4 feat[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j0 = 16 * i + 4 * g;
+      const int jl = j0 + 3 < kFeatures ? j0 : kFeatures - 4;
+      const f32x4 v = *reinterpret_cast<const f32x4_a4*>(fn + jl);
+      const bool shift = jl != j0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s1 = r < 3 ? v[r + 1] : 0.0f;
+        feat[i][r] = j0 + r < kFeatures ? (shift ? s1 : v[r]) : 0.0f;
+      }
+    }
+    // the action's one-hot columns of the curiosity input layer
+    const float* oh = Wp + kP.bcur_onehot + act * 128 + 4 * g;
+    f32x4 ohv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ohv[i] = *reinterpret_cast<const f32x4*>(oh + 16 * i);
+    lds_barrier();  // every wave has read the third layer's output
+    store<BF16, Sh::O4, RT>(h4, s_buf, TS4, q, lane);
+    lds_barrier();
+
+    const uint4* tw = reinterpret_cast<const uint4*>(s_buf) + kTailAt;
+    const float* tb = reinterpret_cast<const float*>(tw + kTailW);
+    // critic 128 -> 64: all four output tiles (weights [s][tile][lane])
+    f32x4 h5[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h5[i] = *reinterpret_cast<const f32x4*>(tb + 16 * i + 4 * g);
+    const uint4* x4 = reinterpret_cast<const uint4*>(s_buf) + q * TS4;
+#pragma unroll
+    for (int s = 0; s < S5; ++s) {
+      const uint4 bx = x4[s * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h5[i] = mfma_bf16(tw[(4 * s + i) * 64 + lane], bx, h5[i]);
+    }
+    // 64 -> 1 on the VALU: per output tile a dot product over the lane's
+    // four units, reduced over the lane groups; tiles added in a fixed order
+    float vp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 w6v = *reinterpret_cast<const f32x4*>(tb + 256 + 16 * i + 4 * g);
+      float part = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part += w6v[r] * bf16_round(fmaxf(h5[i][r], 0.0f));
+      part += lane_xor16f(part, lane);
+      part += lane_xor32f(part, lane);
+      vp[i] = part;
+    }
+    const float value = Wp[kP.critic_b6] + ((vp[0] + vp[1]) + (vp[2] + vp[3]));
+
+    // curiosity layer 1: the row tile's state operands (all 8 output tiles),
+    // plus the one-hot gather
+    f32x4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = *reinterpret_cast<const f32x4*>(tb + 64 + 16 * i + 4 * g);
+    const uint4* xs = reinterpret_cast<const uint4*>(s_opnd) + q * Sh::kOpTile;
+#pragma unroll
+    for (int s = 0; s < SC1; ++s) {
+      const uint4 bx = xs[s * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        c[i] = mfma_bf16(tw[1024 + (8 * s + i) * 64 + lane], bx, c[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] += ohv[i];
+    // this row tile's state operands are read (by this wave only): the next
+    // group's take their place (past the last group the values are unused)
+    scatter_states(tid, v_states);
+
+    // curiosity layer 2: the input never leaves the registers, since k-step
+    // s of the packed order is output tiles 2s and 2s + 1 as this lane holds
+    // them
+    f32x4 pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = *reinterpret_cast<const f32x4*>(tb + 192 + 16 * i + 4 * g);
+#pragma unroll
+    for (int s = 0; s < SC2; ++s) {
+      uint4 bx;
+      bx.x = pack_bf16x2(fmaxf(c[2 * s][0], 0.0f), fmaxf(c[2 * s][1], 0.0f));
+      bx.y = pack_bf16x2(fmaxf(c[2 * s][2], 0.0f), fmaxf(c[2 * s][3], 0.0f));
+      bx.z = pack_bf16x2(fmaxf(c[2 * s + 1][0], 0.0f), fmaxf(c[2 * s + 1][1], 0.0f));
+      bx.w = pack_bf16x2(fmaxf(c[2 * s + 1][2], 0.0f), fmaxf(c[2 * s + 1][3], 0.0f));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = mfma_bf16(tw[2048 + (4 * s + i) * 64 + lane], bx, pr[i]);
+    }
+    begin<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], q, lane);
+    lds_barrier();  // the tail's LDS reads are done; the next group's operands are written
+
+    // MSE against the next bar's features, then step 10: reward = partial +
+    // curiosity - risk
+    float sq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float se = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float d = 16 * i + 4 * g + r < kFeatures ? pr[i][r] - feat[i][r] : 0.0f;
+        se += d * d;
+      }
+      se += lane_xor16f(se, lane);
+      se += lane_xor32f(se, lane);
+      sq[i] = se;
+    }
+    const float sum = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    const float bonus = a.ep.curiosity_coef * (sum / (float)kFeatures);
+    const float ex = s_env[act / 9];
+    const float reward = (partial[0] + bonus) - a.ep.risk_coef * fabsf(ex);
+    // one store per row (lane group 0) through buffer resources that end at
+    // the last row present: the other lanes and rows past the end are
+    // dropped by the range check, so no store sits behind a branch
+    const int64_t left = rows - row0;
+    const int nrec = 4 * (int)(left < RT * kRowsPerWave ? left : RT * kRowsPerWave);
+    const uint32_t so = g == 0 ? 4u * (uint32_t)(q * kRowsPerWave + (lane & 15)) : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b32(
+        __float_as_uint(value),
+        __builtin_amdgcn_make_buffer_rsrc(a.values + row0, 0, nrec, 0x00020000), (int)so, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(
+        __float_as_uint(reward),
+        __builtin_amdgcn_make_buffer_rsrc(a.rewards + row0, 0, nrec, 0x00020000), (int)so, 0, 0);
+    n_bad += (g == 0 && my_raw[0] < rows && (!isfinite(value) || !isfinite(reward))) ? 1u : 0u;
+  } else {
   Stream<BF16, 1> w5;
   begin<S5>(w5, wt, kP.critic_w[4], kP.bcritic_w[4], kP.critic_b[4], q4, lane);
-  if constexpr (BF16) prefetch_next();
 #pragma unroll
   for (int e = 0; e < ER; ++e)
     if (q + W * e < RT && g == 0) {
@@ -388,7 +580,7 @@ void value_kernel(ValueArgs a) {
       feat[rt][r] = j0 + r < kFeatures ? (shift ? s1 : v[r]) : 0.0f;
     }
   }
-  store<BF16, Sh::O4, RT>(h4, s_buf, TS, q, lane);
+  store<BF16, Sh::O4, RT>(h4, s_buf, TS4, q, lane);
   lds_barrier();
 
   f32x4 h5[RTS][1];
@@ -397,16 +589,13 @@ void value_kernel(ValueArgs a) {
   begin<SC1>(c1, wt, kP.cur_w[0], kP.bcur_w[0], kP.cur_b[0], q, lane);
   {
     // 64 -> 1 on the VALU: this wave holds hidden units 16 q4 .. 16 q4 + 15
-    const float* w6 = Wp + (BF16 ? kP.bcritic_w6 : kP.critic_w6) + 16 * q4 + 4 * g;
+    const float* w6 = Wp + kP.critic_w6 + 16 * q4 + 4 * g;
     const f32x4 w6v = *reinterpret_cast<const f32x4*>(w6);
 #pragma unroll
     for (int rt = 0; rt < RTS; ++rt) {
       float part = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = fmaxf(h5[rt][0][r], 0.0f);
-        part += w6v[r] * (BF16 ? bf16_round(x) : x);
-      }
+      for (int r = 0; r < 4; ++r) part += w6v[r] * fmaxf(h5[rt][0][r], 0.0f);
       part += lane_xor16f(part, lane);
       part += lane_xor32f(part, lane);
       if (g == 0) s_part[0][rs0 + rt][q4][lane] = part;
@@ -415,13 +604,13 @@ void value_kernel(ValueArgs a) {
 
   // ---- curiosity layer 1 (reads the state operands, not s_buf) ----------
   f32x4 c[RT][Sh::OC1];
-  run<SC1, BF16 ? SC1 : kFirstSteps>(c1, wt, kP.cur_w[0], kP.bcur_w[0], states_in, c, q, lane);
+  run<SC1, kFirstSteps>(c1, wt, kP.cur_w[0], kP.bcur_w[0], states_in, c, q, lane);
   Stream<BF16, 1> c2;
   begin<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], kP.cur_b[1], q4, lane);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int act = s_act[rt * kRowsPerWave + (lane & 15)];
-    const float* oh = Wp + (BF16 ? kP.bcur_onehot : kP.cur_onehot) + act * 128 + 4 * g;
+    const float* oh = Wp + kP.cur_onehot + act * 128 + 4 * g;
 #pragma unroll
     for (int i = 0; i < Sh::OC1; ++i)
       c[rt][i] += *reinterpret_cast<const f32x4*>(oh + 16 * (Sh::OC1 * q + i));
@@ -443,7 +632,6 @@ void value_kernel(ValueArgs a) {
   // ---- curiosity layer 2, MSE against the next bar's features -------------
   f32x4 pr[RTS][1];
   run<SC2>(c2, wt, kP.cur_w[1], kP.bcur_w[1], acts_s, pr, q4, lane);
-  if constexpr (BF16) begin<S1>(w1, wt, kP.critic_w[0], kP.bcritic_w[0], kP.critic_b[0], q, lane);
 #pragma unroll
   for (int rt = 0; rt < RTS; ++rt) {
     float se = 0.0f;
@@ -477,10 +665,12 @@ void value_kernel(ValueArgs a) {
       if (a.counters && (!isfinite(value[e]) || !isfinite(reward))) atomicAdd(a.counters, 1u);
     }
   }
+  }  // fp32 tail
   // the same value in every lane: keep the loop control scalar
   grp = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)grp_next) |
         ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(grp_next >> 32)) << 32);
   }  // row-tile groups
+  if (n_bad && a.counters) atomicAdd(a.counters, n_bad);
 }
 
 __global__ void zero_u64_kernel(unsigned long long* p) { p[threadIdx.x] = 0ull; }
