@@ -16,6 +16,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -157,6 +158,79 @@ def zero_value_weights(inp):
     w["critic"] = [x * 0 for x in w["critic"]]
     w["curiosity"] = [x * 0 for x in w["curiosity"]]
     return dict(inp, weights=w)
+
+
+def smi_sample():
+    """Socket power (W) and the shader clocks (MHz) of every XCD from
+    amd-smi, or None where the tool is missing or fails."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
+                           text=True, timeout=10)
+        if r.returncode:
+            return None
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clocks = [v["clk"]["value"] for k, v in g["clock"].items()
+                  if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        return dict(power_W=g["power"]["socket_power"]["value"], gfx_MHz=clocks)
+    except Exception:
+        return None
+
+
+def value_power(inp, seconds=3.0):
+    """The N=8192 L=500 collection back to back for about `seconds` each in
+    bf16, in bf16 with the critic and curiosity weights zeroed (the same
+    instructions on zero operands) and in fp32, with the board's socket
+    power and shader clocks read from amd-smi while the device is busy, and
+    the value kernel's time from phase events."""
+    import numpy as np
+    import torch
+    import rl_experience_collection_amd as rx
+
+    N, L = inp["N"], inp["L"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    res = []
+    for name, prec, src in (("bf16", 1, inp), ("bf16, zeroed critic and curiosity weights", 1,
+                                                zero_value_weights(inp)), ("fp32", 0, inp)):
+        w = src["weights"]
+        weights = dict(actor=[dev(x) for x in w["actor"]], critic=[dev(x) for x in w["critic"]],
+                       curiosity=[dev(x) for x in w["curiosity"]])
+        col = rx.Collector(N, L, weights, dev(src["features"]), dev(src["prices"]),
+                           settings=src["settings"], precision=prec)
+        starts, outs = dev(src["starts"]), rx.alloc_outputs(N, L, "cuda")
+        ev = rx.HipEvents(4)
+        col.collect(starts, 1, outputs=outs, phase_events=ev.handles)
+        torch.cuda.synchronize()
+        per = ev.elapsed_ms(0, 3)
+        reps = max(3, int(seconds * 1e3 / per))
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                x = smi_sample()
+                if x:
+                    samples.append(x)
+                stop.wait(0.25)
+        th = threading.Thread(target=sampler)
+        th.start()
+        for i in range(reps):
+            col.collect(starts, 2 + i, outputs=outs,
+                        phase_events=ev.handles if i == reps // 2 else None)
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        value_ms = ev.elapsed_ms(1, 2)
+        ev.close()
+        col.close()
+        busy = samples[1:-1]  # (the first and last may fall outside the busy span)
+        p = [x["power_W"] for x in busy]
+        c = [float(np.mean(x["gfx_MHz"])) for x in busy]
+        res.append(dict(run=name, collections=reps, value_kernel_ms=value_ms,
+                        samples=len(p), power_W_median=float(np.median(p)) if p else None,
+                        power_W_max=float(max(p)) if p else None,
+                        gfx_MHz_median=float(np.median(c)) if c else None))
+    return res
 
 
 def actor_phase_stamps(inp, reps, precision=0):
@@ -355,6 +429,32 @@ def time_gae(spec, reps, traffic_only=False):
     return dict(elements=n, cold_ms=float(np.median(cold)), warm_ms=float(warm))
 
 
+def time_vendor_copy(nbytes, reps=12):
+    """torch's device copy of nbytes / 2 bytes (so nbytes cross HBM: half read,
+    half written), cold as in time_gae: what the vendor's own streaming
+    kernel reaches for a transfer of that size."""
+    import numpy as np
+    import torch
+    import rl_experience_collection_amd as rx
+    a = torch.ones(max(nbytes // 8, 1), device="cuda")
+    b = torch.empty_like(a)
+    flush = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    ev = rx.HipEvents(2)
+    out = []
+    for i in range(reps + 2):
+        flush.sum()
+        ev.record(0)
+        b.copy_(a)
+        ev.record(1)
+        torch.cuda.synchronize()
+        if i >= 2:
+            out.append(ev.elapsed_ms(0, 1))
+    ev.close()
+    ms = float(np.median(out))
+    moved = 2 * 4 * a.numel()
+    return dict(bytes=moved, cold_ms=ms, TBps=moved / (ms * 1e-3) / 1e12)
+
+
 def time_weight_stream(rows, bf16, reps):
     """The value kernel's weight stream alone (no arithmetic) for `rows`
     stored states: the L2-to-register bound of that kernel."""
@@ -533,6 +633,10 @@ def main():
                              "copy_1gib"),
                     help="one workload only (for profiler counter passes); prints its own "
                          "JSON line instead of the benchmark line")
+    ap.add_argument("--value-power", action="store_true",
+                    help="socket power and shader clock (amd-smi) while the N=8192 L=500 "
+                         "collection runs back to back in bf16, bf16 with zeroed value weights "
+                         "and fp32, one JSON line each, instead of the benchmark line")
     ap.add_argument("--actor-stamps", action="store_true",
                     help="per-phase cycles of the sequential step (instrumented kernel) at "
                          "N=128 L=500 fp32 and bf16 and N=8192 L=500 fp32, one JSON line each, "
@@ -551,6 +655,10 @@ def main():
 
     if args.workload != "all":
         print(json.dumps(run_single(args.workload, args.steps, args.warmup)), flush=True)
+        return
+    if args.value_power:
+        for r in value_power(synthdata.ppo_inputs("ppo_n8192_l500")):
+            print(json.dumps(r), flush=True)
         return
     if args.actor_stamps:
         for name, prec in (("ppo_n128_l500", 0), ("ppo_n128_l500", 1), ("ppo_n8192_l500", 0)):
@@ -581,6 +689,10 @@ def main():
     log("timing the ceilings: GAE traffic element-wise, value-kernel weight stream ...")
     gae_x = time_gae(synthdata.WORKLOADS["gae_n4096_l2048"], max(args.steps, 20), traffic_only=True)
     gae_cx = time_gae(dict(N=N, L=L, seed=spec["seed"]), max(args.steps, 20), traffic_only=True)
+    log("timing the vendor copy at the scans' byte counts and at 1 GiB ...")
+    cp_c = time_vendor_copy(GAE_BYTES * N * L)
+    cp_x = time_vendor_copy(GAE_BYTES * gae["elements"])
+    cp_g = time_vendor_copy(1 << 31, reps=5)
     ws_f = time_weight_stream(N * L, False, 5)
     ws_b = time_weight_stream(N * L, True, 5)
     lds_b = time_lds_activation(N * L, 5)
@@ -708,7 +820,9 @@ def main():
                 cold_ms=gae["cold_ms"], warm_ms=gae["warm_ms"],
                 warm_GBps=GAE_BYTES * gae["elements"] / (gae["warm_ms"] * 1e-3) / 1e9,
                 copy_ceiling_cold_ms=gae_x["cold_ms"], copy_ceiling_warm_ms=gae_x["warm_ms"],
-                frac_of_copy_ceiling_cold=gae_x["cold_ms"] / gae["cold_ms"]),
+                frac_of_copy_ceiling_cold=gae_x["cold_ms"] / gae["cold_ms"],
+                vendor_copy_same_bytes_cold_ms=cp_x["cold_ms"],
+                frac_of_vendor_copy_cold=cp_x["cold_ms"] / gae["cold_ms"]),
             gae_scan_n8192_l500=dict(
                 value=GAE_BYTES * gae_c["elements"] / (gae_c["cold_ms"] * 1e-3) / 1e9, unit="GB/s",
                 frac_of_hbm_peak=GAE_BYTES * gae_c["elements"] / (gae_c["cold_ms"] * 1e-3) / PEAK_HBM,
@@ -717,7 +831,14 @@ def main():
                 warm_frac_of_hbm_peak=GAE_BYTES * gae_c["elements"] / (gae_c["warm_ms"] * 1e-3)
                 / PEAK_HBM,
                 copy_ceiling_cold_ms=gae_cx["cold_ms"], copy_ceiling_warm_ms=gae_cx["warm_ms"],
-                frac_of_copy_ceiling_cold=gae_cx["cold_ms"] / gae_c["cold_ms"])),
+                frac_of_copy_ceiling_cold=gae_cx["cold_ms"] / gae_c["cold_ms"],
+                # torch's own device copy moving the same bytes, and a 1 GiB
+                # copy: what HBM streaming reaches here at this size and at
+                # a size where launch and drain no longer count
+                vendor_copy_same_bytes_cold_ms=cp_c["cold_ms"],
+                frac_of_vendor_copy_cold=cp_c["cold_ms"] / gae_c["cold_ms"],
+                vendor_copy_1gib_each_way=dict(cold_ms=cp_g["cold_ms"], TBps=cp_g["TBps"],
+                                               frac_of_hbm_peak=cp_g["TBps"] * 1e12 / PEAK_HBM))),
     )
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")

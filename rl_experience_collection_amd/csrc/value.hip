@@ -10,9 +10,13 @@
 // computes 1/W of the wide layers' outputs for all of them:
 //   critic 54 -> 512 -> 384 -> 256 -> 128 -> 64 (MFMA, ReLU) -> 1 (VALU),
 //   curiosity [state, one-hot(a)] -> 128 (ReLU) -> 51, MSE against the next
-//   bar's 51 features, bonus = coef * MSE;
-// the two 4-tile layers (128 -> 64, 128 -> 51) give wave q tile q % 4 of
-// the row tiles of its group of four.
+//   bar's 51 features, bonus = coef * MSE.
+// fp32: the two 4-tile layers (128 -> 64, 128 -> 51) give wave q tile q % 4
+// of the row tiles of its group of four, through LDS like the wide layers.
+// bf16: after 256 -> 128 each wave finishes its own row tile alone (critic
+// 128 -> 64 -> 1, both curiosity layers, MSE, reward) from weights staged in
+// LDS once per group, with the curiosity activations kept in registers and
+// no barrier between these layers.
 // Every weight operand a wave loads feeds one MFMA per row tile, and the
 // next layer's first weight steps are loaded before the barriers that end
 // the current layer.  Activations live in LDS (a layer's input is read by
