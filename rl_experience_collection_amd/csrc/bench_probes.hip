@@ -4,21 +4,24 @@
 //
 //  * weight_stream_kernel: the value kernel streams the packed critic and
 //    curiosity weights from L2 into registers once per work item (16 x RT
-//    rows; with more than four waves the two 4-tile layers are read once per
-//    group of four).  This kernel issues the same bytes with no arithmetic:
+//    rows; fp32 reads the two 4-tile layers once per group of four waves,
+//    bf16 stages its tail layers in LDS once per item).  This kernel issues
+//    the same bytes with no arithmetic:
 //    a persistent grid of 256-thread workgroups, two per CU (the value
 //    kernel's 8 waves per CU), each reading the block once per work item in
 //    16-byte lanes (1 KiB per wave instruction), 16 loads in flight per
 //    lane.  Its time for the value kernel's work-item count is the stream
 //    bound the MFMA work competes with.
-//  * lds_activation_kernel: the bf16 value kernel's activation traffic
-//    through LDS alone: per 128-row work item, every B-operand read of every
-//    layer (each of the 8 waves reads all row tiles of a layer's input,
-//    16 bytes per lane per k-step and row tile), every ReLU/pack store of a
-//    layer's output, the scatter of the next item's state operands, and the
-//    same barriers, with the value kernel's block shape and LDS footprint
-//    (one workgroup per CU) and no MFMA or weight loads: the bound the LDS
-//    data path sets on that kernel.
+//  * lds_activation_kernel: the bf16 value kernel's LDS traffic alone: per
+//    128-row work item, every B-operand read of the four wide layers (each
+//    of the 8 waves reads all row tiles of a layer's input, 16 bytes per
+//    lane per k-step and row tile), every ReLU/pack store of their outputs,
+//    the staging of the tail layers' weights, each wave's tail reads of its
+//    own row tile (input, staged weights and biases, state operands), the
+//    scatter of the next item's state operands, and the same barriers, with
+//    the value kernel's block shape and LDS footprint (one workgroup per CU)
+//    and no MFMA or global loads: the bound the LDS data path sets on that
+//    kernel.
 //  * gae_traffic_kernel: moves exactly the GAE scan's bytes (reads r, V, d;
 //    writes two float arrays with streaming stores, as the scan does),
 //    element-wise with no recurrence: the copy ceiling of the scan at a
@@ -78,18 +81,27 @@ __device__ __forceinline__ void lds_read_layer(const uint4* buf, int tile_stride
     }
 }
 
-// OTW output tiles x 8 row tiles of one wave, as packed bf16 pairs
+// OTW output tiles x 8 row tiles of one wave, as packed bf16 pairs, row tile
+// rt at buf + rt * tile_stride
 template <int OTW>
-__device__ __forceinline__ void lds_store_layer(uint4* buf, int q, int lane, const uint4& x) {
+__device__ __forceinline__ void lds_store_layer(uint4* buf, int tile_stride, int q, int lane,
+                                                const uint4& x) {
   uint2* half = reinterpret_cast<uint2*>(buf);
 #pragma unroll
   for (int rt = 0; rt < kLRT; ++rt)
 #pragma unroll
     for (int i = 0; i < OTW; ++i) {
       const int t = q * OTW + i;
-      half[rt * kLTile * 2 + ((t >> 1) * 64 + lane) * 2 + (t & 1)] = make_uint2(x.x + rt, x.y ^ i);
+      half[rt * tile_stride * 2 + ((t >> 1) * 64 + lane) * 2 + (t & 1)] = make_uint2(x.x + rt, x.y ^ i);
     }
 }
+
+// The kernel's tail layout: the third and fourth layers' outputs at 8 and 4
+// k-steps per row tile, the staged tail weights (3 x 1024 16-byte operands)
+// and 80 chunks of biases from 16-byte unit kLTailAt.
+constexpr int kLTS3 = 8 * 64, kLTS4 = 4 * 64, kLTailAt = kLRT * kLTS3, kLTailW = 3 * 1024;
+constexpr int kLTailN = kLTailW + 80;
+constexpr int kLStage = (kLTailN + kLThreads - 1) / kLThreads;
 
 __global__ __launch_bounds__(kLThreads) void lds_activation_kernel(int64_t groups,
                                                                    uint32_t* __restrict__ sink) {
@@ -102,31 +114,63 @@ __global__ __launch_bounds__(kLThreads) void lds_activation_kernel(int64_t group
   for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
     // critic 54 -> 512 (2 k-steps from the state operands, 4 tiles per wave)
     lds_read_layer<2>(s_opnd, kLOp, 0, kLRT, lane, x);
-    lds_store_layer<4>(s_buf, q, lane, x);
+    lds_store_layer<4>(s_buf, kLTile, q, lane, x);
     __syncthreads();
     lds_read_layer<16>(s_buf, kLTile, 0, kLRT, lane, x);  // 512 -> 384
     __syncthreads();
-    lds_store_layer<3>(s_buf, q, lane, x);
+    lds_store_layer<3>(s_buf, kLTile, q, lane, x);
     __syncthreads();
     lds_read_layer<12>(s_buf, kLTile, 0, kLRT, lane, x);  // 384 -> 256
     __syncthreads();
-    lds_store_layer<2>(s_buf, q, lane, x);
+    lds_store_layer<2>(s_buf, kLTS3, q, lane, x);
     __syncthreads();
-    lds_read_layer<8>(s_buf, kLTile, 0, kLRT, lane, x);   // 256 -> 128
+    lds_read_layer<8>(s_buf, kLTS3, 0, kLRT, lane, x);    // 256 -> 128
+    // the tail's weights and biases staged beside the third layer's output
+#pragma unroll
+    for (int i = 0; i < kLStage; ++i) {
+      const int c = i * kLThreads + (int)threadIdx.x;
+      s_buf[kLTailAt + (c < kLTailN ? c : kLTailN - 1)] = make_uint4(x.x, x.y + i, x.z, x.w);
+    }
     __syncthreads();
-    lds_store_layer<1>(s_buf, q, lane, x);
+    lds_store_layer<1>(s_buf, kLTS4, q, lane, x);
     __syncthreads();
-    // 128 -> 64: a wave reads half the row tiles (4 output tiles x 2 halves)
-    lds_read_layer<4>(s_buf, kLTile, (q >> 2) * 4, 4, lane, x);
-    // curiosity 54 -> 128 (state operands, 1 tile per wave)
-    lds_read_layer<2>(s_opnd, kLOp, 0, kLRT, lane, x);
-    __syncthreads();
-    // the next item's state operands: 2 chunks of 16 bytes per thread
-    s_opnd[threadIdx.x] = x;
-    s_opnd[threadIdx.x + kLThreads] = x;
-    lds_store_layer<1>(s_buf, q, lane, x);
-    __syncthreads();
-    lds_read_layer<4>(s_buf, kLTile, (q >> 2) * 4, 4, lane, x);  // 128 -> 51
+    // the tail, wave q on row tile q alone: its 128 -> 64 input (4 k-steps),
+    // the three layers' weights (48 operands of 16 bytes per lane), their
+    // biases and the 64 -> 1 row (20 broadcast reads), its state operands
+    // (2 k-steps), then its share of the next item's state operands
+    lds_read_layer<4>(s_buf, kLTS4, q, 1, lane, x);
+    // (8 and 4 reads in flight, as the kernel's MFMA groups keep them)
+    const uint4* tw = s_buf + kLTailAt;
+#pragma unroll 1
+    for (int o = 0; o < 48; o += 8) {
+      uint4 b[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        b[k] = tw[(o + k) * 64 + lane];
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        x.x ^= b[k].x; x.y += b[k].y; x.z ^= b[k].z; x.w += b[k].w;
+      }
+    }
+    const float4* tb = reinterpret_cast<const float4*>(tw + kLTailW);
+#pragma unroll 1
+    for (int o = 0; o < 20; o += 4) {
+      float4 b[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        b[k] = tb[4 * (o + k) + (lane >> 4)];
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x.x ^= __float_as_uint(b[k].x); x.w += __float_as_uint(b[k].w);
+      }
+    }
+    lds_read_layer<2>(s_opnd, kLOp, q, 1, lane, x);
+    s_opnd[q * kLOp + lane] = x;
+    s_opnd[q * kLOp + 64 + lane] = x;
     __syncthreads();
   }
   if ((x.x ^ x.y ^ x.z ^ x.w) == 0x9E3779B9u) sink[threadIdx.x & 255] = x.x;  // keeps it live
@@ -156,14 +200,13 @@ extern "C" {
 int bench_value_stream_shape(int bf16, long long* block_bytes, int* rows_per_item) {
   if (!block_bytes || !rows_per_item) return 1;
   long long floats = 0;
-  // the 4-tile layers (critic 128 -> 64, curiosity 128 -> 51) are read by
-  // every group of four waves
+  // fp32: the 4-tile layers (critic 128 -> 64, curiosity 128 -> 51) are read
+  // by every group of four waves; bf16 reads every layer once per work item
+  // (its tail layers through the copy staged in LDS)
   const int rh = rl::value_waves(bf16 != 0) / rl::kSplit;
   if (bf16) {
-    for (int l = 0; l < 5; ++l)
-      floats += rl::packed_layer_floats_bf16(rl::kCriticB[l]) * (l == 4 ? rh : 1);
-    for (int l = 0; l < 2; ++l)
-      floats += rl::packed_layer_floats_bf16(rl::kCurB[l]) * (l == 1 ? rh : 1);
+    for (int l = 0; l < 5; ++l) floats += rl::packed_layer_floats_bf16(rl::kCriticB[l]);
+    for (int l = 0; l < 2; ++l) floats += rl::packed_layer_floats_bf16(rl::kCurB[l]);
   } else {
     for (int l = 0; l < 5; ++l)
       floats += rl::packed_layer_floats(rl::kCritic[l]) * (l == 4 ? rh : 1);
@@ -204,12 +247,15 @@ int bench_weight_stream(const void* blob, long long bytes, long long groups, uin
 int bench_lds_activation(long long groups, uint32_t* sink, long long* bytes_per_item,
                          void* stream) {
   if (!sink || groups <= 0 || !bytes_per_item) return (int)hipErrorInvalidValue;
-  // reads: 8 waves x (2 + 16 + 12 + 8 + 2) k-steps x 8 row tiles + 8 x 2 x 4 x 4
-  //        (the two 4-tile layers, half the row tiles each), 1 KiB each;
-  // writes: 8 waves x 8 row tiles x (4 + 3 + 2 + 1 + 1) tiles x 512 bytes,
-  //         plus the state operands (16 KiB)
-  const long long reads = (8LL * 40 * 8 + 8LL * 2 * 4 * 4) * 1024;
-  const long long writes = 8LL * 8 * 11 * 512 + kLRT * kLOp * 16;
+  // reads: 8 waves x (2 + 16 + 12 + 8) k-steps x 8 row tiles, then per wave
+  //        4 + 48 + 2 operands of its own row tile, 1 KiB each, and 20
+  //        broadcast bias reads of 64 distinct bytes;
+  // writes: 8 waves x 8 row tiles x (4 + 3 + 2 + 1) tiles x 512 bytes, the
+  //         staged tail (kLStage rounds of 16 bytes per thread) and the
+  //         state operands (16 KiB)
+  const long long reads = (8LL * 38 * 8 + 8LL * 54) * 1024 + 8LL * 20 * 64;
+  const long long writes = 8LL * 8 * 10 * 512 + (long long)kLStage * kLThreads * 16 +
+                           kLRT * kLOp * 16;
   *bytes_per_item = reads + writes;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
