@@ -1,5 +1,5 @@
 // Measurement kernels for the benchmark (not part of the collection path):
-// the ceilings two of the collection's kernels are judged against on the
+// the ceilings two of the collection's kernels are measured against on the
 // machine at hand.
 //
 //  * weight_stream_kernel: the value kernel streams the packed critic and

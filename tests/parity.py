@@ -1,7 +1,7 @@
 """The comparison protocol of the GPU parity tests (test infrastructure): run
 the HIP path and the oracle on the same seeded inputs and compare them.
 
-PPO collection, fp32 (the benchmark spec tolerances):
+PPO collection, fp32 (the stated tolerances):
 * integer outputs (actions, dones, barrier codes) bit-exact;
 * fp32 outputs within |g - o| <= 1e-5 + 1e-4 |o|;
 * at the first action mismatch of an episode, the oracle's distance from u to
@@ -30,9 +30,9 @@ priority as |td|^alpha of the GPU's own td; at the first action mismatch a
 greedy step whose oracle gap between its two largest Q values is below
 1e-5 (1 + max |Q|) is a near tie and the episode is re-run teacher-forced.
 
-Every comparison can append what it saw (near-tie flags, near-boundary draws,
-outlier counts, agreement) to a JSON-lines record: PARITY_RECORD, or
-gpurun_out/parity_record.jsonl under the repository root.
+Every comparison appends what it saw (near-tie flags, near-boundary draws,
+outlier counts, agreement) to a JSON-lines record at the path in the
+environment variable PARITY_RECORD, when it is set.
 """
 from __future__ import annotations
 
@@ -57,13 +57,13 @@ DQN_INT_KEYS = ("actions", "explored", "dones", "barrier")
 DQN_FLOAT_KEYS = ("states", "next_states", "q_values", "q_taken", "q_next_max", "rewards")
 DQN_TIE = 1e-5
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-
 
 def record(name: str, **data):
-    """Append one JSON line describing a comparison to the parity record."""
-    path = os.environ.get("PARITY_RECORD") or os.path.join(ROOT, "gpurun_out",
-                                                            "parity_record.jsonl")
+    """Append one JSON line describing a comparison to the parity record
+    (the file PARITY_RECORD names; nothing when it is unset)."""
+    path = os.environ.get("PARITY_RECORD")
+    if not path:
+        return
     try:
         os.makedirs(os.path.dirname(path), exist_ok=True)
         with open(path, "a") as f:
