@@ -22,10 +22,10 @@
 //
 // The layers use the MFMA layout (lane l computes rows l % 16).  The draw
 // and the environment use another: wave q owns episodes 4q .. 4q+3 of the
-// row group, one 16-lane row each; lane j of a row holds logits j, j + 16
-// and j + 32 (read from LDS), so the softmax sums and the CDF are DPP
-// reductions and scans within the row, and every lane of the row holds the
-// episode's portfolio state.  Each wave writes its own episodes' state
+// row group, one 16-lane row each; lane j of a row holds logits 3j .. 3j+2
+// (read from LDS), so the softmax sum and the CDF are one DPP reduction and
+// one scan within the row, and every lane of the row holds the episode's
+// portfolio state.  Each wave writes its own episodes' state
 // operands, state rows and outputs.
 #include "collect.hpp"
 #include "rows.hpp"
@@ -453,14 +453,17 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     PreStepper<BF16, kS1, kTail, !TABLE> ps(w1, sbuf, lane);
 
     // ---- step 4: softmax, CDF, inverse-CDF draw, log-prob -----------------
-    // lane j of the episode's row holds logits k = j + 16 h, h = 0..2
+    // lane j of the episode's row holds logits k = 3j + h, h = 0..2 (lane 15
+    // none), so the CDF is one scan over the row of the lanes' sums plus
+    // each lane's own prefix of its three
     const float* lg = reinterpret_cast<const float*>(bufA);
     float l[3], ex[3];
     bool ok[3];
 #pragma unroll
     for (int h = 0; h < 3; ++h) {
-      ok[h] = j + 16 * h < kActions;
-      l[h] = lg[(h * 64 + e + 16 * (j >> 2)) * 4 + (j & 3)];
+      const int k = 3 * j + h;  // (< 48: inside the four logit tiles)
+      ok[h] = k < kActions;
+      l[h] = lg[((k >> 4) * 64 + e + 16 * ((k & 15) >> 2)) * 4 + (k & 3)];
     }
     ps.template step<0>(pre);
     int bad = 0;
@@ -476,38 +479,34 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
 #pragma unroll
     for (int h = 0; h < 3; ++h) ex[h] = ok[h] ? expf(l[h] - m) : 0.0f;
     ps.template step<2>(pre);
-    // CDF_k = (totals of the earlier blocks h) + (prefix within block h)
-    float T[3], run[3];
-#pragma unroll
-    for (int h = 0; h < 3; ++h) {
-      T[h] = row_sum(ex[h]);
-      run[h] = row_scan(ex[h]);
-    }
-    run[1] = T[0] + run[1];
+    // CDF_k = (sum of the lanes before j) + (this lane's prefix up to k)
+    float pre3[3];
+    pre3[0] = ex[0];
+    pre3[1] = ex[0] + ex[1];
+    pre3[2] = pre3[1] + ex[2];
+    const float S = row_sum(pre3[2]);
+    const float before = dpp_f<0x111>(row_scan(pre3[2]));  // row_shr:1 (lane 0 reads 0)
     ps.template step<3>(pre);
-
-    run[2] = (T[0] + T[1]) + run[2];
-    const float S = (T[0] + T[1]) + T[2];
     // first k with u < CDF_k, as u * S < (sum of e up to k)
     const float uS = u * S;
     int cand = 64;
 #pragma unroll
     for (int h = 2; h >= 0; --h)
-      if (ok[h] && uS < run[h]) cand = j + 16 * h;
+      if (ok[h] && uS < before + pre3[h]) cand = 3 * j + h;
     int act_a = row_min_i(cand);
     ps.template step<4>(pre);
     if (act_a == 64) {  // rounding left u >= CDF_44: last action with weight
       int lastk = -1;
 #pragma unroll
       for (int h = 0; h < 3; ++h)
-        if (ok[h] && ex[h] > 0.0f) lastk = j + 16 * h;
+        if (ok[h] && ex[h] > 0.0f) lastk = 3 * j + h;
       lastk = row_max_i(lastk);
       act_a = lastk >= 0 ? lastk : kActions - 1;
     }
     float la = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 3; ++h)
-      if (j + 16 * h == act_a) la = l[h];
+      if (3 * j + h == act_a) la = l[h];
     la = row_max(la);
     const float logp = (la - m) - logf(S);
     ps.template step<5>(pre);
@@ -593,10 +592,10 @@ __global__ __launch_bounds__(64 * kSplit) void actor_rollout_kernel(RolloutArgs 
     n_bad += (bad && valid && j == 0) ? 1u : 0u;
     if (a.logits) {
       float* lrow = a.logits + o * kActions;
-      lrow[j] = l[0];
-      lrow[j + 16] = l[1];
-      // lanes past logit 44 repeat their logit j + 16
-      lrow[ok[2] ? j + 32 : j + 16] = ok[2] ? l[2] : l[1];
+      // lane 15 holds no logit: it repeats logit 44 (lane 14's third)
+      const float l44 = dpp_f<0x111>(l[2]);
+#pragma unroll
+      for (int h = 0; h < 3; ++h) lrow[ok[h] ? 3 * j + h : kActions - 1] = ok[h] ? l[h] : l44;
     }
 
     // ---- step 12: reset on done; the bar pointer keeps advancing ------------
