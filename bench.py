@@ -639,7 +639,7 @@ def main():
                          "and fp32, one JSON line each, instead of the benchmark line")
     ap.add_argument("--actor-stamps", action="store_true",
                     help="per-phase cycles of the sequential step (instrumented kernel) at "
-                         "N=128 L=500 fp32 and bf16 and N=8192 L=500 fp32, one JSON line each, "
+                         "N=128 L=500 and N=8192 L=500, fp32 and bf16, one JSON line each, "
                          "instead of the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -661,7 +661,8 @@ def main():
             print(json.dumps(r), flush=True)
         return
     if args.actor_stamps:
-        for name, prec in (("ppo_n128_l500", 0), ("ppo_n128_l500", 1), ("ppo_n8192_l500", 0)):
+        for name, prec in (("ppo_n128_l500", 0), ("ppo_n128_l500", 1), ("ppo_n8192_l500", 0),
+                           ("ppo_n8192_l500", 1)):
             r = actor_phase_stamps(synthdata.ppo_inputs(name), max(3, min(args.steps, 10)), prec)
             print(json.dumps(dict(workload=name, **r)), flush=True)
         return
