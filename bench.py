@@ -499,6 +499,30 @@ def _host_cpu():
     return "unknown"
 
 
+def device_info():
+    """The GPU the figures come from: name, architecture, compute units (from
+    torch) and the engine clock limit rocminfo reports (None if unavailable):
+    the published peaks assume 256 CUs at 2.4 GHz."""
+    import subprocess
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    info = dict(name=p.name, arch=getattr(p, "gcnArchName", None), cus=p.multi_processor_count,
+                max_clock_MHz=None)
+    try:
+        r = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30)
+        gpu = False
+        for line in r.stdout.splitlines():
+            t = line.strip()
+            if t.startswith("Device Type:"):
+                gpu = t.endswith("GPU")
+            elif gpu and t.startswith("Max Clock Freq. (MHz):"):
+                info["max_clock_MHz"] = int(t.split(":", 1)[1].split()[0])
+                break
+    except Exception:
+        pass
+    return info
+
+
 def _threads():
     return int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
 
@@ -753,6 +777,7 @@ def main():
         mlp_mfma_util=mlp_util,
         gae_in_collect_GBps=gae_in / 1e9,
         nonfinite_events=big["nonfinite"],
+        device=device_info(),
         also=dict(
             ppo_collect_n8192_l500_bf16=dict(
                 value=N * L * args.steps / bfr["wall_s"], unit="experiences/s",
