@@ -428,11 +428,17 @@ void value_kernel(ValueArgs a) {
     prefetch_next();
     // the row's action (clamped for the gather) and the MSE targets: the
     // next bar's features at this lane's outputs 16 i + 4 g + r of the
-    // curiosity head, one 16-byte load each (rows are 204 bytes, so 4-byte
-    // aligned; the row's last four where the four run past it, 48 .. 50
-    // then moved down one; outputs past the row are zero)
+    // curiosity head, one 16-byte load each (rows start 4-byte aligned; the
+    // row's last four where the four run past it, 48 .. 50 then moved down
+    // one; outputs past the row are zero).  Without recycling the next bar's
+    // features are also the first 51 elements of the episode's next state,
+    // N rows on, which this launch holds for every step but its last: read
+    // there, a group's targets are one contiguous run of state rows (read
+    // again as states a little later) instead of a scattered feature row each.
     const int act = my_act[0] < 0 ? 0 : (my_act[0] >= kActions ? kActions - 1 : my_act[0]);
-    const float* fn = a.features + (int64_t)(my_nbar[0] + 1) * kFeatures;
+    const int64_t nrow = my_raw[0] + a.N;
+    const float* fn = !a.bars && nrow < rows ? a.states + nrow * kState
+                                             : a.features + (int64_t)(my_nbar[0] + 1) * kFeatures;
     f32x4 feat[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -566,16 +572,21 @@ void value_kernel(ValueArgs a) {
   lds_barrier();
   // next-bar features of this wave's row tiles for the curiosity MSE: lane
   // holds features j0 .. j0 + 3, j0 = 16 q4 + 4g, one 16-byte load per row
-  // (rows are 204 bytes, so 4-byte aligned) with no branch around it: the
-  // row's last four where j0 + 3 lies past it (48 .. 50 are then moved down
-  // one; lanes past the row keep zeros).
+  // (rows start 4-byte aligned) with no branch around it: the row's last
+  // four where j0 + 3 lies past it (48 .. 50 are then moved down one; lanes
+  // past the row keep zeros).  Without recycling they are read from the
+  // episode's next state row, N rows on, for every step but the launch's
+  // last (as in the bf16 tail).
   f32x4 feat[RTS];
   const int j0 = 16 * q4 + 4 * g;
   const int jl = j0 + 3 < kFeatures ? j0 : kFeatures - 4;
 #pragma unroll
   for (int rt = 0; rt < RTS; ++rt) {
+    const int64_t nrow = row0 + (rs0 + rt) * kRowsPerWave + (lane & 15) + a.N;
     const float* fn =
-        a.features + (int64_t)s_nbar[(rs0 + rt) * kRowsPerWave + (lane & 15)] * kFeatures;
+        !a.bars && nrow < rows
+            ? a.states + nrow * kState
+            : a.features + (int64_t)s_nbar[(rs0 + rt) * kRowsPerWave + (lane & 15)] * kFeatures;
     const f32x4 v = *reinterpret_cast<const f32x4_a4*>(fn + jl);
     const bool shift = jl != j0;
 #pragma unroll
