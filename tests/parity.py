@@ -20,7 +20,12 @@ the GPU's actions teacher-forced):
   a bf16 rounding boundary may round the other way on one side); elements
   beyond it are outliers, held to a fixed budget per output (at most
   max(2, 1e-3 of the elements)) and to a hard cap of 2e-2 max(|o|, rms(o))
-  each.
+  each;
+* advantages are returns minus values (A = R - V, exact in fp32 up to one
+  rounding), so an advantage's error is at most its return's plus its
+  value's: its tolerance and cap are the sums of theirs at the same element
+  (where |V| is much larger than |A|, a value's bf16 error within its own
+  tolerance is a large fraction of the advantage).
 
 DQN collection: integers (actions, explore flags, dones, barrier codes)
 bit-exact; states, next states, Q values, Q(s,a), max Q_target and rewards
@@ -242,18 +247,26 @@ def compare_bf16(inputs: dict, gpu: dict, forced: dict, cols, floors: dict):
     g, o = gpu["states"][:, c], forced["states"][:, c]
     if not close_mask(g, o).all():
         fails.append("bf16: states outside the fp32 tolerance")
+    def tol_cap(k):
+        o = forced[ORACLE_NAME.get(k, k)][:, c].astype(np.float64)
+        if k == "advantages":  # A = R - V: the sums of the return's and the value's
+            tr, cr = tol_cap("returns")
+            tv, cv = tol_cap("values")
+            return tr + tv, cr + cv
+        rms = float(np.sqrt((o * o).mean())) if o.size else 0.0
+        return (floors[k] + BF16_RTOL * np.abs(o),
+                BF16_RTOL * np.maximum(np.abs(o), rms) + floors[k])
+
     for k in ("logits", "log_probs", "values", "rewards", "advantages", "returns"):
         if gpu.get(k) is None:
             continue
         g = gpu[k][:, c].astype(np.float64)
         o = forced[ORACLE_NAME.get(k, k)][:, c].astype(np.float64)
         err = np.abs(g - o)
-        tol = floors[k] + BF16_RTOL * np.abs(o)
+        tol, cap = tol_cap(k)
         out = err > tol
         nout = int(out.sum())
         budget = max(BF16_BUDGET_MIN, int(np.ceil(BF16_BUDGET_FRAC * err.size)))
-        rms = float(np.sqrt((o * o).mean())) if o.size else 0.0
-        cap = BF16_RTOL * np.maximum(np.abs(o), rms) + floors[k]
         over_cap = float((err / cap).max()) if err.size else 0.0
         stats[k] = dict(n=int(err.size), outliers=nout, budget=budget,
                         worst_excess=float((err - tol).max()) if err.size else 0.0,
@@ -263,7 +276,7 @@ def compare_bf16(inputs: dict, gpu: dict, forced: dict, cols, floors: dict):
                          f"(budget {budget})")
         if over_cap > 1.0:
             fails.append(f"bf16: {k}: an error reaches {over_cap:.3g} x the cap "
-                         f"2e-2 max(|o|, rms)")
+                         f"2e-2 max(|o|, rms) + floor")
     return fails, stats
 
 

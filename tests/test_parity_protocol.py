@@ -146,6 +146,32 @@ def test_bf16_hard_cap(bf16_run):
     assert any("cap" in f for f in fails)
 
 
+def test_bf16_advantage_takes_return_and_value_tolerance(bf16_run):
+    """An advantage is its return minus its value, so its error may reach
+    the return's and the value's tolerances together: at the element where
+    the value is largest against the advantage such an error passes (though
+    it is beyond 2e-2 |A| plus the advantages' own floor), and budget + 1
+    errors of 1.5 times that tolerance fail."""
+    inp, gpu0, forced, cols, fl = bf16_run
+    A = forced["adv"].astype(np.float64).ravel()
+    R = forced["ret"].astype(np.float64).ravel()
+    V = forced["values"].astype(np.float64).ravel()
+    tol = (fl["returns"] + BF16_RTOL * np.abs(R)) + (fl["values"] + BF16_RTOL * np.abs(V))
+    order = np.argsort(-(np.abs(V) / (np.abs(A) + 1e-6)))
+    budget = max(2, int(np.ceil(1e-3 * A.size)))
+    gpu = copy.deepcopy(gpu0)
+    a = gpu["advantages"].reshape(-1)
+    i = order[0]
+    a[i] = np.float32(A[i] + 0.9 * tol[i])
+    assert 0.9 * tol[i] > fl["advantages"] + BF16_RTOL * abs(A[i])
+    fails, st = compare_bf16(inp, gpu, forced, cols, fl)
+    assert fails == [] and st["advantages"]["outliers"] == 0
+    for j in order[: budget + 1]:
+        a[j] = np.float32(A[j] + 1.5 * tol[j])
+    fails, _ = compare_bf16(inp, gpu, forced, cols, fl)
+    assert any("advantages" in f and "budget" in f for f in fails)
+
+
 def test_bf16_integer_and_state_mismatch(bf16_run):
     inp, gpu0, forced, cols, fl = bf16_run
     gpu = copy.deepcopy(gpu0)
