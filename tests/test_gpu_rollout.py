@@ -415,3 +415,40 @@ def test_feature_table_gives_the_same_collection(monkeypatch, precision, recycle
             if v is not None:
                 assert torch.equal(v, outs[1][k]), (N, k)
         assert int(outs[0]["dones"].sum()) > 0
+
+
+# ---------------------------------------------------- sizes and modes mixed
+def _mixed_cases(seed, count):
+    """Deterministic mixes of the sizes that cut tiles, work items and
+    launch parts unevenly, precisions, recycling, the split rollout forced
+    on or off or left to the default, and markets from the minimum
+    n_bars = L + 1 up."""
+    import random
+    rng = random.Random(seed)
+    for _ in range(count):
+        N = rng.choice([1, 2, 15, 16, 17, 31, 33, 64, 100, 127, 129, 200, 257])
+        L = rng.choice([1, 2, 3, 15, 16, 17, 63, 64, 65, 100, 130, 199])
+        yield (N, L, rng.choice([0, 1]), rng.choice([0, 1]), rng.choice([-1, 0, 1]),
+               rng.choice([L + 1, L + 5, 3000]), rng.randrange(1, 10**6))
+
+
+@pytest.mark.parametrize("N,L,precision,recycle,overlap,n_bars,seed", list(_mixed_cases(7, 24)))
+def test_mixed_sizes_and_modes(N, L, precision, recycle, overlap, n_bars, seed):
+    """Each case against the oracle by its precision's protocol; a case with
+    the rollout split (overlap 1) also equals the single launch bit for bit."""
+    inp = synthdata.ppo_inputs(dict(N=N, L=L, n_bars=n_bars, seed=seed), bias_scale=0.1)
+    inp["settings"] = dict(inp["settings"], recycle=recycle, overlap=overlap)
+    gpu = run_gpu(inp, settings=inp["settings"], precision=precision)
+    if overlap == 1:
+        one = run_gpu(inp, settings=dict(inp["settings"], overlap=0), precision=precision)
+        for k, v in one.items():
+            if v is not None:
+                assert v.tobytes() == gpu[k].tobytes(), k
+    if precision == 0:
+        _assert_parity(inp, gpu, oracle.rollout(inp), name=f"mixed_n{N}_l{L}")
+    else:
+        forced = oracle.rollout(inp, precision=oracle.BF16, forced_actions=gpu["actions"])
+        cols = list(range(N))
+        fails, stats = compare_bf16(inp, gpu, forced, cols, bf16_floors(inp, forced, cols))
+        record(f"mixed_bf16_n{N}_l{L}", N=N, L=L, episodes=N, outputs=stats, failures=fails)
+        assert not fails, "\n".join(fails)
