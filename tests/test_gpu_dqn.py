@@ -192,3 +192,24 @@ def test_dqn_recycle_full_size_sampled_episodes():
     sub = sorted(set(list(range(0, 16384, 2039)) + [16383, 17]))
     orc = oracle.dqn_rollout(inp, subset=sub, with_q=False)
     assert_parity(inp, gpu, orc, episodes=sub)
+
+
+def _mixed_cases(seed, count):
+    """Deterministic mixes of sizes that cut the 16-episode workgroups
+    unevenly, epsilon from all greedy to all random, recycling, and markets
+    from the minimum n_bars = L + 1 up."""
+    import random
+    rng = random.Random(seed)
+    for _ in range(count):
+        N = rng.choice([1, 2, 15, 16, 17, 31, 33, 64, 100, 129])
+        L = rng.choice([1, 2, 3, 16, 17, 63, 100])
+        yield (N, L, rng.choice([0.0, 0.1, 0.5, 1.0]), rng.choice([0, 1]),
+               rng.choice([L + 1, L + 5, 4000]), rng.randrange(1, 10**6))
+
+
+@pytest.mark.parametrize("N,L,epsilon,recycle,n_bars,seed", list(_mixed_cases(5, 16)))
+def test_dqn_mixed_sizes_and_modes(N, L, epsilon, recycle, n_bars, seed):
+    inp = synthdata.dqn_inputs(dict(N=N, L=L, n_bars=n_bars, seed=seed), bias_scale=0.1,
+                               epsilon=epsilon)
+    inp["settings"] = dict(inp["settings"], recycle=recycle)
+    assert_parity(inp, run_gpu(inp), oracle.dqn_rollout(inp), name=f"dqn_mixed_n{N}_l{L}")
